@@ -1,0 +1,26 @@
+"""CPU oracle for the LatentMoE MXFP4 (w4a16) routed-expert layer.
+
+TEST INFRASTRUCTURE ONLY. This package is the plain, slow, float64 statement
+of what the layer computes. It is imported by the test suite, by the graft
+smoke check and by the bench's CPU-baseline leg, and by nothing else: the
+product path (the HIP library and its Python binding) never imports, links or
+calls it, and it shares no code with that path. Inputs come from the seeded
+generators in the separate `workloads` package.
+"""
+from .lmoe_oracle import (  # noqa: F401
+    E2M1_MAGNITUDES,
+    e2m1_table,
+    e8m0_scale,
+    dequant_mxfp4,
+    bf16_from_f64,
+    f64_from_bf16,
+    f32_round,
+    router_logits,
+    topk_select,
+    softmax_selected,
+    permute_routes,
+    glu_ffn,
+    combine,
+    forward,
+    forward_tokens,
+)

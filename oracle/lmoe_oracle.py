@@ -1,0 +1,315 @@
+"""Float64 CPU oracle of the LatentMoE MXFP4 (w4a16) routed-expert layer.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): nothing on the product
+path imports this module.
+
+What the layer computes, step by step, and where the pages state it:
+
+  dequant   MXFP4 weights: E2M1 4-bit codes, one E8M0 power-of-two exponent
+            per 32 consecutive values along the input dimension, bias 127
+            (infervisor.ai "Bringing up Kimi-K3 on day zero", section "The
+            model we hadn't run"; huggingface.co "Notes from an NVFP4 port of
+            Kimi K3.1 Pro", introduction, which also states that the E2M1 grid
+            is the one NVFP4 uses and that the exponent runs along columns).
+  logits    router scores of each token over the 896 experts (dev48.org "Kimi
+            K3 on AMD Instinct GPUs with TokenSpeed", section 4.3, router
+            scores as one projection of the MoE input). Here the router reads
+            the latent activations, as the workloads specify.
+  top-k     16 of 896 experts per token (Bringing up Kimi-K3, "The model we
+            hadn't run"; TokenSpeed section 4). Equal logits are broken toward
+            the lower expert index, and the selected list is ordered by
+            descending logit then ascending index. The block-oracle remark in
+            Bringing up Kimi-K3, "Correctness before latency", is why only the
+            selected set matters for the combine.
+  weights   softmax over the selected logits (the workloads' gating rule; the
+            pages do not state K3's router nonlinearity).
+  permute   routes grouped by expert, stable in route order: counts, exclusive
+            offsets, perm (position -> route), inverse (TokenSpeed section 4.1,
+            sorting routes by expert so one weight panel serves several).
+  experts   per route, a GLU FFN in the latent: g = x Gq^T, u = x Uq^T,
+            h = bf16(silu(g) * u), y = h Dq^T (TokenSpeed section 4; the
+            activation word printed on the pages is garbled, SiLU is used as the
+            workloads state). Route partials stay in high precision (TokenSpeed
+            section 4.3 sums route partials in FP32; here float64).
+  shared    the same GLU with bf16 weights for each always-on shared expert,
+            weight 1 (Bringing up Kimi-K3, "The model we hadn't run").
+  combine   out[t] = bf16(sum_j w[t,j] y[t,j] + sum_s ysh[s,t]) in that order
+            (TokenSpeed section 4.3, fused combine of the selected experts).
+
+Readings where the pages are silent: element 2m of a row is the low nibble of
+byte m; E8M0 byte 255 is NaN; NaN logits rank below -inf, equal NaNs by index;
+-0 and +0 compare equal; h and out are rounded to bf16 nearest-even.
+
+Every product x*w is exact in float64 (bf16 times a 2-significant-bit E2M1
+value times a power of two), so the only deviation from exact arithmetic is
+float64 summation and the stated bf16/fp32 roundings.
+"""
+from __future__ import annotations
+
+from typing import Callable, Dict, Mapping, Optional, Sequence
+
+import numpy as np
+
+# Magnitudes of the E2M1 grid for codes 0..7; bit 3 of a code is the sign.
+E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+E8M0_BIAS = 127
+
+
+# ----------------------------------------------------------------------------
+# Number formats
+# ----------------------------------------------------------------------------
+
+def e2m1_table() -> np.ndarray:
+    """Value of each of the 16 E2M1 codes (float64), code 8 is -0.0."""
+    t = np.empty(16, np.float64)
+    for c in range(16):
+        mag = E2M1_MAGNITUDES[c & 7]
+        t[c] = -mag if (c >> 3) & 1 else mag
+    return t
+
+
+def e8m0_scale(b) -> np.ndarray:
+    """2**(b - 127) for E8M0 byte b; 255 encodes NaN."""
+    b = np.asarray(b, dtype=np.int64)
+    s = np.ldexp(np.ones(b.shape, np.float64), b - E8M0_BIAS)
+    return np.where(b == 255, np.nan, s)
+
+
+def dequant_mxfp4(q: np.ndarray, s: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Values of an [N][K] MXFP4 matrix, float64.
+
+    q: uint8 [N][K/2], element k of row n in byte k//2, low nibble for even k.
+    s: uint8 [N][K/32], exponent of elements 32j .. 32j+31 of row n.
+    """
+    q = np.asarray(q, np.uint8).reshape(N, K // 2)
+    s = np.asarray(s, np.uint8).reshape(N, K // 32)
+    codes = np.empty((N, K), np.uint8)
+    codes[:, 0::2] = q & 0x0F
+    codes[:, 1::2] = q >> 4
+    vals = e2m1_table()[codes]
+    scale = e8m0_scale(s)                          # [N][K/32]
+    return vals * np.repeat(scale, 32, axis=1)
+
+
+def f64_from_bf16(bits: np.ndarray) -> np.ndarray:
+    b = np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def bf16_from_f64(v: np.ndarray) -> np.ndarray:
+    """Round float64 to bf16 (nearest, ties to even) and return the bit pattern.
+
+    Full range: overflow to +-inf, bf16 subnormals, signed zeros, NaN.
+    """
+    v = np.asarray(v, np.float64)
+    out = np.empty(v.shape, np.uint16)
+    sign = np.where(np.signbit(v), 0x8000, 0).astype(np.uint16)
+    a = np.abs(v)
+    nan = np.isnan(v)
+    inf = np.isinf(a)
+    fin = ~(nan | inf)
+    bits = np.zeros(v.shape, np.int64)
+    with np.errstate(invalid="ignore", over="ignore"):
+        # normal range: 8 significant bits
+        m, e = np.frexp(np.where(fin, a, 1.0))        # a = m 2^e, m in [0.5, 1)
+        q = np.rint(m * 256.0).astype(np.int64)       # 128..256, ties to even
+        carry = q == 256
+        q = np.where(carry, 128, q)
+        e = np.where(carry, e + 1, e)
+        biased = e + 126                              # bf16 exponent field
+        normal_bits = (biased << 7) | (q - 128)
+        # subnormal range: multiples of 2^-133
+        sub_q = np.rint(np.ldexp(np.where(fin, a, 0.0), 133)).astype(np.int64)
+        is_sub = a < 2.0 ** -126
+        bits = np.where(is_sub, sub_q, normal_bits)
+        bits = np.where(~is_sub & (biased >= 255), 0x7F80, bits)
+    bits = np.where(inf, 0x7F80, bits)
+    out[...] = (bits.astype(np.uint16) | sign)
+    out[nan] = 0x7FC0
+    return out
+
+
+def f32_round(v: np.ndarray) -> np.ndarray:
+    """float64 -> float32, nearest-even (IEEE conversion)."""
+    return np.asarray(v, np.float64).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Routing
+# ----------------------------------------------------------------------------
+
+def router_logits(x_bits: np.ndarray, router_bits: np.ndarray) -> np.ndarray:
+    """logits[t,e] = fp32(sum_l x[t,l] W[l,e]), float64 sum. W is [L][E]."""
+    x = f64_from_bf16(x_bits)
+    wr = f64_from_bf16(router_bits)
+    return f32_round(x @ wr)
+
+
+def topk_select(logits: np.ndarray, k: int) -> np.ndarray:
+    """First k experts of each row under the total order
+    a before b  <=>  l_a > l_b  or  (l_a == l_b and a < b),
+    compared as IEEE values (-0 == +0), NaN after every number.
+    Returns int32 [T][k] listed in that order."""
+    lg = np.asarray(logits, np.float32).astype(np.float64)
+    T, E = lg.shape
+    isnan = np.isnan(lg)
+    val = np.where(isnan, 0.0, lg)
+    val = np.where(val == 0.0, 0.0, val)     # -0 and +0 are the same key
+    out = np.empty((T, k), np.int32)
+    expert = np.arange(E)
+    for t in range(T):
+        order = np.lexsort((expert, -val[t], isnan[t]))
+        out[t] = order[:k]
+    return out
+
+
+def softmax_selected(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """w[t,j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the selected experts
+    (l_0 the first, largest), in float64, stored as float32."""
+    lg = np.asarray(logits, np.float32).astype(np.float64)
+    sel = np.take_along_axis(lg, np.asarray(idx, np.int64), axis=1)
+    z = np.exp(sel - sel[:, :1])
+    return f32_round(z / z.sum(axis=1, keepdims=True))
+
+
+def permute_routes(idx: np.ndarray, E: int):
+    """Group routes r = t*k + j by expert, stable in r.
+
+    Returns counts [E], offsets [E+1] (exclusive prefix sums), perm [T*k]
+    (perm[pos] = r) and inv [T*k] (inv[r] = pos), all int32.
+    Written as an explicit counting sort.
+    """
+    flat = np.asarray(idx, np.int64).ravel()
+    R = flat.size
+    counts = np.zeros(E, np.int64)
+    for r in range(R):
+        counts[flat[r]] += 1
+    offsets = np.zeros(E + 1, np.int64)
+    run = 0
+    for e in range(E):
+        offsets[e] = run
+        run += counts[e]
+    offsets[E] = run
+    cursor = offsets[:E].copy()
+    perm = np.empty(R, np.int64)
+    inv = np.empty(R, np.int64)
+    for r in range(R):
+        e = flat[r]
+        pos = cursor[e]
+        cursor[e] += 1
+        perm[pos] = r
+        inv[r] = pos
+    return (counts.astype(np.int32), offsets.astype(np.int32),
+            perm.astype(np.int32), inv.astype(np.int32))
+
+
+# ----------------------------------------------------------------------------
+# Experts
+# ----------------------------------------------------------------------------
+
+def silu(z: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def glu_ffn(xs: np.ndarray, gate: np.ndarray, up: np.ndarray, down: np.ndarray):
+    """One expert on the rows xs [m][L] (float64 values).
+
+    gate, up: [I][L]; down: [L][I] (float64 values).
+    Returns (h_bits uint16 [m][I], y float64 [m][L]) with
+    h = bf16(silu(xs gate^T) * (xs up^T)) and y = h down^T.
+    """
+    g = xs @ gate.T
+    u = xs @ up.T
+    h_bits = bf16_from_f64(silu(g) * u)
+    y = f64_from_bf16(h_bits) @ down.T
+    return h_bits, y
+
+
+def combine(y_routed: np.ndarray, w: np.ndarray, y_shared: Optional[np.ndarray]):
+    """out[t] = sum_j w[t,j] y_routed[t,j] + sum_s y_shared[s,t], in that order.
+
+    y_routed: [T][k][L] float64; w: [T][k] float32; y_shared: [S][T][L] or None.
+    Returns (out float64 [T][L], out bf16 bits [T][L]).
+    """
+    T, k, L = y_routed.shape
+    acc = np.zeros((T, L), np.float64)
+    w64 = np.asarray(w, np.float32).astype(np.float64)
+    for j in range(k):
+        acc = acc + w64[:, j:j + 1] * y_routed[:, j, :]
+    if y_shared is not None:
+        for s in range(y_shared.shape[0]):
+            acc = acc + y_shared[s]
+    return acc, bf16_from_f64(acc)
+
+
+def _expert_values(ex: Mapping[str, np.ndarray], L: int, I: int):
+    gate = dequant_mxfp4(ex["gate_q"], ex["gate_s"], I, L)
+    up = dequant_mxfp4(ex["up_q"], ex["up_s"], I, L)
+    down = dequant_mxfp4(ex["down_q"], ex["down_s"], L, I)
+    return gate, up, down
+
+
+def _shared_outputs(x64: np.ndarray, shared: Mapping[str, np.ndarray]):
+    sg, su, sd = shared["sh_gate"], shared["sh_up"], shared["sh_down"]
+    S = sg.shape[0]
+    ys = []
+    for s in range(S):
+        _, y = glu_ffn(x64, f64_from_bf16(sg[s]), f64_from_bf16(su[s]), f64_from_bf16(sd[s]))
+        ys.append(y)
+    if not ys:
+        return None
+    return np.stack(ys, axis=0)
+
+
+def forward_tokens(x_bits: np.ndarray, idx: np.ndarray, w: np.ndarray,
+                   get_expert: Callable[[int], Mapping[str, np.ndarray]],
+                   shared: Mapping[str, np.ndarray], L: int, I: int,
+                   tokens: Optional[Sequence[int]] = None):
+    """Routed + shared FFN and combine for the listed tokens (all by default),
+    given their routing (idx [T][k], w [T][k]).
+
+    get_expert(e) returns expert e's codes and scales (the generator's layout).
+    Experts are visited once each, serving every listed route that selects
+    them. Returns (out float64 [n][L], out bf16 bits [n][L]).
+    """
+    T, k = idx.shape
+    toks = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    n = toks.size
+    x64 = f64_from_bf16(np.asarray(x_bits)[toks])
+    sel = np.asarray(idx)[toks]
+    y_routed = np.zeros((n, k, L), np.float64)
+    for e in np.unique(sel):
+        rows, slots = np.nonzero(sel == e)
+        gate, up, down = _expert_values(get_expert(int(e)), L, I)
+        _, y = glu_ffn(x64[rows], gate, up, down)
+        y_routed[rows, slots] = y
+    y_sh = _shared_outputs(x64, shared)
+    return combine(y_routed, np.asarray(w)[toks], y_sh)
+
+
+def forward(x_bits: np.ndarray, router_bits: Optional[np.ndarray],
+            experts: Mapping[str, np.ndarray], shared: Mapping[str, np.ndarray],
+            k: int, logits: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """The whole layer on every token.
+
+    experts holds stacked [E][...] codes and scales; logits, when given, replace
+    the router step. Returns every intermediate the layer exposes.
+    """
+    T, L = np.asarray(x_bits).shape
+    E, I = experts["gate_q"].shape[0], experts["gate_q"].shape[1]
+    if logits is None:
+        logits = router_logits(x_bits, router_bits)
+    logits = np.asarray(logits, np.float32)
+    idx = topk_select(logits, k)
+    w = softmax_selected(logits, idx)
+    counts, offsets, perm, inv = permute_routes(idx, E)
+
+    def get(e):
+        return {key: experts[key][e] for key in
+                ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")}
+
+    out64, out_bits = forward_tokens(x_bits, idx, w, get, shared, L, I)
+    return {"logits": logits, "idx": idx, "w": w, "counts": counts,
+            "offsets": offsets, "perm": perm, "inv": inv,
+            "out64": out64, "out": out_bits}
