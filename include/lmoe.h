@@ -1,0 +1,159 @@
+/*
+ * lmoe.h — C ABI of the LatentMoE MXFP4 (w4a16) routed-expert layer on MI355X.
+ *
+ * The layer (dev48.org "Kimi K3 on AMD Instinct GPUs with TokenSpeed",
+ * section 4 "Latent MoE"; infervisor.ai "Bringing up Kimi-K3 on day zero",
+ * section "The model we hadn't run"): every token of a bf16 activation block
+ * in the latent width L is scored by a router over E experts, sent to its k
+ * best experts plus S always-on shared experts, and each expert applies a GLU
+ * feed-forward network
+ *     h = bf16( silu(x Gq^T) * (x Uq^T) ),   y = h Dq^T
+ * whose routed weights are MXFP4: 4-bit E2M1 codes with one E8M0 exponent
+ * (bias 127) per 32 consecutive values of a row. The output is
+ *     out[t] = bf16( sum_j w[t,j] y_(t,j) + sum_s ysh_s[t] ).
+ *
+ * Conventions for every call:
+ *  - Pointers marked "device" are HIP device pointers owned by the caller and
+ *    must be 16-byte aligned; "host" pointers are read during the call only.
+ *  - The library never allocates, frees or synchronises. Temporary storage
+ *    comes from the caller's workspace (see lmoe_workspace_bytes).
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    default stream). Arguments are validated on the host before anything is
+ *    enqueued: a non-zero status means nothing was launched.
+ *  - Calls are re-entrant provided concurrent calls use distinct workspaces
+ *    and outputs.
+ *  - Results are deterministic: the same inputs give bit-identical outputs
+ *    (no floating-point atomics anywhere).
+ */
+#ifndef LMOE_H_
+#define LMOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  LMOE_OK = 0,
+  LMOE_ERR_NULL = 1,      /* a required pointer is NULL */
+  LMOE_ERR_SHAPE = 2,     /* dimensions violate the constraints below */
+  LMOE_ERR_ALIGN = 3,     /* a device pointer is not 16-byte aligned */
+  LMOE_ERR_WORKSPACE = 4, /* workspace smaller than lmoe_workspace_bytes() */
+  LMOE_ERR_HIP = 5        /* a kernel launch failed */
+};
+
+/* Layer dimensions.
+ *   T  tokens (T >= 0; T == 0 is a no-op)
+ *   L  latent width: input of gate/up, output of down (L % 32 == 0, 32..16384)
+ *   E  routed experts (1..1024)
+ *   k  experts selected per token (1 <= k <= min(E, 32))
+ *   I  routed-expert intermediate width (I % 32 == 0, 32..16384)
+ *   S  shared experts (0..8)
+ *   Is shared-expert intermediate width (Is % 32 == 0 when S > 0)
+ * The Kimi-K3 LatentMoE has L = 3584, E = 896, k = 16, S = 2 (pages above).
+ */
+typedef struct lmoe_dims {
+  int32_t T, L, E, k, I, S, Is;
+} lmoe_dims;
+
+/* Weights, all device pointers, row-major.
+ *   router_w  bf16 [L][E]      router projection of the latent
+ *   gate_q    uint8 [E][I][L/2]   E2M1 codes of the gate rows; element 2m of a
+ *                                 row is the low nibble of byte m
+ *   gate_s    uint8 [E][I][L/32]  E8M0 exponent of elements 32j..32j+31 of a
+ *                                 row; value = E2M1(code) * 2^(byte - 127),
+ *                                 byte 255 is NaN
+ *   up_q, up_s      same layout as gate
+ *   down_q    uint8 [E][L][I/2], down_s uint8 [E][L][I/32]
+ *   sh_gate, sh_up  bf16 [S][Is][L];  sh_down bf16 [S][L][Is]
+ * The per-32 exponent along the input dimension is the checkpoint format
+ * described in huggingface.co "Notes from an NVFP4 port of Kimi K3.1 Pro"
+ * (introduction). router_w may be NULL when logits are given. The shared
+ * pointers may be NULL when S == 0.
+ */
+typedef struct lmoe_weights {
+  const uint16_t* router_w;
+  const uint8_t* gate_q;
+  const uint8_t* gate_s;
+  const uint8_t* up_q;
+  const uint8_t* up_s;
+  const uint8_t* down_q;
+  const uint8_t* down_s;
+  const uint16_t* sh_gate;
+  const uint16_t* sh_up;
+  const uint16_t* sh_down;
+} lmoe_weights;
+
+/* Routing results, all device pointers; any member may be NULL, in which case
+ * the value lives only in the workspace.
+ *   logits    float [T][E]  router logits. INPUT when logits_given != 0 (then
+ *                           required), otherwise written if non-NULL.
+ *   topk_idx  int32 [T][k]  selected experts of each token, ordered by
+ *                           descending logit, equal logits by ascending expert
+ *                           index (NaN ranks below -inf, -0 equals +0)
+ *   topk_w    float [T][k]  softmax over the selected logits
+ *   counts    int32 [E]     routes per expert
+ *   offsets   int32 [E+1]   exclusive prefix sum of counts (offsets[E] = T*k)
+ *   perm      int32 [T*k]   perm[pos] = route r = t*k + j, routes grouped by
+ *                           expert and stable in r
+ *   inv_perm  int32 [T*k]   inv_perm[r] = pos
+ * Selection is the exact top-k of the fp32 logits (the tie rule mirrors the
+ * boundary rule of huggingface.co "Notes from an NVFP4 port of Kimi K3.1 Pro",
+ * "Details that silently change the answer" (4)); grouping routes by expert so
+ * that one weight panel serves several routes follows TokenSpeed section 4.1.
+ */
+typedef struct lmoe_routing {
+  float* logits;
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv_perm;
+} lmoe_routing;
+
+/* Bytes of device workspace lmoe_route / lmoe_forward need for these
+ * dimensions (the same value serves both). Returns 0 for invalid dims. */
+size_t lmoe_workspace_bytes(const lmoe_dims* dims);
+
+/* Routing only: router logits (unless logits_given), top-k selection with
+ * softmax weights, and the expert grouping (counts, offsets, perm, inv_perm).
+ *   dims      host; x bf16 [T][L] device (may be NULL if logits_given)
+ *   router_w  bf16 [L][E] device (ignored if logits_given)
+ *   r         host struct of device pointers (may be NULL: nothing returned)
+ *   ws        device workspace of ws_bytes >= lmoe_workspace_bytes(dims)
+ * Errors: LMOE_ERR_NULL, _SHAPE, _ALIGN, _WORKSPACE, _HIP. */
+int lmoe_route(const lmoe_dims* dims, const uint16_t* x, const uint16_t* router_w,
+               int logits_given, const lmoe_routing* r, void* ws, size_t ws_bytes,
+               void* stream);
+
+/* The whole layer: routing, routed experts, shared experts and combine.
+ *   x    bf16 [T][L] device;  w  host struct of device weight pointers
+ *   r    optional routing outputs (see lmoe_routing); when logits_given,
+ *        r->logits is the input logits and r must not be NULL
+ *   out  bf16 [T][L] device, written with the combined output
+ *   ws   device workspace of ws_bytes >= lmoe_workspace_bytes(dims)
+ * Errors: LMOE_ERR_NULL, _SHAPE, _ALIGN, _WORKSPACE, _HIP. */
+int lmoe_forward(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights* w,
+                 int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
+                 size_t ws_bytes, void* stream);
+
+/* Test hook: dequantise an MXFP4 matrix with the same device routine the
+ * expert kernels use.
+ *   q    uint8 [rows][K/2] device codes;  s  uint8 [rows][K/32] device exponents
+ *   out  bf16 [rows][K] device
+ * K % 32 == 0, rows >= 0. Errors: LMOE_ERR_NULL, _SHAPE, _ALIGN, _HIP. */
+int lmoe_debug_dequant_mxfp4(const uint8_t* q, const uint8_t* s, int32_t rows, int32_t K,
+                             uint16_t* out, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* lmoe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMOE_H_ */

@@ -1,0 +1,162 @@
+"""Python binding of liblmoe.so, the LatentMoE MXFP4 (w4a16) layer for MI355X.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. torch supplies device memory and the current stream. The library is
+loaded from this package directory; importing the binding when it is missing
+raises, there is no fallback of any kind.
+
+Functions mirror the C ABI in include/lmoe.h:
+  workspace_bytes(dims)
+  route(dims, x, router_w, logits_given, routing, ws)
+  forward(dims, x, weights, logits_given, routing, out, ws)
+  debug_dequant_mxfp4(q, s, rows, K, out)
+  status_string(code)
+`dims` is a Dims-like object (attributes T, L, E, k, I, S, Is) or a tuple in
+that order; tensors are torch CUDA tensors (bf16 data may be torch.bfloat16,
+torch.int16 or torch.uint16 views), `weights` and `routing` are dicts keyed by
+the C struct member names.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Mapping, Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblmoe.so")
+
+LMOE_OK = 0
+LMOE_ERR_NULL = 1
+LMOE_ERR_SHAPE = 2
+LMOE_ERR_ALIGN = 3
+LMOE_ERR_WORKSPACE = 4
+LMOE_ERR_HIP = 5
+
+EXPORTS = ("lmoe_workspace_bytes", "lmoe_route", "lmoe_forward",
+           "lmoe_debug_dequant_mxfp4", "lmoe_status_string")
+
+
+class lmoe_dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "L", "E", "k", "I", "S", "Is")]
+
+
+class lmoe_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "router_w", "gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s",
+        "sh_gate", "sh_up", "sh_down")]
+
+
+class lmoe_routing(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "logits", "topk_idx", "topk_w", "counts", "offsets", "perm", "inv_perm")]
+
+
+class LmoeError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn}: status {code} ({msg})")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python mxfp4_latent_mixture_amd/build.py` "
+            "(hipcc, gfx950). There is no CPU fallback.")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    dp = ctypes.POINTER(lmoe_dims)
+    lib.lmoe_workspace_bytes.argtypes = [dp]
+    lib.lmoe_workspace_bytes.restype = sz
+    lib.lmoe_route.argtypes = [dp, vp, vp, ctypes.c_int, ctypes.POINTER(lmoe_routing), vp, sz, vp]
+    lib.lmoe_route.restype = ctypes.c_int
+    lib.lmoe_forward.argtypes = [dp, vp, ctypes.POINTER(lmoe_weights), ctypes.c_int,
+                                 ctypes.POINTER(lmoe_routing), vp, vp, sz, vp]
+    lib.lmoe_forward.restype = ctypes.c_int
+    lib.lmoe_debug_dequant_mxfp4.argtypes = [vp, vp, i32, i32, vp, vp]
+    lib.lmoe_debug_dequant_mxfp4.restype = ctypes.c_int
+    lib.lmoe_status_string.argtypes = [ctypes.c_int]
+    lib.lmoe_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def status_string(code: int) -> str:
+    return _lib.lmoe_status_string(int(code)).decode()
+
+
+def _check(fn: str, code: int) -> None:
+    if code != LMOE_OK:
+        raise LmoeError(fn, code, status_string(code))
+
+
+def _dims(d) -> lmoe_dims:
+    if isinstance(d, lmoe_dims):
+        return d
+    if isinstance(d, (tuple, list)):
+        return lmoe_dims(*[int(v) for v in d])
+    return lmoe_dims(int(d.T), int(d.L), int(d.E), int(d.k), int(d.I), int(d.S), int(d.Is))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _routing(r: Optional[Mapping]) -> Optional[lmoe_routing]:
+    if r is None:
+        return None
+    return lmoe_routing(*[_ptr(r.get(n)) for n, _ in lmoe_routing._fields_])
+
+
+def _weights(w: Mapping) -> lmoe_weights:
+    return lmoe_weights(*[_ptr(w.get(n)) for n, _ in lmoe_weights._fields_])
+
+
+def workspace_bytes(dims) -> int:
+    d = _dims(dims)
+    return int(_lib.lmoe_workspace_bytes(ctypes.byref(d)))
+
+
+def route(dims, x, router_w, logits_given: bool, routing: Optional[Mapping], ws,
+          stream=None) -> None:
+    d = _dims(dims)
+    r = _routing(routing)
+    code = _lib.lmoe_route(ctypes.byref(d), _ptr(x), _ptr(router_w), int(bool(logits_given)),
+                           ctypes.byref(r) if r is not None else None, _ptr(ws),
+                           ws.numel() * ws.element_size() if ws is not None else 0,
+                           _stream(stream))
+    _check("lmoe_route", code)
+
+
+def forward(dims, x, weights: Mapping, logits_given: bool, routing: Optional[Mapping], out, ws,
+            stream=None) -> None:
+    d = _dims(dims)
+    r = _routing(routing)
+    w = _weights(weights)
+    code = _lib.lmoe_forward(ctypes.byref(d), _ptr(x), ctypes.byref(w), int(bool(logits_given)),
+                             ctypes.byref(r) if r is not None else None, _ptr(out), _ptr(ws),
+                             ws.numel() * ws.element_size() if ws is not None else 0,
+                             _stream(stream))
+    _check("lmoe_forward", code)
+
+
+def debug_dequant_mxfp4(q, s, rows: int, K: int, out, stream=None) -> None:
+    code = _lib.lmoe_debug_dequant_mxfp4(_ptr(q), _ptr(s), int(rows), int(K), _ptr(out),
+                                         _stream(stream))
+    _check("lmoe_debug_dequant_mxfp4", code)

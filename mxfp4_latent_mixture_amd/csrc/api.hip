@@ -1,0 +1,211 @@
+// C ABI of the LatentMoE layer: argument validation, workspace layout and the
+// launch sequence (router -> top-k -> grouping -> experts -> combine).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "lmoe_internal.h"
+
+namespace lmoe {
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+static bool dims_ok(const lmoe_dims& d) {
+  if (d.T < 0 || d.T > (1 << 20)) return false;
+  if (d.L < 32 || d.L > 16384 || d.L % 32) return false;
+  if (d.E < 1 || d.E > 1024) return false;
+  if (d.k < 1 || d.k > 32 || d.k > d.E) return false;
+  if (d.I < 32 || d.I > 16384 || d.I % 32) return false;
+  if (d.S < 0 || d.S > 8) return false;
+  if (d.S > 0 && (d.Is < 32 || d.Is > 16384 || d.Is % 32)) return false;
+  return true;
+}
+
+Plan make_plan(const lmoe_dims& d) {
+  Plan p;
+  p.d = d;
+  if (p.d.S == 0) p.d.Is = 0;
+  p.R = d.T * d.k;
+  // Router: enough (tile x split) workgroups to spread the weight stream.
+  const int nsteps = d.L / 32;
+  const int tiles = ((d.E + 63) / 64) * ((d.T + 63) / 64);
+  int ks = std::max(1, std::min(nsteps, (512 + tiles - 1) / std::max(1, tiles)));
+  int per = (nsteps + ks - 1) / ks;
+  ks = (nsteps + per - 1) / per;
+  p.router.ks = ks;
+  p.router.steps_per = per;
+  // Grouped GEMM tile height: decode-sized groups use single 16-row tiles.
+  const double avg = (double)p.R / (double)std::max(1, std::min(d.E, p.R));
+  p.rows_per_tile = (avg <= 8.0) ? kSmallRows : kLargeRows;
+  p.max_tiles = std::min(d.E, p.R) + p.R / p.rows_per_tile;
+  return p;
+}
+
+Workspace carve_workspace(const Plan& p, void* base) {
+  const lmoe_dims& d = p.d;
+  Workspace w = {};
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  auto take = [&](size_t bytes) -> char* {
+    char* r = b ? b + off : nullptr;
+    off = align_up(off + bytes, 256);
+    return r;
+  };
+  const size_t T = d.T, E = d.E, R = p.R, L = d.L, I = d.I, S = d.S, Is = d.Is;
+  w.part = reinterpret_cast<float*>(take((size_t)p.router.ks * T * E * 4));
+  w.idx = reinterpret_cast<int32_t*>(take(R * 4));
+  w.w = reinterpret_cast<float*>(take(R * 4));
+  w.counts = reinterpret_cast<int32_t*>(take(E * 4));
+  w.offsets = reinterpret_cast<int32_t*>(take((E + 1) * 4));
+  w.perm = reinterpret_cast<int32_t*>(take(R * 4));
+  w.inv = reinterpret_cast<int32_t*>(take(R * 4));
+  w.tiles = reinterpret_cast<int32_t*>(take((size_t)p.max_tiles * 3 * 4));
+  w.ntiles = reinterpret_cast<int32_t*>(take(4));
+  w.h = reinterpret_cast<uint16_t*>(take(R * I * 2));
+  w.h_sh = reinterpret_cast<uint16_t*>(take(S * T * Is * 2));
+  w.y = reinterpret_cast<float*>(take(R * L * 4));
+  w.y_sh = reinterpret_cast<float*>(take(S * T * L * 4));
+  w.bytes = off;
+  return w;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static int check_opt_ptr(const void* p) {
+  if (p && !aligned16(p)) return LMOE_ERR_ALIGN;
+  return LMOE_OK;
+}
+
+// Validate and run steps router -> top-k -> grouping. Fills the resolved
+// routing buffers (user's when given, workspace otherwise).
+struct Routing {
+  int32_t* idx;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv;
+};
+
+static int run_route(const Plan& p, const Workspace& ws, const uint16_t* x, const uint16_t* wr,
+                     int logits_given, const lmoe_routing* r, Routing* out, hipStream_t s) {
+  Routing rt;
+  rt.idx = (r && r->topk_idx) ? r->topk_idx : ws.idx;
+  rt.w = (r && r->topk_w) ? r->topk_w : ws.w;
+  rt.counts = (r && r->counts) ? r->counts : ws.counts;
+  rt.offsets = (r && r->offsets) ? r->offsets : ws.offsets;
+  rt.perm = (r && r->perm) ? r->perm : ws.perm;
+  rt.inv = (r && r->inv_perm) ? r->inv_perm : ws.inv;
+  hipError_t e;
+  const float* part;
+  int ks;
+  float* logits_out = nullptr;
+  if (logits_given) {
+    part = r->logits;
+    ks = 1;
+  } else {
+    e = launch_router(p, x, wr, ws.part, s);
+    if (e != hipSuccess) return LMOE_ERR_HIP;
+    part = ws.part;
+    ks = p.router.ks;
+    logits_out = r ? r->logits : nullptr;
+  }
+  e = launch_topk(p, part, ks, logits_out, rt.idx, rt.w, s);
+  if (e != hipSuccess) return LMOE_ERR_HIP;
+  e = launch_permute(p, rt.idx, rt.counts, rt.offsets, rt.perm, rt.inv, ws.tiles, ws.ntiles, s);
+  if (e != hipSuccess) return LMOE_ERR_HIP;
+  *out = rt;
+  return LMOE_OK;
+}
+
+static int check_routing(const lmoe_routing* r, int logits_given) {
+  if (logits_given && (!r || !r->logits)) return LMOE_ERR_NULL;
+  if (!r) return LMOE_OK;
+  const void* ps[] = {r->logits, r->topk_idx, r->topk_w, r->counts,
+                      r->offsets, r->perm, r->inv_perm};
+  for (const void* q : ps) {
+    int st = check_opt_ptr(q);
+    if (st) return st;
+  }
+  return LMOE_OK;
+}
+
+}  // namespace lmoe
+
+using namespace lmoe;
+
+extern "C" size_t lmoe_workspace_bytes(const lmoe_dims* dims) {
+  if (!dims || !dims_ok(*dims)) return 0;
+  Plan p = make_plan(*dims);
+  return carve_workspace(p, nullptr).bytes;
+}
+
+extern "C" const char* lmoe_status_string(int status) {
+  switch (status) {
+    case LMOE_OK: return "ok";
+    case LMOE_ERR_NULL: return "required pointer is NULL";
+    case LMOE_ERR_SHAPE: return "dimensions violate the layer constraints";
+    case LMOE_ERR_ALIGN: return "device pointer is not 16-byte aligned";
+    case LMOE_ERR_WORKSPACE: return "workspace smaller than lmoe_workspace_bytes()";
+    case LMOE_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int lmoe_route(const lmoe_dims* dims, const uint16_t* x, const uint16_t* router_w,
+                          int logits_given, const lmoe_routing* r, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (!dims) return LMOE_ERR_NULL;
+  if (!dims_ok(*dims)) return LMOE_ERR_SHAPE;
+  int st = check_routing(r, logits_given);
+  if (st) return st;
+  if (dims->T == 0) return LMOE_OK;
+  if (!logits_given && (!x || !router_w)) return LMOE_ERR_NULL;
+  if (!ws) return LMOE_ERR_NULL;
+  if (check_opt_ptr(x) || check_opt_ptr(router_w) || !aligned16(ws)) return LMOE_ERR_ALIGN;
+  Plan p = make_plan(*dims);
+  Workspace w = carve_workspace(p, ws);
+  if (ws_bytes < w.bytes) return LMOE_ERR_WORKSPACE;
+  Routing rt;
+  return run_route(p, w, x, router_w, logits_given, r, &rt, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int lmoe_forward(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights* wts,
+                            int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!dims || !wts) return LMOE_ERR_NULL;
+  if (!dims_ok(*dims)) return LMOE_ERR_SHAPE;
+  int st = check_routing(r, logits_given);
+  if (st) return st;
+  if (dims->T == 0) return LMOE_OK;
+  const lmoe_weights& w = *wts;
+  if (!x || !out || !ws) return LMOE_ERR_NULL;
+  if (!logits_given && !w.router_w) return LMOE_ERR_NULL;
+  if (!w.gate_q || !w.gate_s || !w.up_q || !w.up_s || !w.down_q || !w.down_s)
+    return LMOE_ERR_NULL;
+  if (dims->S > 0 && (!w.sh_gate || !w.sh_up || !w.sh_down)) return LMOE_ERR_NULL;
+  const void* ptrs[] = {x, out, ws, w.router_w, w.gate_q, w.gate_s, w.up_q,
+                        w.up_s, w.down_q, w.down_s, w.sh_gate, w.sh_up, w.sh_down};
+  for (const void* q : ptrs)
+    if (check_opt_ptr(q)) return LMOE_ERR_ALIGN;
+  Plan p = make_plan(*dims);
+  Workspace wsp = carve_workspace(p, ws);
+  if (ws_bytes < wsp.bytes) return LMOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Routing rt;
+  st = run_route(p, wsp, x, w.router_w, logits_given, r, &rt, s);
+  if (st) return st;
+  hipError_t e = launch_experts(p, x, w, wsp, rt.perm, rt.inv, rt.w, out, s);
+  return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
+}
+
+extern "C" int lmoe_debug_dequant_mxfp4(const uint8_t* q, const uint8_t* s, int32_t rows,
+                                        int32_t K, uint16_t* out, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32) return LMOE_ERR_SHAPE;
+  if (rows == 0) return LMOE_OK;
+  if (!q || !s || !out) return LMOE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out)) return LMOE_ERR_ALIGN;
+  hipError_t e = launch_dequant(q, s, rows, K, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
+}

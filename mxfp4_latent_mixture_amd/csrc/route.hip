@@ -1,0 +1,310 @@
+// Routing kernels: router logits, top-k selection with softmax weights, and
+// the stable grouping of routes by expert.
+//
+// Router scores over the experts are one projection of the MoE input (dev48.org
+// "Kimi K3 on AMD Instinct GPUs with TokenSpeed", section 4.3); here the router
+// reads the latent activations. Each token keeps its 16 best of 896 experts
+// (infervisor.ai "Bringing up Kimi-K3 on day zero", "The model we hadn't run").
+// Routes are then sorted by expert so one loaded weight panel serves every
+// route of that expert (TokenSpeed section 4.1).
+#include "lmoe_device.h"
+#include "lmoe_internal.h"
+
+namespace lmoe {
+
+// ---------------------------------------------------------------------------
+// Router: part[split][t][e] = sum over the split's K range of x[t][k] W[k][e].
+// Tile: 64 tokens x 64 experts per 256-thread workgroup, one 32-wide K step
+// per pass; each wave owns 16 tokens and four 16-expert MFMA tiles.
+// ---------------------------------------------------------------------------
+constexpr int kRtTok = 64;
+constexpr int kRtExp = 64;
+constexpr int kRtPad = 40;  // LDS row length in bf16 (32 + 8): 80-byte rows
+
+__global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict__ x,
+                                                     const uint16_t* __restrict__ wr,
+                                                     float* __restrict__ part, int T, int L,
+                                                     int E, int steps_per) {
+  __shared__ __attribute__((aligned(16))) uint16_t sx[kRtTok][kRtPad];
+  __shared__ __attribute__((aligned(16))) uint16_t sw[kRtExp][kRtPad];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int e0 = blockIdx.x * kRtExp;
+  const int t0 = blockIdx.y * kRtTok;
+  const int split = blockIdx.z;
+  const int nsteps = L / 32;
+  const int st0 = split * steps_per;
+  const int st1 = min(nsteps, st0 + steps_per);
+  const bool vecw = (E % 8) == 0;
+
+  f32x4_t acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int st = st0; st < st1; ++st) {
+    __syncthreads();
+    {  // activations: 64 rows x 32 values, 16 bytes per thread
+      const int row = tid >> 2, q = tid & 3;
+      const int t = t0 + row;
+      u32x4_t v = zero16();
+      if (t < T) v = load16(x + (size_t)t * L + st * 32 + q * 8);
+      *reinterpret_cast<u32x4_t*>(&sx[row][q * 8]) = v;
+    }
+    {  // router weights: 32 K rows x 64 experts, stored transposed
+      const int kr = tid >> 3, q = tid & 7;
+      const int e = e0 + q * 8;
+      const uint16_t* src = wr + (size_t)(st * 32 + kr) * E + e;
+      uint16_t vals[8];
+      if (vecw && e + 8 <= E) {
+        u32x4_t v = load16(src);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          vals[2 * i] = (uint16_t)(v[i] & 0xFFFFu);
+          vals[2 * i + 1] = (uint16_t)(v[i] >> 16);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vals[i] = (e + i < E) ? src[i] : (uint16_t)0;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sw[q * 8 + i][kr] = vals[i];
+    }
+    __syncthreads();
+    const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sx[wave * 16 + col][grp * 8]);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(&sw[nt * 16 + col][grp * 8]);
+      acc[nt] = mfma16(a, b, acc[nt]);
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int e = e0 + nt * 16 + col;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = t0 + wave * 16 + grp * 4 + j;
+      if (t < T && e < E) part[((size_t)split * T + t) * E + e] = acc[nt][j];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top-k. Order: larger logit first, equal logits by lower expert index, NaN
+// after every number, -0 == +0. Encoded as one 64-bit key per expert:
+// high word an order-preserving image of the float, low word ~expert.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t order_key(float f, int e) {
+  uint32_t u = __float_as_uint(f);
+  if (f == 0.0f) u = 0u;
+  uint32_t k32;
+  if (f != f) {
+    k32 = 0u;
+  } else {
+    k32 = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return ((uint64_t)k32 << 32) | (uint64_t)(~(uint32_t)e);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint64_t o = __shfl_xor(v, off, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+constexpr int kMaxE = 1024;
+constexpr int kPerLane = kMaxE / kWave;  // 16
+
+// One 256-thread workgroup per token: all threads sum the K-split partials
+// into LDS, then wave 0 selects.
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ part, int ks, int T,
+                                                   int E, int k, float* __restrict__ logits_out,
+                                                   int32_t* __restrict__ idx,
+                                                   float* __restrict__ wout) {
+  __shared__ float sl[kMaxE];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 256) {
+    float s = 0.f;
+    for (int i = 0; i < ks; ++i) s += part[((size_t)i * T + t) * E + e];
+    sl[e] = s;
+    if (logits_out) logits_out[(size_t)t * E + e] = s;
+  }
+  __syncthreads();
+  if (tid >= kWave) return;
+  const int lane = tid;
+
+  uint64_t key[kPerLane];
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    const int e = lane + kWave * i;
+    key[i] = (e < E) ? order_key(sl[e], e) : 0ull;
+  }
+  uint64_t best = 0ull;
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) best = key[i] > best ? key[i] : best;
+
+  int my_e = 0;
+  float my_l = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const uint64_t b = wave_max_u64(best);
+    const int ew = (int)(~(uint32_t)b);
+    if (lane == j) {
+      my_e = ew;
+      my_l = sl[ew];
+    }
+    if ((ew & (kWave - 1)) == lane) {
+      const int slot = ew / kWave;
+      best = 0ull;
+#pragma unroll
+      for (int i = 0; i < kPerLane; ++i) {
+        if (i == slot) key[i] = 0ull;
+        best = key[i] > best ? key[i] : best;
+      }
+    }
+  }
+  // softmax over the selected logits, relative to the largest (the first)
+  const float l0 = __shfl(my_l, 0, kWave);
+  const float z = (lane < k) ? expf(my_l - l0) : 0.f;
+  float s = z;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_down(s, off, kWave);
+  s = __shfl(s, 0, kWave);
+  if (lane < k) {
+    idx[(size_t)t * k + lane] = my_e;
+    wout[(size_t)t * k + lane] = z / s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Grouping of routes by expert (one 1024-thread workgroup).
+// counts by LDS histogram; offsets by an exclusive scan; then positions: a
+// token selects each expert at most once, so within expert e the routes are
+// ordered by token and pos(t, e) = offsets[e] + #{t' < t selecting e}. Tokens
+// are processed 64 at a time with one 64-bit membership mask per expert.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int block_exclusive_scan_1024(int v, int* s_wave, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int w = (lane < 16) ? s_wave[lane] : 0;
+    int wi = w;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      int o = __shfl_up(wi, off, kWave);
+      if (lane >= off) wi += o;
+    }
+    if (lane < 16) s_wave[16 + lane] = wi - w;  // exclusive prefix of wave totals
+    if (lane == 15) s_wave[32] = wi;
+  }
+  __syncthreads();
+  const int r = s_wave[16 + wave] + incl - v;
+  *total = s_wave[32];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ idx, int T,
+                                                       int k, int E, int32_t* __restrict__ counts,
+                                                       int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ perm,
+                                                       int32_t* __restrict__ inv,
+                                                       int32_t* __restrict__ tiles,
+                                                       int32_t* __restrict__ ntiles, int rows) {
+  __shared__ int s_cnt[kMaxE];
+  __shared__ int s_run[kMaxE];
+  __shared__ unsigned long long s_mask[kMaxE];
+  __shared__ int s_wave[48];
+  const int tid = threadIdx.x;
+  const int R = T * k;
+  s_cnt[tid] = 0;
+  __syncthreads();
+  for (int r = tid; r < R; r += 1024) atomicAdd(&s_cnt[idx[r]], 1);
+  __syncthreads();
+
+  const int c = (tid < E) ? s_cnt[tid] : 0;
+  int total = 0;
+  const int off = block_exclusive_scan_1024(c, s_wave, &total);
+  const int nt = (c + rows - 1) / rows;
+  int ntot = 0;
+  const int tbase = block_exclusive_scan_1024(nt, s_wave, &ntot);
+  if (tid < E) {
+    counts[tid] = c;
+    offsets[tid] = off;
+    s_run[tid] = off;
+    for (int i = 0; i < nt; ++i) {
+      tiles[3 * (tbase + i) + 0] = tid;
+      tiles[3 * (tbase + i) + 1] = off + i * rows;
+      tiles[3 * (tbase + i) + 2] = min(rows, c - i * rows);
+    }
+  }
+  if (tid == 0) {
+    offsets[E] = total;
+    *ntiles = ntot;
+  }
+  __syncthreads();
+
+  for (int tg = 0; tg < T; tg += 64) {
+    if (tid < E) s_mask[tid] = 0ull;
+    __syncthreads();
+    const int r0 = tg * k;
+    const int r1 = min(T, tg + 64) * k;
+    for (int r = r0 + tid; r < r1; r += 1024) {
+      const int t = r / k;
+      atomicOr(&s_mask[idx[r]], 1ull << (t - tg));
+    }
+    __syncthreads();
+    for (int r = r0 + tid; r < r1; r += 1024) {
+      const int t = r / k;
+      const int e = idx[r];
+      const unsigned long long below = (1ull << (t - tg)) - 1ull;
+      const int pos = s_run[e] + __popcll(s_mask[e] & below);
+      perm[pos] = r;
+      inv[r] = pos;
+    }
+    __syncthreads();
+    if (tid < E) s_run[tid] += __popcll(s_mask[tid]);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_router(const Plan& p, const uint16_t* x, const uint16_t* wr, float* part,
+                         hipStream_t s) {
+  const lmoe_dims& d = p.d;
+  dim3 grid((d.E + kRtExp - 1) / kRtExp, (d.T + kRtTok - 1) / kRtTok, p.router.ks);
+  hipLaunchKernelGGL(router_kernel, grid, dim3(256), 0, s, x, wr, part, d.T, d.L, d.E,
+                     p.router.steps_per);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const Plan& p, const float* part, int ks, float* logits_out,
+                       int32_t* idx, float* w, hipStream_t s) {
+  const lmoe_dims& d = p.d;
+  hipLaunchKernelGGL(topk_kernel, dim3(d.T), dim3(256), 0, s, part, ks, d.T, d.E, d.k,
+                     logits_out, idx, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const Plan& p, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, int32_t* inv, int32_t* tiles, int32_t* ntiles,
+                          hipStream_t s) {
+  const lmoe_dims& d = p.d;
+  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, idx, d.T, d.k, d.E, counts,
+                     offsets, perm, inv, tiles, ntiles, p.rows_per_tile);
+  return hipGetLastError();
+}
+
+}  // namespace lmoe

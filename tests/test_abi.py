@@ -1,0 +1,145 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry
+point, sizes its workspace, and rejects bad arguments on the host before any
+launch (every call below fails validation, so no kernel is ever enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lmoe.h")
+
+
+@pytest.fixture(scope="module")
+def lm():
+    import mxfp4_latent_mixture_amd as lm
+    return lm
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lmoe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    assert names == sorted(["lmoe_workspace_bytes", "lmoe_route", "lmoe_forward",
+                            "lmoe_debug_dequant_mxfp4", "lmoe_status_string"]), names
+
+
+def test_library_exports_every_declared_symbol(lm):
+    lib = ctypes.CDLL(lm.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert set(lm.EXPORTS) == set(_declared())
+
+
+def test_status_strings(lm):
+    for code in range(6):
+        assert lm.status_string(code)
+    assert lm.status_string(0) == "ok"
+    assert "unknown" in lm.status_string(99)
+
+
+K3 = (1, 3584, 896, 16, 2048, 2, 2048)
+
+
+def test_workspace_bytes_valid_and_invalid(lm):
+    assert lm.workspace_bytes(K3) > 0
+    big = lm.workspace_bytes((4096,) + K3[1:])
+    assert big > lm.workspace_bytes(K3)
+    # T=8192: route partials dominate (131072 routes x 3584 fp32)
+    w8 = lm.workspace_bytes((8192,) + K3[1:])
+    assert w8 >= 131072 * 3584 * 4
+    for bad in [(1, 3583, 896, 16, 2048, 2, 2048),   # L % 32
+                (1, 3584, 1025, 16, 2048, 2, 2048),  # E > 1024
+                (1, 3584, 896, 33, 2048, 2, 2048),   # k > 32
+                (1, 3584, 8, 9, 2048, 2, 2048),      # k > E
+                (1, 3584, 896, 16, 2040, 2, 2048),   # I % 32
+                (1, 3584, 896, 16, 2048, 2, 100),    # Is % 32
+                (-1, 3584, 896, 16, 2048, 2, 2048),
+                (1, 3584, 896, 0, 2048, 2, 2048)]:
+        assert lm.workspace_bytes(bad) == 0, bad
+    assert lm.workspace_bytes((0,) + K3[1:]) > 0
+
+
+def _weights(lm, base=0x10000000):
+    vals = [base + 0x100000 * i for i in range(10)]
+    return lm.lmoe_weights(*vals)
+
+
+def _call_forward(lm, dims, x=0x20000000, w=None, logits_given=0, r=None, out=0x30000000,
+                  ws=0x40000000, ws_bytes=None):
+    d = lm._dims(dims)
+    if w is None:
+        w = _weights(lm)
+    if ws_bytes is None:
+        ws_bytes = 1
+    return lm._lib.lmoe_forward(ctypes.byref(d), x, ctypes.byref(w), logits_given,
+                                ctypes.byref(r) if r is not None else None, out, ws,
+                                ws_bytes, None)
+
+
+def test_forward_rejects_bad_arguments(lm):
+    assert lm._lib.lmoe_forward(None, 0, None, 0, None, 0, 0, 0, None) == lm.LMOE_ERR_NULL
+    assert _call_forward(lm, (1, 3583, 896, 16, 2048, 2, 2048)) == lm.LMOE_ERR_SHAPE
+    assert _call_forward(lm, K3, x=None) == lm.LMOE_ERR_NULL
+    assert _call_forward(lm, K3, out=None) == lm.LMOE_ERR_NULL
+    assert _call_forward(lm, K3, ws=None) == lm.LMOE_ERR_NULL
+    w = _weights(lm)
+    w.gate_s = None
+    assert _call_forward(lm, K3, w=w) == lm.LMOE_ERR_NULL
+    w = _weights(lm)
+    w.sh_down = None
+    assert _call_forward(lm, K3, w=w) == lm.LMOE_ERR_NULL
+    # logits given without a routing struct / without logits
+    assert _call_forward(lm, K3, logits_given=1) == lm.LMOE_ERR_NULL
+    assert _call_forward(lm, K3, logits_given=1, r=lm.lmoe_routing()) == lm.LMOE_ERR_NULL
+    # misaligned pointers
+    assert _call_forward(lm, K3, x=0x20000008) == lm.LMOE_ERR_ALIGN
+    w = _weights(lm)
+    w.down_q = 0x10000001
+    assert _call_forward(lm, K3, w=w) == lm.LMOE_ERR_ALIGN
+    r = lm.lmoe_routing()
+    r.perm = 0x50000004
+    assert _call_forward(lm, K3, r=r) == lm.LMOE_ERR_ALIGN
+    # workspace one byte short
+    need = lm.workspace_bytes(K3)
+    assert _call_forward(lm, K3, ws_bytes=need - 1) == lm.LMOE_ERR_WORKSPACE
+
+
+def test_forward_zero_tokens_needs_no_pointers(lm):
+    d = lm._dims((0,) + K3[1:])
+    w = lm.lmoe_weights()
+    assert lm._lib.lmoe_forward(ctypes.byref(d), None, ctypes.byref(w), 0, None, None, None,
+                                0, None) == lm.LMOE_OK
+
+
+def test_route_rejects_bad_arguments(lm):
+    d = lm._dims(K3)
+    assert lm._lib.lmoe_route(ctypes.byref(d), None, None, 0, None, 0x40000000, 1 << 40,
+                              None) == lm.LMOE_ERR_NULL
+    assert lm._lib.lmoe_route(ctypes.byref(d), 0x20000000, 0x21000000, 0, None, None, 0,
+                              None) == lm.LMOE_ERR_NULL
+    assert lm._lib.lmoe_route(ctypes.byref(d), 0x20000000, 0x21000000, 0, None, 0x40000000,
+                              16, None) == lm.LMOE_ERR_WORKSPACE
+    bad = lm._dims((1, 3584, 896, 17, 2048, 2, 2048 + 1))
+    assert lm._lib.lmoe_route(ctypes.byref(bad), 0x20000000, 0x21000000, 0, None,
+                              0x40000000, 1 << 40, None) == lm.LMOE_ERR_SHAPE
+
+
+def test_dequant_hook_rejects_bad_arguments(lm):
+    f = lm._lib.lmoe_debug_dequant_mxfp4
+    assert f(0x1000, 0x2000, 4, 48, 0x3000, None) == lm.LMOE_ERR_SHAPE
+    assert f(0x1000, 0x2000, -1, 64, 0x3000, None) == lm.LMOE_ERR_SHAPE
+    assert f(None, 0x2000, 4, 64, 0x3000, None) == lm.LMOE_ERR_NULL
+    assert f(0x1008, 0x2000, 4, 64, 0x3000, None) == lm.LMOE_ERR_ALIGN
+    assert f(0x1000, 0x2000, 0, 64, 0x3000, None) == lm.LMOE_OK
+
+
+def test_binding_rejects_host_tensors(lm):
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        lm._ptr(torch.zeros(4))

@@ -1,0 +1,293 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer and byte results (dequantised bf16 weights, routing indices, counts,
+offsets, permutations) must match bit for bit. Floating-point outputs must lie
+within 1e-2 * rms(ref) of the float64 reference plus half a bf16 ulp of the
+reference (the final bf16 rounding of the output), and their rms error must
+stay below 3e-3 * rms(ref). Router logits must lie within the fp32 summation
+bound; the selected expert sets must then agree wherever the oracle's top-k
+boundary gap is wider than twice that bound.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from workloads import get_workload, gen_all, gen_logits, gen_expert, gen_x, gen_router
+from workloads.configs import Dims, Workload
+
+from lmoe_testutil import (log, to_dev, upload, alloc_routing, run_forward, check_out,
+                           logits_bound, check_routing_against_oracle)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lm():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import mxfp4_latent_mixture_amd as lm
+    return lm
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+# ----------------------------------------------------------------------------
+# Dequantisation
+# ----------------------------------------------------------------------------
+
+def _dequant_gpu(lm, dev, q, s, rows, K):
+    import torch
+    out = torch.empty((rows, K), dtype=torch.int16, device=dev)
+    lm.debug_dequant_mxfp4(to_dev(q, dev), to_dev(s, dev), rows, K, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint16)
+
+
+def _compare_dequant(got, ref64):
+    ref = O.bf16_from_f64(ref64)
+    nan = np.isnan(ref64)
+    got_nan = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+    assert np.array_equal(nan, got_nan), "NaN placement differs"
+    mism = np.nonzero((got != ref) & ~nan)
+    assert mism[0].size == 0, (
+        f"{mism[0].size} mismatches, first {tuple(m[0] for m in mism)}: "
+        f"got {hex(got[mism][0])} want {hex(ref[mism][0])}")
+
+
+def test_dequant_exhaustive_codes_and_exponents(lm, dev):
+    log("dequant: 16 codes x 256 exponents")
+    N, K = 256, 64
+    codes = np.tile(np.arange(K) % 16, (N, 1)).astype(np.uint8)
+    q = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    s = np.stack([np.arange(256), (np.arange(256) + 97) % 256], axis=1).astype(np.uint8)
+    got = _dequant_gpu(lm, dev, q, s, N, K)
+    _compare_dequant(got, O.dequant_mxfp4(q, s, N, K))
+
+
+def test_dequant_k3_expert_matrix(lm, dev):
+    log("dequant: one K3 gate matrix (2048 x 3584) and one down matrix")
+    w = get_workload("decode")
+    ex = gen_expert(w, 5)
+    for qk, sk, N, K in (("gate_q", "gate_s", 2048, 3584), ("down_q", "down_s", 3584, 2048)):
+        got = _dequant_gpu(lm, dev, ex[qk], ex[sk], N, K)
+        _compare_dequant(got, O.dequant_mxfp4(ex[qk], ex[sk], N, K))
+
+
+# ----------------------------------------------------------------------------
+# Routing on given logits: bit-exact
+# ----------------------------------------------------------------------------
+
+def _route_given(lm, dev, logits: np.ndarray, k: int):
+    import torch
+    T, E = logits.shape
+    d = Dims(T=T, L=32, E=E, k=k, I=32, S=0, Is=0)
+    r = alloc_routing(d, dev)
+    r["logits"] = to_dev(logits.astype(np.float32), dev)
+    ws = torch.empty(max(1, lm.workspace_bytes(d)), dtype=torch.uint8, device=dev)
+    lm.route(d, None, None, True, r, ws)
+    torch.cuda.synchronize()
+    return {kk: v.cpu().numpy() for kk, v in r.items()}
+
+
+def _check_route_exact(res, logits, k, what):
+    E = logits.shape[1]
+    idx = O.topk_select(logits, k)
+    w = O.softmax_selected(logits, idx)
+    counts, offsets, perm, inv = O.permute_routes(idx, E)
+    assert np.array_equal(res["topk_idx"], idx), f"{what}: top-k indices differ"
+    fin = np.isfinite(w)
+    assert np.all(np.abs(res["topk_w"][fin] - w[fin]) <= 4e-6 * np.abs(w[fin]) + 1e-12), \
+        f"{what}: weights differ"
+    assert np.array_equal(res["counts"], counts), f"{what}: counts differ"
+    assert np.array_equal(res["offsets"], offsets), f"{what}: offsets differ"
+    assert np.array_equal(res["perm"], perm), f"{what}: perm differs"
+    assert np.array_equal(res["inv_perm"], inv), f"{what}: inv_perm differs"
+    log(f"{what}: routing bit-exact ({logits.shape[0]} tokens, E={E}, k={k})")
+
+
+@pytest.mark.parametrize("E,k", [(8, 1), (8, 8), (40, 16), (33, 5), (1024, 32), (896, 16)])
+def test_topk_edge_values(lm, dev, E, k):
+    rng = np.random.default_rng(E * 7 + k)
+    pool = np.array([1.5, 1.5, 0.0, -0.0, -2.0, 3.0, np.nan, -np.inf, np.inf, 0.25], np.float32)
+    T = 70
+    lg = rng.choice(pool, size=(T, E)).astype(np.float32)
+    lg[:30] = rng.normal(size=(30, E)).astype(np.float32)
+    lg[30:40] = 0.0                       # every logit tied
+    res = _route_given(lm, dev, lg, k)
+    _check_route_exact(res, lg, k, f"edge values E={E} k={k}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_skew"])
+def test_route_given_logits_small(lm, dev, name):
+    w = get_workload(name)
+    lg = gen_logits(Workload(name, w.seed, w.dims, logits_given=True, tie_group=min(12, w.dims.E)))
+    res = _route_given(lm, dev, lg, w.dims.k)
+    _check_route_exact(res, lg, w.dims.k, name)
+
+
+def test_route_given_logits_skewed_full(lm, dev):
+    w = get_workload("skewed")
+    log("skewed: generating 8192 x 896 logits")
+    lg = gen_logits(w)
+    res = _route_given(lm, dev, lg, w.dims.k)
+    _check_route_exact(res, lg, w.dims.k, "skewed T=8192")
+
+
+# ----------------------------------------------------------------------------
+# Whole layer on small shapes: every token
+# ----------------------------------------------------------------------------
+
+def _full_small(lm, dev, w: Workload):
+    d = w.dims
+    inp = gen_all(w)
+    dinp = upload(inp, dev)
+    got, r = run_forward(lm, w, dinp)
+    ref = O.forward(inp["x"], inp["router_w"], inp, inp, d.k,
+                    logits=inp.get("logits"))
+    if w.logits_given:
+        assert np.array_equal(r["topk_idx"], ref["idx"])
+        same = np.ones(d.T, bool)
+    else:
+        same = check_routing_against_oracle(r["topk_idx"], r["logits"], ref["logits"],
+                                            logits_bound(inp["x"], inp["router_w"]), d.k, w.name)
+        assert same.mean() >= 0.9
+    if same.all():
+        assert np.array_equal(r["counts"], ref["counts"])
+        assert np.array_equal(r["offsets"], ref["offsets"])
+        assert np.array_equal(r["perm"], ref["perm"])
+        assert np.array_equal(r["inv_perm"], ref["inv"])
+    rms = float(np.sqrt(np.mean(ref["out64"] ** 2)))
+    check_out(got[same], ref["out64"][same], f"{w.name} T={d.T}", rms)
+    return got
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "ragged_prefill", "ragged_skew"])
+def test_forward_small_workloads(lm, dev, name):
+    _full_small(lm, dev, get_workload(name))
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 31, 33, 64, 65, 255, 700])
+def test_forward_token_counts(lm, dev, T):
+    """Both tile paths, partial row tiles and single-token decode."""
+    _full_small(lm, dev, get_workload("tiny").with_T(T))
+
+
+@pytest.mark.parametrize("variant", ["k1", "kE", "noshared", "Is_ne_I", "wide_scales"])
+def test_forward_degenerate_cases(lm, dev, variant):
+    base = get_workload("ragged")
+    d = base.dims
+    if variant == "k1":
+        w = Workload("k1", 21, Dims(T=50, L=d.L, E=d.E, k=1, I=d.I, S=2, Is=d.Is))
+    elif variant == "kE":
+        w = Workload("kE", 22, Dims(T=20, L=160, E=12, k=12, I=96, S=1, Is=64))
+    elif variant == "noshared":
+        w = Workload("noshared", 23, Dims(T=40, L=d.L, E=d.E, k=d.k, I=d.I, S=0, Is=0))
+    elif variant == "Is_ne_I":
+        w = Workload("Is_ne_I", 24, Dims(T=90, L=288, E=20, k=4, I=64, S=3, Is=416))
+    else:
+        w = Workload("wide_scales", 25, Dims(T=30, L=256, E=16, k=4, I=128, S=1, Is=128),
+                     scales=("uniform", 100, 140))
+    _full_small(lm, dev, w)
+
+
+def test_forward_deterministic(lm, dev):
+    w = get_workload("ragged_prefill")
+    inp = gen_all(w)
+    dinp = upload(inp, dev)
+    a, _ = run_forward(lm, w, dinp)
+    b, _ = run_forward(lm, w, dinp)
+    assert np.array_equal(a, b)
+
+
+def test_forward_without_routing_outputs(lm, dev):
+    import torch
+    w = get_workload("tiny")
+    d = w.dims
+    inp = gen_all(w)
+    dinp = upload(inp, dev)
+    ref, _ = run_forward(lm, w, dinp)
+    out = torch.empty((d.T, d.L), dtype=torch.int16, device=dev)
+    ws = torch.empty(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
+    lm.forward(d, dinp["x"], dinp, False, None, out, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), ref)
+
+
+def test_zero_tokens_is_noop(lm, dev):
+    import torch
+    w = get_workload("tiny")
+    inp = gen_all(w)
+    dinp = upload(inp, dev)
+    d = Dims(T=0, L=w.dims.L, E=w.dims.E, k=w.dims.k, I=w.dims.I, S=w.dims.S, Is=w.dims.Is)
+    out = torch.zeros((1, d.L), dtype=torch.int16, device=dev)
+    ws = torch.empty(16, dtype=torch.uint8, device=dev)
+    lm.forward(d, dinp["x"], dinp, False, None, out, ws)
+    torch.cuda.synchronize()
+    assert int(out.abs().sum()) == 0
+
+
+# ----------------------------------------------------------------------------
+# Full K3-sized workloads: routing on every token, outputs on sampled tokens
+# ----------------------------------------------------------------------------
+
+def _full_size(lm, dev, name, n_sample):
+    import torch
+    w = get_workload(name)
+    d = w.dims
+    log(f"{name}: generating inputs (T={d.T}, E={d.E}, L={d.L}, I={d.I})")
+    inp = gen_all(w)
+    dinp = upload(inp, dev)
+    for key in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s"):
+        del inp[key]                      # experts are regenerated per expert below
+    log(f"{name}: running lmoe_forward")
+    got, r = run_forward(lm, w, dinp)
+    del dinp
+    torch.cuda.empty_cache()
+    if w.logits_given:
+        lg = inp["logits"]
+        _check_route_exact({"topk_idx": r["topk_idx"], "topk_w": r["topk_w"],
+                            "counts": r["counts"], "offsets": r["offsets"], "perm": r["perm"],
+                            "inv_perm": r["inv_perm"]}, lg, d.k, name)
+        same = np.ones(d.T, bool)
+        ref_lg = lg
+    else:
+        log(f"{name}: oracle logits")
+        ref_lg = O.router_logits(inp["x"], inp["router_w"])
+        same = check_routing_against_oracle(r["topk_idx"], r["logits"], ref_lg,
+                                            logits_bound(inp["x"], inp["router_w"]), d.k, name)
+        assert same.mean() >= 0.99
+    ref_idx = O.topk_select(ref_lg, d.k)
+    ref_w = O.softmax_selected(ref_lg, ref_idx)
+    rng = np.random.default_rng(99)
+    cand = np.nonzero(same)[0]
+    toks = list(rng.choice(cand, size=min(n_sample, cand.size), replace=False))
+    if w.logits_given:
+        tied = [t for t in cand if (ref_lg[t] == ref_lg[t].max()).sum() > d.k]
+        hot = int(np.argmax(r["counts"]))
+        hot_tok = [t for t in cand if hot in ref_idx[t]]
+        toks = sorted(set(toks[: max(1, n_sample - 2)]) | {tied[0], hot_tok[-1]})
+    toks = sorted(int(t) for t in toks)
+    log(f"{name}: oracle on tokens {toks}")
+    o64, _ = O.forward_tokens(inp["x"], ref_idx, ref_w, lambda e: gen_expert(w, e), inp,
+                              d.L, d.I, toks)
+    check_out(got[toks], o64, f"{name} sampled tokens")
+
+
+def test_full_decode(lm, dev):
+    _full_size(lm, dev, "decode", 1)
+
+
+def test_full_batched_decode(lm, dev):
+    _full_size(lm, dev, "batched_decode", 3)
+
+
+def test_full_prefill(lm, dev):
+    _full_size(lm, dev, "prefill", 3)
+
+
+def test_full_skewed(lm, dev):
+    _full_size(lm, dev, "skewed", 3)
