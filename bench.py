@@ -1,0 +1,429 @@
+#!/usr/bin/env python3
+"""Benchmark of the LatentMoE MXFP4 (w4a16) layer on one MI355X.
+
+One step = one lmoe_forward over one batch: router, top-k, grouping, routed
+experts, shared experts, combine. Headline: K3-shaped batch-1 decode (T=1,
+L=3584, E=896 resident experts, k=16, I=2048, two shared experts), reported as
+algorithmic HBM GB/s. Each decode step takes the next of 64 distinct tokens and
+the next of 4 device copies of the dense (router + shared) weights, so neither
+the routed experts nor the dense weights are served from the 256 MB last-level
+cache across steps. A same-token, same-weights figure is reported separately as
+"warm". The prefill chunk (T=4096) is measured too and reported as bf16 MFMA
+TFLOP/s in the "prefill" object.
+
+Algorithmic work (only what the layer must move or compute):
+  bytes = D*3*L*I*17/32 + S*3*L*Is*2 + 2*L*E + 4*T*L     (D = distinct experts)
+  flops = 6*L*I*T*k + 6*L*Is*T*S + 2*T*L*E
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+N_TOKENS = 64
+N_REPLICAS = 4
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+HOLD_MS = 30.0               # spin the GPU this long while the host enqueues
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# HIP events (ctypes on the HIP runtime torch already loaded)
+# ---------------------------------------------------------------------------
+class Hip:
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        return e.value
+
+    def record(self, ev: int, stream: int) -> None:
+        rc = self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        self.lib.hipEventSynchronize(ctypes.c_void_p(b))
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
+
+
+# ---------------------------------------------------------------------------
+# Work model
+# ---------------------------------------------------------------------------
+def algorithmic(d, D: int, logits_given: bool):
+    L, I, E, T, k, S, Is = d.L, d.I, d.E, d.T, d.k, d.S, d.Is
+    fp4_row = 17.0 / 32.0  # bytes per MXFP4 weight: half a byte + one byte per 32
+    st_bytes = {
+        "router": 0 if logits_given else 2 * L * E + 2 * T * L,
+        "topk": 0, "permute": 0,
+        "gate_up": D * 2 * I * L * fp4_row + 2 * T * L,
+        "down": D * L * I * fp4_row,
+        "shared_gate_up": S * 2 * Is * L * 2 + (2 * T * L if S else 0),
+        "shared_down": S * L * Is * 2,
+        "combine": 2 * T * L,
+    }
+    st_flops = {
+        "router": 0 if logits_given else 2 * T * L * E,
+        "topk": 0, "permute": 0,
+        "gate_up": 4 * L * I * T * k, "down": 2 * L * I * T * k,
+        "shared_gate_up": 4 * L * Is * T * S, "shared_down": 2 * L * Is * T * S,
+        "combine": 0,
+    }
+    total_bytes = D * 3 * L * I * fp4_row + S * 3 * L * Is * 2 + \
+        (0 if logits_given else 2 * L * E) + 4 * T * L
+    total_flops = 6 * L * I * T * k + 6 * L * Is * T * S + (0 if logits_given else 2 * T * L * E)
+    return total_bytes, total_flops, st_bytes, st_flops
+
+
+# Kernel that does each stage's work (names as rocprofv3 reports them).
+STAGE_KERNEL = {
+    "router": "router_kernel", "topk": "topk_kernel", "permute": "permute_kernel",
+    "combine": "combine_kernel",
+}
+
+
+def stage_kernel(stage: str, large: bool, sh_large: bool) -> str:
+    if stage in STAGE_KERNEL:
+        return STAGE_KERNEL[stage]
+    kind = {"gate_up": ("true", "true"), "down": ("false", "true"),
+            "shared_gate_up": ("true", "false"), "shared_down": ("false", "false")}[stage]
+    big = sh_large if stage.startswith("shared") else large
+    return f"gemm_{'large' if big else 'small'}_kernel<{kind[0]}, {kind[1]}>"
+
+
+def sources_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mxfp4_latent_mixture_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed PMC summary, or None
+    when absent or taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha") != sources_sha():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("traffic_bytes")
+
+
+# ---------------------------------------------------------------------------
+# Device setup
+# ---------------------------------------------------------------------------
+def upload(a: np.ndarray, dev):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(dev)
+
+
+def setup(name: str, dev, n_tokens: int = 1, replicas: int = 1):
+    from workloads import get_workload, gen_x, gen_router, gen_experts, gen_shared, gen_logits
+    w = get_workload(name)
+    t0 = time.time()
+    ex = gen_experts(w)
+    weights = {k: upload(v, dev) for k, v in ex.items()}
+    del ex
+    dense = []
+    rw = upload(gen_router(w), dev)
+    sh = {k: upload(v, dev) for k, v in gen_shared(w).items()}
+    for r in range(replicas):
+        dense.append({"router_w": rw if r == 0 else rw.clone(),
+                      **{k: (v if r == 0 else v.clone()) for k, v in sh.items()}})
+    xs = gen_x(w.with_T(max(w.dims.T, n_tokens)))
+    x = upload(xs, dev)
+    logits = upload(gen_logits(w), dev) if w.logits_given else None
+    log(f"{name}: inputs generated and resident in {time.time() - t0:.1f}s")
+    return w, weights, dense, x, logits
+
+
+def hold_cycles(hip, stream, ms_target: float) -> int:
+    """Argument of torch.cuda._sleep that spins the GPU for about ms_target."""
+    import torch
+    e0, e1 = hip.event(), hip.event()
+    n = 1 << 20
+    hip.record(e0, stream)
+    torch.cuda._sleep(n)
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    per = max(hip.elapsed_ms(e0, e1), 1e-3) / n
+    return int(ms_target / per)
+
+
+def routing_buffers(d, dev):
+    import torch
+    return {
+        "topk_idx": torch.empty((d.T, d.k), dtype=torch.int32, device=dev),
+        "counts": torch.empty((d.E,), dtype=torch.int32, device=dev),
+    }
+
+
+def run_case(lm, hip, name, dev, steps, warmup, rotate: bool, traced_steps: int):
+    """Time `steps` layer calls; returns a dict of measurements."""
+    import torch
+    n_tok = N_TOKENS if rotate else 1
+    reps = N_REPLICAS if rotate else 1
+    w, experts, dense, x_pool, logits = setup(name, dev, n_tok, reps)
+    d = w.dims
+    T = d.T
+    ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, d.L), dtype=torch.int16, device=dev)
+    rbuf = routing_buffers(d, dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def args(i):
+        if rotate:
+            xi = x_pool[i % n_tok: i % n_tok + 1]
+            wi = {**experts, **dense[i % reps]}
+        else:
+            xi = x_pool[:T]
+            wi = {**experts, **dense[0]}
+        r = {"logits": logits} if w.logits_given else None
+        return xi, wi, r
+
+    # distinct experts per step (untimed)
+    D = []
+    for i in range(n_tok):
+        xi, wi, r = args(i)
+        rr = dict(rbuf)
+        if r:
+            rr.update(r)
+        lm.forward(d, xi, wi, w.logits_given, rr, out, ws)
+        D.append(int((rbuf["counts"] > 0).sum().item()))
+    D_mean = float(np.mean(D))
+
+    pre = [args(i) for i in range(max(steps, warmup, traced_steps, 1))]
+    for i in range(warmup):
+        xi, wi, r = pre[i % len(pre)]
+        lm.forward(d, xi, wi, w.logits_given, r, out, ws)
+    torch.cuda.synchronize()
+
+    # The GPU is held in a spin kernel while the host enqueues, so the timed
+    # region measures back-to-back execution, not the host's launch rate.
+    sleep_cycles = hold_cycles(hip, stream, HOLD_MS)
+    e0, e1 = hip.event(), hip.event()
+
+    def timed(calls):
+        torch.cuda._sleep(sleep_cycles)
+        hip.record(e0, stream)
+        t = time.perf_counter()
+        for c in calls:
+            c()
+        enq = time.perf_counter() - t
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        return hip.elapsed_ms(e0, e1), enq * 1e3
+
+    def call(i):
+        xi, wi, r = pre[i]
+        return lambda: lm.forward(d, xi, wi, w.logits_given, r, out, ws)
+
+    tot_ms, enq_ms = timed([call(i) for i in range(steps)])
+    ms = tot_ms / steps
+    if enq_ms > HOLD_MS + tot_ms:
+        log(f"{name}: host enqueue ({enq_ms:.1f} ms) outran the hold; GPU time may include gaps")
+
+    warm_ms = None
+    if rotate:  # the same token and weights every step
+        warm_ms = timed([call(0) for _ in range(steps)])[0] / steps
+
+    # per-stage times from events the library records at stage boundaries
+    evs = [[hip.event() for _ in range(lm.NUM_STAGE_EVENTS)] for _ in range(traced_steps)]
+
+    def traced(i):
+        xi, wi, r = pre[i]
+        return lambda: lm.forward_traced(d, xi, wi, w.logits_given, r, out, ws, evs[i])
+
+    timed([traced(i) for i in range(traced_steps)])
+    stage_ms = {s: 0.0 for s in lm.STAGES[1:]}
+    for i in range(traced_steps):
+        for j in range(1, lm.NUM_STAGE_EVENTS):
+            stage_ms[lm.STAGES[j]] += hip.elapsed_ms(evs[i][j - 1], evs[i][j]) / traced_steps
+    traced_total = sum(stage_ms.values())
+
+    del experts, dense, x_pool, ws, out
+    torch.cuda.empty_cache()
+    return {"w": w, "D": D_mean, "ms": ms, "enqueue_ms": enq_ms / steps, "warm_ms": warm_ms,
+            "stage_ms": stage_ms, "traced_ms": traced_total}
+
+
+def roofline_for(res, bound: str):
+    d = res["w"].dims
+    logits_given = res["w"].logits_given
+    tb, tf, sb, sf = algorithmic(d, res["D"], logits_given)
+    R = d.T * d.k
+    large = (R / max(1, min(d.E, R))) > 8.0
+    sh_large = d.T > 64
+    if bound == "hbm":
+        stage = max((s for s in sb if sb[s] > 0), key=lambda s: res["stage_ms"][s])
+        achieved = sb[stage] / (res["stage_ms"][stage] * 1e-3) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+    else:
+        stage = max((s for s in sf if sf[s] > 0), key=lambda s: res["stage_ms"][s])
+        achieved = sf[stage] / (res["stage_ms"][stage] * 1e-3) / 1e12
+        peak, unit = BF16_PEAK_TFLOPS, "TFLOP/s"
+    kernel = stage_kernel(stage, large, sh_large)
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": measured_traffic(kernel),
+            "kernel": kernel, "stage": stage,
+            "kernel_us": round(res["stage_ms"][stage] * 1e3, 2),
+            "algorithmic_bytes": round(sb[stage]), "algorithmic_flops": round(sf[stage])}
+
+
+def cpu_baseline(n_tokens: int):
+    """The oracle as it stands, on decode tokens (same layer), host cores."""
+    import oracle as O
+    from workloads import get_workload, gen_x, gen_router, gen_expert, gen_shared
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    w = get_workload("decode")
+    d = w.dims
+    xs = gen_x(w.with_T(n_tokens))
+    rw = gen_router(w)
+    sh = gen_shared(w)
+    lg = O.router_logits(xs, rw)
+    idx = O.topk_select(lg, d.k)
+    need = sorted(set(idx.ravel().tolist()))
+    experts = {e: gen_expert(w, e) for e in need}
+    t0 = time.perf_counter()
+    for t in range(n_tokens):
+        lgt = O.router_logits(xs[t:t + 1], rw)
+        it = O.topk_select(lgt, d.k)
+        wt = O.softmax_selected(lgt, it)
+        O.forward_tokens(xs[t:t + 1], it, wt, lambda e: experts[e], sh, d.L, d.I)
+    sec = time.perf_counter() - t0
+    tb, _, _, _ = algorithmic(d, d.k, False)
+    return {"value": round(tb * n_tokens / sec / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{n_tokens} decode tokens (T=1 each, 16 experts + 2 shared, float64 "
+                      f"numpy oracle), {sec:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=3)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one device copy of this size (PMC calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this layer is measured on a single MI355X "
+              f"(asked for --gpus {args.gpus}); multi-GPU sharding is not built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mxfp4_latent_mixture_amd as lm
+    dev = torch.device("cuda:0")
+    hip = Hip()
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {n} bytes done")
+        del a, b
+
+    dec = run_case(lm, hip, "decode", dev, args.steps, args.warmup, rotate=True,
+                   traced_steps=min(args.steps, 50))
+    d = dec["w"].dims
+    tb, tf, _, _ = algorithmic(d, dec["D"], False)
+    value = tb / (dec["ms"] * 1e-3) / 1e9
+    log(f"decode: {dec['ms'] * 1e3:.1f} us/step, {value:.0f} GB/s; warm "
+        f"{dec['warm_ms'] * 1e3:.1f} us; stages {({k: round(v * 1e3, 1) for k, v in dec['stage_ms'].items()})}")
+    result = {
+        "metric": "MoE-layer HBM GB/s at T=1 (K3 LatentMoE decode, MXFP4 w4a16)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "K3 LatentMoE decode: T=1, L=3584, E=896 resident MXFP4 experts, "
+                               "k=16, I=2048, 2 bf16 shared experts (Is=2048), seed 1; "
+                               "64 rotating tokens, 4 rotating copies of router+shared weights",
+                   "tokens": d.T, "latent": d.L, "experts": d.E, "top_k": d.k,
+                   "intermediate": d.I, "shared": d.S},
+        "roofline": roofline_for(dec, "hbm"),
+        "algorithmic_bytes_per_step": round(tb),
+        "warm_gb_s": round(tb / (dec["warm_ms"] * 1e-3) / 1e9, 2),
+        "stage_us": {k: round(v * 1e3, 2) for k, v in dec["stage_ms"].items()},
+    }
+    if not args.no_prefill:
+        pf = run_case(lm, hip, "prefill", dev, args.prefill_steps, 2, rotate=False,
+                      traced_steps=min(args.prefill_steps, 5))
+        pd = pf["w"].dims
+        ptb, ptf, _, _ = algorithmic(pd, pf["D"], False)
+        tfl = ptf / (pf["ms"] * 1e-3) / 1e12
+        log(f"prefill: {pf['ms']:.3f} ms/step, {tfl:.1f} TFLOP/s; stages "
+            f"{({k: round(v * 1e3, 1) for k, v in pf['stage_ms'].items()})}")
+        result["prefill"] = {
+            "metric": "MoE-layer bf16 MFMA TFLOP/s at T=4096",
+            "value": round(tfl, 2), "unit": "TFLOP/s", "ms_per_step": round(pf["ms"], 4),
+            "steps": args.prefill_steps, "frac_of_peak": round(tfl / BF16_PEAK_TFLOPS, 4),
+            "gb_s": round(ptb / (pf["ms"] * 1e-3) / 1e9, 1),
+            "workload": "K3 LatentMoE prefill chunk: T=4096, same layer, seed 3",
+            "roofline": roofline_for(pf, "mfma"),
+            "stage_us": {k: round(v * 1e3, 1) for k, v in pf["stage_ms"].items()},
+        }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

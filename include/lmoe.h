@@ -116,7 +116,10 @@ typedef struct lmoe_routing {
 } lmoe_routing;
 
 /* Bytes of device workspace lmoe_route / lmoe_forward need for these
- * dimensions (the same value serves both). Returns 0 for invalid dims. */
+ * dimensions (the same value serves both). Returns 0 for invalid dims.
+ * The workspace must be zero-filled before its first use; every call leaves
+ * its first 32 KiB (the single-token decode kernel's dependency counters)
+ * zeroed again, so a workspace can be reused across calls and dimensions. */
 size_t lmoe_workspace_bytes(const lmoe_dims* dims);
 
 /* Routing only: router logits (unless logits_given), top-k selection with
@@ -140,6 +143,50 @@ int lmoe_route(const lmoe_dims* dims, const uint16_t* x, const uint16_t* router_
 int lmoe_forward(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights* w,
                  int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
                  size_t ws_bytes, void* stream);
+
+/* Stage boundaries recorded by lmoe_forward_traced. Event i is recorded on
+ * the stream right after stage i has been enqueued (event 0 before the first
+ * one); a stage that does not run for these arguments (the router when logits
+ * are given, the shared experts when S == 0) records its event right after the
+ * previous one. Stage i's time is the elapsed time between events i-1 and i.
+ * When one kernel runs several stages (the single-token decode path, see
+ * lmoe_path_name), all their events are recorded after it, so its whole time
+ * is attributed to the first of them.
+ * Per-stage attribution follows the per-opcode rate attribution of
+ * infervisor.ai "Bringing up Kimi-K3 on day zero", "The 28.9 ms, taken apart". */
+enum {
+  LMOE_STAGE_BEGIN = 0,
+  LMOE_STAGE_ROUTER = 1,
+  LMOE_STAGE_TOPK = 2,
+  LMOE_STAGE_PERMUTE = 3,
+  LMOE_STAGE_GATEUP = 4,
+  LMOE_STAGE_DOWN = 5,
+  LMOE_STAGE_SHARED_GATEUP = 6,
+  LMOE_STAGE_SHARED_DOWN = 7,
+  LMOE_STAGE_COMBINE = 8,
+  LMOE_NUM_STAGE_EVENTS = 9
+};
+
+/* lmoe_forward, additionally recording the LMOE_NUM_STAGE_EVENTS events
+ * (hipEvent_t handles created by the caller, host array `events`) at the stage
+ * boundaries above. Same arguments, results and errors as lmoe_forward, plus
+ * LMOE_ERR_NULL when events or any of its entries is NULL. */
+int lmoe_forward_traced(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights* w,
+                        int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
+                        size_t ws_bytes, void* stream, void* const* events);
+
+/* Short name of stage i (0 <= i < LMOE_NUM_STAGE_EVENTS), else "?". */
+const char* lmoe_stage_name(int stage);
+
+/* Which implementation lmoe_forward uses for these dimensions (static
+ * string): "fused_decode" (T == 1 with computed logits: the whole layer in
+ * one persistent kernel), "grouped_small" (expert groups of at most 16 rows)
+ * or "grouped_large" (groups of up to 128 rows), "invalid" for bad dims.
+ * Decode streams the active weights once per token (infervisor.ai "Bringing
+ * up Kimi-K3 on day zero", "The roofline"); the grouped forms follow the
+ * expert-sorted tiling of dev48.org "Kimi K3 on AMD Instinct GPUs with
+ * TokenSpeed", section 4.1. */
+const char* lmoe_path_name(const lmoe_dims* dims, int logits_given);
 
 /* Test hook: dequantise an MXFP4 matrix with the same device routine the
  * expert kernels use.

@@ -32,8 +32,14 @@ LMOE_ERR_ALIGN = 3
 LMOE_ERR_WORKSPACE = 4
 LMOE_ERR_HIP = 5
 
-EXPORTS = ("lmoe_workspace_bytes", "lmoe_route", "lmoe_forward",
-           "lmoe_debug_dequant_mxfp4", "lmoe_status_string")
+EXPORTS = ("lmoe_workspace_bytes", "lmoe_route", "lmoe_forward", "lmoe_forward_traced",
+           "lmoe_stage_name", "lmoe_path_name", "lmoe_debug_dequant_mxfp4",
+           "lmoe_status_string")
+
+# Stage boundaries recorded by forward_traced (LMOE_STAGE_* in lmoe.h).
+STAGES = ("begin", "router", "topk", "permute", "gate_up", "down", "shared_gate_up",
+          "shared_down", "combine")
+NUM_STAGE_EVENTS = len(STAGES)
 
 
 class lmoe_dims(ctypes.Structure):
@@ -72,6 +78,14 @@ def _load() -> ctypes.CDLL:
     lib.lmoe_forward.argtypes = [dp, vp, ctypes.POINTER(lmoe_weights), ctypes.c_int,
                                  ctypes.POINTER(lmoe_routing), vp, vp, sz, vp]
     lib.lmoe_forward.restype = ctypes.c_int
+    lib.lmoe_forward_traced.argtypes = [dp, vp, ctypes.POINTER(lmoe_weights), ctypes.c_int,
+                                        ctypes.POINTER(lmoe_routing), vp, vp, sz, vp,
+                                        ctypes.POINTER(vp)]
+    lib.lmoe_forward_traced.restype = ctypes.c_int
+    lib.lmoe_path_name.argtypes = [dp, ctypes.c_int]
+    lib.lmoe_path_name.restype = ctypes.c_char_p
+    lib.lmoe_stage_name.argtypes = [ctypes.c_int]
+    lib.lmoe_stage_name.restype = ctypes.c_char_p
     lib.lmoe_debug_dequant_mxfp4.argtypes = [vp, vp, i32, i32, vp, vp]
     lib.lmoe_debug_dequant_mxfp4.restype = ctypes.c_int
     lib.lmoe_status_string.argtypes = [ctypes.c_int]
@@ -154,6 +168,33 @@ def forward(dims, x, weights: Mapping, logits_given: bool, routing: Optional[Map
                              ws.numel() * ws.element_size() if ws is not None else 0,
                              _stream(stream))
     _check("lmoe_forward", code)
+
+
+def forward_traced(dims, x, weights: Mapping, logits_given: bool, routing: Optional[Mapping], out,
+                   ws, events, stream=None) -> None:
+    """forward() that also records NUM_STAGE_EVENTS caller-created hipEvent_t
+    handles (ints) at the stage boundaries listed in STAGES."""
+    d = _dims(dims)
+    r = _routing(routing)
+    w = _weights(weights)
+    if len(events) != NUM_STAGE_EVENTS:
+        raise ValueError(f"need {NUM_STAGE_EVENTS} events")
+    ev = (ctypes.c_void_p * NUM_STAGE_EVENTS)(*[int(e) for e in events])
+    code = _lib.lmoe_forward_traced(ctypes.byref(d), _ptr(x), ctypes.byref(w),
+                                    int(bool(logits_given)),
+                                    ctypes.byref(r) if r is not None else None, _ptr(out),
+                                    _ptr(ws), ws.numel() * ws.element_size() if ws is not None
+                                    else 0, _stream(stream), ev)
+    _check("lmoe_forward_traced", code)
+
+
+def path_name(dims, logits_given: bool = False) -> str:
+    d = _dims(dims)
+    return _lib.lmoe_path_name(ctypes.byref(d), int(bool(logits_given))).decode()
+
+
+def stage_name(i: int) -> str:
+    return _lib.lmoe_stage_name(int(i)).decode()
 
 
 def debug_dequant_mxfp4(q, s, rows: int, K: int, out, stream=None) -> None:

@@ -39,6 +39,8 @@ Plan make_plan(const lmoe_dims& d) {
   const double avg = (double)p.R / (double)std::max(1, std::min(d.E, p.R));
   p.rows_per_tile = (avg <= 8.0) ? kSmallRows : kLargeRows;
   p.max_tiles = std::min(d.E, p.R) + p.R / p.rows_per_tile;
+  p.fused_decode = d.T == 1 && d.L <= kDecodeMaxWidth && d.I <= kDecodeMaxWidth &&
+                   d.S * d.Is <= kDecodeMaxWidth;
   return p;
 }
 
@@ -53,6 +55,7 @@ Workspace carve_workspace(const Plan& p, void* base) {
     return r;
   };
   const size_t T = d.T, E = d.E, R = p.R, L = d.L, I = d.I, S = d.S, Is = d.Is;
+  w.ctr = reinterpret_cast<int32_t*>(take(kCtrBytes));
   w.part = reinterpret_cast<float*>(take((size_t)p.router.ks * T * E * 4));
   w.idx = reinterpret_cast<int32_t*>(take(R * 4));
   w.w = reinterpret_cast<float*>(take(R * 4));
@@ -66,6 +69,15 @@ Workspace carve_workspace(const Plan& p, void* base) {
   w.h_sh = reinterpret_cast<uint16_t*>(take(S * T * Is * 2));
   w.y = reinterpret_cast<float*>(take(R * L * 4));
   w.y_sh = reinterpret_cast<float*>(take(S * T * L * 4));
+  if (p.fused_decode) {
+    DecodeArgs da;
+    make_decode_args(p, da);
+    w.dpart = reinterpret_cast<float*>(take((size_t)da.nks * E * 4));
+    w.dh = reinterpret_cast<uint16_t*>(take((size_t)d.k * I * 2));
+    w.dhsh = reinterpret_cast<uint16_t*>(take(S * Is * 2));
+    w.dy = reinterpret_cast<float*>(take((size_t)d.k * L * 4));
+    w.dysh = reinterpret_cast<float*>(take(L * 4));
+  }
   w.bytes = off;
   return w;
 }
@@ -89,7 +101,8 @@ struct Routing {
 };
 
 static int run_route(const Plan& p, const Workspace& ws, const uint16_t* x, const uint16_t* wr,
-                     int logits_given, const lmoe_routing* r, Routing* out, hipStream_t s) {
+                     int logits_given, const lmoe_routing* r, Routing* out, hipStream_t s,
+                     const hipEvent_t* ev) {
   Routing rt;
   rt.idx = (r && r->topk_idx) ? r->topk_idx : ws.idx;
   rt.w = (r && r->topk_w) ? r->topk_w : ws.w;
@@ -97,7 +110,8 @@ static int run_route(const Plan& p, const Workspace& ws, const uint16_t* x, cons
   rt.offsets = (r && r->offsets) ? r->offsets : ws.offsets;
   rt.perm = (r && r->perm) ? r->perm : ws.perm;
   rt.inv = (r && r->inv_perm) ? r->inv_perm : ws.inv;
-  hipError_t e;
+  hipError_t e = record_stage(ev, LMOE_STAGE_BEGIN, s);
+  if (e != hipSuccess) return LMOE_ERR_HIP;
   const float* part;
   int ks;
   float* logits_out = nullptr;
@@ -111,11 +125,53 @@ static int run_route(const Plan& p, const Workspace& ws, const uint16_t* x, cons
     ks = p.router.ks;
     logits_out = r ? r->logits : nullptr;
   }
+  if (record_stage(ev, LMOE_STAGE_ROUTER, s) != hipSuccess) return LMOE_ERR_HIP;
   e = launch_topk(p, part, ks, logits_out, rt.idx, rt.w, s);
-  if (e != hipSuccess) return LMOE_ERR_HIP;
+  if (e != hipSuccess || record_stage(ev, LMOE_STAGE_TOPK, s) != hipSuccess) return LMOE_ERR_HIP;
   e = launch_permute(p, rt.idx, rt.counts, rt.offsets, rt.perm, rt.inv, ws.tiles, ws.ntiles, s);
-  if (e != hipSuccess) return LMOE_ERR_HIP;
+  if (e != hipSuccess || record_stage(ev, LMOE_STAGE_PERMUTE, s) != hipSuccess)
+    return LMOE_ERR_HIP;
   *out = rt;
+  return LMOE_OK;
+}
+
+// T == 1: the whole layer as one persistent kernel. Stage events: BEGIN
+// before the kernel, every other stage's event after it (the fused stages'
+// time is attributed to the first of them, the router).
+static int run_fused_decode(const Plan& p, const Workspace& ws, const uint16_t* x,
+                            const lmoe_weights& w, const lmoe_routing* r, uint16_t* out,
+                            hipStream_t s, const hipEvent_t* ev) {
+  DecodeArgs a;
+  make_decode_args(p, a);
+  a.x = x;
+  a.wr = w.router_w;
+  a.gq = w.gate_q;
+  a.gs = w.gate_s;
+  a.uq = w.up_q;
+  a.us = w.up_s;
+  a.dq = w.down_q;
+  a.ds = w.down_s;
+  a.shg = w.sh_gate;
+  a.shu = w.sh_up;
+  a.shd = w.sh_down;
+  a.logits_out = r ? r->logits : nullptr;
+  a.idx = (r && r->topk_idx) ? r->topk_idx : ws.idx;
+  a.w = (r && r->topk_w) ? r->topk_w : ws.w;
+  a.counts = (r && r->counts) ? r->counts : ws.counts;
+  a.offsets = (r && r->offsets) ? r->offsets : ws.offsets;
+  a.perm = (r && r->perm) ? r->perm : ws.perm;
+  a.inv = (r && r->inv_perm) ? r->inv_perm : ws.inv;
+  a.out = out;
+  a.ctr = ws.ctr;
+  a.part = ws.dpart;
+  a.h = ws.dh;
+  a.hsh = ws.dhsh;
+  a.y = ws.dy;
+  a.ysh = ws.dysh;
+  if (record_stage(ev, LMOE_STAGE_BEGIN, s) != hipSuccess) return LMOE_ERR_HIP;
+  if (launch_decode(a, s) != hipSuccess) return LMOE_ERR_HIP;
+  for (int i = LMOE_STAGE_ROUTER; i < LMOE_NUM_STAGE_EVENTS; ++i)
+    if (record_stage(ev, i, s) != hipSuccess) return LMOE_ERR_HIP;
   return LMOE_OK;
 }
 
@@ -168,12 +224,13 @@ extern "C" int lmoe_route(const lmoe_dims* dims, const uint16_t* x, const uint16
   Workspace w = carve_workspace(p, ws);
   if (ws_bytes < w.bytes) return LMOE_ERR_WORKSPACE;
   Routing rt;
-  return run_route(p, w, x, router_w, logits_given, r, &rt, static_cast<hipStream_t>(stream));
+  return run_route(p, w, x, router_w, logits_given, r, &rt, static_cast<hipStream_t>(stream),
+                   nullptr);
 }
 
-extern "C" int lmoe_forward(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights* wts,
-                            int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
-                            size_t ws_bytes, void* stream) {
+static int forward_impl(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights* wts,
+                        int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
+                        size_t ws_bytes, void* stream, const hipEvent_t* ev) {
   if (!dims || !wts) return LMOE_ERR_NULL;
   if (!dims_ok(*dims)) return LMOE_ERR_SHAPE;
   int st = check_routing(r, logits_given);
@@ -193,11 +250,45 @@ extern "C" int lmoe_forward(const lmoe_dims* dims, const uint16_t* x, const lmoe
   Workspace wsp = carve_workspace(p, ws);
   if (ws_bytes < wsp.bytes) return LMOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.fused_decode && !logits_given) return run_fused_decode(p, wsp, x, w, r, out, s, ev);
   Routing rt;
-  st = run_route(p, wsp, x, w.router_w, logits_given, r, &rt, s);
+  st = run_route(p, wsp, x, w.router_w, logits_given, r, &rt, s, ev);
   if (st) return st;
-  hipError_t e = launch_experts(p, x, w, wsp, rt.perm, rt.inv, rt.w, out, s);
+  hipError_t e = launch_experts(p, x, w, wsp, rt.perm, rt.inv, rt.w, out, s, ev);
   return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
+}
+
+extern "C" int lmoe_forward(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights* wts,
+                            int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
+                            size_t ws_bytes, void* stream) {
+  return forward_impl(dims, x, wts, logits_given, r, out, ws, ws_bytes, stream, nullptr);
+}
+
+extern "C" int lmoe_forward_traced(const lmoe_dims* dims, const uint16_t* x,
+                                   const lmoe_weights* wts, int logits_given,
+                                   const lmoe_routing* r, uint16_t* out, void* ws,
+                                   size_t ws_bytes, void* stream, void* const* events) {
+  if (!events) return LMOE_ERR_NULL;
+  hipEvent_t ev[LMOE_NUM_STAGE_EVENTS];
+  for (int i = 0; i < LMOE_NUM_STAGE_EVENTS; ++i) {
+    if (!events[i]) return LMOE_ERR_NULL;
+    ev[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  return forward_impl(dims, x, wts, logits_given, r, out, ws, ws_bytes, stream, ev);
+}
+
+extern "C" const char* lmoe_path_name(const lmoe_dims* dims, int logits_given) {
+  if (!dims || !dims_ok(*dims)) return "invalid";
+  Plan p = make_plan(*dims);
+  if (p.fused_decode && !logits_given) return "fused_decode";
+  return p.rows_per_tile == kSmallRows ? "grouped_small" : "grouped_large";
+}
+
+extern "C" const char* lmoe_stage_name(int stage) {
+  static const char* names[LMOE_NUM_STAGE_EVENTS] = {
+      "begin", "router", "topk", "permute", "gate_up", "down", "shared_gate_up",
+      "shared_down", "combine"};
+  return (stage >= 0 && stage < LMOE_NUM_STAGE_EVENTS) ? names[stage] : "?";
 }
 
 extern "C" int lmoe_debug_dequant_mxfp4(const uint8_t* q, const uint8_t* s, int32_t rows,

@@ -83,13 +83,32 @@ __device__ __forceinline__ int64_t out_row(const GemmArgs& a, const TileInfo& ti
 }
 
 // ---------------------------------------------------------------------------
-// Small groups (<= 16 rows): one 16x16 output tile per workgroup. The four
-// waves x four lane groups split K into 16 contiguous slices of MX blocks;
-// each wave's MFMA already sums its four slices, and the four waves' partial
-// tiles are added in LDS in a fixed order.
+// Small groups (<= 16 rows): one 16-row x 16-column output tile per
+// workgroup, K split over the four waves in contiguous quarters. In a wave
+// iteration the four lane groups take adjacent runs of U MX blocks, so one
+// wave-wide load covers 4*U*16 contiguous bytes of every weight row it touches
+// (whole cache lines, nothing fetched twice). The next iteration's weight
+// loads are issued before the current iteration's MFMAs. The four waves'
+// partial tiles are added in LDS in a fixed order.
 // ---------------------------------------------------------------------------
+template <bool FP4>
+struct SmallOps;
+
+template <>
+struct SmallOps<true> {  // two MX blocks of codes and their exponents per matrix
+  u32x4_t c0[2], c1[2];
+  uint32_t s0[2], s1[2];
+};
+
+template <>
+struct SmallOps<false> {  // one 32-value block of bf16 weights per matrix
+  u32x4_t b0[4], b1[4];
+};
+
 template <bool GLU, bool FP4>
 __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
+  constexpr int U = FP4 ? 2 : 1;   // MX blocks per lane per iteration
+  constexpr int SPAN = 4 * U;      // blocks per wave iteration
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
@@ -101,10 +120,9 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
   const int K = a.K, N = a.N;
   const int n0 = nt * 16;
   const int nblk = K / 32;
-  const int slot = wave * 4 + grp;
-  const int b_lo = (slot * nblk) / 16;
-  const int b_hi = ((slot + 1) * nblk) / 16;
-  const int iters = (nblk + 15) / 16;
+  const int bw_lo = (wave * nblk) / 4;
+  const int bw_hi = ((wave + 1) * nblk) / 4;
+  const int iters = (bw_hi - bw_lo + SPAN - 1) / SPAN;
 
   const bool mvalid = col < ti.cnt;
   const uint16_t* ap = mvalid ? act_row(a, ti, col) : a.act;
@@ -130,39 +148,67 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
     if (GLU) b1r = a.b1 + ti.e * a.b_estride + (int64_t)nn * K;
   }
 
-  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f};
-  f32x4_t acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int it = 0; it < iters; ++it) {
-    const int blk = b_lo + it;
-    const bool kv = blk < b_hi;
-    const bool wv = kv && nvalid;
-    const bool av_ok = kv && mvalid;
-    u32x4_t c0 = zero16(), c1 = zero16();
-    float sc0 = 1.f, sc1 = 1.f;
-    if (FP4) {
-      if (wv) {
-        c0 = load16(q0r + blk * 16);
-        sc0 = e8m0_to_f32(s0r[blk]);
+  // first block of this lane in iteration it
+  auto first_blk = [&](int it) { return bw_lo + it * SPAN + grp * U; };
+
+  auto load_ops = [&](int it, SmallOps<FP4>& o) {
+    const int b0 = first_blk(it);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int blk = b0 + u;
+      const bool ok = nvalid && it < iters && blk < bw_hi;
+      if constexpr (FP4) {
+        o.c0[u] = ok ? load16(q0r + blk * 16) : zero16();
+        o.s0[u] = ok ? (uint32_t)s0r[blk] : 127u;
         if (GLU) {
-          c1 = load16(q1r + blk * 16);
-          sc1 = e8m0_to_f32(s1r[blk]);
+          o.c1[u] = ok ? load16(q1r + blk * 16) : zero16();
+          o.s1[u] = ok ? (uint32_t)s1r[blk] : 127u;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          o.b0[q] = ok ? load16(b0r + blk * 32 + q * 8) : zero16();
+          if (GLU) o.b1[q] = ok ? load16(b1r + blk * 32 + q * 8) : zero16();
         }
       }
     }
+  };
+
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc1 = {0.f, 0.f, 0.f, 0.f};
+  SmallOps<FP4> cur, nxt;
+  load_ops(0, cur);
+  for (int it = 0; it < iters; ++it) {
+    load_ops(it + 1, nxt);
+    const int b0 = first_blk(it);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8_t av = as_bf16x8(av_ok ? load16(ap + blk * 32 + s * 8) : zero16());
-      bf16x8_t bv0, bv1;
-      if (FP4) {
-        bv0 = dequant8(c0[s], sc0);
-        if (GLU) bv1 = dequant8(c1[s], sc1);
-      } else {
-        bv0 = as_bf16x8(wv ? load16(b0r + blk * 32 + s * 8) : zero16());
-        if (GLU) bv1 = as_bf16x8(wv ? load16(b1r + blk * 32 + s * 8) : zero16());
+    for (int u = 0; u < U; ++u) {
+      const int blk = b0 + u;
+      const bool aok = mvalid && blk < bw_hi;
+      u32x4_t xv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xv[q] = aok ? load16(ap + blk * 32 + q * 8) : zero16();
+      float sc0 = 1.f, sc1 = 1.f;
+      if constexpr (FP4) {
+        sc0 = e8m0_to_f32(cur.s0[u]);
+        if (GLU) sc1 = e8m0_to_f32(cur.s1[u]);
       }
-      acc0 = mfma16(av, bv0, acc0);
-      if (GLU) acc1 = mfma16(av, bv1, acc1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x8_t bv0, bv1;
+        if constexpr (FP4) {
+          bv0 = dequant8(cur.c0[u][q], sc0);
+          if (GLU) bv1 = dequant8(cur.c1[u][q], sc1);
+        } else {
+          bv0 = as_bf16x8(cur.b0[q]);
+          if (GLU) bv1 = as_bf16x8(cur.b1[q]);
+        }
+        const bf16x8_t av = as_bf16x8(xv[q]);
+        acc0 = mfma16(av, bv0, acc0);
+        if (GLU) acc1 = mfma16(av, bv1, acc1);
+      }
     }
+    cur = nxt;
   }
 
   __shared__ f32x4_t red[2][4][64];
@@ -359,14 +405,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int t = (int)(id / L4);
   const int l = (int)(id % L4) * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const int r = t * k + j;
-    const float wj = w[r];
-    const float4 v = *reinterpret_cast<const float4*>(y + (int64_t)inv[r] * L + l);
-    acc.x = fmaf(wj, v.x, acc.x);
-    acc.y = fmaf(wj, v.y, acc.y);
-    acc.z = fmaf(wj, v.z, acc.z);
-    acc.w = fmaf(wj, v.w, acc.w);
+  // routes in groups of 8: indices and weights first, then the partial rows,
+  // so the loads of a group are in flight together
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int pos[8];
+    float wj[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      pos[u] = j < k ? inv[t * k + j] : 0;
+      wj[u] = j < k ? w[t * k + j] : 0.f;
+    }
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = (j0 + u < k) ? *reinterpret_cast<const float4*>(y + (int64_t)pos[u] * L + l)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (j0 + u < k) {
+        acc.x = fmaf(wj[u], v[u].x, acc.x);
+        acc.y = fmaf(wj[u], v[u].y, acc.y);
+        acc.z = fmaf(wj[u], v[u].z, acc.z);
+        acc.w = fmaf(wj[u], v[u].w, acc.w);
+      }
+    }
   }
   for (int s = 0; s < S; ++s) {
     const float4 v = *reinterpret_cast<const float4*>(ysh + ((int64_t)s * T + t) * L + l);
@@ -417,7 +480,8 @@ static hipError_t launch_gemm(const GemmArgs& a0, bool large, int row_tiles, int
 
 hipError_t launch_experts(const Plan& p, const uint16_t* x, const lmoe_weights& w,
                           const Workspace& ws, const int32_t* perm, const int32_t* inv,
-                          const float* topk_w, uint16_t* out, hipStream_t s) {
+                          const float* topk_w, uint16_t* out, hipStream_t s,
+                          const hipEvent_t* ev) {
   const lmoe_dims& d = p.d;
   const bool large = p.rows_per_tile == kLargeRows;
   hipError_t err;
@@ -441,6 +505,7 @@ hipError_t launch_experts(const Plan& p, const uint16_t* x, const lmoe_weights& 
     a.out_stride = d.I;
     err = launch_gemm<true, true>(a, large, p.max_tiles, 1, s);
     if (err != hipSuccess) return err;
+    if ((err = record_stage(ev, LMOE_STAGE_GATEUP, s)) != hipSuccess) return err;
   }
   {  // routed down
     GemmArgs a = {};
@@ -458,6 +523,7 @@ hipError_t launch_experts(const Plan& p, const uint16_t* x, const lmoe_weights& 
     a.out_stride = d.L;
     err = launch_gemm<false, true>(a, large, p.max_tiles, 1, s);
     if (err != hipSuccess) return err;
+    if ((err = record_stage(ev, LMOE_STAGE_DOWN, s)) != hipSuccess) return err;
   }
   if (d.S > 0) {
     const bool sh_large = d.T > 64;
@@ -479,6 +545,7 @@ hipError_t launch_experts(const Plan& p, const uint16_t* x, const lmoe_weights& 
       err = launch_gemm<true, false>(a, sh_large, row_tiles, d.S, s);
       if (err != hipSuccess) return err;
     }
+    if ((err = record_stage(ev, LMOE_STAGE_SHARED_GATEUP, s)) != hipSuccess) return err;
     {  // shared down
       GemmArgs a = {};
       a.act = ws.h_sh;
@@ -494,6 +561,10 @@ hipError_t launch_experts(const Plan& p, const uint16_t* x, const lmoe_weights& 
       err = launch_gemm<false, false>(a, sh_large, row_tiles, d.S, s);
       if (err != hipSuccess) return err;
     }
+    if ((err = record_stage(ev, LMOE_STAGE_SHARED_DOWN, s)) != hipSuccess) return err;
+  } else {
+    if ((err = record_stage(ev, LMOE_STAGE_SHARED_GATEUP, s)) != hipSuccess) return err;
+    if ((err = record_stage(ev, LMOE_STAGE_SHARED_DOWN, s)) != hipSuccess) return err;
   }
   {
     const int64_t n = (int64_t)d.T * (d.L / 4);
@@ -501,6 +572,8 @@ hipError_t launch_experts(const Plan& p, const uint16_t* x, const lmoe_weights& 
     hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, ws.y, ws.y_sh, inv, topk_w,
                        d.T, d.k, d.L, d.S, out);
     err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    err = record_stage(ev, LMOE_STAGE_COMBINE, s);
   }
   return err;
 }

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/lmoe.h"
 
 namespace lmoe {
@@ -20,8 +22,25 @@ struct RouterPlan {
   int steps_per;   // 32-wide K steps per split
 };
 
+// Counter block at the start of every workspace (int32 slots, each counter on
+// its own 64- or 128-byte line). Only the single-token decode kernel uses it;
+// it must be zero when that kernel starts and is left zeroed when it ends.
+constexpr int kQueues = 8;        // ticket queues: item i is in queue i % kQueues
+constexpr int kCtrTicket = 0;     // + 32 * queue
+constexpr int kCtrExit = 256;
+constexpr int kCtrRouter = 288;
+constexpr int kCtrTopk = 320;
+constexpr int kCtrShared = 352;   // + 32 * (item % kQueues)
+constexpr int kCtrError = 608;
+constexpr int kCtrRoute = 640;    // + 16 * route, route < 32
+constexpr int kCtrBlock = 1152;   // + 16 * block, block < 256 (64-row blocks of L)
+constexpr size_t kCtrBytes = 32768;
+// The single-token decode kernel keeps the token and one A row in LDS.
+constexpr int kDecodeMaxWidth = 4096;
+
 struct Plan {
   lmoe_dims d;
+  bool fused_decode;  // T == 1: the whole layer in one persistent kernel
   int R;              // T * k routes
   RouterPlan router;
   int rows_per_tile;  // kSmallRows or kLargeRows
@@ -29,6 +48,7 @@ struct Plan {
 };
 
 struct Workspace {
+  int32_t* ctr;       // counter block (kCtrBytes)
   float* part;        // [ks][T][E] router partial sums
   int32_t* idx;       // [R]
   float* w;           // [R]
@@ -42,7 +62,36 @@ struct Workspace {
   uint16_t* h_sh;     // [S][T][Is] bf16
   float* y;           // [R][L] fp32 route partials, sorted route order
   float* y_sh;        // [S][T][L] fp32
+  // single-token decode
+  float* dpart;       // [nks][E] partial logits
+  uint16_t* dh;       // [k][I] bf16
+  uint16_t* dhsh;     // [S][Is] bf16
+  float* dy;          // [k][L]
+  float* dysh;        // [L]
   size_t bytes;       // total bytes needed
+};
+
+struct DecodeArgs {
+  const uint16_t* x;   // [L] bf16
+  const uint16_t* wr;  // [L][E] bf16
+  const uint8_t *gq, *gs, *uq, *us, *dq, *ds;
+  const uint16_t *shg, *shu, *shd;
+  int L, E, k, I, S, Is;
+  float* logits_out;   // optional
+  int32_t* idx;
+  float* w;
+  int32_t *counts, *offsets, *perm, *inv;
+  uint16_t* out;
+  int32_t* ctr;
+  float* part;
+  uint16_t* h;
+  uint16_t* hsh;
+  float* y;
+  float* ysh;
+  int nks, rk, neg;
+  int n_router, n_shgu, n_gu, n_shd, n_dn;
+  int t_shgu, t_gu, t_shd, t_dn, t_total;
+  int gu_per_route, dn_per_route;
 };
 
 Plan make_plan(const lmoe_dims& d);
@@ -58,9 +107,20 @@ hipError_t launch_permute(const Plan& p, const int32_t* idx, int32_t* counts, in
                           hipStream_t s);
 
 // ---- kernel launchers (experts.hip) ----
+// ev: optional stage events (LMOE_NUM_STAGE_EVENTS entries), recorded after
+// each stage.
 hipError_t launch_experts(const Plan& p, const uint16_t* x, const lmoe_weights& w,
                           const Workspace& ws, const int32_t* perm, const int32_t* inv,
-                          const float* topk_w, uint16_t* out, hipStream_t s);
+                          const float* topk_w, uint16_t* out, hipStream_t s,
+                          const hipEvent_t* ev);
+
+inline hipError_t record_stage(const hipEvent_t* ev, int stage, hipStream_t s) {
+  return ev ? hipEventRecord(ev[stage], s) : hipSuccess;
+}
+// ---- single-token decode (decode.hip) ----
+void make_decode_args(const Plan& p, DecodeArgs& a);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* sc, int rows, int K, uint16_t* out,
                           hipStream_t s);
 

@@ -129,6 +129,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += 256) {
     float s = 0.f;
+    // fixed summation order; unrolled so the partial loads are in flight together
+#pragma unroll 8
     for (int i = 0; i < ks; ++i) s += part[((size_t)i * T + t) * E + e];
     sl[e] = s;
     if (logits_out) logits_out[(size_t)t * E + e] = s;

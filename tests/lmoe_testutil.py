@@ -60,7 +60,7 @@ def run_forward(lm, w: Workload, dev_inp: Dict[str, object], routing: Optional[d
     if w.logits_given:
         routing["logits"] = dev_inp["logits"]
     out = torch.empty((d.T, d.L), dtype=torch.int16, device=dev)
-    ws = torch.empty(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
     lm.forward(d, dev_inp["x"], dev_inp, w.logits_given, routing, out, ws)
     torch.cuda.synchronize()
     res = {k: v.cpu().numpy() for k, v in routing.items()}

@@ -26,6 +26,7 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     assert names == sorted(["lmoe_workspace_bytes", "lmoe_route", "lmoe_forward",
+                            "lmoe_forward_traced", "lmoe_stage_name", "lmoe_path_name",
                             "lmoe_debug_dequant_mxfp4", "lmoe_status_string"]), names
 
 
@@ -34,6 +35,31 @@ def test_library_exports_every_declared_symbol(lm):
     for name in _declared():
         assert hasattr(lib, name), name
     assert set(lm.EXPORTS) == set(_declared())
+
+
+def test_stage_names(lm):
+    assert [lm.stage_name(i) for i in range(lm.NUM_STAGE_EVENTS)] == list(lm.STAGES)
+    assert lm.stage_name(-1) == "?" and lm.stage_name(lm.NUM_STAGE_EVENTS) == "?"
+
+
+def test_traced_forward_rejects_missing_events(lm):
+    d = lm._dims(K3)
+    w = _weights(lm)
+    ev = (ctypes.c_void_p * lm.NUM_STAGE_EVENTS)(*([0x1000] * (lm.NUM_STAGE_EVENTS - 1) + [0]))
+    f = lm._lib.lmoe_forward_traced
+    assert f(ctypes.byref(d), 0x20000000, ctypes.byref(w), 0, None, 0x30000000, 0x40000000, 1,
+             None, None) == lm.LMOE_ERR_NULL
+    assert f(ctypes.byref(d), 0x20000000, ctypes.byref(w), 0, None, 0x30000000, 0x40000000, 1,
+             None, ev) == lm.LMOE_ERR_NULL
+
+
+def test_path_names(lm):
+    assert lm.path_name(K3) == "fused_decode"
+    assert lm.path_name(K3, True) == "grouped_small"
+    assert lm.path_name((64,) + K3[1:]) == "grouped_small"
+    assert lm.path_name((4096,) + K3[1:]) == "grouped_large"
+    assert lm.path_name((1, 8192, 896, 16, 2048, 2, 2048)) == "grouped_small"  # L too wide
+    assert lm.path_name((1, 3583, 896, 16, 2048, 2, 2048)) == "invalid"
 
 
 def test_status_strings(lm):

@@ -1,0 +1,106 @@
+"""GPU parity of the single-token decode path (one persistent kernel) against
+the CPU oracle, including its dependency counters being left at zero and
+back-to-back calls reusing one workspace."""
+import numpy as np
+import pytest
+
+import oracle as O
+from workloads import gen_all, gen_x, get_workload
+from workloads.configs import Dims, Workload
+
+from lmoe_testutil import (log, upload, alloc_routing, check_out, logits_bound,
+                           check_routing_against_oracle)
+
+pytestmark = pytest.mark.gpu
+
+CTR_INTS = 32768 // 4
+ERROR_SLOT = 160
+
+
+@pytest.fixture(scope="module")
+def lm():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import mxfp4_latent_mixture_amd as lm
+    return lm
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+def _run_tokens(lm, dev, w: Workload, n_tokens: int):
+    """n_tokens consecutive T=1 calls on one zero-filled workspace; each output
+    checked against the oracle; the counter block must be all zero after."""
+    import torch
+    d = w.dims
+    assert d.T == 1
+    assert lm.path_name(d) == "fused_decode"
+    inp = gen_all(w)
+    dinp = upload(inp, dev)
+    xs = gen_x(w.with_T(n_tokens))
+    ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
+    for t in range(n_tokens):
+        x = torch.from_numpy(xs[t:t + 1].view(np.int16).copy()).to(dev)
+        r = alloc_routing(d, dev)
+        out = torch.empty((1, d.L), dtype=torch.int16, device=dev)
+        lm.forward(d, x, dinp, False, r, out, ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint16)
+        res = {k: v.cpu().numpy() for k, v in r.items()}
+        ref = O.forward(xs[t:t + 1], inp["router_w"], inp, inp, d.k)
+        same = check_routing_against_oracle(res["topk_idx"], res["logits"], ref["logits"],
+                                            logits_bound(xs[t:t + 1], inp["router_w"]), d.k,
+                                            f"{w.name} token {t}")
+        if not same.all():
+            log(f"{w.name} token {t}: routing differs inside the rounding band; skipped")
+            continue
+        assert np.array_equal(res["topk_idx"], ref["idx"])
+        assert np.all(np.abs(res["topk_w"] - ref["w"]) <= 1e-5 * np.abs(ref["w"]) + 1e-9)
+        assert np.array_equal(res["counts"], ref["counts"])
+        assert np.array_equal(res["offsets"], ref["offsets"])
+        assert np.array_equal(res["perm"], ref["perm"])
+        assert np.array_equal(res["inv_perm"], ref["inv"])
+        check_out(got, ref["out64"], f"{w.name} token {t}")
+    ctr = ws[:32768].view(torch.int32).cpu().numpy()
+    assert ctr[ERROR_SLOT] == 0, "a dependency wait timed out"
+    assert not ctr.any(), f"counters left non-zero at {np.nonzero(ctr)[0][:8]}"
+
+
+@pytest.mark.parametrize("name,dims,scales", [
+    ("tiny1", Dims(T=1, L=256, E=32, k=4, I=128, S=2, Is=128), ("uniform", 120, 130)),
+    ("ragged1", Dims(T=1, L=416, E=48, k=6, I=352, S=2, Is=224), ("uniform", 118, 132)),
+    ("odd_experts", Dims(T=1, L=544, E=37, k=5, I=160, S=1, Is=96), ("uniform", 118, 132)),
+    ("no_shared", Dims(T=1, L=320, E=64, k=8, I=256, S=0, Is=0), ("uniform", 118, 132)),
+    ("k1", Dims(T=1, L=256, E=16, k=1, I=64, S=3, Is=64), ("uniform", 118, 132)),
+    ("wide_k", Dims(T=1, L=288, E=1024, k=32, I=96, S=1, Is=4096), ("uniform", 118, 132)),
+])
+def test_fused_decode_shapes(lm, dev, name, dims, scales):
+    _run_tokens(lm, dev, Workload(name, 40 + len(name), dims, scales=scales), 3)
+
+
+def test_fused_decode_k3_back_to_back(lm, dev):
+    w = get_workload("decode")
+    log("decode: 4 consecutive K3 tokens on one workspace")
+    _run_tokens(lm, dev, w, 4)
+
+
+def test_single_token_with_given_logits_uses_grouped_path(lm, dev):
+    import torch
+    w = Workload("given1", 51, Dims(T=1, L=256, E=32, k=4, I=128, S=2, Is=128),
+                 scales=("uniform", 120, 130), logits_given=True)
+    d = w.dims
+    assert lm.path_name(d, True) == "grouped_small"
+    inp = gen_all(w)
+    dinp = upload(inp, dev)
+    r = alloc_routing(d, dev)
+    r["logits"] = dinp["logits"]
+    out = torch.empty((1, d.L), dtype=torch.int16, device=dev)
+    ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
+    lm.forward(d, dinp["x"], dinp, True, r, out, ws)
+    torch.cuda.synchronize()
+    ref = O.forward(inp["x"], inp["router_w"], inp, inp, d.k, logits=inp["logits"])
+    assert np.array_equal(r["topk_idx"].cpu().numpy(), ref["idx"])
+    check_out(out.cpu().numpy().view(np.uint16), ref["out64"], "given-logits T=1")

@@ -87,7 +87,7 @@ def _route_given(lm, dev, logits: np.ndarray, k: int):
     d = Dims(T=T, L=32, E=E, k=k, I=32, S=0, Is=0)
     r = alloc_routing(d, dev)
     r["logits"] = to_dev(logits.astype(np.float32), dev)
-    ws = torch.empty(max(1, lm.workspace_bytes(d)), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(1, lm.workspace_bytes(d)), dtype=torch.uint8, device=dev)
     lm.route(d, None, None, True, r, ws)
     torch.cuda.synchronize()
     return {kk: v.cpu().numpy() for kk, v in r.items()}
@@ -211,7 +211,7 @@ def test_forward_without_routing_outputs(lm, dev):
     dinp = upload(inp, dev)
     ref, _ = run_forward(lm, w, dinp)
     out = torch.empty((d.T, d.L), dtype=torch.int16, device=dev)
-    ws = torch.empty(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
     lm.forward(d, dinp["x"], dinp, False, None, out, ws)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().view(np.uint16), ref)
