@@ -60,7 +60,7 @@ typedef struct lmoe_dims {
 } lmoe_dims;
 
 /* Weights, all device pointers, row-major.
- *   router_w  bf16 [L][E]      router projection of the latent
+ *   router_w  bf16 [E][L]      router projection of the latent, one row per expert
  *   gate_q    uint8 [E][I][L/2]   E2M1 codes of the gate rows; element 2m of a
  *                                 row is the low nibble of byte m
  *   gate_s    uint8 [E][I][L/32]  E8M0 exponent of elements 32j..32j+31 of a
@@ -125,7 +125,7 @@ size_t lmoe_workspace_bytes(const lmoe_dims* dims);
 /* Routing only: router logits (unless logits_given), top-k selection with
  * softmax weights, and the expert grouping (counts, offsets, perm, inv_perm).
  *   dims      host; x bf16 [T][L] device (may be NULL if logits_given)
- *   router_w  bf16 [L][E] device (ignored if logits_given)
+ *   router_w  bf16 [E][L] device (ignored if logits_given)
  *   r         host struct of device pointers (may be NULL: nothing returned)
  *   ws        device workspace of ws_bytes >= lmoe_workspace_bytes(dims)
  * Errors: LMOE_ERR_NULL, _SHAPE, _ALIGN, _WORKSPACE, _HIP. */

@@ -70,13 +70,11 @@ Workspace carve_workspace(const Plan& p, void* base) {
   w.y = reinterpret_cast<float*>(take(R * L * 4));
   w.y_sh = reinterpret_cast<float*>(take(S * T * L * 4));
   if (p.fused_decode) {
-    DecodeArgs da;
-    make_decode_args(p, da);
-    w.dpart = reinterpret_cast<float*>(take((size_t)da.nks * E * 4));
+    w.dlogit = reinterpret_cast<float*>(take(E * 4));
     w.dh = reinterpret_cast<uint16_t*>(take((size_t)d.k * I * 2));
     w.dhsh = reinterpret_cast<uint16_t*>(take(S * Is * 2));
     w.dy = reinterpret_cast<float*>(take((size_t)d.k * L * 4));
-    w.dysh = reinterpret_cast<float*>(take(L * 4));
+    w.dysh = reinterpret_cast<float*>(take(S * L * 4));
   }
   w.bytes = off;
   return w;
@@ -135,9 +133,8 @@ static int run_route(const Plan& p, const Workspace& ws, const uint16_t* x, cons
   return LMOE_OK;
 }
 
-// T == 1: the whole layer as one persistent kernel. Stage events: BEGIN
-// before the kernel, every other stage's event after it (the fused stages'
-// time is attributed to the first of them, the router).
+// T == 1: the whole layer as one persistent kernel. Stage events: the
+// kernel's time lands on the router stage.
 static int run_fused_decode(const Plan& p, const Workspace& ws, const uint16_t* x,
                             const lmoe_weights& w, const lmoe_routing* r, uint16_t* out,
                             hipStream_t s, const hipEvent_t* ev) {
@@ -163,16 +160,12 @@ static int run_fused_decode(const Plan& p, const Workspace& ws, const uint16_t* 
   a.inv = (r && r->inv_perm) ? r->inv_perm : ws.inv;
   a.out = out;
   a.ctr = ws.ctr;
-  a.part = ws.dpart;
+  a.logit = ws.dlogit;
   a.h = ws.dh;
   a.hsh = ws.dhsh;
   a.y = ws.dy;
   a.ysh = ws.dysh;
-  if (record_stage(ev, LMOE_STAGE_BEGIN, s) != hipSuccess) return LMOE_ERR_HIP;
-  if (launch_decode(a, s) != hipSuccess) return LMOE_ERR_HIP;
-  for (int i = LMOE_STAGE_ROUTER; i < LMOE_NUM_STAGE_EVENTS; ++i)
-    if (record_stage(ev, i, s) != hipSuccess) return LMOE_ERR_HIP;
-  return LMOE_OK;
+  return launch_decode(a, s, ev) == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
 }
 
 static int check_routing(const lmoe_routing* r, int logits_given) {

@@ -2,43 +2,47 @@
 //
 // Batch-1 decode streams the active weights once per token and is bound by
 // HBM bandwidth (infervisor.ai "Bringing up Kimi-K3 on day zero", "The
-// roofline"): for this layer that is the router, the two bf16 shared experts
-// and the 16 selected MXFP4 experts. Launch boundaries between dependent
-// steps leave the memory system idle, so the whole layer runs as one launch:
-// workgroups draw work items from ticket counters in dependency order and
-// resolve dependencies with on-device counters (the pages' decode runtime
-// likewise orders work with device counters instead of host launches:
-// "One kernel, no host in the loop").
+// roofline"): the router, the two bf16 shared experts and the 16 selected
+// MXFP4 experts. Launch boundaries between dependent steps leave the memory
+// system idle, so the whole layer is one launch in which every wave draws work
+// items from ticket queues in dependency order and resolves dependencies with
+// on-device counters (the pages' decode runtime likewise orders work with
+// device counters rather than host launches: "One kernel, no host in the
+// loop").
 //
-// Work items, in ticket order:
-//   router      partial logits of a K slice x 128 experts; the last one to
-//               finish sums the partials in a fixed order, selects the top-k
-//               with softmax weights and publishes them
-//   shared g/u  one shared expert, 8 intermediate columns (gate and up in one
-//               16-column MFMA tile), h = bf16(silu(g) * u)
-//   routed g/u  one selected expert, 16 intermediate columns; waits for the
-//               routing
-//   shared dn   16 output rows of the shared experts (both experts' K
-//               concatenated); waits for all shared g/u items
-//   routed dn   one selected expert, 64 output rows; waits for that expert's
-//               g/u items
+// Waves work independently: an item covers the whole K range of its rows, so
+// no item needs a workgroup barrier or a cross-wave reduction, and a wave keeps
+// its next burst of weights in flight while it computes the current one.
+//
+// Work items, in ticket order (sizes for the Kimi-K3 layer):
+//   router      the logit of one expert: its 7 KB router row against the
+//               token; published with a device counter
+//   shared g/u  one shared expert, 8 intermediate columns, gate and up in one
+//               16-column MFMA tile: h = bf16(silu(g) * u)          (115 KB)
+//   routed g/u  one selected expert, 16 intermediate columns         (61 KB)
+//   shared dn   16 output rows of one shared expert                  (64 KB)
+//   routed dn   one selected expert, 32 output rows                  (35 KB)
 //   combine     done by whichever item completes a 64-row block last:
-//               out = bf16(sum_j w_j y_j + ysh), j ascending
-// Items are dealt round-robin into eight ticket queues (device-scope atomics
-// on one address serialise, at about 12 ns each on MI355X, so one queue for
-// ~3800 items would cost ~45 us). A workgroup only ever waits for smaller
-// items: the smallest unfinished item is either being processed (all its
-// inputs are done) or is the head of its queue, which a resident workgroup of
-// that queue will draw next. Workgroups are dispatched in index order and a
-// workgroup leaves only when its queue is empty, so each queue with work left
-// keeps a resident workgroup and the kernel cannot deadlock.
+//               out = bf16(sum_j w_j y_j + sum_s ysh_s), in that order
+// The routing decision is not broadcast: every workgroup that needs it waits
+// for all logits to be published and selects the top-k itself into LDS (a
+// deterministic function of the published logits, so all copies agree), which
+// saves the round trips of a single selecting wave writing and every consumer
+// reading back the choice. Workgroup 0 writes the routing outputs.
 //
-// Cross-workgroup data (partial logits, routing, h, y) is written with
-// device-scope stores and read with device-scope loads, which the MI355X
-// keeps coherent across its eight L2 partitions; a producer waits for its
-// stores to complete before bumping a counter. No L2 writeback or invalidate
-// is needed. Counters live in the first bytes of the workspace, must be zero
-// when the kernel starts and are zeroed again by the last workgroup to exit.
+// Tickets: items are dealt round-robin into eight queues (device-scope
+// atomics on one address serialise, about 12 ns each on MI355X). A wave only
+// ever waits for smaller items. The smallest unfinished item is either being
+// processed (its inputs are all done) or heads its queue, and a resident wave
+// of that queue will draw it: waves are dispatched in index order and a wave
+// leaves only when its queue is empty. So the kernel cannot deadlock.
+//
+// Memory ordering: data passed between waves (logits, h, y) is written with
+// device-scope stores and read with device-scope loads, which stay coherent
+// across the eight L2 partitions; a producer waits for its stores to complete
+// before it bumps a counter. No L2 writeback or invalidate is issued. Counters
+// sit in the first 32 KiB of the workspace, are zero when a launch starts and
+// are zeroed again by its last wave to leave.
 #include "lmoe_device.h"
 #include "lmoe_internal.h"
 
@@ -47,6 +51,11 @@ namespace lmoe {
 namespace {
 
 constexpr long kSpinLimit = 1l << 22;
+constexpr int kMaxK = 32;         // routes per token on this path
+constexpr int kKeysPerLane = 16;  // E <= 1024 logits, 16 per lane
+// Workgroups per compute unit. Four streaming waves per CU keep enough bytes
+// in flight; more concurrent items only lengthen each item and the tail.
+constexpr int kWgPerCu = 1;
 
 __device__ __forceinline__ int ld_dev(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -69,7 +78,7 @@ __device__ __forceinline__ void st_dev_f32(float* p, float v) {
 __device__ __forceinline__ float ld_dev_f32(const float* p) {
   return __uint_as_float(ld_dev(reinterpret_cast<const uint32_t*>(p)));
 }
-// 16 bytes written by another workgroup of this launch
+// 16 bytes written by another wave of this launch
 __device__ __forceinline__ u32x4_t ld16_dev(const void* p) {
   const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
   const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -78,52 +87,65 @@ __device__ __forceinline__ u32x4_t ld16_dev(const void* p) {
   return r;
 }
 
-// Every thread's device-scope stores have completed; then one bump.
-__device__ __forceinline__ int publish(int* ctr) {
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// All of this wave's stores have completed; then lane 0 bumps the counter.
+// Returns the previous value (uniform) when `want_old`.
+__device__ __forceinline__ int publish(int* ctr, bool want_old) {
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  __shared__ int s_old;
-  if (threadIdx.x == 0) s_old = add_dev(ctr, 1);
-  __syncthreads();
-  return s_old;
+  int old = 0;
+  if (lane_id() == 0) {
+    if (want_old)
+      old = add_dev(ctr, 1);
+    else
+      __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return __builtin_amdgcn_readfirstlane(old);
 }
 
-// Thread 0 waits until *ctr >= target; a wait that outlives the spin limit
+// Waits until the counter reaches target. A wait that outlives the spin limit
 // (a broken producer) is counted in the error slot and abandoned.
 __device__ __forceinline__ void wait_geq(const int* ctr, int target, int* err) {
-  if (threadIdx.x == 0) {
-    long it = 0;
-    while (ld_dev(ctr) < target) {
-      if (++it > kSpinLimit) {
-        add_dev(err, 1);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
+  long it = 0;
+  for (;;) {
+    int s = 0;
+    if (lane_id() == 0) s = ld_dev(ctr);
+    s = __builtin_amdgcn_readfirstlane(s);
+    if (s >= target) break;
+    if (++it > kSpinLimit) {
+      if (lane_id() == 0) add_dev(err, 1);
+      break;
     }
+    __builtin_amdgcn_s_sleep(2);
   }
-  __syncthreads();
 }
 
-// Thread 0 waits until the kQueues spread counters at ctr, ctr + 32, ... sum
-// to at least target.
-__device__ __forceinline__ void wait_sum_geq(const int* ctr, int target, int* err) {
-  if (threadIdx.x == 0) {
-    long it = 0;
-    for (;;) {
-      int s = 0;
-#pragma unroll
-      for (int q = 0; q < kQueues; ++q) s += ld_dev(ctr + 32 * q);
-      if (s >= target) break;
-      if (++it > kSpinLimit) {
-        add_dev(err, 1);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
+// Wave-wide maximum of a 64-bit key with DPP row shifts and row broadcasts;
+// the result is returned to every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+#define LMOE_DPP_MAX(ctrl, rmask, bmask)                                                   \
+  {                                                                                        \
+    const uint32_t tlo = __builtin_amdgcn_update_dpp(lo, lo, ctrl, rmask, bmask, false);   \
+    const uint32_t thi = __builtin_amdgcn_update_dpp(hi, hi, ctrl, rmask, bmask, false);   \
+    const bool gt = (thi > hi) || (thi == hi && tlo > lo);                                 \
+    lo = gt ? tlo : lo;                                                                    \
+    hi = gt ? thi : hi;                                                                    \
   }
-  __syncthreads();
+  LMOE_DPP_MAX(0x111, 0xf, 0xf)  // row_shr:1
+  LMOE_DPP_MAX(0x112, 0xf, 0xf)  // row_shr:2
+  LMOE_DPP_MAX(0x114, 0xf, 0xf)  // row_shr:4
+  LMOE_DPP_MAX(0x118, 0xf, 0xf)  // row_shr:8: lane 15 of each row holds the row max
+  LMOE_DPP_MAX(0x142, 0xa, 0xf)  // row_bcast:15 into rows 1 and 3
+  LMOE_DPP_MAX(0x143, 0xc, 0xf)  // row_bcast:31 into rows 2 and 3: lane 63 holds the max
+#undef LMOE_DPP_MAX
+  lo = __builtin_amdgcn_readlane(lo, 63);
+  hi = __builtin_amdgcn_readlane(hi, 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
+// Order: larger logit first, equal logits by lower expert index, NaN after
+// every number, -0 == +0; one distinct 64-bit key per expert.
 __device__ __forceinline__ uint64_t order_key(float f, int e) {
   uint32_t u = __float_as_uint(f);
   if (f == 0.0f) u = 0u;
@@ -131,522 +153,569 @@ __device__ __forceinline__ uint64_t order_key(float f, int e) {
   return ((uint64_t)k32 << 32) | (uint64_t)(~(uint32_t)e);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off, kWave);
-    v = o > v ? o : v;
-  }
-  return v;
-}
+// Per-wave state kept across items.
+struct WaveState {
+  int staged;  // what the wave's LDS A row holds: -1 none, route j, or 1000 + shared expert
+};
 
-constexpr int kMaxL = kDecodeMaxWidth;    // largest latent / intermediate width
-constexpr int kMaxSIs = kDecodeMaxWidth;  // largest S * Is
-constexpr int kMaxKs = 16;                // router K slices
-
-struct Smem {
-  uint16_t xs[kMaxL];          // the token, bf16
-  uint16_t as[kMaxSIs];        // A row of the current down item: h_j or both shared h
-  float red[16][129];          // router phase partials / cross-wave tile sums
-  float logit[1024];
-  int sel[32];
-  int misc[8];
+// Per-workgroup routing decision in LDS.
+struct TopkLds {
+  int state;  // 0 not started, 1 being computed, 2 ready
+  int sel[kMaxK];
+  float w[kMaxK];
 };
 
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Router item: partial logits for rows [r0, r1) x experts [e0, e0 + 128).
-// Thread (c, ph): experts e0 + 8c .. +8, rows r0 + ph + 16 i.
+// Weight streaming. Weights are read through buffer resources: an offset past
+// the end of the matrix returns zeros, so padding rows and past-the-end blocks
+// need no branches around loads, and each burst of loads is issued as a group
+// (pinned by scheduling barriers) one burst ahead of the MFMAs that consume
+// it.
+//
+// Every lane of a lane group reads the same A values (an LDS broadcast), so
+// all 16 rows of each MFMA result equal the token's row; lanes 0..15 of
+// acc[t][0] hold the tile's 16 results.
+//
+// MXFP4 rows (16 bytes of codes per 32-value block): in iteration it, lane
+// group g takes blocks 8 it + 2 g + u (u = 0, 1), so the four groups read 128
+// contiguous bytes of every row per iteration. Each 64-block window's 64
+// exponent bytes are fetched with dword-aligned loads (the range check of a
+// buffer load zeroes a whole dword that reaches past the end), realigned,
+// reduced to the 16 bytes the lane uses, and prefetched one window ahead.
+//
+// bf16 rows: in iteration it, instruction j, lane group g reads values
+// 128 it + 32 j + 8 g .. +8, so each instruction reads 64 contiguous bytes of
+// every row.
 // ---------------------------------------------------------------------------
-__device__ void router_item(const DecodeArgs& a, int item, Smem& sm) {
-  const int tid = threadIdx.x;
-  const int c = tid & 15, ph = tid >> 4;
-  const int kr = item / a.neg, eg = item % a.neg;
-  const int e0 = eg * 128 + c * 8;
-  const int r0 = kr * a.rk;
-  const int r1 = min(a.L, r0 + a.rk);
-  const bool vec = (a.E % 8) == 0 && e0 + 8 <= a.E;
-  float acc[8];
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kOob = 0x40000000;  // an offset past the end of every matrix
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4_t bload16(rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// One tile of 16 weight rows: the lane's row starts at byte `row` of its
+// resource(s) (kOob for a padding row).
+struct Tile4 {
+  rsrc_t codes, scales;
+  int code_row, scale_row;
+};
+struct Tile16 {
+  rsrc_t w;
+  int row;
+};
+
+template <int NT, int IPB>
+__device__ __forceinline__ void gemv_fp4(const uint16_t* arow, int nblk, const Tile4 (&tl)[NT],
+                                         f32x4_t (&acc)[NT]) {
+  static_assert(8 % IPB == 0 && (8 / IPB) % 2 == 0, "a window is an even number of bursts");
+  constexpr int BPW = 8 / IPB;  // bursts per 64-block window
+  const int grp = lane_id() >> 4;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  u32x4_t wv[16];
-  float xv[16];
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nwin = (nblk + 63) / 64;
+
+  // raw exponent window: 17 dwords from the dword at or below the window start
+  struct Raw {
+    u32x4_t q[4];
+    uint32_t tail;
+  };
+  Raw raw[NT];
+  uint32_t ex[NT][4];  // the lane's 16 exponent bytes of the current window
+  uint32_t shift[NT];
+  auto load_exps = [&](int w) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = r0 + ph + 16 * i;
-    const bool ok = r < r1;
-    xv[i] = ok ? bf16_bits_to_f32(sm.xs[r]) : 0.f;
-    if (ok && vec) {
-      wv[i] = load16(a.wr + (size_t)r * a.E + e0);
-    } else {
-      uint32_t p[4] = {0u, 0u, 0u, 0u};
-      if (ok) {
-        for (int q = 0; q < 8; ++q) {
-          const uint32_t v = (e0 + q < a.E) ? a.wr[(size_t)r * a.E + e0 + q] : 0u;
-          p[q >> 1] |= v << (16 * (q & 1));
+    for (int t = 0; t < NT; ++t) {
+      const int off = 64 * w < nblk ? tl[t].scale_row + 64 * w : kOob;
+      const int sh = off & 3;
+      const int a0 = off - sh;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) raw[t].q[j] = bload16(tl[t].scales, a0 + 16 * j);
+      raw[t].tail = bload4(tl[t].scales, sh ? a0 + 64 : kOob);
+      shift[t] = (uint32_t)sh;
+    }
+  };
+  // exponent of block 8 p + 2 g + u of the window is byte 2 p + u of ex:
+  // the lane's two bytes of iteration p are halfword g of window bytes 8p..8p+7
+  auto take_exps = [&]() {
+    const uint32_t gs = 16u * (uint32_t)grp;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      uint32_t d[17];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) d[4 * j + c] = raw[t].q[j][c];
+      d[16] = raw[t].tail;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) d[i] = __builtin_amdgcn_alignbyte(d[i + 1], d[i], shift[t]);
+      uint32_t hw[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const uint64_t v = ((uint64_t)d[2 * p + 1] << 32) | d[2 * p];
+        hw[p] = (uint32_t)(v >> gs) & 0xFFFFu;
+      }
+#pragma unroll
+      for (int p = 0; p < 8; p += 2) ex[t][p >> 1] = hw[p] | (hw[p + 1] << 16);
+    }
+  };
+  struct Buf {
+    u32x4_t c[IPB][NT][2];
+  };
+  // bp is a compile-time constant at every call
+  auto load = [&](int w, const int bp, Buf& b) {
+#pragma unroll
+    for (int c = 0; c < IPB; ++c) {
+      const int it = w * 8 + bp * IPB + c;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int blk = 8 * it + 2 * grp + u;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          b.c[c][t][u] = bload16(tl[t].codes, blk < nblk ? tl[t].code_row + blk * 16 : kOob);
+      }
+    }
+  };
+  auto compute = [&](int w, const int bp, const Buf& b) {
+#pragma unroll
+    for (int c = 0; c < IPB; ++c) {
+      const int p = bp * IPB + c;  // iteration within the window
+      const int it = w * 8 + p;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int blk = 8 * it + 2 * grp + u;
+        const bool ok = blk < nblk;
+        // past-the-end blocks carry zero codes and exponent 2^0 (never NaN);
+        // their A reads stay inside the row
+        const int ablk = ok ? blk : nblk - 1;
+        float scale[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const uint32_t e8 = (ex[t][p >> 1] >> (8 * (2 * (p & 1) + u))) & 0xFFu;
+          scale[t] = e8m0_to_f32(ok ? e8 : 127u);
+        }
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(arow + ablk * 32 + qq * 8);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            acc[t] = mfma16(av, dequant8(b.c[c][t][u][qq], scale[t]), acc[t]);
         }
       }
-      wv[i] = u32x4_t{p[0], p[1], p[2], p[3]};
     }
-  }
+  };
+  Buf buf[2];
+  load_exps(0);
+  __builtin_amdgcn_sched_barrier(0);
+  load(0, 0, buf[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  take_exps();
+  for (int w = 0; w < nwin; ++w) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] = fmaf(xv[i], __uint_as_float(wv[i][q] << 16), acc[2 * q]);
-      acc[2 * q + 1] = fmaf(xv[i], __uint_as_float(wv[i][q] & 0xFFFF0000u), acc[2 * q + 1]);
+    for (int bp = 0; bp < BPW; ++bp) {
+      // the next burst (the next window's first at the end of this one)
+      if (bp + 1 < BPW)
+        load(w, bp + 1, buf[(bp + 1) & 1]);
+      else
+        load(w + 1, 0, buf[0]);
+      if (bp == 0) load_exps(w + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(w, bp, buf[bp & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) sm.red[ph][c * 8 + i] = acc[i];
-  __syncthreads();
-  if (tid < 128) {
-    float s = 0.f;
-#pragma unroll
-    for (int p = 0; p < 16; ++p) s += sm.red[p][tid];
-    const int e = eg * 128 + tid;
-    if (e < a.E) st_dev_f32(a.part + (size_t)kr * a.E + e, s);
+    take_exps();
   }
 }
 
-// ---------------------------------------------------------------------------
-// Top-k of the summed partial logits, softmax weights, routing outputs; then
-// the routing flag is raised.
-// ---------------------------------------------------------------------------
-__device__ void topk_item(const DecodeArgs& a, Smem& sm) {
-  const int tid = threadIdx.x;
-  {
-    // every partial of this thread's experts in flight at once, then summed
-    // in K-slice order
-    float v[4][kMaxKs];
+template <int NT, int IPB>
+__device__ __forceinline__ void gemv_bf16(const uint16_t* arow, int nblk, const Tile16 (&tl)[NT],
+                                          f32x4_t (&acc)[NT]) {
+  const int grp = lane_id() >> 4;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = tid + 256 * r;
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int iters = (nblk + 3) / 4;  // 4 blocks of 32 values per iteration
+  const int bursts = (iters + IPB - 1) / IPB;
+  struct Buf {
+    u32x4_t b[IPB][NT][4];
+  };
+  auto load = [&](int burst, Buf& w) {
 #pragma unroll
-      for (int kr = 0; kr < kMaxKs; ++kr)
-        v[r][kr] = (e < a.E && kr < a.nks) ? ld_dev_f32(a.part + (size_t)kr * a.E + e) : 0.f;
+    for (int c = 0; c < IPB; ++c) {
+      const int it = burst * IPB + c;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int blk = 4 * it + j;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          w.b[c][t][j] = bload16(tl[t].w, blk < nblk ? tl[t].row + blk * 64 + grp * 16 : kOob);
+      }
     }
+  };
+  auto compute = [&](int burst, const Buf& w) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = tid + 256 * r;
-      float s = 0.f;
+    for (int c = 0; c < IPB; ++c) {
+      const int it = burst * IPB + c;
 #pragma unroll
-      for (int kr = 0; kr < kMaxKs; ++kr)
-        if (kr < a.nks) s += v[r][kr];
-      if (e < a.E) {
-        sm.logit[e] = s;
-        if (a.logits_out) a.logits_out[e] = s;
+      for (int j = 0; j < 4; ++j) {
+        const int blk = min(4 * it + j, nblk - 1);
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(arow + blk * 32 + grp * 8);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = mfma16(av, as_bf16x8(w.b[c][t][j]), acc[t]);
+      }
+    }
+  };
+  // no load is conditional: bursts past the end read out of bounds (zeros)
+  Buf wa, wb;
+  load(0, wa);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int b = 0; b < bursts; b += 2) {
+    load(b + 1, wb);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    load(b + 2, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b + 1, wb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Copy n bf16 values written by other waves of this launch into the wave's
+// LDS row (n a multiple of 8).
+__device__ __forceinline__ void stage_row(uint16_t* dst, const uint16_t* src, int n) {
+  for (int i = lane_id() * 8; i < n; i += kWave * 8)
+    *reinterpret_cast<u32x4_t*>(dst + i) = ld16_dev(src + i);
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+}
+
+// h = bf16(silu(g) * u) for n consecutive intermediate columns held as g in
+// lanes 0..n-1 and u in lanes un..un+n-1 of `u_src`; stored in pairs with
+// device-scope stores (columns below `limit` only).
+__device__ __forceinline__ void store_glu(uint16_t* dst, float g, float u_src, int n, int un,
+                                          int limit) {
+  const int lane = lane_id();
+  const float u = __shfl(u_src, (lane + un) & 63, kWave);
+  const uint32_t h = f32_to_bf16_bits(silu(g) * u);
+  const uint32_t h_next = __shfl_down(h, 1, kWave);
+  if (lane < n && (lane & 1) == 0 && lane < limit)
+    st_dev(reinterpret_cast<uint32_t*>(dst + lane), h | (h_next << 16));
+}
+
+// ---------------------------------------------------------------------------
+// Router: the logit of expert e, fp32 sum of x[l] W[e][l] over the row.
+// ---------------------------------------------------------------------------
+__device__ void router_item(const DecodeArgs& a, int e, const uint16_t* xs) {
+  const int lane = lane_id();
+  const uint32_t bytes = (uint32_t)a.E * a.L * 2;
+  const rsrc_t r = make_rsrc(a.wr, bytes);
+  const int row = e * a.L * 2;
+  // the row in 1 KB chunks, 16 bytes (8 values) per lane and chunk
+  constexpr int kMaxChunks = kDecodeMaxWidth * 2 / 1024;
+  u32x4_t v[kMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int off = c * 1024 + lane * 16;
+    v[c] = bload16(r, off < a.L * 2 ? row + off : kOob);
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int l0 = c * 512 + lane * 8;
+    if (l0 < a.L) {
+      const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xs + l0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc = fmaf(__uint_as_float(xv[q] << 16), __uint_as_float(v[c][q] << 16), acc);
+        acc = fmaf(__uint_as_float(xv[q] & 0xFFFF0000u), __uint_as_float(v[c][q] & 0xFFFF0000u),
+                   acc);
       }
     }
   }
-  __syncthreads();
-  if (tid < kWave) {
-    const int lane = tid;
-    uint64_t key[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = lane + kWave * i;
-      key[i] = (e < a.E) ? order_key(sm.logit[e], e) : 0ull;
-    }
-    uint64_t best = 0ull;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) best = key[i] > best ? key[i] : best;
-    int my_e = 0;
-    float my_l = 0.f;
-    for (int j = 0; j < a.k; ++j) {
-      const uint64_t b = wave_max_u64(best);
-      const int ew = (int)(~(uint32_t)b);
-      if (lane == j) {
-        my_e = ew;
-        my_l = sm.logit[ew];
-      }
-      if ((ew & (kWave - 1)) == lane) {
-        const int slot = ew / kWave;
-        best = 0ull;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (i == slot) key[i] = 0ull;
-          best = key[i] > best ? key[i] : best;
-        }
-      }
-    }
-    const float l0 = __shfl(my_l, 0, kWave);
-    const float z = (lane < a.k) ? expf(my_l - l0) : 0.f;
-    float s = z;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_down(s, off, kWave);
-    s = __shfl(s, 0, kWave);
-    if (lane < a.k) {
-      st_dev(reinterpret_cast<uint32_t*>(a.idx) + lane, (uint32_t)my_e);
-      st_dev_f32(a.w + lane, z / s);
-      sm.sel[lane] = my_e;
-    }
+  for (int off = 1; off < 64; off <<= 1) acc += __shfl_xor(acc, off, kWave);
+  if (lane == 0) {
+    st_dev_f32(a.logit + e, acc);
+    if (a.logits_out) a.logits_out[e] = acc;
   }
-  __syncthreads();
-  // grouping outputs for one token: each route is its own group, in expert order
-  for (int e = tid; e < a.E; e += 256) {
+  publish(a.ctr + kCtrRouterDone, false);
+}
+
+// The routing decision of this workgroup: computed by the first wave that
+// needs it once every logit is published; other waves wait for it in LDS.
+__device__ void ensure_topk(const DecodeArgs& a, TopkLds& tk) {
+  if (__hip_atomic_load(&tk.state, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 2) return;
+  int claim = 0;
+  if (lane_id() == 0) {
+    int expected = 0;
+    claim = __hip_atomic_compare_exchange_strong(&tk.state, &expected, 1, __ATOMIC_ACQ_REL,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  if (!__builtin_amdgcn_readfirstlane(claim)) {
+    while (__hip_atomic_load(&tk.state, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 2)
+      __builtin_amdgcn_s_sleep(1);
+    return;
+  }
+  wait_geq(a.ctr + kCtrRouterDone, a.n_router, a.ctr + kCtrError);
+  const int lane = lane_id();
+  uint64_t key[kKeysPerLane];
+#pragma unroll
+  for (int i = 0; i < kKeysPerLane; ++i) {
+    const int e = lane + kWave * i;
+    key[i] = (e < a.E) ? order_key(ld_dev_f32(a.logit + e), e) : 0ull;
+  }
+  uint64_t best = 0ull;
+#pragma unroll
+  for (int i = 0; i < kKeysPerLane; ++i) best = key[i] > best ? key[i] : best;
+  int my_e = 0;
+  float my_l = 0.f;
+  for (int j = 0; j < a.k; ++j) {
+    const uint64_t b = wave_max_u64(best);
+    const int ew = (int)(~(uint32_t)b);
+    if ((ew & (kWave - 1)) == lane) {
+      const int slot = ew / kWave;
+      best = 0ull;
+#pragma unroll
+      for (int i = 0; i < kKeysPerLane; ++i) {
+        if (i == slot) key[i] = 0ull;
+        best = key[i] > best ? key[i] : best;
+      }
+    }
+    if (lane == j) my_e = ew;
+  }
+  if (lane < a.k) my_l = ld_dev_f32(a.logit + my_e);
+  // softmax over the selected logits, relative to the largest
+  const float l0 = __shfl(my_l, 0, kWave);
+  const float z = (lane < a.k) ? expf(my_l - l0) : 0.f;
+  float s = z;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_down(s, off, kWave);
+  s = __shfl(s, 0, kWave);
+  if (lane < a.k) {
+    tk.sel[lane] = my_e;
+    tk.w[lane] = z / s;
+  }
+  __hip_atomic_store(&tk.state, 2, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Routing outputs for one token: the selection, its weights, and the grouping
+// (each route is its own group, in expert order).
+__device__ void write_routing(const DecodeArgs& a, const TopkLds& tk) {
+  const int lane = lane_id();
+  const int my_e = lane < a.k ? tk.sel[lane] : 0x7fffffff;
+  if (lane < a.k) {
+    a.idx[lane] = my_e;
+    a.w[lane] = tk.w[lane];
+  }
+  for (int e = lane; e < a.E; e += kWave) {
     int below = 0, hit = 0;
     for (int j = 0; j < a.k; ++j) {
-      below += sm.sel[j] < e;
-      hit += sm.sel[j] == e;
+      const int sj = tk.sel[j];
+      below += sj < e;
+      hit += sj == e;
     }
     a.counts[e] = hit;
     a.offsets[e] = below;
   }
-  if (tid == 0) a.offsets[a.E] = a.k;
-  if (tid < a.k) {
+  if (lane == 0) a.offsets[a.E] = a.k;
+  if (lane < a.k) {
     int pos = 0;
-    for (int j = 0; j < a.k; ++j) pos += sm.sel[j] < sm.sel[tid];
-    a.perm[pos] = tid;
-    a.inv[tid] = pos;
-  }
-  publish(a.ctr + kCtrTopk);
-}
-
-// ---------------------------------------------------------------------------
-// GEMV core: NT weight tiles of 16 rows each against the token row held in
-// LDS. K is split over the four waves in contiguous quarters; in a wave
-// iteration the four lane groups take adjacent runs of U MX blocks (full
-// cache lines per wave-wide load). Weights are fetched in bursts of CH
-// iterations (all loads of a burst in flight together), then consumed. Every
-// lane of a lane group reads the same A values (an LDS broadcast), so all 16
-// rows of each MFMA result equal the token's row; row 0 is used.
-// ---------------------------------------------------------------------------
-template <bool FP4>
-struct WOps;
-template <>
-struct WOps<true> {
-  u32x4_t c[2];
-  uint32_t s[2];
-};
-template <>
-struct WOps<false> {
-  u32x4_t b[4];
-};
-
-// wrow(t, col, q, sc, b) gives tile t's weight row for this lane (codes and
-// exponents, or bf16), nullptr for a padding column.
-template <bool FP4, int NT, int CH, typename WRow>
-__device__ __forceinline__ void gemv_tiles(const uint16_t* arow_lds, int K, WRow wrow,
-                                           f32x4_t (&acc)[NT]) {
-  constexpr int U = FP4 ? 2 : 1;
-  constexpr int SPAN = 4 * U;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col = lane & 15, grp = lane >> 4;
-  const int nblk = K / 32;
-  const int bw_lo = (wave * nblk) / 4;
-  const int bw_hi = ((wave + 1) * nblk) / 4;
-  const int iters = (bw_hi - bw_lo + SPAN - 1) / SPAN;
-
-  const uint8_t* q[NT];
-  const uint8_t* sc[NT];
-  const uint16_t* bw[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    wrow(t, col, q[t], sc[t], bw[t]);
-    acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-
-  for (int it0 = 0; it0 < iters; it0 += CH) {
-    WOps<FP4> w[CH][NT];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int b0 = bw_lo + (it0 + c) * SPAN + grp * U;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int blk = b0 + u;
-          const bool ok = it0 + c < iters && blk < bw_hi;
-          if constexpr (FP4) {
-            const bool w_ok = ok && q[t] != nullptr;
-            w[c][t].c[u] = w_ok ? load16(q[t] + blk * 16) : zero16();
-            w[c][t].s[u] = w_ok ? (uint32_t)sc[t][blk] : 127u;
-          } else {
-            const bool w_ok = ok && bw[t] != nullptr;
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq)
-              w[c][t].b[qq] = w_ok ? load16(bw[t] + blk * 32 + qq * 8) : zero16();
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int b0 = bw_lo + (it0 + c) * SPAN + grp * U;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        // past-the-end blocks carry zero weights; their A reads stay inside the row
-        const int blk = min(b0 + u, nblk - 1);
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const bf16x8_t av =
-              *reinterpret_cast<const bf16x8_t*>(arow_lds + blk * 32 + qq * 8);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            bf16x8_t bv;
-            if constexpr (FP4)
-              bv = dequant8(w[c][t].c[u][qq], e8m0_to_f32(w[c][t].s[u]));
-            else
-              bv = as_bf16x8(w[c][t].b[qq]);
-            acc[t] = mfma16(av, bv, acc[t]);
-          }
-        }
-      }
-    }
+    for (int j = 0; j < a.k; ++j) pos += tk.sel[j] < my_e;
+    a.perm[pos] = lane;
+    a.inv[lane] = pos;
   }
 }
 
-// Sum the 16 row-0 results of every wave's tile(s) into sm.red[tile * 4 + wave][col].
-template <int NT>
-__device__ __forceinline__ void reduce_row0(const f32x4_t (&acc)[NT], Smem& sm) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane < 16) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) sm.red[t * 4 + wave][lane] = acc[t][0];
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ float sum_waves(const Smem& sm, int t, int c) {
-  float s = sm.red[t * 4 + 0][c];
-  s += sm.red[t * 4 + 1][c];
-  s += sm.red[t * 4 + 2][c];
-  s += sm.red[t * 4 + 3][c];
-  return s;
-}
-
-// Copy n bf16 values written by other workgroups of this launch into LDS.
-__device__ __forceinline__ void stage_dev(uint16_t* dst, const uint16_t* src, int n) {
-  for (int i = threadIdx.x * 8; i < n; i += 256 * 8)
-    *reinterpret_cast<u32x4_t*>(dst + i) = ld16_dev(src + i);
-  __syncthreads();
-}
-
 // ---------------------------------------------------------------------------
-// Items
+// Expert items
 // ---------------------------------------------------------------------------
-__device__ void shared_gu_item(const DecodeArgs& a, int item, Smem& sm) {
-  const int per = (a.Is + 7) / 8;
-  const int s = item / per;
-  const int i0 = (item % per) * 8;
+__device__ void shared_gu_item(const DecodeArgs& a, int item, const uint16_t* xs) {
+  const int s = item / a.shgu_per_expert;
+  const int i0 = (item % a.shgu_per_expert) * 8;
+  const int col = lane_id() & 15;
+  const int i = i0 + (col & 7);
+  const uint32_t mbytes = (uint32_t)a.Is * a.L * 2;
+  Tile16 tl[1];
+  tl[0].w = make_rsrc((col < 8 ? a.shg : a.shu) + (size_t)s * a.Is * a.L, mbytes);
+  tl[0].row = i < a.Is ? i * a.L * 2 : kOob;
   f32x4_t acc[1];
-  gemv_tiles<false, 1, 4>(sm.xs, a.L,
-      [&](int, int col, const uint8_t*& q, const uint8_t*& sc, const uint16_t*& b) {
-        q = sc = nullptr;
-        const int i = i0 + (col & 7);
-        const uint16_t* m = (col < 8) ? a.shg : a.shu;
-        b = (i < a.Is) ? m + ((size_t)s * a.Is + i) * a.L : nullptr;
-      }, acc);
-  reduce_row0<1>(acc, sm);
-  const int tid = threadIdx.x;
-  if (tid < 8) {
-    const float g = sum_waves(sm, 0, tid);
-    const float u = sum_waves(sm, 0, tid + 8);
-    sm.logit[tid] = __uint_as_float((uint32_t)f32_to_bf16_bits(silu(g) * u));
-  }
-  __syncthreads();
-  if (tid < 4) {
-    const int i = i0 + 2 * tid;
-    if (i < a.Is) {  // Is % 32 == 0, so i + 1 < Is too
-      const uint32_t lo = __float_as_uint(sm.logit[2 * tid]);
-      const uint32_t hi = __float_as_uint(sm.logit[2 * tid + 1]);
-      st_dev(reinterpret_cast<uint32_t*>(a.hsh + (size_t)s * a.Is + i), lo | (hi << 16));
-    }
-  }
-  publish(a.ctr + kCtrShared + 32 * (item % kQueues));
+  gemv_bf16<1, 2>(xs, a.L / 32, tl, acc);
+  // g in lanes 0..7, u in lanes 8..15
+  store_glu(a.hsh + (size_t)s * a.Is + i0, acc[0][0], acc[0][0], 8, 8, a.Is - i0);
+  publish(a.ctr + kCtrShared + 16 * s, false);
 }
 
-__device__ void routed_gu_item(const DecodeArgs& a, int item, Smem& sm, bool& routed) {
+__device__ void routed_gu_item(const DecodeArgs& a, int item, const uint16_t* xs,
+                               TopkLds& tk) {
   const int j = item / a.gu_per_route;
   const int i0 = (item % a.gu_per_route) * 16;
-  if (!routed) {
-    wait_geq(a.ctr + kCtrTopk, 1, a.ctr + kCtrError);
-    routed = true;
-  }
-  if (threadIdx.x == 0) sm.misc[0] = (int)ld_dev(reinterpret_cast<const uint32_t*>(a.idx) + j);
-  __syncthreads();
-  const int e = min(max(sm.misc[0], 0), a.E - 1);  // in range even after a timed-out wait
+  ensure_topk(a, tk);
+  const int e = min(max(__builtin_amdgcn_readfirstlane(tk.sel[j]), 0), a.E - 1);
+  const int i = i0 + (lane_id() & 15);
   const size_t qoff = (size_t)e * a.I * (a.L / 2);
   const size_t soff = (size_t)e * a.I * (a.L / 32);
+  const uint32_t qbytes = (uint32_t)a.I * (a.L / 2), sbytes = (uint32_t)a.I * (a.L / 32);
+  Tile4 tl[2];
+  tl[0].codes = make_rsrc(a.gq + qoff, qbytes);
+  tl[0].scales = make_rsrc(a.gs + soff, sbytes);
+  tl[1].codes = make_rsrc(a.uq + qoff, qbytes);
+  tl[1].scales = make_rsrc(a.us + soff, sbytes);
+  tl[0].code_row = tl[1].code_row = i < a.I ? i * (a.L / 2) : kOob;
+  tl[0].scale_row = tl[1].scale_row = i < a.I ? i * (a.L / 32) : kOob;
   f32x4_t acc[2];
-  gemv_tiles<true, 2, 4>(sm.xs, a.L,
-      [&](int t, int col, const uint8_t*& q, const uint8_t*& sc, const uint16_t*& b) {
-        b = nullptr;
-        const int i = i0 + col;
-        if (i < a.I) {
-          q = (t == 0 ? a.gq : a.uq) + qoff + (size_t)i * (a.L / 2);
-          sc = (t == 0 ? a.gs : a.us) + soff + (size_t)i * (a.L / 32);
-        } else {
-          q = sc = nullptr;
-        }
-      }, acc);
-  reduce_row0<2>(acc, sm);
-  const int tid = threadIdx.x;
-  if (tid < 16) {
-    const float g = sum_waves(sm, 0, tid);
-    const float u = sum_waves(sm, 1, tid);
-    sm.logit[tid] = __uint_as_float((uint32_t)f32_to_bf16_bits(silu(g) * u));
-  }
-  __syncthreads();
-  if (tid < 8) {
-    const int i = i0 + 2 * tid;
-    if (i < a.I) {
-      const uint32_t lo = __float_as_uint(sm.logit[2 * tid]);
-      const uint32_t hi = __float_as_uint(sm.logit[2 * tid + 1]);
-      st_dev(reinterpret_cast<uint32_t*>(a.h + (size_t)j * a.I + i), lo | (hi << 16));
-    }
-  }
-  publish(a.ctr + kCtrRoute + 16 * j);
+  gemv_fp4<2, 2>(xs, a.L / 32, tl, acc);
+  // g in lanes 0..15 of tile 0, u in lanes 0..15 of tile 1
+  store_glu(a.h + (size_t)j * a.I + i0, acc[0][0], acc[1][0], 16, 0, a.I - i0);
+  publish(a.ctr + kCtrRoute + 16 * j, false);
 }
 
-__device__ void combine_block(const DecodeArgs& a, int b) {
-  const int tid = threadIdx.x;
-  const int l = b * 64 + tid;
-  if (tid < 64 && l < a.L) {
+__device__ void combine_block(const DecodeArgs& a, int b, const TopkLds& tk) {
+  const int l = b * 64 + lane_id();
+  if (l < a.L) {
     float acc = 0.f;
     for (int j = 0; j < a.k; ++j)
-      acc = fmaf(ld_dev_f32(a.w + j), ld_dev_f32(a.y + (size_t)j * a.L + l), acc);
-    if (a.S > 0) acc += ld_dev_f32(a.ysh + l);
+      acc = fmaf(tk.w[j], ld_dev_f32(a.y + (size_t)j * a.L + l), acc);
+    for (int s = 0; s < a.S; ++s) acc += ld_dev_f32(a.ysh + (size_t)s * a.L + l);
     a.out[l] = f32_to_bf16_bits(acc);
   }
 }
 
-__device__ void finish_block_part(const DecodeArgs& a, int b) {
-  const int old = publish(a.ctr + kCtrBlock + 16 * b);
-  const int nt16 = a.L / 16;
-  const int nsub = min(4, nt16 - 4 * b);
-  const int target = a.k + (a.S > 0 ? nsub : 0);
-  if (old == target - 1) combine_block(a, b);
+// One more input of 64-row block b is ready; the last one combines the block.
+__device__ void finish_block_part(const DecodeArgs& a, int b, TopkLds& tk) {
+  const int old = publish(a.ctr + kCtrBlock + 16 * b, true);
+  const int nparts = min(2, a.dn_per_route - 2 * b);    // 32-row routed items in the block
+  const int ntiles = min(4, a.shd_per_expert - 4 * b);  // 16-row shared items in the block
+  const int target = a.k * nparts + a.S * ntiles;
+  if (old != target - 1) return;
+  ensure_topk(a, tk);
+  combine_block(a, b, tk);
 }
 
-__device__ void shared_dn_item(const DecodeArgs& a, int item, Smem& sm, bool& shared_ready) {
-  if (!shared_ready) {
-    wait_sum_geq(a.ctr + kCtrShared, a.n_shgu, a.ctr + kCtrError);
-    shared_ready = true;
+__device__ void shared_dn_item(const DecodeArgs& a, int item, uint16_t* arow, WaveState& st,
+                               TopkLds& tk) {
+  // item = (expert, tile): 16 output rows of shared expert s over its whole K
+  const int s = item / a.shd_per_expert;
+  const int tile = item % a.shd_per_expert;
+  if (st.staged != 1000 + s) {
+    wait_geq(a.ctr + kCtrShared + 16 * s, a.shgu_per_expert, a.ctr + kCtrError);
+    stage_row(arow, a.hsh + (size_t)s * a.Is, a.Is);
+    st.staged = 1000 + s;
   }
-  const int l0 = item * 16;
-  const int K = a.S * a.Is;  // both experts' inputs, concatenated: A = [h_0 | h_1 | ...]
-  stage_dev(sm.as, a.hsh, K);
+  const int l0 = tile * 16;
+  const int l = l0 + (lane_id() & 15);
+  Tile16 tl[1];
+  tl[0].w = make_rsrc(a.shd + (size_t)s * a.L * a.Is, (uint32_t)a.L * a.Is * 2);
+  tl[0].row = l < a.L ? l * a.Is * 2 : kOob;
   f32x4_t acc[1];
-  // tile row l of expert s is at shd[s][l]; the concatenated K is addressed per
-  // expert, so the row pointer handed to the core is expert 0's and the core's
-  // block index runs on into the next experts' rows (see below)
-  if (a.S == 1) {
-    gemv_tiles<false, 1, 4>(sm.as, K,
-        [&](int, int col, const uint8_t*& q, const uint8_t*& sc, const uint16_t*& b) {
-          q = sc = nullptr;
-          const int l = l0 + col;
-          b = (l < a.L) ? a.shd + (size_t)l * a.Is : nullptr;
-        }, acc);
-  } else {
-    // one pass per shared expert, summed in expert order
-    f32x4_t part[1];
-    acc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s2 = 0; s2 < a.S; ++s2) {
-      gemv_tiles<false, 1, 4>(sm.as + (size_t)s2 * a.Is, a.Is,
-          [&](int, int col, const uint8_t*& q, const uint8_t*& sc, const uint16_t*& b) {
-            q = sc = nullptr;
-            const int l = l0 + col;
-            b = (l < a.L) ? a.shd + ((size_t)s2 * a.L + l) * a.Is : nullptr;
-          }, part);
-      acc[0] += part[0];
-    }
-  }
-  reduce_row0<1>(acc, sm);
-  const int tid = threadIdx.x;
-  if (tid < 16 && l0 + tid < a.L) st_dev_f32(a.ysh + l0 + tid, sum_waves(sm, 0, tid));
-  finish_block_part(a, item / 4);
+  gemv_bf16<1, 2>(arow, a.Is / 32, tl, acc);
+  const int lane = lane_id();
+  if (lane < 16 && l0 + lane < a.L) st_dev_f32(a.ysh + (size_t)s * a.L + l0 + lane, acc[0][0]);
+  finish_block_part(a, tile / 4, tk);
 }
 
-__device__ void routed_dn_item(const DecodeArgs& a, int item, Smem& sm) {
+__device__ void routed_dn_item(const DecodeArgs& a, int item, uint16_t* arow, WaveState& st,
+                               TopkLds& tk) {
   const int j = item / a.dn_per_route;
-  const int b = item % a.dn_per_route;
-  wait_geq(a.ctr + kCtrRoute + 16 * j, a.gu_per_route, a.ctr + kCtrError);
-  if (threadIdx.x == 0) sm.misc[0] = (int)ld_dev(reinterpret_cast<const uint32_t*>(a.idx) + j);
-  __syncthreads();
-  const int e = min(max(sm.misc[0], 0), a.E - 1);  // in range even after a timed-out wait
+  const int p = item % a.dn_per_route;  // 32-row part of the output
+  ensure_topk(a, tk);
+  const int e = min(max(__builtin_amdgcn_readfirstlane(tk.sel[j]), 0), a.E - 1);
+  if (st.staged != j) {
+    wait_geq(a.ctr + kCtrRoute + 16 * j, a.gu_per_route, a.ctr + kCtrError);
+    stage_row(arow, a.h + (size_t)j * a.I, a.I);
+    st.staged = j;
+  }
   const size_t qoff = (size_t)e * a.L * (a.I / 2);
   const size_t soff = (size_t)e * a.L * (a.I / 32);
-  stage_dev(sm.as, a.h + (size_t)j * a.I, a.I);
-  f32x4_t acc[4];
-  gemv_tiles<true, 4, 2>(sm.as, a.I,
-      [&](int t, int col, const uint8_t*& q, const uint8_t*& sc, const uint16_t*& bb) {
-        bb = nullptr;
-        const int l = b * 64 + t * 16 + col;
-        if (l < a.L) {
-          q = a.dq + qoff + (size_t)l * (a.I / 2);
-          sc = a.ds + soff + (size_t)l * (a.I / 32);
-        } else {
-          q = sc = nullptr;
-        }
-      }, acc);
-  reduce_row0<4>(acc, sm);
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    const int l = b * 64 + tid;
-    if (l < a.L) st_dev_f32(a.y + (size_t)j * a.L + l, sum_waves(sm, tid >> 4, tid & 15));
+  const uint32_t qbytes = (uint32_t)a.L * (a.I / 2), sbytes = (uint32_t)a.L * (a.I / 32);
+  Tile4 tl[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int l = p * 32 + t * 16 + (lane_id() & 15);
+    tl[t].codes = make_rsrc(a.dq + qoff, qbytes);
+    tl[t].scales = make_rsrc(a.ds + soff, sbytes);
+    tl[t].code_row = l < a.L ? l * (a.I / 2) : kOob;
+    tl[t].scale_row = l < a.L ? l * (a.I / 32) : kOob;
   }
-  finish_block_part(a, b);
+  f32x4_t acc[2];
+  gemv_fp4<2, 2>(arow, a.I / 32, tl, acc);
+  const int lane = lane_id();
+  if (lane < 16) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int l = p * 32 + t * 16 + lane;
+      if (l < a.L) st_dev_f32(a.y + (size_t)j * a.L + l, acc[t][0]);
+    }
+  }
+  finish_block_part(a, p / 2, tk);
 }
 
+// ---------------------------------------------------------------------------
+// The kernel: four independent waves per workgroup sharing the token and the
+// routing decision in LDS.
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
-  __shared__ Smem sm;
-  __shared__ int s_ticket;
-  const int tid = threadIdx.x;
-  // Items are dealt round-robin into kQueues ticket queues; this workgroup
-  // draws from queue blockIdx.x % kQueues. Each queue is in item order, so a
-  // workgroup only waits for smaller items; the first kQueues workgroups are
-  // dispatched first and each stays until its queue is empty, so every queue
-  // with work left always has a resident workgroup.
-  const int q = blockIdx.x % kQueues;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  __shared__ TopkLds tk;
+  uint16_t* xs = lds;
+  const int wave = threadIdx.x >> 6;
+  uint16_t* arow = lds + ((a.L + 7) & ~7) + wave * a.a_region;
+  for (int i = threadIdx.x * 8; i < a.L; i += 256 * 8)
+    *reinterpret_cast<u32x4_t*>(xs + i) = load16(a.x + i);
+  if (threadIdx.x == 0) tk.state = 0;
+  __syncthreads();
+
+  const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);
+  const int q = gw % kQueues;
   int* ticket = a.ctr + kCtrTicket + 32 * q;
-  bool routed = false, shared_ready = false;
-  for (int i = tid * 8; i < a.L; i += 256 * 8)
-    *reinterpret_cast<u32x4_t*>(sm.xs + i) = load16(a.x + i);
-  if (tid == 0) s_ticket = q + kQueues * add_dev(ticket, 1);
-  __syncthreads();
-  int t = s_ticket;
+  WaveState st{-1};
+  auto draw = [&]() {
+    int t = 0;
+    if (lane_id() == 0) t = q + kQueues * add_dev(ticket, 1);
+    return __builtin_amdgcn_readfirstlane(t);
+  };
+  int t = draw();
   while (t < a.t_total) {
-    int next = 0;
-    if (tid == 0) next = q + kQueues * add_dev(ticket, 1);
-    if (t < a.t_shgu) {
-      router_item(a, t, sm);
-      const int old = publish(a.ctr + kCtrRouter);
-      if (old == a.n_router - 1) topk_item(a, sm);
-    } else if (t < a.t_gu) {
-      shared_gu_item(a, t - a.t_shgu, sm);
-    } else if (t < a.t_shd) {
-      routed_gu_item(a, t - a.t_gu, sm, routed);
-    } else if (t < a.t_dn) {
-      shared_dn_item(a, t - a.t_shd, sm, shared_ready);
-    } else {
-      routed_dn_item(a, t - a.t_dn, sm);
-    }
-    __syncthreads();
-    if (tid == 0) s_ticket = next;
-    __syncthreads();
-    t = s_ticket;
+    const int next = draw();  // in flight while this item runs
+    if (t < a.t_shgu)
+      router_item(a, t, xs);
+    else if (t < a.t_gu)
+      shared_gu_item(a, t - a.t_shgu, xs);
+    else if (t < a.t_shd)
+      routed_gu_item(a, t - a.t_gu, xs, tk);
+    else if (t < a.t_dn)
+      shared_dn_item(a, t - a.t_shd, arow, st, tk);
+    else
+      routed_dn_item(a, t - a.t_dn, arow, st, tk);
+    t = next;
   }
-  // the last workgroup out zeroes the counters for the next launch
-  if (tid == 0) {
-    const int old = add_dev(a.ctr + kCtrExit, 1);
-    s_ticket = (old == (int)gridDim.x - 1);
+  if (blockIdx.x == 0 && wave == 0) {
+    ensure_topk(a, tk);
+    write_routing(a, tk);
   }
-  __syncthreads();
-  if (s_ticket) {
+  // the last wave out zeroes the counters for the next launch
+  int last = 0;
+  if (lane_id() == 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    last = add_dev(a.ctr + kCtrExit, 1) == (int)gridDim.x * 4 - 1;
+  }
+  if (__builtin_amdgcn_readfirstlane(last)) {
+    const int lane = lane_id();
     const int nb = (a.L + 63) / 64;
-    for (int i = tid; i < a.k; i += 256) st_dev(a.ctr + kCtrRoute + 16 * i, 0);
-    for (int i = tid; i < nb; i += 256) st_dev(a.ctr + kCtrBlock + 16 * i, 0);
-    if (tid < kQueues) {
-      st_dev(a.ctr + kCtrTicket + 32 * tid, 0);
-      st_dev(a.ctr + kCtrShared + 32 * tid, 0);
-    }
-    if (tid == 0) {
-      st_dev(a.ctr + kCtrRouter, 0);
-      st_dev(a.ctr + kCtrTopk, 0);
+    for (int i = lane; i < a.k; i += kWave) st_dev(a.ctr + kCtrRoute + 16 * i, 0);
+    for (int i = lane; i < nb; i += kWave) st_dev(a.ctr + kCtrBlock + 16 * i, 0);
+    for (int i = lane; i < a.S; i += kWave) st_dev(a.ctr + kCtrShared + 16 * i, 0);
+    if (lane < kQueues) st_dev(a.ctr + kCtrTicket + 32 * lane, 0);
+    if (lane == 0) {
+      st_dev(a.ctr + kCtrRouterDone, 0);
       st_dev(a.ctr + kCtrExit, 0);
     }
   }
@@ -655,19 +724,22 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-static int decode_grid() {
+static int decode_grid(size_t lds_bytes) {
   static int cached[64] = {0};
+  static size_t cached_lds[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] > 0) return cached[dev];
-  int cus = 0, per = 0;
+  if (cached[dev] > 0 && cached_lds[dev] == lds_bytes) return cached[dev];
+  int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel, 256, 0) != hipSuccess ||
-      per <= 0)
-    per = 2;
-  cached[dev] = cus * per;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel, 256, lds_bytes) !=
+          hipSuccess ||
+      per_cu <= 0)
+    per_cu = 1;
+  cached[dev] = cus * std::min(per_cu, kWgPerCu);
+  cached_lds[dev] = lds_bytes;
   return cached[dev];
 }
 
@@ -679,33 +751,36 @@ void make_decode_args(const Plan& p, DecodeArgs& a) {
   a.I = d.I;
   a.S = d.S;
   a.Is = d.Is;
-  const int nsteps = d.L / 32;
-  int nks = std::min(nsteps, 16);
-  int rk = 32 * ((nsteps + nks - 1) / nks);
-  if (rk > 256) rk = 256;
-  nks = (d.L + rk - 1) / rk;
-  a.nks = nks;
-  a.rk = rk;
-  a.neg = (d.E + 127) / 128;
-  a.n_router = nks * a.neg;
-  a.n_shgu = d.S > 0 ? d.S * ((d.Is + 7) / 8) : 0;
+  a.n_router = d.E;
+  a.shgu_per_expert = d.S > 0 ? (d.Is + 7) / 8 : 0;
+  a.n_shgu = d.S * a.shgu_per_expert;
   a.gu_per_route = (d.I + 15) / 16;
-  a.dn_per_route = (d.L + 63) / 64;
   a.n_gu = d.k * a.gu_per_route;
-  a.n_shd = d.S > 0 ? d.L / 16 : 0;
+  a.shd_per_expert = d.L / 16;
+  a.n_shd = d.S * a.shd_per_expert;
+  a.dn_per_route = (d.L + 31) / 32;
   a.n_dn = d.k * a.dn_per_route;
   a.t_shgu = a.n_router;
   a.t_gu = a.t_shgu + a.n_shgu;
   a.t_shd = a.t_gu + a.n_gu;
   a.t_dn = a.t_shd + a.n_shd;
   a.t_total = a.t_dn + a.n_dn;
+  // per-wave A row: h of one route or of one shared expert
+  a.a_region = std::max(d.I, d.S > 0 ? d.Is : 0);
+  a.lds_bytes = (size_t)(((d.L + 7) & ~7) + 4 * a.a_region) * 2;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  // at least one workgroup per ticket queue
-  const int grid = std::max(kQueues, std::min(decode_grid(), a.t_total));
-  hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(256), 0, s, a);
-  return hipGetLastError();
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, const hipEvent_t* ev) {
+  hipError_t e = record_stage(ev, LMOE_STAGE_BEGIN, s);
+  if (e != hipSuccess) return e;
+  // at least one wave per ticket queue
+  const int grid = std::max((kQueues + 3) / 4, decode_grid(a.lds_bytes));
+  hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(256), a.lds_bytes, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // one kernel holds every stage
+  for (int i = LMOE_STAGE_ROUTER; i < LMOE_NUM_STAGE_EVENTS; ++i)
+    if ((e = record_stage(ev, i, s)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 }  // namespace lmoe

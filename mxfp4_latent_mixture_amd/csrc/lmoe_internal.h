@@ -25,15 +25,14 @@ struct RouterPlan {
 // Counter block at the start of every workspace (int32 slots, each counter on
 // its own 64- or 128-byte line). Only the single-token decode kernel uses it;
 // it must be zero when that kernel starts and is left zeroed when it ends.
-constexpr int kQueues = 8;        // ticket queues: item i is in queue i % kQueues
-constexpr int kCtrTicket = 0;     // + 32 * queue
-constexpr int kCtrExit = 256;
-constexpr int kCtrRouter = 288;
-constexpr int kCtrTopk = 320;
-constexpr int kCtrShared = 352;   // + 32 * (item % kQueues)
-constexpr int kCtrError = 608;
-constexpr int kCtrRoute = 640;    // + 16 * route, route < 32
-constexpr int kCtrBlock = 1152;   // + 16 * block, block < 256 (64-row blocks of L)
+constexpr int kQueues = 8;          // ticket queues: item i is in queue i % kQueues
+constexpr int kCtrTicket = 0;       // + 32 * queue
+constexpr int kCtrExit = 256;       // waves that have left
+constexpr int kCtrRouterDone = 288; // router items whose logit is published
+constexpr int kCtrError = 608;      // dependency waits abandoned at the spin limit
+constexpr int kCtrRoute = 640;      // + 16 * route (< 32): gate/up items done
+constexpr int kCtrBlock = 1152;     // + 16 * block (< 64): parts of a 64-row output block done
+constexpr int kCtrShared = 2176;    // + 16 * shared expert (< 128): gate/up items done
 constexpr size_t kCtrBytes = 32768;
 // The single-token decode kernel keeps the token and one A row in LDS.
 constexpr int kDecodeMaxWidth = 4096;
@@ -63,17 +62,17 @@ struct Workspace {
   float* y;           // [R][L] fp32 route partials, sorted route order
   float* y_sh;        // [S][T][L] fp32
   // single-token decode
-  float* dpart;       // [nks][E] partial logits
+  float* dlogit;      // [E] logits
   uint16_t* dh;       // [k][I] bf16
   uint16_t* dhsh;     // [S][Is] bf16
   float* dy;          // [k][L]
-  float* dysh;        // [L]
+  float* dysh;        // [S][L]
   size_t bytes;       // total bytes needed
 };
 
 struct DecodeArgs {
   const uint16_t* x;   // [L] bf16
-  const uint16_t* wr;  // [L][E] bf16
+  const uint16_t* wr;  // [E][L] bf16
   const uint8_t *gq, *gs, *uq, *us, *dq, *ds;
   const uint16_t *shg, *shu, *shd;
   int L, E, k, I, S, Is;
@@ -83,15 +82,17 @@ struct DecodeArgs {
   int32_t *counts, *offsets, *perm, *inv;
   uint16_t* out;
   int32_t* ctr;
-  float* part;
-  uint16_t* h;
-  uint16_t* hsh;
-  float* y;
-  float* ysh;
-  int nks, rk, neg;
+  float* logit;        // [E] published logits
+  uint16_t* h;         // [k][I] bf16
+  uint16_t* hsh;       // [S][Is] bf16
+  float* y;            // [k][L] routed down outputs
+  float* ysh;          // [S][L] shared down outputs
+  // work items by kind, in ticket order, and where each kind starts
   int n_router, n_shgu, n_gu, n_shd, n_dn;
   int t_shgu, t_gu, t_shd, t_dn, t_total;
-  int gu_per_route, dn_per_route;
+  int shgu_per_expert, gu_per_route, dn_per_route, shd_per_expert;
+  int a_region;        // per-wave LDS A row, bf16 elements
+  size_t lds_bytes;    // dynamic LDS per workgroup
 };
 
 Plan make_plan(const lmoe_dims& d);
@@ -119,7 +120,7 @@ inline hipError_t record_stage(const hipEvent_t* ev, int stage, hipStream_t s) {
 }
 // ---- single-token decode (decode.hip) ----
 void make_decode_args(const Plan& p, DecodeArgs& a);
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, const hipEvent_t* ev);
 
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* sc, int rows, int K, uint16_t* out,
                           hipStream_t s);

@@ -13,7 +13,7 @@
 namespace lmoe {
 
 // ---------------------------------------------------------------------------
-// Router: part[split][t][e] = sum over the split's K range of x[t][k] W[k][e].
+// Router: part[split][t][e] = sum over the split's K range of x[t][k] W[e][k].
 // Tile: 64 tokens x 64 experts per 256-thread workgroup, one 32-wide K step
 // per pass; each wave owns 16 tokens and four 16-expert MFMA tiles.
 // ---------------------------------------------------------------------------
@@ -36,7 +36,6 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict_
   const int nsteps = L / 32;
   const int st0 = split * steps_per;
   const int st1 = min(nsteps, st0 + steps_per);
-  const bool vecw = (E % 8) == 0;
 
   f32x4_t acc[4];
 #pragma unroll
@@ -51,24 +50,12 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict_
       if (t < T) v = load16(x + (size_t)t * L + st * 32 + q * 8);
       *reinterpret_cast<u32x4_t*>(&sx[row][q * 8]) = v;
     }
-    {  // router weights: 32 K rows x 64 experts, stored transposed
-      const int kr = tid >> 3, q = tid & 7;
-      const int e = e0 + q * 8;
-      const uint16_t* src = wr + (size_t)(st * 32 + kr) * E + e;
-      uint16_t vals[8];
-      if (vecw && e + 8 <= E) {
-        u32x4_t v = load16(src);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          vals[2 * i] = (uint16_t)(v[i] & 0xFFFFu);
-          vals[2 * i + 1] = (uint16_t)(v[i] >> 16);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vals[i] = (e + i < E) ? src[i] : (uint16_t)0;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sw[q * 8 + i][kr] = vals[i];
+    {  // router weights: 64 expert rows x 32 values, 16 bytes per thread
+      const int er = tid >> 2, q = tid & 3;
+      const int e = e0 + er;
+      u32x4_t v = zero16();
+      if (e < E) v = load16(wr + (size_t)e * L + st * 32 + q * 8);
+      *reinterpret_cast<u32x4_t*>(&sw[er][q * 8]) = v;
     }
     __syncthreads();
     const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sx[wave * 16 + col][grp * 8]);

@@ -139,10 +139,11 @@ def f32_round(v: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 def router_logits(x_bits: np.ndarray, router_bits: np.ndarray) -> np.ndarray:
-    """logits[t,e] = fp32(sum_l x[t,l] W[l,e]), float64 sum. W is [L][E]."""
+    """logits[t,e] = fp32(sum_l x[t,l] W[e,l]), float64 sum. W is [E][L]: one
+    row of the router projection per expert."""
     x = f64_from_bf16(x_bits)
     wr = f64_from_bf16(router_bits)
-    return f32_round(x @ wr)
+    return f32_round(x @ wr.T)
 
 
 def topk_select(logits: np.ndarray, k: int) -> np.ndarray:

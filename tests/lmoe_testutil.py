@@ -102,7 +102,7 @@ def logits_bound(x_bits: np.ndarray, wr_bits: np.ndarray) -> np.ndarray:
     ax = np.abs(O.f64_from_bf16(x_bits))
     aw = np.abs(O.f64_from_bf16(wr_bits))
     L = ax.shape[1]
-    s = ax @ aw
+    s = ax @ aw.T
     return (L + 2) * 2.0 ** -24 * s + 2.0 ** -24 * s
 
 

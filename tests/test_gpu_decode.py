@@ -14,7 +14,7 @@ from lmoe_testutil import (log, upload, alloc_routing, check_out, logits_bound,
 pytestmark = pytest.mark.gpu
 
 CTR_INTS = 32768 // 4
-ERROR_SLOT = 160
+ERROR_SLOT = 608 // 4  # kCtrError is a byte offset
 
 
 @pytest.fixture(scope="module")

@@ -269,15 +269,16 @@ def test_softmax_weights_against_scipy_and_closed_forms():
 def test_router_logits_one_hot_and_ones():
     L, E = 64, 12
     rng = np.random.default_rng(1)
-    wr = O.bf16_from_f64(rng.normal(0, 0.02, size=(L, E)))
+    wr = O.bf16_from_f64(rng.normal(0, 0.02, size=(E, L)))
     x = np.zeros((L, L), np.uint16)
     for t in range(L):
         x[t, t] = 0x3F80          # 1.0
     lg = O.router_logits(x, wr)
-    assert np.array_equal(lg, O.f64_from_bf16(wr).astype(np.float32))
+    # token t picks column t of W: the logit of expert e is W[e, t]
+    assert np.array_equal(lg, O.f64_from_bf16(wr).T.astype(np.float32))
     # x = 1 and W = 0.5 everywhere: logits are exactly L/2
     ones = np.full((2, L), 0x3F80, np.uint16)
-    half = np.full((L, E), 0x3F00, np.uint16)
+    half = np.full((E, L), 0x3F00, np.uint16)
     assert np.all(O.router_logits(ones, half) == L / 2)
 
 
@@ -350,7 +351,7 @@ def test_glu_closed_form_all_ones():
 def _small_layer(seed=0, T=9, L=64, E=6, k=3, I=64, S=2, Is=32):
     rng = np.random.default_rng(seed)
     x = O.bf16_from_f64(rng.normal(size=(T, L)))
-    wr = O.bf16_from_f64(rng.normal(0, 0.1, size=(L, E)))
+    wr = O.bf16_from_f64(rng.normal(0, 0.1, size=(E, L)))
     ex = {
         "gate_q": rng.integers(0, 256, size=(E, I, L // 2)).astype(np.uint8),
         "up_q": rng.integers(0, 256, size=(E, I, L // 2)).astype(np.uint8),
@@ -391,7 +392,7 @@ def test_forward_matches_independent_torch_layer():
     res = O.forward(x, wr, ex, sh, k)
 
     xt = torch.from_numpy(O.f64_from_bf16(x))
-    lg = (xt @ torch.from_numpy(O.f64_from_bf16(wr))).to(torch.float32).numpy()
+    lg = (xt @ torch.from_numpy(O.f64_from_bf16(wr)).T).to(torch.float32).numpy()
     assert np.array_equal(lg, res["logits"])
     W = {}
     for e in range(E):
@@ -458,7 +459,7 @@ def test_relabelling_experts_leaves_output_unchanged():
     base = O.forward(x, wr, ex, sh, 3)
     p = np.random.default_rng(0).permutation(7)       # new label of old expert e is inv[e]
     ex2 = {k: v[p] for k, v in ex.items()}
-    wr2 = wr[:, p]
+    wr2 = wr[p]                                       # router rows follow their experts
     res = O.forward(x, wr2, ex2, sh, 3)
     assert np.array_equal(res["out"], base["out"])
     assert np.array_equal(p[res["idx"]], base["idx"])

@@ -7,7 +7,7 @@ oracle, the GPU tests and the bench.
 
 Byte layouts produced here (the layout the layer consumes):
   x          bf16 bits, uint16 [T][L]            N(0, x_std)
-  router_w   bf16 bits, uint16 [L][E]            N(0, router_std)
+  router_w   bf16 bits, uint16 [E][L]            N(0, router_std)
   gate_q     uint8 [E][I][L/2]   E2M1 codes, element 2m in the low nibble of byte m
   gate_s     uint8 [E][I][L/32]  E8M0 exponents, one per 32 consecutive inputs
   up_q/up_s  same shapes as gate
@@ -66,7 +66,7 @@ def gen_x(w: Workload) -> np.ndarray:
 
 def gen_router(w: Workload) -> np.ndarray:
     d = w.dims
-    v = _rng(w.seed, TID_ROUTER).normal(0.0, w.router_std, size=(d.L, d.E))
+    v = _rng(w.seed, TID_ROUTER).normal(0.0, w.router_std, size=(d.E, d.L))
     return _normal_to_bf16_bits(v)
 
 
