@@ -30,8 +30,8 @@
 // saves the round trips of a single selecting wave writing and every consumer
 // reading back the choice. Workgroup 0 writes the routing outputs.
 //
-// Tickets: items are dealt round-robin into eight queues (device-scope
-// atomics on one address serialise, about 12 ns each on MI355X). A wave only
+// Tickets: items are dealt round-robin into 32 queues (device-scope atomics
+// on one address serialise, about 12 ns each on MI355X). A wave only
 // ever waits for smaller items. The smallest unfinished item is either being
 // processed (its inputs are all done) or heads its queue, and a resident wave
 // of that queue will draw it: waves are dispatched in index order and a wave
@@ -53,6 +53,8 @@ namespace {
 constexpr long kSpinLimit = 1l << 22;
 constexpr int kMaxK = 32;         // routes per token on this path
 constexpr int kKeysPerLane = 16;  // E <= 1024 logits, 16 per lane
+constexpr int kMaxShared = 8;     // shared experts
+constexpr int kDepth = 1;         // bursts of weights in flight ahead of the MFMAs
 // Workgroups per compute unit. Four streaming waves per CU keep enough bytes
 // in flight; more concurrent items only lengthen each item and the tail.
 constexpr int kWgPerCu = 1;
@@ -103,13 +105,17 @@ __device__ __forceinline__ int publish(int* ctr, bool want_old) {
   return __builtin_amdgcn_readfirstlane(old);
 }
 
-// Waits until the counter reaches target. A wait that outlives the spin limit
-// (a broken producer) is counted in the error slot and abandoned.
-__device__ __forceinline__ void wait_geq(const int* ctr, int target, int* err) {
+// Waits until the sum of n (<= 64) counters spaced `stride` ints apart reaches
+// target. A wait that outlives the spin limit (a broken producer) is counted in
+// the error slot and abandoned.
+__device__ __forceinline__ void wait_geq(const int* ctr, int target, int* err, int n = 1,
+                                         int stride = 0) {
   long it = 0;
   for (;;) {
     int s = 0;
-    if (lane_id() == 0) s = ld_dev(ctr);
+    if (lane_id() < n) s = ld_dev(ctr + stride * lane_id());
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off, kWave);
     s = __builtin_amdgcn_readfirstlane(s);
     if (s >= target) break;
     if (++it > kSpinLimit) {
@@ -120,30 +126,6 @@ __device__ __forceinline__ void wait_geq(const int* ctr, int target, int* err) {
   }
 }
 
-// Wave-wide maximum of a 64-bit key with DPP row shifts and row broadcasts;
-// the result is returned to every lane.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-#define LMOE_DPP_MAX(ctrl, rmask, bmask)                                                   \
-  {                                                                                        \
-    const uint32_t tlo = __builtin_amdgcn_update_dpp(lo, lo, ctrl, rmask, bmask, false);   \
-    const uint32_t thi = __builtin_amdgcn_update_dpp(hi, hi, ctrl, rmask, bmask, false);   \
-    const bool gt = (thi > hi) || (thi == hi && tlo > lo);                                 \
-    lo = gt ? tlo : lo;                                                                    \
-    hi = gt ? thi : hi;                                                                    \
-  }
-  LMOE_DPP_MAX(0x111, 0xf, 0xf)  // row_shr:1
-  LMOE_DPP_MAX(0x112, 0xf, 0xf)  // row_shr:2
-  LMOE_DPP_MAX(0x114, 0xf, 0xf)  // row_shr:4
-  LMOE_DPP_MAX(0x118, 0xf, 0xf)  // row_shr:8: lane 15 of each row holds the row max
-  LMOE_DPP_MAX(0x142, 0xa, 0xf)  // row_bcast:15 into rows 1 and 3
-  LMOE_DPP_MAX(0x143, 0xc, 0xf)  // row_bcast:31 into rows 2 and 3: lane 63 holds the max
-#undef LMOE_DPP_MAX
-  lo = __builtin_amdgcn_readlane(lo, 63);
-  hi = __builtin_amdgcn_readlane(hi, 63);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 // Order: larger logit first, equal logits by lower expert index, NaN after
 // every number, -0 == +0; one distinct 64-bit key per expert.
 __device__ __forceinline__ uint64_t order_key(float f, int e) {
@@ -151,6 +133,32 @@ __device__ __forceinline__ uint64_t order_key(float f, int e) {
   if (f == 0.0f) u = 0u;
   const uint32_t k32 = (f != f) ? 0u : ((u & 0x80000000u) ? ~u : (u | 0x80000000u));
   return ((uint64_t)k32 << 32) | (uint64_t)(~(uint32_t)e);
+}
+
+// The logit a key was made from (-0 reads back as +0, NaN as a NaN).
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t k32 = (uint32_t)(key >> 32);
+  return __uint_as_float((k32 & 0x80000000u) ? (k32 & 0x7fffffffu) : ~k32);
+}
+
+// Wave-wide maximum of a 32-bit value with DPP row shifts and row broadcasts;
+// the result is returned to every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+// lanes without a source (and rows outside the mask) read 0, the identity of
+// the maximum, which lets the move fold into one v_max_u32 with DPP
+#define LMOE_DPP_MAX32(ctrl, rmask)                                                        \
+  {                                                                                        \
+    const uint32_t t = __builtin_amdgcn_update_dpp(0u, v, ctrl, rmask, 0xf, false);        \
+    v = t > v ? t : v;                                                                     \
+  }
+  LMOE_DPP_MAX32(0x111, 0xf)  // row_shr:1
+  LMOE_DPP_MAX32(0x112, 0xf)  // row_shr:2
+  LMOE_DPP_MAX32(0x114, 0xf)  // row_shr:4
+  LMOE_DPP_MAX32(0x118, 0xf)  // row_shr:8: lane 15 of each row holds the row max
+  LMOE_DPP_MAX32(0x142, 0xa)  // row_bcast:15 into rows 1 and 3
+  LMOE_DPP_MAX32(0x143, 0xc)  // row_bcast:31 into rows 2 and 3: lane 63 holds the max
+#undef LMOE_DPP_MAX32
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Per-wave state kept across items.
@@ -214,11 +222,15 @@ struct Tile16 {
   int row;
 };
 
-template <int NT, int IPB>
+// D bursts are kept in flight ahead of the one being computed, in a ring of
+// RING buffers. `pre` runs once the first bursts are in flight and before arow
+// is first read: a dependency wait and the staging of arow overlap those loads.
+template <int NT, int IPB, int D, typename Pre>
 __device__ __forceinline__ void gemv_fp4(const uint16_t* arow, int nblk, const Tile4 (&tl)[NT],
-                                         f32x4_t (&acc)[NT]) {
-  static_assert(8 % IPB == 0 && (8 / IPB) % 2 == 0, "a window is an even number of bursts");
+                                         f32x4_t (&acc)[NT], Pre&& pre) {
   constexpr int BPW = 8 / IPB;  // bursts per 64-block window
+  constexpr int RING = D == 1 ? 2 : 4;
+  static_assert(8 % IPB == 0 && BPW % RING == 0 && D < RING, "the ring must tile a window");
   const int grp = lane_id() >> 4;
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -313,32 +325,36 @@ __device__ __forceinline__ void gemv_fp4(const uint16_t* arow, int nblk, const T
       }
     }
   };
-  Buf buf[2];
+  Buf buf[RING];
   load_exps(0);
   __builtin_amdgcn_sched_barrier(0);
-  load(0, 0, buf[0]);
+#pragma unroll
+  for (int b = 0; b < D; ++b) load(0, b, buf[b]);
   __builtin_amdgcn_sched_barrier(0);
+  pre();
   take_exps();
   for (int w = 0; w < nwin; ++w) {
 #pragma unroll
     for (int bp = 0; bp < BPW; ++bp) {
-      // the next burst (the next window's first at the end of this one)
-      if (bp + 1 < BPW)
-        load(w, bp + 1, buf[(bp + 1) & 1]);
+      // the burst D ahead (in the next window near the end of this one)
+      if (bp + D < BPW)
+        load(w, bp + D, buf[(bp + D) % RING]);
       else
-        load(w + 1, 0, buf[0]);
+        load(w + 1, bp + D - BPW, buf[(bp + D) % RING]);
       if (bp == 0) load_exps(w + 1);
       __builtin_amdgcn_sched_barrier(0);
-      compute(w, bp, buf[bp & 1]);
+      compute(w, bp, buf[bp % RING]);
       __builtin_amdgcn_sched_barrier(0);
     }
     take_exps();
   }
 }
 
-template <int NT, int IPB>
+template <int NT, int IPB, int D, typename Pre>
 __device__ __forceinline__ void gemv_bf16(const uint16_t* arow, int nblk, const Tile16 (&tl)[NT],
-                                          f32x4_t (&acc)[NT]) {
+                                          f32x4_t (&acc)[NT], Pre&& pre) {
+  constexpr int RING = D == 1 ? 2 : 4;
+  static_assert(D < RING, "the ring holds the bursts in flight");
   const int grp = lane_id() >> 4;
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -374,26 +390,35 @@ __device__ __forceinline__ void gemv_bf16(const uint16_t* arow, int nblk, const 
     }
   };
   // no load is conditional: bursts past the end read out of bounds (zeros)
-  Buf wa, wb;
-  load(0, wa);
+  Buf buf[RING];
+#pragma unroll
+  for (int b = 0; b < D; ++b) load(b, buf[b]);
   __builtin_amdgcn_sched_barrier(0);
-  for (int b = 0; b < bursts; b += 2) {
-    load(b + 1, wb);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(b, wa);
-    __builtin_amdgcn_sched_barrier(0);
-    load(b + 2, wa);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(b + 1, wb);
-    __builtin_amdgcn_sched_barrier(0);
+  pre();
+  for (int b = 0; b < bursts; b += RING) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      load(b + r + D, buf[(r + D) % RING]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(b + r, buf[r]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
-// Copy n bf16 values written by other waves of this launch into the wave's
-// LDS row (n a multiple of 8).
+// Copy n (<= kDecodeMaxWidth, a multiple of 8) bf16 values written by other
+// waves of this launch into the wave's LDS row. Every load is issued before
+// the first store (indices clamped in range).
 __device__ __forceinline__ void stage_row(uint16_t* dst, const uint16_t* src, int n) {
-  for (int i = lane_id() * 8; i < n; i += kWave * 8)
-    *reinterpret_cast<u32x4_t*>(dst + i) = ld16_dev(src + i);
+  constexpr int kChunks = kDecodeMaxWidth / (kWave * 8);
+  u32x4_t v[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) v[c] = ld16_dev(src + min(c * kWave * 8 + lane_id() * 8, n - 8));
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int i = c * kWave * 8 + lane_id() * 8;
+    if (i < n) *reinterpret_cast<u32x4_t*>(dst + i) = v[c];
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
 }
@@ -447,7 +472,7 @@ __device__ void router_item(const DecodeArgs& a, int e, const uint16_t* xs) {
     st_dev_f32(a.logit + e, acc);
     if (a.logits_out) a.logits_out[e] = acc;
   }
-  publish(a.ctr + kCtrRouterDone, false);
+  publish(a.ctr + kCtrRouter + 16 * (e % kRouterSlots), false);
 }
 
 // The routing decision of this workgroup: computed by the first wave that
@@ -465,34 +490,64 @@ __device__ void ensure_topk(const DecodeArgs& a, TopkLds& tk) {
       __builtin_amdgcn_s_sleep(1);
     return;
   }
-  wait_geq(a.ctr + kCtrRouterDone, a.n_router, a.ctr + kCtrError);
+  wait_geq(a.ctr + kCtrRouter, a.n_router, a.ctr + kCtrError, kRouterSlots, 16);
   const int lane = lane_id();
+  // every load is issued before the first is used (indices clamped in range)
+  float lv[kKeysPerLane];
+#pragma unroll
+  for (int i = 0; i < kKeysPerLane; ++i) lv[i] = ld_dev_f32(a.logit + min(lane + kWave * i, a.E - 1));
   uint64_t key[kKeysPerLane];
 #pragma unroll
   for (int i = 0; i < kKeysPerLane; ++i) {
     const int e = lane + kWave * i;
-    key[i] = (e < a.E) ? order_key(ld_dev_f32(a.logit + e), e) : 0ull;
+    key[i] = (e < a.E) ? order_key(lv[i], e) : 0ull;
   }
-  uint64_t best = 0ull;
+  // k rounds of a wave-wide maximum over each lane's best remaining key. A
+  // lane keeps its best two keys, so a win usually costs a register move; a
+  // lane that wins a third time rescans its keys below the last one it gave.
+  uint64_t b1 = 0ull, b2 = 0ull;
 #pragma unroll
-  for (int i = 0; i < kKeysPerLane; ++i) best = key[i] > best ? key[i] : best;
-  int my_e = 0;
-  float my_l = 0.f;
+  for (int i = 0; i < kKeysPerLane; ++i) {
+    const uint64_t kk = key[i];
+    b2 = kk > b1 ? b1 : (kk > b2 ? kk : b2);
+    b1 = kk > b1 ? kk : b1;
+  }
+  bool have2 = true, need = false;
+  uint64_t last = ~0ull;
+  uint64_t mine = 0ull;  // lane j: the key chosen in round j
   for (int j = 0; j < a.k; ++j) {
-    const uint64_t b = wave_max_u64(best);
-    const int ew = (int)(~(uint32_t)b);
-    if ((ew & (kWave - 1)) == lane) {
-      const int slot = ew / kWave;
-      best = 0ull;
-#pragma unroll
-      for (int i = 0; i < kKeysPerLane; ++i) {
-        if (i == slot) key[i] = 0ull;
-        best = key[i] > best ? key[i] : best;
+    const uint32_t hi = (uint32_t)(b1 >> 32), lo = (uint32_t)b1;
+    const uint32_t mhi = wave_max_u32(hi);
+    // the low word decides only between lanes holding the same high word
+    const uint64_t at_max = __builtin_amdgcn_ballot_w64(hi == mhi);
+    uint32_t mlo;
+    if (__builtin_popcountll(at_max) == 1)
+      mlo = __builtin_amdgcn_readlane(lo, __builtin_ctzll(at_max));
+    else
+      mlo = wave_max_u32(hi == mhi ? lo : 0u);
+    const uint64_t won = ((uint64_t)mhi << 32) | mlo;
+    if (lane == j) mine = won;
+    if (b1 == won) {  // keys are distinct: exactly one lane wins
+      last = won;
+      if (have2) {
+        b1 = b2;
+        have2 = false;
+      } else {
+        need = true;
       }
     }
-    if (lane == j) my_e = ew;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      if (need) {
+        b1 = 0ull;
+#pragma unroll
+        for (int i = 0; i < kKeysPerLane; ++i)
+          b1 = (key[i] < last && key[i] > b1) ? key[i] : b1;
+        need = false;
+      }
+    }
   }
-  if (lane < a.k) my_l = ld_dev_f32(a.logit + my_e);
+  const int my_e = (int)(~(uint32_t)mine);
+  const float my_l = lane < a.k ? key_value(mine) : 0.f;
   // softmax over the selected logits, relative to the largest
   const float l0 = __shfl(my_l, 0, kWave);
   const float z = (lane < a.k) ? expf(my_l - l0) : 0.f;
@@ -548,7 +603,7 @@ __device__ void shared_gu_item(const DecodeArgs& a, int item, const uint16_t* xs
   tl[0].w = make_rsrc((col < 8 ? a.shg : a.shu) + (size_t)s * a.Is * a.L, mbytes);
   tl[0].row = i < a.Is ? i * a.L * 2 : kOob;
   f32x4_t acc[1];
-  gemv_bf16<1, 2>(xs, a.L / 32, tl, acc);
+  gemv_bf16<1, 2, kDepth>(xs, a.L / 32, tl, acc, [] {});
   // g in lanes 0..7, u in lanes 8..15
   store_glu(a.hsh + (size_t)s * a.Is + i0, acc[0][0], acc[0][0], 8, 8, a.Is - i0);
   publish(a.ctr + kCtrShared + 16 * s, false);
@@ -572,21 +627,29 @@ __device__ void routed_gu_item(const DecodeArgs& a, int item, const uint16_t* xs
   tl[0].code_row = tl[1].code_row = i < a.I ? i * (a.L / 2) : kOob;
   tl[0].scale_row = tl[1].scale_row = i < a.I ? i * (a.L / 32) : kOob;
   f32x4_t acc[2];
-  gemv_fp4<2, 2>(xs, a.L / 32, tl, acc);
+  gemv_fp4<2, 2, kDepth>(xs, a.L / 32, tl, acc, [] {});
   // g in lanes 0..15 of tile 0, u in lanes 0..15 of tile 1
   store_glu(a.h + (size_t)j * a.I + i0, acc[0][0], acc[1][0], 16, 0, a.I - i0);
   publish(a.ctr + kCtrRoute + 16 * j, false);
 }
 
 __device__ void combine_block(const DecodeArgs& a, int b, const TopkLds& tk) {
-  const int l = b * 64 + lane_id();
-  if (l < a.L) {
-    float acc = 0.f;
-    for (int j = 0; j < a.k; ++j)
-      acc = fmaf(tk.w[j], ld_dev_f32(a.y + (size_t)j * a.L + l), acc);
-    for (int s = 0; s < a.S; ++s) acc += ld_dev_f32(a.ysh + (size_t)s * a.L + l);
-    a.out[l] = f32_to_bf16_bits(acc);
-  }
+  // every load is issued before the first is used (indices clamped in range)
+  const int l = min(b * 64 + lane_id(), a.L - 1);
+  float yv[kMaxK], sv[kMaxShared];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) yv[j] = ld_dev_f32(a.y + (size_t)min(j, a.k - 1) * a.L + l);
+#pragma unroll
+  for (int s = 0; s < kMaxShared; ++s)
+    sv[s] = a.S > 0 ? ld_dev_f32(a.ysh + (size_t)min(s, a.S - 1) * a.L + l) : 0.f;
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < a.k) acc = fmaf(tk.w[j], yv[j], acc);
+#pragma unroll
+  for (int s = 0; s < kMaxShared; ++s)
+    if (s < a.S) acc += sv[s];
+  if (b * 64 + lane_id() < a.L) a.out[l] = f32_to_bf16_bits(acc);
 }
 
 // One more input of 64-row block b is ready; the last one combines the block.
@@ -605,18 +668,19 @@ __device__ void shared_dn_item(const DecodeArgs& a, int item, uint16_t* arow, Wa
   // item = (expert, tile): 16 output rows of shared expert s over its whole K
   const int s = item / a.shd_per_expert;
   const int tile = item % a.shd_per_expert;
-  if (st.staged != 1000 + s) {
-    wait_geq(a.ctr + kCtrShared + 16 * s, a.shgu_per_expert, a.ctr + kCtrError);
-    stage_row(arow, a.hsh + (size_t)s * a.Is, a.Is);
-    st.staged = 1000 + s;
-  }
   const int l0 = tile * 16;
   const int l = l0 + (lane_id() & 15);
   Tile16 tl[1];
   tl[0].w = make_rsrc(a.shd + (size_t)s * a.L * a.Is, (uint32_t)a.L * a.Is * 2);
   tl[0].row = l < a.L ? l * a.Is * 2 : kOob;
   f32x4_t acc[1];
-  gemv_bf16<1, 2>(arow, a.Is / 32, tl, acc);
+  gemv_bf16<1, 2, kDepth>(arow, a.Is / 32, tl, acc, [&] {
+    if (st.staged != 1000 + s) {
+      wait_geq(a.ctr + kCtrShared + 16 * s, a.shgu_per_expert, a.ctr + kCtrError);
+      stage_row(arow, a.hsh + (size_t)s * a.Is, a.Is);
+      st.staged = 1000 + s;
+    }
+  });
   const int lane = lane_id();
   if (lane < 16 && l0 + lane < a.L) st_dev_f32(a.ysh + (size_t)s * a.L + l0 + lane, acc[0][0]);
   finish_block_part(a, tile / 4, tk);
@@ -628,11 +692,6 @@ __device__ void routed_dn_item(const DecodeArgs& a, int item, uint16_t* arow, Wa
   const int p = item % a.dn_per_route;  // 32-row part of the output
   ensure_topk(a, tk);
   const int e = min(max(__builtin_amdgcn_readfirstlane(tk.sel[j]), 0), a.E - 1);
-  if (st.staged != j) {
-    wait_geq(a.ctr + kCtrRoute + 16 * j, a.gu_per_route, a.ctr + kCtrError);
-    stage_row(arow, a.h + (size_t)j * a.I, a.I);
-    st.staged = j;
-  }
   const size_t qoff = (size_t)e * a.L * (a.I / 2);
   const size_t soff = (size_t)e * a.L * (a.I / 32);
   const uint32_t qbytes = (uint32_t)a.L * (a.I / 2), sbytes = (uint32_t)a.L * (a.I / 32);
@@ -646,7 +705,13 @@ __device__ void routed_dn_item(const DecodeArgs& a, int item, uint16_t* arow, Wa
     tl[t].scale_row = l < a.L ? l * (a.I / 32) : kOob;
   }
   f32x4_t acc[2];
-  gemv_fp4<2, 2>(arow, a.I / 32, tl, acc);
+  gemv_fp4<2, 2, kDepth>(arow, a.I / 32, tl, acc, [&] {
+    if (st.staged != j) {
+      wait_geq(a.ctr + kCtrRoute + 16 * j, a.gu_per_route, a.ctr + kCtrError);
+      stage_row(arow, a.h + (size_t)j * a.I, a.I);
+      st.staged = j;
+    }
+  });
   const int lane = lane_id();
   if (lane < 16) {
 #pragma unroll
@@ -662,7 +727,7 @@ __device__ void routed_dn_item(const DecodeArgs& a, int item, uint16_t* arow, Wa
 // The kernel: four independent waves per workgroup sharing the token and the
 // routing decision in LDS.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ TopkLds tk;
   uint16_t* xs = lds;
@@ -675,7 +740,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 
   const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);
   const int q = gw % kQueues;
-  int* ticket = a.ctr + kCtrTicket + 32 * q;
+  int* ticket = a.ctr + kCtrTicket + 16 * q;
   WaveState st{-1};
   auto draw = [&]() {
     int t = 0;
@@ -713,11 +778,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     for (int i = lane; i < a.k; i += kWave) st_dev(a.ctr + kCtrRoute + 16 * i, 0);
     for (int i = lane; i < nb; i += kWave) st_dev(a.ctr + kCtrBlock + 16 * i, 0);
     for (int i = lane; i < a.S; i += kWave) st_dev(a.ctr + kCtrShared + 16 * i, 0);
-    if (lane < kQueues) st_dev(a.ctr + kCtrTicket + 32 * lane, 0);
-    if (lane == 0) {
-      st_dev(a.ctr + kCtrRouterDone, 0);
-      st_dev(a.ctr + kCtrExit, 0);
-    }
+    if (lane < kQueues) st_dev(a.ctr + kCtrTicket + 16 * lane, 0);
+    if (lane < kRouterSlots) st_dev(a.ctr + kCtrRouter + 16 * lane, 0);
+    if (lane == 0) st_dev(a.ctr + kCtrExit, 0);
   }
 }
 

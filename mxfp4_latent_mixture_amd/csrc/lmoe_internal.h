@@ -23,16 +23,18 @@ struct RouterPlan {
 };
 
 // Counter block at the start of every workspace (int32 slots, each counter on
-// its own 64- or 128-byte line). Only the single-token decode kernel uses it;
+// its own 64-byte line; device-scope atomics on one address serialise, so
+// heavily bumped counts are spread over several slots). Only the single-token decode kernel uses it;
 // it must be zero when that kernel starts and is left zeroed when it ends.
-constexpr int kQueues = 8;          // ticket queues: item i is in queue i % kQueues
-constexpr int kCtrTicket = 0;       // + 32 * queue
-constexpr int kCtrExit = 256;       // waves that have left
-constexpr int kCtrRouterDone = 288; // router items whose logit is published
-constexpr int kCtrError = 608;      // dependency waits abandoned at the spin limit
-constexpr int kCtrRoute = 640;      // + 16 * route (< 32): gate/up items done
-constexpr int kCtrBlock = 1152;     // + 16 * block (< 64): parts of a 64-row output block done
-constexpr int kCtrShared = 2176;    // + 16 * shared expert (< 128): gate/up items done
+constexpr int kQueues = 32;         // ticket queues: item i is in queue i % kQueues
+constexpr int kCtrTicket = 0;       // + 16 * queue
+constexpr int kCtrExit = 1024;      // waves that have left
+constexpr int kCtrError = 1040;     // dependency waits abandoned at the spin limit
+constexpr int kCtrRoute = 1056;     // + 16 * route (< 32): gate/up items done
+constexpr int kCtrBlock = 1568;     // + 16 * block (< 64): parts of a 64-row output block done
+constexpr int kCtrShared = 2592;    // + 16 * shared expert (< 8): gate/up items done
+constexpr int kRouterSlots = 64;    // the router's done count, spread over slots
+constexpr int kCtrRouter = 2720;    // + 16 * (expert % kRouterSlots): published logits
 constexpr size_t kCtrBytes = 32768;
 // The single-token decode kernel keeps the token and one A row in LDS.
 constexpr int kDecodeMaxWidth = 4096;

@@ -112,12 +112,14 @@ def check_routing_against_oracle(gpu_idx: np.ndarray, gpu_logits: np.ndarray,
     oracle's wherever the oracle's top-k boundary gap exceeds twice the bound,
     and elsewhere every GPU choice is a valid top-k choice within the bound.
     Returns the boolean mask of tokens whose sets agree."""
-    d = np.abs(gpu_logits.astype(np.float64) - ref_logits.astype(np.float64))
-    assert np.all(d <= bound), f"{what}: logits off by {np.max(d - bound):.3e} beyond bound"
+    g64, r64 = gpu_logits.astype(np.float64), ref_logits.astype(np.float64)
+    both_nan = np.isnan(g64) & np.isnan(r64)
+    d = np.where(both_nan, 0.0, np.abs(g64 - r64))
+    assert np.all(d <= bound), f"{what}: logits off by {np.nanmax(d - bound):.3e} beyond bound"
     ref_idx = O.topk_select(ref_logits, k)
     same = np.array([set(a) == set(b) for a, b in zip(gpu_idx.tolist(), ref_idx.tolist())])
     lg = ref_logits.astype(np.float64)
-    srt = -np.sort(-lg, axis=1)
+    srt = -np.sort(-np.nan_to_num(lg, nan=-np.inf), axis=1)
     for t in np.nonzero(~same)[0]:
         tb = bound[t].max()
         gap = srt[t, k - 1] - srt[t, k] if lg.shape[1] > k else np.inf

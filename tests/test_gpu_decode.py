@@ -14,7 +14,7 @@ from lmoe_testutil import (log, upload, alloc_routing, check_out, logits_bound,
 pytestmark = pytest.mark.gpu
 
 CTR_INTS = 32768 // 4
-ERROR_SLOT = 608 // 4  # kCtrError is a byte offset
+ERROR_SLOT = 1040  # int32 slot of the abandoned-wait count
 
 
 @pytest.fixture(scope="module")
@@ -79,6 +79,52 @@ def _run_tokens(lm, dev, w: Workload, n_tokens: int):
 ])
 def test_fused_decode_shapes(lm, dev, name, dims, scales):
     _run_tokens(lm, dev, Workload(name, 40 + len(name), dims, scales=scales), 3)
+
+
+def _tied_router(inp, d):
+    """Router rows with exact logit ties: groups of four identical rows, the
+    strongest row copied onto experts 5, 69, 133 and 197 (one lane of the
+    selecting wave holds all four), a NaN row and an all-zero row."""
+    wr = inp["router_w"].copy()
+    for g in range(8, 48, 4):
+        wr[g + 1:g + 4] = wr[g]
+    top = int(np.argmax(O.router_logits(inp["x"], wr)[0]))
+    for e in (5, 69, 133, 197):
+        wr[e] = wr[top]
+    wr[50] = 0x7FC0                    # bf16 NaN: logit NaN
+    wr[51] = 0                         # logit +0
+    return wr
+
+
+def test_fused_decode_router_ties_and_nan(lm, dev):
+    """Selection inside the fused kernel on exact logit ties (lower expert
+    index first), one lane winning four times, a NaN logit (ordered after
+    every number) and an all-zero row (logit +0); the oracle decides."""
+    import torch
+    d = Dims(T=1, L=256, E=256, k=10, I=128, S=1, Is=64)
+    w = Workload("ties1", 61, d, scales=("uniform", 118, 132))
+    inp = gen_all(w)
+    wr = _tied_router(inp, d)
+    inp["router_w"] = wr
+    dinp = upload(inp, dev)
+    ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
+    r = alloc_routing(d, dev)
+    out = torch.empty((1, d.L), dtype=torch.int16, device=dev)
+    lm.forward(d, dinp["x"], dinp, False, r, out, ws)
+    torch.cuda.synchronize()
+    ref = O.forward(inp["x"], wr, inp, inp, d.k)
+    assert {5, 69, 133, 197} <= set(ref["idx"][0].tolist())
+    res = {k: v.cpu().numpy() for k, v in r.items()}
+    lg = res["logits"][0]
+    assert np.isnan(lg[50]) and lg[51] == 0.0
+    for r0 in (1, 2, 3):                                 # the ties are exact on the GPU
+        assert np.array_equal(lg[8 + r0:48:4], lg[8:48:4])
+    assert lg[5] == lg[69] == lg[133] == lg[197]
+    assert np.array_equal(res["topk_idx"], ref["idx"])
+    assert np.array_equal(res["perm"], ref["perm"])
+    assert np.all(np.abs(res["topk_w"] - ref["w"]) <= 1e-5 * np.abs(ref["w"]) + 1e-9)
+    check_out(out.cpu().numpy().view(np.uint16), ref["out64"], "ties1")
+    assert not ws[:32768].view(torch.int32).cpu().numpy().any()
 
 
 def test_fused_decode_k3_back_to_back(lm, dev):
