@@ -247,15 +247,21 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
 // owns 32 columns (two 16-wide MFMA tiles, paired gate/up tiles for the GLU)
 // over all row tiles. Activations are staged in LDS one 128-wide K chunk at a
 // time; in a chunk lane group g takes MX block g, so one 16-byte code load
-// and one scale feed the four MFMA steps of that block.
+// and one scale feed the four MFMA steps of that block. The chunk after the
+// current one (activations into registers, then LDS; MXFP4 weights into
+// registers) is loaded while the current one is multiplied, the LDS chunk is
+// double-buffered with one barrier per chunk, and two workgroups share a CU
+// (accumulators in AGPRs) so one's loads overlap the other's MFMAs.
 // ---------------------------------------------------------------------------
 constexpr int kLgCols = 128;
 constexpr int kLgKc = 128;
 constexpr int kLgPad = kLgKc + 8;  // LDS row length in bf16
 
 template <bool GLU, bool FP4>
-__global__ __launch_bounds__(256) void gemm_large_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sx[kLargeRows][kLgPad];
+__global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a) {
+  // two K chunks of the tile's activations: the MFMAs read one while the next
+  // is written
+  __shared__ __attribute__((aligned(16))) uint16_t sx[2][kLargeRows][kLgPad];
   __shared__ const uint16_t* s_arow[kLargeRows];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -270,8 +276,8 @@ __global__ __launch_bounds__(256) void gemm_large_kernel(GemmArgs a) {
   const int n0 = nt * kLgCols + wave * 32;
   const int mtiles = (ti.cnt + 15) / 16;
 
-  for (int r = tid; r < kLargeRows; r += 256)
-    s_arow[r] = (r < ti.cnt) ? act_row(a, ti, r) : nullptr;
+  // rows past the tile repeat its last row: finite values, never stored
+  for (int r = tid; r < kLargeRows; r += 256) s_arow[r] = act_row(a, ti, min(r, ti.cnt - 1));
 
   int nrow[2];
   bool nvalid[2];
@@ -285,16 +291,16 @@ __global__ __launch_bounds__(256) void gemm_large_kernel(GemmArgs a) {
   for (int w = 0; w < 2; ++w) {
     nrow[w] = n0 + w * 16 + col;
     nvalid[w] = nrow[w] < N;
-    const int nn = nvalid[w] ? nrow[w] : 0;
+    const int nn = nvalid[w] ? nrow[w] : 0;  // padding columns read row 0, never stored
     if (FP4) {
       q0r[w] = a.q0 + ti.e * a.q_estride + (int64_t)nn * (K / 2);
       s0r[w] = a.s0 + ti.e * a.s_estride + (int64_t)nn * (K / 32);
-      q1r[w] = GLU ? a.q1 + ti.e * a.q_estride + (int64_t)nn * (K / 2) : nullptr;
-      s1r[w] = GLU ? a.s1 + ti.e * a.s_estride + (int64_t)nn * (K / 32) : nullptr;
+      q1r[w] = GLU ? a.q1 + ti.e * a.q_estride + (int64_t)nn * (K / 2) : q0r[w];
+      s1r[w] = GLU ? a.s1 + ti.e * a.s_estride + (int64_t)nn * (K / 32) : s0r[w];
       b0r[w] = b1r[w] = nullptr;
     } else {
       b0r[w] = a.b0 + ti.e * a.b_estride + (int64_t)nn * K;
-      b1r[w] = GLU ? a.b1 + ti.e * a.b_estride + (int64_t)nn * K : nullptr;
+      b1r[w] = GLU ? a.b1 + ti.e * a.b_estride + (int64_t)nn * K : b0r[w];
       q0r[w] = s0r[w] = q1r[w] = s1r[w] = nullptr;
     }
   }
@@ -308,56 +314,69 @@ __global__ __launch_bounds__(256) void gemm_large_kernel(GemmArgs a) {
       acc1[m][w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-  for (int c = 0; c < nchunks; ++c) {
-    __syncthreads();
-    // stage activations: 128 rows x 128 values (16 pieces of 16 bytes per row)
+  // Activation staging: thread tid moves row (tid >> 4) + 16 i, values
+  // q * 8 .. q * 8 + 7 of the chunk, for the tile's 16-row groups i < mtiles.
+  const int srow = tid >> 4, sq = tid & 15;
+  u32x4_t xr[8];
+  auto load_x = [&](int c) {
+    const int kk = c * kLgKc + sq * 8;
+    const int kc = min(kk, K - 8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int id = tid + 256 * i;
-      const int row = id >> 4, q = id & 15;
-      const int kk = c * kLgKc + q * 8;
-      const uint16_t* src = s_arow[row];
-      u32x4_t v = zero16();
-      if (src && kk < K) v = load16(src + kk);
-      *reinterpret_cast<u32x4_t*>(&sx[row][q * 8]) = v;
-    }
-    const int blk = c * 4 + grp;
-    const bool kv = blk < nblk;
+    for (int i = 0; i < 8; ++i)
+      if (i < mtiles) {
+        const u32x4_t v = load16(s_arow[srow + 16 * i] + kc);
+        xr[i] = kk < K ? v : zero16();
+      }
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < mtiles) *reinterpret_cast<u32x4_t*>(&sx[buf][srow + 16 * i][sq * 8]) = xr[i];
+  };
+  // MXFP4 weights of a chunk: one 32-value block per lane, codes and exponent
+  struct Bfp4 {
     u32x4_t c0[2], c1[2];
-    float sc0[2], sc1[2];
+    uint32_t e0[2], e1[2];
+  };
+  auto load_b = [&](int c, Bfp4& b) {
+    const int blk = min(c * 4 + grp, nblk - 1);
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
-      c0[w] = c1[w] = zero16();
-      sc0[w] = sc1[w] = 1.f;
-      if (FP4 && kv && nvalid[w]) {
-        c0[w] = load16(q0r[w] + blk * 16);
-        sc0[w] = e8m0_to_f32(s0r[w][blk]);
-        if (GLU) {
-          c1[w] = load16(q1r[w] + blk * 16);
-          sc1[w] = e8m0_to_f32(s1r[w][blk]);
-        }
+      b.c0[w] = load16(q0r[w] + blk * 16);
+      b.e0[w] = s0r[w][blk];
+      if (GLU) {
+        b.c1[w] = load16(q1r[w] + blk * 16);
+        b.e1[w] = s1r[w][blk];
       }
     }
-    __syncthreads();
+  };
+
+  auto compute = [&](int c, int buf, const Bfp4& bq) {
+    const int blk = c * 4 + grp;
+    const bool kv = blk < nblk;  // past-the-end blocks: zero codes
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8_t bv0[2], bv1[2];
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
         if (FP4) {
-          bv0[w] = dequant8(c0[w][s], sc0[w]);
-          if (GLU) bv1[w] = dequant8(c1[w][s], sc1[w]);
+          bv0[w] = dequant8(kv ? bq.c0[w][s] : 0u, e8m0_to_f32(kv ? bq.e0[w] : 127u));
+          if (GLU) bv1[w] = dequant8(kv ? bq.c1[w][s] : 0u, e8m0_to_f32(kv ? bq.e1[w] : 127u));
         } else {
-          const bool ok = kv && nvalid[w];
-          bv0[w] = as_bf16x8(ok ? load16(b0r[w] + blk * 32 + s * 8) : zero16());
-          if (GLU) bv1[w] = as_bf16x8(ok ? load16(b1r[w] + blk * 32 + s * 8) : zero16());
+          const int bb = min(blk, nblk - 1);
+          const u32x4_t v0 = load16(b0r[w] + bb * 32 + s * 8);
+          bv0[w] = as_bf16x8(kv ? v0 : zero16());
+          if (GLU) {
+            const u32x4_t v1 = load16(b1r[w] + bb * 32 + s * 8);
+            bv1[w] = as_bf16x8(kv ? v1 : zero16());
+          }
         }
       }
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         if (m < mtiles) {
           const bf16x8_t av =
-              *reinterpret_cast<const bf16x8_t*>(&sx[m * 16 + col][grp * 32 + s * 8]);
+              *reinterpret_cast<const bf16x8_t*>(&sx[buf][m * 16 + col][grp * 32 + s * 8]);
 #pragma unroll
           for (int w = 0; w < 2; ++w) {
             acc0[m][w] = mfma16(av, bv0[w], acc0[m][w]);
@@ -366,6 +385,24 @@ __global__ __launch_bounds__(256) void gemm_large_kernel(GemmArgs a) {
         }
       }
     }
+  };
+
+  __syncthreads();  // s_arow
+  Bfp4 bc, bn;
+  load_x(0);
+  if (FP4) load_b(0, bc);
+  store_x(0);
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    // the next chunk's activations and weights are in flight during this one
+    // (the last iteration reloads its own chunk: harmless, never stored)
+    const int cn = min(c + 1, nchunks - 1);
+    load_x(cn);
+    if (FP4) load_b(cn, bn);
+    compute(c, c & 1, bc);
+    store_x((c + 1) & 1);
+    __syncthreads();
+    if (FP4) bc = bn;
   }
 
 #pragma unroll
