@@ -243,26 +243,39 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Large groups (<= 128 rows): 128 rows x 128 columns per workgroup; each wave
-// owns 32 columns (two 16-wide MFMA tiles, paired gate/up tiles for the GLU)
-// over all row tiles. Activations are staged in LDS one 128-wide K chunk at a
-// time; in a chunk lane group g takes MX block g, so one 16-byte code load
-// and one scale feed the four MFMA steps of that block. The chunk after the
-// current one (activations into registers, then LDS; MXFP4 weights into
-// registers) is loaded while the current one is multiplied, the LDS chunk is
-// double-buffered with one barrier per chunk, and two workgroups share a CU
-// (accumulators in AGPRs) so one's loads overlap the other's MFMAs.
+// Large groups (<= 128 rows): 128 rows x 128 (gate/up) or 256 (down)
+// columns per workgroup with MXFP4 weights, half that with bf16 ones; each
+// wave owns two paired gate/up 16-wide MFMA tiles for the GLU, or four tiles
+// of the down projection, over all row tiles, so both kinds issue the same
+// MFMAs per chunk.
+//
+// K runs in chunks of 128 values; in a chunk lane group g takes MX block g, so
+// one 16-byte code load and one exponent feed four MFMA steps. A chunk of the
+// tile's activations (its row groups only) is copied straight into LDS by the
+// load unit (16-byte global-to-LDS loads, no registers) while the previous
+// chunk is multiplied, with the chunk's weights loaded into registers beside
+// it; two LDS buffers and one barrier per chunk. Rows are stored with their
+// 16-byte segments XOR-swizzled by the row index, so the MFMA operand reads of
+// 16 rows hit distinct banks, and the operands of four row tiles are read
+// back to back before their MFMAs. Two workgroups share a CU.
 // ---------------------------------------------------------------------------
-constexpr int kLgCols = 128;
-constexpr int kLgKc = 128;
-constexpr int kLgPad = kLgKc + 8;  // LDS row length in bf16
+constexpr int kLgKc = 128;  // K values per chunk
+
+// 16-column MFMA tiles per wave: two gate/up pairs or four down tiles; half
+// as many for bf16 weights, whose chunk takes four times the registers.
+__host__ __device__ constexpr int lg_tiles_per_wave(bool glu, bool fp4) {
+  return (glu ? 2 : 4) / (fp4 ? 1 : 2);
+}
+
+// One array per buffer, so the compiler can tell a copy into one buffer from
+// a read of the other and does not wait for every copy before every read.
+typedef uint16_t LgChunk[kLargeRows][kLgKc];
 
 template <bool GLU, bool FP4>
 __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a) {
-  // two K chunks of the tile's activations: the MFMAs read one while the next
-  // is written
-  __shared__ __attribute__((aligned(16))) uint16_t sx[2][kLargeRows][kLgPad];
+  __shared__ __attribute__((aligned(16))) LgChunk sx0, sx1;
   __shared__ const uint16_t* s_arow[kLargeRows];
+  auto slot = [&](int r) -> LgChunk& { return r == 0 ? sx0 : sx1; };
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
@@ -270,117 +283,127 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a) {
   const int tile = blockIdx.x / a.n_tiles_n;
   TileInfo ti;
   if (!resolve_tile(a, tile, kLargeRows, &ti)) return;
+  constexpr int NW = lg_tiles_per_wave(GLU, FP4);  // 16-column tiles per wave
+  constexpr int NM = GLU ? 2 : 1;                   // weight matrices per column tile
   const int K = a.K, N = a.N;
   const int nblk = K / 32;
-  const int nchunks = (nblk + 3) / 4;
-  const int n0 = nt * kLgCols + wave * 32;
+  const int nchunks = (K + kLgKc - 1) / kLgKc;
+  const int n0 = nt * (64 * NW) + wave * (16 * NW);
   const int mtiles = (ti.cnt + 15) / 16;
 
   // rows past the tile repeat its last row: finite values, never stored
   for (int r = tid; r < kLargeRows; r += 256) s_arow[r] = act_row(a, ti, min(r, ti.cnt - 1));
 
-  int nrow[2];
-  bool nvalid[2];
-  const uint8_t* q0r[2];
-  const uint8_t* s0r[2];
-  const uint8_t* q1r[2];
-  const uint8_t* s1r[2];
-  const uint16_t* b0r[2];
-  const uint16_t* b1r[2];
+  int nrow[NW];
+  bool nvalid[NW];
+  const uint8_t* qr[NW][NM];
+  const uint8_t* er[NW][NM];
+  const uint16_t* br[NW][NM];
 #pragma unroll
-  for (int w = 0; w < 2; ++w) {
+  for (int w = 0; w < NW; ++w) {
     nrow[w] = n0 + w * 16 + col;
     nvalid[w] = nrow[w] < N;
     const int nn = nvalid[w] ? nrow[w] : 0;  // padding columns read row 0, never stored
-    if (FP4) {
-      q0r[w] = a.q0 + ti.e * a.q_estride + (int64_t)nn * (K / 2);
-      s0r[w] = a.s0 + ti.e * a.s_estride + (int64_t)nn * (K / 32);
-      q1r[w] = GLU ? a.q1 + ti.e * a.q_estride + (int64_t)nn * (K / 2) : q0r[w];
-      s1r[w] = GLU ? a.s1 + ti.e * a.s_estride + (int64_t)nn * (K / 32) : s0r[w];
-      b0r[w] = b1r[w] = nullptr;
-    } else {
-      b0r[w] = a.b0 + ti.e * a.b_estride + (int64_t)nn * K;
-      b1r[w] = GLU ? a.b1 + ti.e * a.b_estride + (int64_t)nn * K : b0r[w];
-      q0r[w] = s0r[w] = q1r[w] = s1r[w] = nullptr;
+#pragma unroll
+    for (int mm = 0; mm < NM; ++mm) {
+      if (FP4) {
+        qr[w][mm] = (mm ? a.q1 : a.q0) + ti.e * a.q_estride + (int64_t)nn * (K / 2);
+        er[w][mm] = (mm ? a.s1 : a.s0) + ti.e * a.s_estride + (int64_t)nn * (K / 32);
+        br[w][mm] = nullptr;
+      } else {
+        br[w][mm] = (mm ? a.b1 : a.b0) + ti.e * a.b_estride + (int64_t)nn * K;
+        qr[w][mm] = er[w][mm] = nullptr;
+      }
     }
   }
 
-  f32x4_t acc0[8][2], acc1[8][2];
+  f32x4_t acc[8][NW][NM];
 #pragma unroll
   for (int m = 0; m < 8; ++m)
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      acc0[m][w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      acc1[m][w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+      for (int mm = 0; mm < NM; ++mm) acc[m][w][mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Activation staging: thread tid moves row (tid >> 4) + 16 i, values
-  // q * 8 .. q * 8 + 7 of the chunk, for the tile's 16-row groups i < mtiles.
-  const int srow = tid >> 4, sq = tid & 15;
-  u32x4_t xr[8];
-  auto load_x = [&](int c) {
-    const int kk = c * kLgKc + sq * 8;
-    const int kc = min(kk, K - 8);
+  // copy of chunk c (clamped to the last chunk) into LDS buffer `buf`:
+  // instruction j of wave w moves rows w*32 + 4j .. +4, lane l the 16-byte
+  // segment at physical slot l % 16 of row l / 16 (logical segment slot ^ row
+  // % 16); instructions wholly past the tile's row groups are skipped
+  auto copy_x = [&](int c, int buf) {
+    const int cc = min(c, nchunks - 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i < mtiles) {
-        const u32x4_t v = load16(s_arow[srow + 16 * i] + kc);
-        xr[i] = kk < K ? v : zero16();
+    for (int j = 0; j < 8; ++j) {
+      const int row0 = wave * 32 + j * 4;
+      if (row0 < mtiles * 16) {
+        const int row = row0 + (lane >> 4);
+        const int seg = (lane & 15) ^ (row & 15);
+        const int k = min(cc * kLgKc + seg * 8, K - 8);  // K % 32 == 0, so k + 8 <= K
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(s_arow[row] + k),
+            (__attribute__((address_space(3))) void*)(&slot(buf)[row0][0]), 16, 0, 0);
       }
+    }
   };
-  auto store_x = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i < mtiles) *reinterpret_cast<u32x4_t*>(&sx[buf][srow + 16 * i][sq * 8]) = xr[i];
+  // weights of chunk c for this lane: MX block c*4 + grp
+  struct Bq {
+    u32x4_t q[NW][NM];     // MXFP4: 32 codes
+    uint32_t e[NW][NM];    //        their exponent
+    u32x4_t h[NW][NM][4];  // bf16: 32 values
   };
-  // MXFP4 weights of a chunk: one 32-value block per lane, codes and exponent
-  struct Bfp4 {
-    u32x4_t c0[2], c1[2];
-    uint32_t e0[2], e1[2];
-  };
-  auto load_b = [&](int c, Bfp4& b) {
+  auto load_b = [&](int c, Bq& b) {
     const int blk = min(c * 4 + grp, nblk - 1);
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      b.c0[w] = load16(q0r[w] + blk * 16);
-      b.e0[w] = s0r[w][blk];
-      if (GLU) {
-        b.c1[w] = load16(q1r[w] + blk * 16);
-        b.e1[w] = s1r[w][blk];
-      }
-    }
-  };
-
-  auto compute = [&](int c, int buf, const Bfp4& bq) {
-    const int blk = c * 4 + grp;
-    const bool kv = blk < nblk;  // past-the-end blocks: zero codes
+    for (int w = 0; w < NW; ++w)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8_t bv0[2], bv1[2];
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
+      for (int mm = 0; mm < NM; ++mm) {
         if (FP4) {
-          bv0[w] = dequant8(kv ? bq.c0[w][s] : 0u, e8m0_to_f32(kv ? bq.e0[w] : 127u));
-          if (GLU) bv1[w] = dequant8(kv ? bq.c1[w][s] : 0u, e8m0_to_f32(kv ? bq.e1[w] : 127u));
+          b.q[w][mm] = load16(qr[w][mm] + blk * 16);
+          b.e[w][mm] = er[w][mm][blk];
         } else {
-          const int bb = min(blk, nblk - 1);
-          const u32x4_t v0 = load16(b0r[w] + bb * 32 + s * 8);
-          bv0[w] = as_bf16x8(kv ? v0 : zero16());
-          if (GLU) {
-            const u32x4_t v1 = load16(b1r[w] + bb * 32 + s * 8);
-            bv1[w] = as_bf16x8(kv ? v1 : zero16());
-          }
+#pragma unroll
+          for (int s = 0; s < 4; ++s) b.h[w][mm][s] = load16(br[w][mm] + blk * 32 + s * 8);
         }
       }
+  };
+  auto compute = [&](int c, int buf, const Bq& b) {
+    const bool kv = c * 4 + grp < nblk;  // past the end: zero weights
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        if (m < mtiles) {
-          const bf16x8_t av =
-              *reinterpret_cast<const bf16x8_t*>(&sx[buf][m * 16 + col][grp * 32 + s * 8]);
+    for (int s = 0; s < 4; ++s) {
+      bf16x8_t bv[NW][NM];
 #pragma unroll
-          for (int w = 0; w < 2; ++w) {
-            acc0[m][w] = mfma16(av, bv0[w], acc0[m][w]);
-            if (GLU) acc1[m][w] = mfma16(av, bv1[w], acc1[m][w]);
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int mm = 0; mm < NM; ++mm) {
+          if (FP4)
+            bv[w][mm] = dequant8(kv ? b.q[w][mm][s] : 0u, e8m0_to_f32(kv ? b.e[w][mm] : 127u));
+          else
+            bv[w][mm] = as_bf16x8(kv ? b.h[w][mm][s] : zero16());
+        }
+      // the operands of four row tiles are read back to back, then their
+      // MFMAs run; the second four only when the tile has them
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h == 0 || mtiles > 4) {
+          bf16x8_t av[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = (4 * h + i) * 16 + col;
+            const int phys = (grp * 4 + s) ^ (row & 15);
+            av[i] = *reinterpret_cast<const bf16x8_t*>(&slot(buf)[row][phys * 8]);
+          }
+          // keeps the reads ahead of the branches below (the compiler would
+          // otherwise sink each into its branch and wait for it alone)
+          asm volatile("" ::"v"(av[0]), "v"(av[1]), "v"(av[2]), "v"(av[3]));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = 4 * h + i;
+            if (m < mtiles) {
+#pragma unroll
+              for (int w = 0; w < NW; ++w)
+#pragma unroll
+                for (int mm = 0; mm < NM; ++mm)
+                  acc[m][w][mm] = mfma16(av[i], bv[w][mm], acc[m][w][mm]);
+            }
           }
         }
       }
@@ -388,38 +411,43 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a) {
   };
 
   __syncthreads();  // s_arow
-  Bfp4 bc, bn;
-  load_x(0);
-  if (FP4) load_b(0, bc);
-  store_x(0);
-  __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    // the next chunk's activations and weights are in flight during this one
-    // (the last iteration reloads its own chunk: harmless, never stored)
-    const int cn = min(c + 1, nchunks - 1);
-    load_x(cn);
-    if (FP4) load_b(cn, bn);
-    compute(c, c & 1, bc);
-    store_x((c + 1) & 1);
-    __syncthreads();
-    if (FP4) bc = bn;
+  Bq bq[2];
+  copy_x(0, 0);
+  load_b(0, bq[0]);
+  // No step is conditional (a branch around the loads would make the compiler
+  // wait for all of them): a chunk past the end multiplies zero weights.
+  for (int cb = 0; cb < nchunks; cb += 2) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int c = cb + r;
+      // chunk c (loaded during the previous step) has landed for this thread,
+      // then for every thread, and every wave is done with the other buffer
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      copy_x(c + 1, r ^ 1);
+      load_b(c + 1, bq[r ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(c, r, bq[r]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
+  __builtin_amdgcn_s_waitcnt(0);
 
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     if (m >= mtiles) continue;
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
+    for (int w = 0; w < NW; ++w) {
       if (!nvalid[w]) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = m * 16 + grp * 4 + j;
         if (r < ti.cnt) {
           const int64_t o = out_row(a, ti, r) * a.out_stride + nrow[w];
-          if (GLU) {
-            a.h_out[o] = f32_to_bf16_bits(silu(acc0[m][w][j]) * acc1[m][w][j]);
+          if constexpr (GLU) {
+            a.h_out[o] = f32_to_bf16_bits(silu(acc[m][w][0][j]) * acc[m][w][1][j]);
           } else {
-            a.y_out[o] = acc0[m][w][j];
+            a.y_out[o] = acc[m][w][0][j];
           }
         }
       }
@@ -505,7 +533,8 @@ template <bool GLU, bool FP4>
 static hipError_t launch_gemm(const GemmArgs& a0, bool large, int row_tiles, int z,
                               hipStream_t s) {
   GemmArgs a = a0;
-  const int cols = large ? kLgCols : 16;
+  // large tiles: four waves of lg_tiles_per_wave 16-column MFMA tiles
+  const int cols = large ? 64 * lg_tiles_per_wave(GLU, FP4) : 16;
   a.n_tiles_n = (a.N + cols - 1) / cols;
   dim3 grid((unsigned)(row_tiles * a.n_tiles_n), 1, (unsigned)z);
   if (large)
