@@ -171,7 +171,14 @@ struct TopkLds {
   int state;  // 0 not started, 1 being computed, 2 ready
   int sel[kMaxK];
   float w[kMaxK];
+  uint64_t cand[kWave];    // the selecting wave's working space
+  uint64_t sorted[kMaxK];  // selected keys, largest first
 };
+
+// Orders a wave's LDS accesses before and after this point (a wave's LDS
+// operations complete in issue order; this keeps the compiler from moving
+// them across lanes' exchanges).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 }  // namespace
 
@@ -475,6 +482,64 @@ __device__ void router_item(const DecodeArgs& a, int e, const uint16_t* xs) {
   publish(a.ctr + kCtrRouter + 16 * (e % kRouterSlots), false);
 }
 
+__device__ void compute_topk(const DecodeArgs& a, TopkLds& tk);
+__device__ void finish_topk(const DecodeArgs& a, TopkLds& tk, uint64_t mine);
+
+// Selection of the k largest of the wave's keys (kKeysPerLane per lane,
+// distinct, valid ones nonzero, at least k valid and at least min(E, 64)
+// lanes holding one) without k serial rounds. The k-th largest of the lanes'
+// own maxima is a threshold that at least k keys reach; the keys that reach
+// it are gathered in LDS and each is ranked by counting the larger ones.
+// Returns false, leaving the selection to the caller, when more keys reach
+// the threshold than the wave has lanes (possible only when the largest keys
+// crowd into a few lanes).
+__device__ bool select_by_threshold(int k, const uint64_t* key, TopkLds& tk, uint64_t& mine) {
+  const int lane = lane_id();
+  uint64_t m = 0ull;
+#pragma unroll
+  for (int i = 0; i < kKeysPerLane; ++i) m = key[i] > m ? key[i] : m;
+  tk.cand[lane] = m;
+  wave_lds_sync();
+  // all 64 maxima are read before the first comparison: one LDS latency
+  uint64_t v[kWave];
+#pragma unroll
+  for (int j = 0; j < kWave; ++j) v[j] = tk.cand[j];
+  int rank = 0;
+#pragma unroll
+  for (int j = 0; j < kWave; ++j) rank += v[j] > m ? 1 : 0;
+  // nonzero maxima are distinct, so exactly one lane has rank k - 1
+  const uint64_t at = __builtin_amdgcn_ballot_w64(rank == k - 1);
+  const int tl = __builtin_ctzll(at);
+  // (the builtin returns a signed int: widen each word without extension)
+  const uint64_t tau = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(m >> 32), tl) << 32) |
+                       (uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)m, tl);
+  wave_lds_sync();
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < kKeysPerLane; ++i) {
+    const bool p = key[i] >= tau;
+    const uint64_t bits = __builtin_amdgcn_ballot_w64(p);
+    const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bits >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0u));
+    if (p && pos < kWave) tk.cand[pos] = key[i];
+    n += __builtin_popcountll(bits);
+  }
+  if (n > kWave) return false;
+  wave_lds_sync();
+  const uint64_t c = lane < n ? tk.cand[lane] : 0ull;
+  int r = 0;
+  for (int j0 = 0; j0 < n; j0 += 16) {  // 16 candidates per LDS latency
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = tk.cand[j0 + q];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) r += (j0 + q < n && v[q] > c) ? 1 : 0;
+  }
+  if (lane < n && r < k) tk.sorted[r] = c;
+  wave_lds_sync();
+  mine = lane < k ? tk.sorted[lane] : 0ull;
+  return true;
+}
+
 // The routing decision of this workgroup: computed by the first wave that
 // needs it once every logit is published; other waves wait for it in LDS.
 __device__ void ensure_topk(const DecodeArgs& a, TopkLds& tk) {
@@ -485,11 +550,16 @@ __device__ void ensure_topk(const DecodeArgs& a, TopkLds& tk) {
     claim = __hip_atomic_compare_exchange_strong(&tk.state, &expected, 1, __ATOMIC_ACQ_REL,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
-  if (!__builtin_amdgcn_readfirstlane(claim)) {
-    while (__hip_atomic_load(&tk.state, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 2)
-      __builtin_amdgcn_s_sleep(1);
+  if (__builtin_amdgcn_readfirstlane(claim)) {
+    compute_topk(a, tk);
     return;
   }
+  while (__hip_atomic_load(&tk.state, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 2)
+    __builtin_amdgcn_s_sleep(1);
+}
+
+// Computed once every logit is published: selection, then softmax weights.
+__device__ void compute_topk(const DecodeArgs& a, TopkLds& tk) {
   wait_geq(a.ctr + kCtrRouter, a.n_router, a.ctr + kCtrError, kRouterSlots, 16);
   const int lane = lane_id();
   // every load is issued before the first is used (indices clamped in range)
@@ -501,6 +571,11 @@ __device__ void ensure_topk(const DecodeArgs& a, TopkLds& tk) {
   for (int i = 0; i < kKeysPerLane; ++i) {
     const int e = lane + kWave * i;
     key[i] = (e < a.E) ? order_key(lv[i], e) : 0ull;
+  }
+  uint64_t mine = 0ull;  // lane j: the j-th largest key
+  if (select_by_threshold(a.k, key, tk, mine)) {
+    finish_topk(a, tk, mine);
+    return;
   }
   // k rounds of a wave-wide maximum over each lane's best remaining key. A
   // lane keeps its best two keys, so a win usually costs a register move; a
@@ -514,7 +589,6 @@ __device__ void ensure_topk(const DecodeArgs& a, TopkLds& tk) {
   }
   bool have2 = true, need = false;
   uint64_t last = ~0ull;
-  uint64_t mine = 0ull;  // lane j: the key chosen in round j
   for (int j = 0; j < a.k; ++j) {
     const uint32_t hi = (uint32_t)(b1 >> 32), lo = (uint32_t)b1;
     const uint32_t mhi = wave_max_u32(hi);
@@ -546,6 +620,13 @@ __device__ void ensure_topk(const DecodeArgs& a, TopkLds& tk) {
       }
     }
   }
+  finish_topk(a, tk, mine);
+}
+
+// Softmax weights of the selected keys (lane j holds the j-th largest) and
+// the release of the decision to the workgroup.
+__device__ void finish_topk(const DecodeArgs& a, TopkLds& tk, uint64_t mine) {
+  const int lane = lane_id();
   const int my_e = (int)(~(uint32_t)mine);
   const float my_l = lane < a.k ? key_value(mine) : 0.f;
   // softmax over the selected logits, relative to the largest
@@ -593,6 +674,9 @@ __device__ void write_routing(const DecodeArgs& a, const TopkLds& tk) {
 // ---------------------------------------------------------------------------
 // Expert items
 // ---------------------------------------------------------------------------
+// One K half of 8 gate and 8 up columns of shared expert s. The second half to
+// finish adds the two partial sums (half 0 first) and applies the GLU; splitting
+// K gives twice the items, so every wave can stream while the routing resolves.
 __device__ void shared_gu_item(const DecodeArgs& a, int item, const uint16_t* xs) {
   const int s = item / a.shgu_per_expert;
   const int i0 = (item % a.shgu_per_expert) * 8;
@@ -750,8 +834,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   int t = draw();
   while (t < a.t_total) {
     const int next = draw();  // in flight while this item runs
-    if (t < a.t_shgu)
+    if (t < a.t_shgu) {
       router_item(a, t, xs);
+    }
     else if (t < a.t_gu)
       shared_gu_item(a, t - a.t_shgu, xs);
     else if (t < a.t_shd)

@@ -127,6 +127,51 @@ def test_fused_decode_router_ties_and_nan(lm, dev):
     assert not ws[:32768].view(torch.int32).cpu().numpy().any()
 
 
+def _crowded_router(inp, d):
+    """Router rows that put the 128 largest logits on experts e with
+    e % 64 < 32 (four per lane of the selecting wave), arranged so that lane
+    31 holds the four smallest of them: the k-th largest lane maximum is then
+    reached by 125 keys, more than the wave has lanes. Each such logit is one
+    exact product: x[0] = 1 and the row's only nonzero entry is its first."""
+    x = inp["x"].copy()
+    x[0, 0] = 0x3F80                       # bf16 1.0
+    wr = inp["router_w"].copy()
+    lanes = [l for l in range(32) if l != 31] + [31]
+    experts = [l + 64 * i for l in lanes for i in range(4)]
+    for r, e in enumerate(experts):        # values 127.5, 127, ..., 64
+        v = np.float32(128.0 - 0.5 * (r + 1))
+        wr[e] = 0
+        wr[e, 0] = np.array([v], dtype=np.float32).view(np.uint32)[0] >> 16
+    return x, wr
+
+
+def test_fused_decode_router_crowded_lanes(lm, dev):
+    """Selection when the largest logits crowd into a few lanes of the
+    selecting wave (the threshold admits more keys than the wave has lanes);
+    the oracle decides."""
+    import torch
+    d = Dims(T=1, L=256, E=256, k=32, I=128, S=1, Is=64)
+    w = Workload("crowd1", 67, d, scales=("uniform", 118, 132))
+    inp = gen_all(w)
+    x, wr = _crowded_router(inp, d)
+    inp["x"], inp["router_w"] = x, wr
+    dinp = upload(inp, dev)
+    ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
+    r = alloc_routing(d, dev)
+    out = torch.empty((1, d.L), dtype=torch.int16, device=dev)
+    lm.forward(d, dinp["x"], dinp, False, r, out, ws)
+    torch.cuda.synchronize()
+    ref = O.forward(x, wr, inp, inp, d.k)
+    lg = O.router_logits(x, wr)[0]
+    assert np.sum(lg >= 64.0) == 128 and np.max(np.delete(lg, np.flatnonzero(lg >= 64.0))) < 64.0
+    res = {k: v.cpu().numpy() for k, v in r.items()}
+    assert np.array_equal(res["topk_idx"], ref["idx"])
+    assert np.array_equal(res["perm"], ref["perm"])
+    assert np.all(np.abs(res["topk_w"] - ref["w"]) <= 1e-5 * np.abs(ref["w"]) + 1e-9)
+    check_out(out.cpu().numpy().view(np.uint16), ref["out64"], "crowd1")
+    assert not ws[:32768].view(torch.int32).cpu().numpy().any()
+
+
 def test_fused_decode_k3_back_to_back(lm, dev):
     w = get_workload("decode")
     log("decode: 4 consecutive K3 tokens on one workspace")
