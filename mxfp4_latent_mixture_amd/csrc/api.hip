@@ -70,7 +70,6 @@ Workspace carve_workspace(const Plan& p, void* base) {
   w.y = reinterpret_cast<float*>(take(R * L * 4));
   w.y_sh = reinterpret_cast<float*>(take(S * T * L * 4));
   if (p.fused_decode) {
-    w.dlogit = reinterpret_cast<float*>(take(E * 4));
     w.dh = reinterpret_cast<uint16_t*>(take((size_t)d.k * I * 2));
     w.dhsh = reinterpret_cast<uint16_t*>(take(S * Is * 2));
     w.dy = reinterpret_cast<float*>(take((size_t)d.k * L * 4));
@@ -160,7 +159,6 @@ static int run_fused_decode(const Plan& p, const Workspace& ws, const uint16_t* 
   a.inv = (r && r->inv_perm) ? r->inv_perm : ws.inv;
   a.out = out;
   a.ctr = ws.ctr;
-  a.logit = ws.dlogit;
   a.h = ws.dh;
   a.hsh = ws.dhsh;
   a.y = ws.dy;

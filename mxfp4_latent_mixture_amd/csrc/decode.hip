@@ -16,7 +16,7 @@
 //
 // Work items, in ticket order (sizes for the Kimi-K3 layer):
 //   router      the logit of one expert: its 7 KB router row against the
-//               token; published with a device counter
+//               token; published as one 64-bit word that carries a flag
 //   shared g/u  one shared expert, 8 intermediate columns, gate and up in one
 //               16-column MFMA tile: h = bf16(silu(g) * u)          (115 KB)
 //   routed g/u  one selected expert, 16 intermediate columns         (61 KB)
@@ -40,9 +40,12 @@
 // Memory ordering: data passed between waves (logits, h, y) is written with
 // device-scope stores and read with device-scope loads, which stay coherent
 // across the eight L2 partitions; a producer waits for its stores to complete
-// before it bumps a counter. No L2 writeback or invalidate is issued. Counters
-// sit in the first 32 KiB of the workspace, are zero when a launch starts and
-// are zeroed again by its last wave to leave.
+// before it bumps a counter. A logit needs no counter: its flag and value are
+// one aligned 64-bit word, so a reader that sees the flag sees the value,
+// which saves the selecting wave one round trip. No L2 writeback or
+// invalidate is issued. Counters and flagged logits sit in the first 32 KiB
+// of the workspace, are zero when a launch starts and are zeroed again by its
+// last wave to leave.
 #include "lmoe_device.h"
 #include "lmoe_internal.h"
 
@@ -476,10 +479,11 @@ __device__ void router_item(const DecodeArgs& a, int e, const uint16_t* xs) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) acc += __shfl_xor(acc, off, kWave);
   if (lane == 0) {
-    st_dev_f32(a.logit + e, acc);
     if (a.logits_out) a.logits_out[e] = acc;
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(a.ctr + kCtrLogit) + e,
+                       (1ull << 32) | __float_as_uint(acc), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
-  publish(a.ctr + kCtrRouter + 16 * (e % kRouterSlots), false);
 }
 
 __device__ void compute_topk(const DecodeArgs& a, TopkLds& tk);
@@ -560,12 +564,30 @@ __device__ void ensure_topk(const DecodeArgs& a, TopkLds& tk) {
 
 // Computed once every logit is published: selection, then softmax weights.
 __device__ void compute_topk(const DecodeArgs& a, TopkLds& tk) {
-  wait_geq(a.ctr + kCtrRouter, a.n_router, a.ctr + kCtrError, kRouterSlots, 16);
   const int lane = lane_id();
-  // every load is issued before the first is used (indices clamped in range)
+  // every logit with its flag, all loads issued before the first is used
+  // (indices clamped in range), until every flag is set
+  const uint64_t* pub = reinterpret_cast<const uint64_t*>(a.ctr + kCtrLogit);
   float lv[kKeysPerLane];
+  for (long it = 0;; ++it) {
+    uint64_t w[kKeysPerLane];
 #pragma unroll
-  for (int i = 0; i < kKeysPerLane; ++i) lv[i] = ld_dev_f32(a.logit + min(lane + kWave * i, a.E - 1));
+    for (int i = 0; i < kKeysPerLane; ++i)
+      w[i] = __hip_atomic_load(pub + min(lane + kWave * i, a.E - 1), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    bool in = true;
+#pragma unroll
+    for (int i = 0; i < kKeysPerLane; ++i) {
+      in = in && (w[i] >> 32) != 0;
+      lv[i] = __uint_as_float((uint32_t)w[i]);
+    }
+    if (__builtin_amdgcn_ballot_w64(!in) == 0) break;
+    if (it > kSpinLimit) {  // a broken producer: counted, and the wait abandoned
+      if (lane == 0) add_dev(a.ctr + kCtrError, 1);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
   uint64_t key[kKeysPerLane];
 #pragma unroll
   for (int i = 0; i < kKeysPerLane; ++i) {
@@ -864,7 +886,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     for (int i = lane; i < nb; i += kWave) st_dev(a.ctr + kCtrBlock + 16 * i, 0);
     for (int i = lane; i < a.S; i += kWave) st_dev(a.ctr + kCtrShared + 16 * i, 0);
     if (lane < kQueues) st_dev(a.ctr + kCtrTicket + 16 * lane, 0);
-    if (lane < kRouterSlots) st_dev(a.ctr + kCtrRouter + 16 * lane, 0);
+    uint64_t* pub = reinterpret_cast<uint64_t*>(a.ctr + kCtrLogit);
+    for (int i = lane; i < a.E; i += kWave)
+      __hip_atomic_store(pub + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (lane == 0) st_dev(a.ctr + kCtrExit, 0);
   }
 }

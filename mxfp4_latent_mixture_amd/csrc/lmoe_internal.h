@@ -33,8 +33,10 @@ constexpr int kCtrError = 1040;     // dependency waits abandoned at the spin li
 constexpr int kCtrRoute = 1056;     // + 16 * route (< 32): gate/up items done
 constexpr int kCtrBlock = 1568;     // + 16 * block (< 64): parts of a 64-row output block done
 constexpr int kCtrShared = 2592;    // + 16 * shared expert (< 8): gate/up items done
-constexpr int kRouterSlots = 64;    // the router's done count, spread over slots
-constexpr int kCtrRouter = 2720;    // + 16 * (expert % kRouterSlots): published logits
+// Published logits, one 64-bit word per expert (E <= 1024): the float's bits
+// in the low half and 1 in the high half once written, so a reader sees
+// every logit and whether it is in with one load, without a done count.
+constexpr int kCtrLogit = 4096;
 constexpr size_t kCtrBytes = 32768;
 // The single-token decode kernel keeps the token and one A row in LDS.
 constexpr int kDecodeMaxWidth = 4096;
@@ -64,7 +66,6 @@ struct Workspace {
   float* y;           // [R][L] fp32 route partials, sorted route order
   float* y_sh;        // [S][T][L] fp32
   // single-token decode
-  float* dlogit;      // [E] logits
   uint16_t* dh;       // [k][I] bf16
   uint16_t* dhsh;     // [S][Is] bf16
   float* dy;          // [k][L]
@@ -84,7 +85,6 @@ struct DecodeArgs {
   int32_t *counts, *offsets, *perm, *inv;
   uint16_t* out;
   int32_t* ctr;
-  float* logit;        // [E] published logits
   uint16_t* h;         // [k][I] bf16
   uint16_t* hsh;       // [S][Is] bf16
   float* y;            // [k][L] routed down outputs
