@@ -696,9 +696,6 @@ __device__ void write_routing(const DecodeArgs& a, const TopkLds& tk) {
 // ---------------------------------------------------------------------------
 // Expert items
 // ---------------------------------------------------------------------------
-// One K half of 8 gate and 8 up columns of shared expert s. The second half to
-// finish adds the two partial sums (half 0 first) and applies the GLU; splitting
-// K gives twice the items, so every wave can stream while the routing resolves.
 __device__ void shared_gu_item(const DecodeArgs& a, int item, const uint16_t* xs) {
   const int s = item / a.shgu_per_expert;
   const int i0 = (item % a.shgu_per_expert) * 8;
