@@ -58,9 +58,10 @@ __device__ __forceinline__ bool resolve_tile(const GemmArgs& a, int tile, int ro
                                              TileInfo* ti) {
   if (a.tiles) {
     if (tile >= *a.ntiles) return false;
-    ti->e = a.tiles[3 * tile + 0];
-    ti->p0 = a.tiles[3 * tile + 1];
-    ti->cnt = a.tiles[3 * tile + 2];
+    // the same for every lane: kept in scalar registers
+    ti->e = __builtin_amdgcn_readfirstlane(a.tiles[3 * tile + 0]);
+    ti->p0 = __builtin_amdgcn_readfirstlane(a.tiles[3 * tile + 1]);
+    ti->cnt = __builtin_amdgcn_readfirstlane(a.tiles[3 * tile + 2]);
   } else {
     ti->e = blockIdx.z;
     ti->p0 = tile * rows;
@@ -68,6 +69,18 @@ __device__ __forceinline__ bool resolve_tile(const GemmArgs& a, int tile, int ro
     if (ti->cnt <= 0) return false;
   }
   return true;
+}
+
+// The tile of this workgroup. Workgroups are dealt to the chip's eight XCDs
+// in turn (workgroup i runs on XCD i % 8, each XCD with its own L2), so the
+// column tiles of one row tile go to workgroups of one XCD: the tile's
+// activation rows are fetched into that L2 once and read there by all of them.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void tile_of_block(int n_tiles_n, int* tile, int* nt) {
+  const int b = blockIdx.x;
+  const int s = b / kXcds;
+  *nt = s % n_tiles_n;
+  *tile = (s / n_tiles_n) * kXcds + b % kXcds;
 }
 
 __device__ __forceinline__ const uint16_t* act_row(const GemmArgs& a, const TileInfo& ti, int r) {
@@ -112,8 +125,8 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
-  const int nt = blockIdx.x % a.n_tiles_n;
-  const int tile = blockIdx.x / a.n_tiles_n;
+  int tile, nt;
+  tile_of_block(a.n_tiles_n, &tile, &nt);
   TileInfo ti;
   if (!resolve_tile(a, tile, kSmallRows, &ti)) return;
 
@@ -279,8 +292,8 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
-  const int nt = blockIdx.x % a.n_tiles_n;
-  const int tile = blockIdx.x / a.n_tiles_n;
+  int tile, nt;
+  tile_of_block(a.n_tiles_n, &tile, &nt);
   TileInfo ti;
   if (!resolve_tile(a, tile, kLargeRows, &ti)) return;
   constexpr int NW = lg_tiles_per_wave(GLU, FP4);  // 16-column tiles per wave
@@ -536,7 +549,9 @@ static hipError_t launch_gemm(const GemmArgs& a0, bool large, int row_tiles, int
   // large tiles: four waves of lg_tiles_per_wave 16-column MFMA tiles
   const int cols = large ? 64 * lg_tiles_per_wave(GLU, FP4) : 16;
   a.n_tiles_n = (a.N + cols - 1) / cols;
-  dim3 grid((unsigned)(row_tiles * a.n_tiles_n), 1, (unsigned)z);
+  // row tiles rounded up to whole rounds of the XCDs (tile_of_block)
+  const int rounds = (row_tiles + kXcds - 1) / kXcds;
+  dim3 grid((unsigned)(rounds * kXcds * a.n_tiles_n), 1, (unsigned)z);
   if (large)
     hipLaunchKernelGGL((gemm_large_kernel<GLU, FP4>), grid, dim3(256), 0, s, a);
   else
