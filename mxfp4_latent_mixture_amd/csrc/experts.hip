@@ -284,10 +284,12 @@ __host__ __device__ constexpr int lg_tiles_per_wave(bool glu, bool fp4) {
 // a read of the other and does not wait for every copy before every read.
 typedef uint16_t LgChunk[kLargeRows][kLgKc];
 
-template <bool GLU, bool FP4>
+template <bool GLU, bool FP4, bool EXW>
 __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) LgChunk sx0, sx1;
   __shared__ const uint16_t* s_arow[kLargeRows];
+  // EXW: each wave's exponent windows (its 64 weight rows x 16 blocks)
+  __shared__ __attribute__((aligned(16))) uint8_t s_ex[EXW ? 4 : 1][64][16];
   auto slot = [&](int r) -> LgChunk& { return r == 0 ? sx0 : sx1; };
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -330,6 +332,43 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a) {
     }
   }
 
+  // Exponents, EXW: MX blocks 16W .. 16W + 15 of a row (window W, chunks
+  // 4W .. 4W + 3) reach LDS in one 16-byte global-to-LDS load per row, one
+  // load instruction per wave and window, instead of one byte load per lane
+  // and chunk; each wave reads only its own rows, so no barrier is needed.
+  // Lane l of the copy moves the window of row (w, mm, col) = l / 16 / NM,
+  // l / 16 % NM, l % 16 of this wave.
+  static_assert(!EXW || (FP4 && NW * NM == 4), "one copy lane per weight row of the wave");
+  const uint8_t* ex_row = nullptr;
+  if constexpr (EXW) {
+    const int w = (lane >> 4) / NM, mm = (lane >> 4) % NM;
+    const int n = n0 + w * 16 + (lane & 15);
+    ex_row = (mm ? a.s1 : a.s0) + ti.e * a.s_estride + (int64_t)(n < N ? n : 0) * nblk;
+  }
+  const int nwin = nblk / 16;
+  auto copy_ex = [&](int win) {
+    if constexpr (EXW)
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(ex_row + 16 * min(win, nwin - 1)),
+          (__attribute__((address_space(3))) void*)(&s_ex[wave][0][0]), 16, 0, 0);
+  };
+  // the window's exponents of this lane's blocks (4c + grp for its 4 chunks),
+  // packed one byte per chunk
+  uint32_t exw[NW][NM];
+  auto read_ex = [&]() {
+    if constexpr (EXW) {
+      const uint32_t sel = (uint32_t)grp | ((uint32_t)(4 + grp) << 8) | 0x0c0c0000u;
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int mm = 0; mm < NM; ++mm) {
+          const u32x4_t d = *reinterpret_cast<const u32x4_t*>(&s_ex[wave][(w * NM + mm) * 16 + col][0]);
+          exw[w][mm] = __builtin_amdgcn_perm(d[1], d[0], sel) |
+                       (__builtin_amdgcn_perm(d[3], d[2], sel) << 16);
+        }
+    }
+  };
+
   f32x4_t acc[8][NW][NM];
 #pragma unroll
   for (int m = 0; m < 8; ++m)
@@ -371,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a) {
       for (int mm = 0; mm < NM; ++mm) {
         if (FP4) {
           b.q[w][mm] = load16(qr[w][mm] + blk * 16);
-          b.e[w][mm] = er[w][mm][blk];
+          if (!EXW) b.e[w][mm] = er[w][mm][blk];
         } else {
 #pragma unroll
           for (int s = 0; s < 4; ++s) b.h[w][mm][s] = load16(br[w][mm] + blk * 32 + s * 8);
@@ -387,8 +426,10 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a) {
       for (int w = 0; w < NW; ++w)
 #pragma unroll
         for (int mm = 0; mm < NM; ++mm) {
-          if (FP4)
-            bv[w][mm] = dequant8(kv ? b.q[w][mm][s] : 0u, e8m0_to_f32(kv ? b.e[w][mm] : 127u));
+          if (FP4) {
+            const uint32_t ex = EXW ? (exw[w][mm] >> (8 * (c & 3))) & 0xffu : b.e[w][mm];
+            bv[w][mm] = dequant8(kv ? b.q[w][mm][s] : 0u, e8m0_to_f32(kv ? ex : 127u));
+          }
           else
             bv[w][mm] = as_bf16x8(kv ? b.h[w][mm][s] : zero16());
         }
@@ -425,10 +466,12 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a) {
 
   __syncthreads();  // s_arow
   Bq bq[2];
+  copy_ex(0);
   copy_x(0, 0);
   load_b(0, bq[0]);
-  // No step is conditional (a branch around the loads would make the compiler
-  // wait for all of them): a chunk past the end multiplies zero weights.
+  // No chunk load is conditional (a branch around the loads would make the
+  // compiler wait for all of them): a chunk past the end multiplies zero
+  // weights.
   for (int cb = 0; cb < nchunks; cb += 2) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -437,6 +480,12 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a) {
       // then for every thread, and every wave is done with the other buffer
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __builtin_amdgcn_s_barrier();
+      if (EXW && (c & 3) == 0) {
+        // window c / 4 into registers, then the next window into its place
+        read_ex();
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the reads are done
+        copy_ex(c / 4 + 1);
+      }
       copy_x(c + 1, r ^ 1);
       load_b(c + 1, bq[r ^ 1]);
       __builtin_amdgcn_sched_barrier(0);
@@ -545,6 +594,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 template <bool GLU, bool FP4>
 static hipError_t launch_gemm(const GemmArgs& a0, bool large, int row_tiles, int z,
                               hipStream_t s) {
+  // exponent windows through LDS when every row holds whole 16-block windows
+  const bool exw = FP4 && (a0.K / 32) % 16 == 0;
   GemmArgs a = a0;
   // large tiles: four waves of lg_tiles_per_wave 16-column MFMA tiles
   const int cols = large ? 64 * lg_tiles_per_wave(GLU, FP4) : 16;
@@ -552,8 +603,10 @@ static hipError_t launch_gemm(const GemmArgs& a0, bool large, int row_tiles, int
   // row tiles rounded up to whole rounds of the XCDs (tile_of_block)
   const int rounds = (row_tiles + kXcds - 1) / kXcds;
   dim3 grid((unsigned)(rounds * kXcds * a.n_tiles_n), 1, (unsigned)z);
-  if (large)
-    hipLaunchKernelGGL((gemm_large_kernel<GLU, FP4>), grid, dim3(256), 0, s, a);
+  if (large && exw)
+    hipLaunchKernelGGL((gemm_large_kernel<GLU, FP4, FP4>), grid, dim3(256), 0, s, a);
+  else if (large)
+    hipLaunchKernelGGL((gemm_large_kernel<GLU, FP4, false>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((gemm_small_kernel<GLU, FP4>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
