@@ -113,13 +113,19 @@ STAGE_KERNEL = {
 }
 
 
-def stage_kernel(stage: str, large: bool, sh_large: bool) -> str:
+def stage_kernel(stage: str, large: bool, sh_large: bool, d=None) -> str:
     if stage in STAGE_KERNEL:
         return STAGE_KERNEL[stage]
     kind = {"gate_up": ("true", "true"), "down": ("false", "true"),
             "shared_gate_up": ("true", "false"), "shared_down": ("false", "false")}[stage]
     big = sh_large if stage.startswith("shared") else large
-    return f"gemm_{'large' if big else 'small'}_kernel<{kind[0]}, {kind[1]}>"
+    if not big:
+        return f"gemm_small_kernel<{kind[0]}, {kind[1]}>"
+    # the large MXFP4 kernels read exponents through LDS when K/32 is a
+    # multiple of 16 (third template argument)
+    K = None if d is None else {"gate_up": d.L, "down": d.I}.get(stage)
+    exw = "true" if (K is not None and (K // 32) % 16 == 0) else "false"
+    return f"gemm_large_kernel<{kind[0]}, {kind[1]}, {exw}>"
 
 
 def sources_sha() -> str:
@@ -302,7 +308,7 @@ def kernel_units(res, lm):
     R = d.T * d.k
     large = (R / max(1, min(d.E, R))) > 8.0
     sh_large = d.T > 64
-    return [(stage_kernel(s, large, sh_large), sb[s], sf[s], res["stage_ms"][s] * 1e-3)
+    return [(stage_kernel(s, large, sh_large, d), sb[s], sf[s], res["stage_ms"][s] * 1e-3)
             for s in sb if res["stage_ms"][s] > 0]
 
 
