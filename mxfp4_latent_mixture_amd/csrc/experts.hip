@@ -118,7 +118,19 @@ struct SmallOps<false> {  // one 32-value block of bf16 weights per matrix
   u32x4_t b0[4], b1[4];
 };
 
-template <bool GLU, bool FP4>
+// A buffer resource over `bytes` bytes at `base`, a pointer that is the same
+// for every lane: said so, so the resource stays in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int64_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint64_t u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p) |
+                     ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) << 32);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
+}
+
+// EXR: the MX exponents of a wave's whole K range sit in registers, loaded
+// once (K/32 a multiple of 16 and at most 128: at most 32 bytes per row).
+template <bool GLU, bool FP4, bool EXR>
 __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
   constexpr int U = FP4 ? 2 : 1;   // MX blocks per lane per iteration
   constexpr int SPAN = 4 * U;      // blocks per wave iteration
@@ -164,6 +176,28 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
   // first block of this lane in iteration it
   auto first_blk = [&](int it) { return bw_lo + it * SPAN + grp * U; };
 
+  // EXR: exponents of blocks bw_lo .. bw_lo + 31 of the lane's row, one
+  // aligned 16-byte buffer load per half (past the matrix the range check
+  // returns zeros, in whole words: its N * K / 32 bytes are a multiple of 16);
+  // iteration it reads words 0 and 1 (blocks 8 it .. 8 it + 7), then the
+  // window moves on by two words
+  static_assert(!EXR || (FP4 && U == 2 && SPAN == 8), "eight blocks per iteration");
+  uint32_t ex[2][8];
+  if constexpr (EXR) {
+#pragma unroll
+    for (int mm = 0; mm < (GLU ? 2 : 1); ++mm) {
+      const auto r = uniform_rsrc((mm ? a.s1 : a.s0) + ti.e * a.s_estride, (int64_t)N * nblk);
+      const int off = nn * nblk + bw_lo;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4_t v = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * h, 0, 0));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ex[mm][4 * h + j] = v[j];
+      }
+    }
+  }
+
   auto load_ops = [&](int it, SmallOps<FP4>& o) {
     const int b0 = first_blk(it);
 #pragma unroll
@@ -172,10 +206,10 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
       const bool ok = nvalid && it < iters && blk < bw_hi;
       if constexpr (FP4) {
         o.c0[u] = ok ? load16(q0r + blk * 16) : zero16();
-        o.s0[u] = ok ? (uint32_t)s0r[blk] : 127u;
+        if (!EXR) o.s0[u] = ok ? (uint32_t)s0r[blk] : 127u;
         if (GLU) {
           o.c1[u] = ok ? load16(q1r + blk * 16) : zero16();
-          o.s1[u] = ok ? (uint32_t)s1r[blk] : 127u;
+          if (!EXR) o.s1[u] = ok ? (uint32_t)s1r[blk] : 127u;
         }
       } else {
 #pragma unroll
@@ -202,7 +236,18 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) xv[q] = aok ? load16(ap + blk * 32 + q * 8) : zero16();
       float sc0 = 1.f, sc1 = 1.f;
-      if constexpr (FP4) {
+      if constexpr (EXR) {
+        // block 8 it + 2 grp + u of the window: word grp / 2, byte 2 (grp % 2) + u;
+        // blocks past the range keep 127 (their codes are zero)
+        const bool ok = nvalid && blk < bw_hi;
+        const int sh = 8 * (2 * (grp & 1) + u);
+        const uint32_t e0 = ((grp & 2) ? ex[0][1] : ex[0][0]) >> sh;
+        sc0 = e8m0_to_f32(ok ? e0 & 0xffu : 127u);
+        if (GLU) {
+          const uint32_t e1 = ((grp & 2) ? ex[1][1] : ex[1][0]) >> sh;
+          sc1 = e8m0_to_f32(ok ? e1 & 0xffu : 127u);
+        }
+      } else if constexpr (FP4) {
         sc0 = e8m0_to_f32(cur.s0[u]);
         if (GLU) sc1 = e8m0_to_f32(cur.s1[u]);
       }
@@ -222,6 +267,12 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
       }
     }
     cur = nxt;
+    if constexpr (EXR) {
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+        for (int j = 0; j < 6; ++j) ex[mm][j] = ex[mm][j + 2];
+    }
   }
 
   __shared__ f32x4_t red[2][4][64];
@@ -607,8 +658,10 @@ static hipError_t launch_gemm(const GemmArgs& a0, bool large, int row_tiles, int
     hipLaunchKernelGGL((gemm_large_kernel<GLU, FP4, FP4>), grid, dim3(256), 0, s, a);
   else if (large)
     hipLaunchKernelGGL((gemm_large_kernel<GLU, FP4, false>), grid, dim3(256), 0, s, a);
+  else if (FP4 && (a0.K / 32) % 16 == 0 && a0.K / 32 <= 128)
+    hipLaunchKernelGGL((gemm_small_kernel<GLU, FP4, FP4>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_small_kernel<GLU, FP4>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_small_kernel<GLU, FP4, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -176,12 +176,13 @@ def test_forward_token_counts(lm, dev, T):
     _full_small(lm, dev, get_workload("tiny").with_T(T))
 
 
-@pytest.mark.parametrize("T", [160, 400])
+@pytest.mark.parametrize("T", [16, 160, 400])
 def test_forward_whole_exponent_windows(lm, dev, T):
     """Widths whose rows hold whole 16-block exponent windows (L/32 and I/32
-    multiples of 16, as on the Kimi-K3 layer), on which the large-tile path
-    reads exponents through LDS; at 400 tokens over 8 experts groups exceed
-    96 rows."""
+    multiples of 16, as on the Kimi-K3 layer), on which the grouped kernels
+    read exponents through LDS (large tiles) or hold a wave's K range of them
+    in registers (small tiles, 16 tokens); at 400 tokens over 8 experts groups
+    exceed 96 rows."""
     _full_small(lm, dev, Workload(f"windows{T}", 26, Dims(T=T, L=1024, E=8, k=2, I=512, S=1,
                                                            Is=256)))
 
