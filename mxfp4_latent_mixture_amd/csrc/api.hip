@@ -65,6 +65,7 @@ Workspace carve_workspace(const Plan& p, void* base) {
   w.inv = reinterpret_cast<int32_t*>(take(R * 4));
   w.tiles = reinterpret_cast<int32_t*>(take((size_t)p.max_tiles * 3 * 4));
   w.ntiles = reinterpret_cast<int32_t*>(take(4));
+  w.chunk_base = reinterpret_cast<int32_t*>(take(((T + 63) / 64) * E * 4));
   w.h = reinterpret_cast<uint16_t*>(take(R * I * 2));
   w.h_sh = reinterpret_cast<uint16_t*>(take(S * T * Is * 2));
   w.y = reinterpret_cast<float*>(take(R * L * 4));
@@ -125,7 +126,8 @@ static int run_route(const Plan& p, const Workspace& ws, const uint16_t* x, cons
   if (record_stage(ev, LMOE_STAGE_ROUTER, s) != hipSuccess) return LMOE_ERR_HIP;
   e = launch_topk(p, part, ks, logits_out, rt.idx, rt.w, s);
   if (e != hipSuccess || record_stage(ev, LMOE_STAGE_TOPK, s) != hipSuccess) return LMOE_ERR_HIP;
-  e = launch_permute(p, rt.idx, rt.counts, rt.offsets, rt.perm, rt.inv, ws.tiles, ws.ntiles, s);
+  e = launch_permute(p, rt.idx, rt.counts, rt.offsets, rt.perm, rt.inv, ws.tiles, ws.ntiles,
+                     ws.chunk_base, s);
   if (e != hipSuccess || record_stage(ev, LMOE_STAGE_PERMUTE, s) != hipSuccess)
     return LMOE_ERR_HIP;
   *out = rt;

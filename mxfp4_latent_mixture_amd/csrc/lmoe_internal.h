@@ -61,6 +61,7 @@ struct Workspace {
   int32_t* inv;       // [R]
   int32_t* tiles;     // [max_tiles][3]: expert, first sorted position, rows
   int32_t* ntiles;    // [1]
+  int32_t* chunk_base;  // [ceil(T/64)][E] permutation chunk counts, then first positions
   uint16_t* h;        // [R][I] bf16, sorted route order
   uint16_t* h_sh;     // [S][T][Is] bf16
   float* y;           // [R][L] fp32 route partials, sorted route order
@@ -105,9 +106,13 @@ hipError_t launch_router(const Plan& p, const uint16_t* x, const uint16_t* wr, f
                          hipStream_t s);
 hipError_t launch_topk(const Plan& p, const float* part, int ks, float* logits_out,
                        int32_t* idx, float* w, hipStream_t s);
+// Up to kPermManyFrom tokens one workgroup builds the permutation; beyond,
+// chunks of 64 tokens are counted, scanned and placed by separate kernels
+// (chunk_base: [ceil(T/64)][E] int32 of workspace).
+constexpr int kPermManyFrom = 512;
 hipError_t launch_permute(const Plan& p, const int32_t* idx, int32_t* counts, int32_t* offsets,
                           int32_t* perm, int32_t* inv, int32_t* tiles, int32_t* ntiles,
-                          hipStream_t s);
+                          int32_t* chunk_base, hipStream_t s);
 
 // ---- kernel launchers (experts.hip) ----
 // ev: optional stage events (LMOE_NUM_STAGE_EVENTS entries), recorded after

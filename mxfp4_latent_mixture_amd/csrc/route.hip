@@ -268,6 +268,92 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// The same permutation over many workgroups, for large T: tokens in chunks of
+// 64 (one bit each in the membership masks above); each chunk's routes to an
+// expert are placed after those of all earlier chunks, so the order stays
+// by expert, then by route.
+// ---------------------------------------------------------------------------
+constexpr int kPermChunk = 64;  // tokens per chunk
+
+// cnt[b][e]: routes of chunk b (tokens 64b .. 64b + 63) to expert e
+__global__ __launch_bounds__(256) void chunk_count_kernel(const int32_t* __restrict__ idx, int T,
+                                                          int k, int E,
+                                                          int32_t* __restrict__ cnt) {
+  __shared__ int s_cnt[kMaxE];
+  const int b = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += 256) s_cnt[e] = 0;
+  __syncthreads();
+  const int r0 = b * kPermChunk * k, r1 = min(T, (b + 1) * kPermChunk) * k;
+  for (int r = r0 + threadIdx.x; r < r1; r += 256) atomicAdd(&s_cnt[idx[r]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) cnt[(size_t)b * E + e] = s_cnt[e];
+}
+
+// counts, offsets and the tile list from the chunk counts, which become each
+// chunk's first sorted position per expert (one thread per expert)
+__global__ __launch_bounds__(1024) void chunk_scan_kernel(int32_t* __restrict__ cnt, int nb, int E,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ tiles,
+                                                         int32_t* __restrict__ ntiles, int rows) {
+  __shared__ int s_wave[48];
+  const int e = threadIdx.x;
+  int c = 0;
+  if (e < E) {
+#pragma unroll 8
+    for (int b = 0; b < nb; ++b) c += cnt[(size_t)b * E + e];
+  }
+  int total = 0;
+  const int off = block_exclusive_scan_1024(c, s_wave, &total);
+  const int nt = (c + rows - 1) / rows;
+  int ntot = 0;
+  const int tbase = block_exclusive_scan_1024(nt, s_wave, &ntot);
+  if (e < E) {
+    counts[e] = c;
+    offsets[e] = off;
+    for (int i = 0; i < nt; ++i) {
+      tiles[3 * (tbase + i) + 0] = e;
+      tiles[3 * (tbase + i) + 1] = off + i * rows;
+      tiles[3 * (tbase + i) + 2] = min(rows, c - i * rows);
+    }
+    int run = off;
+    for (int b = 0; b < nb; ++b) {
+      const int v = cnt[(size_t)b * E + e];
+      cnt[(size_t)b * E + e] = run;
+      run += v;
+    }
+  }
+  if (e == 0) {
+    offsets[E] = total;
+    *ntiles = ntot;
+  }
+}
+
+// each route's position: its chunk's first position for the expert plus the
+// rank of its token among the chunk's tokens routed there (a token routes to
+// an expert at most once)
+__global__ __launch_bounds__(256) void chunk_scatter_kernel(const int32_t* __restrict__ idx, int T,
+                                                            int k, int E,
+                                                            const int32_t* __restrict__ base,
+                                                            int32_t* __restrict__ perm,
+                                                            int32_t* __restrict__ inv) {
+  __shared__ unsigned long long s_mask[kMaxE];
+  const int b = blockIdx.x, tg = b * kPermChunk;
+  for (int e = threadIdx.x; e < E; e += 256) s_mask[e] = 0ull;
+  __syncthreads();
+  const int r0 = tg * k, r1 = min(T, tg + kPermChunk) * k;
+  for (int r = r0 + threadIdx.x; r < r1; r += 256) atomicOr(&s_mask[idx[r]], 1ull << (r / k - tg));
+  __syncthreads();
+  for (int r = r0 + threadIdx.x; r < r1; r += 256) {
+    const int t = r / k;
+    const int e = idx[r];
+    const int pos = base[(size_t)b * E + e] + __popcll(s_mask[e] & ((1ull << (t - tg)) - 1ull));
+    perm[pos] = r;
+    inv[r] = pos;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_router(const Plan& p, const uint16_t* x, const uint16_t* wr, float* part,
@@ -289,10 +375,20 @@ hipError_t launch_topk(const Plan& p, const float* part, int ks, float* logits_o
 
 hipError_t launch_permute(const Plan& p, const int32_t* idx, int32_t* counts, int32_t* offsets,
                           int32_t* perm, int32_t* inv, int32_t* tiles, int32_t* ntiles,
-                          hipStream_t s) {
+                          int32_t* chunk_base, hipStream_t s) {
   const lmoe_dims& d = p.d;
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, idx, d.T, d.k, d.E, counts,
-                     offsets, perm, inv, tiles, ntiles, p.rows_per_tile);
+  if (d.T <= kPermManyFrom) {
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, idx, d.T, d.k, d.E, counts,
+                       offsets, perm, inv, tiles, ntiles, p.rows_per_tile);
+    return hipGetLastError();
+  }
+  const int nb = (d.T + kPermChunk - 1) / kPermChunk;
+  hipLaunchKernelGGL(chunk_count_kernel, dim3(nb), dim3(256), 0, s, idx, d.T, d.k, d.E,
+                     chunk_base);
+  hipLaunchKernelGGL(chunk_scan_kernel, dim3(1), dim3(1024), 0, s, chunk_base, nb, d.E, counts,
+                     offsets, tiles, ntiles, p.rows_per_tile);
+  hipLaunchKernelGGL(chunk_scatter_kernel, dim3(nb), dim3(256), 0, s, idx, d.T, d.k, d.E,
+                     chunk_base, perm, inv);
   return hipGetLastError();
 }
 
