@@ -14,12 +14,17 @@ namespace lmoe {
 
 // ---------------------------------------------------------------------------
 // Router: part[split][t][e] = sum over the split's K range of x[t][k] W[e][k].
-// Tile: 64 tokens x 64 experts per 256-thread workgroup, one 32-wide K step
-// per pass; each wave owns 16 tokens and four 16-expert MFMA tiles.
+// Tile: 64 tokens x 64 experts per 256-thread workgroup; each wave owns 16
+// tokens and four 16-expert MFMA tiles. K runs in chunks of 128 values (four
+// MFMA steps per pair of barriers); the next chunk is loaded into registers
+// while the current one is multiplied from LDS. A split's range is whole
+// 32-value steps; values past it are loaded as zeros.
 // ---------------------------------------------------------------------------
 constexpr int kRtTok = 64;
 constexpr int kRtExp = 64;
-constexpr int kRtPad = 40;  // LDS row length in bf16 (32 + 8): 80-byte rows
+constexpr int kRtKc = 128;             // K values per chunk
+constexpr int kRtPad = kRtKc + 8;      // LDS row length in bf16: rows 272 bytes apart
+constexpr int kRtVec = kRtKc / 8 / 4;  // 16-byte pieces per thread and matrix (4)
 
 __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ wr,
@@ -34,44 +39,56 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict_
   const int t0 = blockIdx.y * kRtTok;
   const int split = blockIdx.z;
   const int nsteps = L / 32;
-  const int st0 = split * steps_per;
-  const int st1 = min(nsteps, st0 + steps_per);
+  const int k0 = split * steps_per * 32;
+  const int k1 = min(nsteps, (split + 1) * steps_per) * 32;
+
+  // thread tid moves row tid / 4, 16-byte pieces (tid % 4) + 4 i of a chunk row
+  const int row = tid >> 2, q = tid & 3;
+  const int t = t0 + row, e = e0 + row;
+  const uint16_t* xr = x + (size_t)min(t, T - 1) * L;
+  const uint16_t* wrr = wr + (size_t)min(e, E - 1) * L;
+  u32x4_t vx[kRtVec], vw[kRtVec];
+  auto load = [&](int kc) {
+#pragma unroll
+    for (int i = 0; i < kRtVec; ++i) {
+      const int k = kc + (q + 4 * i) * 8;
+      const bool ok = k < k1;
+      vx[i] = (ok && t < T) ? load16(xr + k) : zero16();
+      vw[i] = (ok && e < E) ? load16(wrr + k) : zero16();
+    }
+  };
 
   f32x4_t acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int st = st0; st < st1; ++st) {
-    __syncthreads();
-    {  // activations: 64 rows x 32 values, 16 bytes per thread
-      const int row = tid >> 2, q = tid & 3;
-      const int t = t0 + row;
-      u32x4_t v = zero16();
-      if (t < T) v = load16(x + (size_t)t * L + st * 32 + q * 8);
-      *reinterpret_cast<u32x4_t*>(&sx[row][q * 8]) = v;
-    }
-    {  // router weights: 64 expert rows x 32 values, 16 bytes per thread
-      const int er = tid >> 2, q = tid & 3;
-      const int e = e0 + er;
-      u32x4_t v = zero16();
-      if (e < E) v = load16(wr + (size_t)e * L + st * 32 + q * 8);
-      *reinterpret_cast<u32x4_t*>(&sw[er][q * 8]) = v;
-    }
-    __syncthreads();
-    const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sx[wave * 16 + col][grp * 8]);
+  load(k0);
+  for (int kc = k0; kc < k1; kc += kRtKc) {
+    __syncthreads();  // every wave is done with the previous chunk
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(&sw[nt * 16 + col][grp * 8]);
-      acc[nt] = mfma16(a, b, acc[nt]);
+    for (int i = 0; i < kRtVec; ++i) {
+      *reinterpret_cast<u32x4_t*>(&sx[row][(q + 4 * i) * 8]) = vx[i];
+      *reinterpret_cast<u32x4_t*>(&sw[row][(q + 4 * i) * 8]) = vw[i];
+    }
+    __syncthreads();
+    load(kc + kRtKc);  // in flight while this chunk is multiplied
+#pragma unroll
+    for (int s = 0; s < kRtKc / 32; ++s) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sx[wave * 16 + col][s * 32 + grp * 8]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(&sw[nt * 16 + col][s * 32 + grp * 8]);
+        acc[nt] = mfma16(a, b, acc[nt]);
+      }
     }
   }
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
-    const int e = e0 + nt * 16 + col;
+    const int ee = e0 + nt * 16 + col;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int t = t0 + wave * 16 + grp * 4 + j;
-      if (t < T && e < E) part[((size_t)split * T + t) * E + e] = acc[nt][j];
+      const int tt = t0 + wave * 16 + grp * 4 + j;
+      if (tt < T && ee < E) part[((size_t)split * T + tt) * E + ee] = acc[nt][j];
     }
   }
 }
