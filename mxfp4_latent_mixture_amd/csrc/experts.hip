@@ -333,32 +333,43 @@ __host__ __device__ constexpr int lg_tiles_per_wave(bool glu, bool fp4) {
 
 // One array per buffer, so the compiler can tell a copy into one buffer from
 // a read of the other and does not wait for every copy before every read.
-typedef uint16_t LgChunk[kLargeRows][kLgKc];
+template <int ROWS>
+using LgChunk = uint16_t[ROWS][kLgKc];
+
+// Routed groups (MXFP4): four waves, up to 128 rows, two workgroups per CU.
+// Shared experts (bf16, dense): eight waves and 256 rows, one workgroup per
+// CU, so each weight chunk serves twice the rows (every row tile reads all of
+// the shared weights) and each activation chunk eight waves.
+__host__ __device__ constexpr int lg_waves(bool fp4) { return fp4 ? 4 : 8; }
+__host__ __device__ constexpr int lg_rows(bool fp4) { return fp4 ? kLargeRows : kDenseRows; }
 
 template <bool GLU, bool FP4, bool EXW>
-__global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) LgChunk sx0, sx1;
-  __shared__ const uint16_t* s_arow[kLargeRows];
+__global__ __launch_bounds__(64 * lg_waves(FP4), FP4 ? 2 : 1) void gemm_large_kernel(GemmArgs a) {
+  constexpr int WAVES = lg_waves(FP4);
+  constexpr int ROWS = lg_rows(FP4);
+  constexpr int MTMAX = ROWS / 16;
+  __shared__ __attribute__((aligned(16))) LgChunk<ROWS> sx0, sx1;
+  __shared__ const uint16_t* s_arow[ROWS];
   // EXW: each wave's exponent windows (its 64 weight rows x 16 blocks)
-  __shared__ __attribute__((aligned(16))) uint8_t s_ex[EXW ? 4 : 1][64][16];
-  auto slot = [&](int r) -> LgChunk& { return r == 0 ? sx0 : sx1; };
+  __shared__ __attribute__((aligned(16))) uint8_t s_ex[EXW ? WAVES : 1][64][16];
+  auto slot = [&](int r) -> LgChunk<ROWS>& { return r == 0 ? sx0 : sx1; };
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
   int tile, nt;
   tile_of_block(a.n_tiles_n, &tile, &nt);
   TileInfo ti;
-  if (!resolve_tile(a, tile, kLargeRows, &ti)) return;
+  if (!resolve_tile(a, tile, ROWS, &ti)) return;
   constexpr int NW = lg_tiles_per_wave(GLU, FP4);  // 16-column tiles per wave
   constexpr int NM = GLU ? 2 : 1;                   // weight matrices per column tile
   const int K = a.K, N = a.N;
   const int nblk = K / 32;
   const int nchunks = (K + kLgKc - 1) / kLgKc;
-  const int n0 = nt * (64 * NW) + wave * (16 * NW);
+  const int n0 = nt * (WAVES * 16 * NW) + wave * (16 * NW);
   const int mtiles = (ti.cnt + 15) / 16;
 
   // rows past the tile repeat its last row: finite values, never stored
-  for (int r = tid; r < kLargeRows; r += 256) s_arow[r] = act_row(a, ti, min(r, ti.cnt - 1));
+  for (int r = tid; r < ROWS; r += 64 * WAVES) s_arow[r] = act_row(a, ti, min(r, ti.cnt - 1));
 
   int nrow[NW];
   bool nvalid[NW];
@@ -420,9 +431,9 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a) {
     }
   };
 
-  f32x4_t acc[8][NW][NM];
+  f32x4_t acc[MTMAX][NW][NM];
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
+  for (int m = 0; m < MTMAX; ++m)
 #pragma unroll
     for (int w = 0; w < NW; ++w)
 #pragma unroll
@@ -435,8 +446,8 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a) {
   auto copy_x = [&](int c, int buf) {
     const int cc = min(c, nchunks - 1);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row0 = wave * 32 + j * 4;
+    for (int j = 0; j < ROWS / WAVES / 4; ++j) {
+      const int row0 = wave * (ROWS / WAVES) + j * 4;
       if (row0 < mtiles * 16) {
         const int row = row0 + (lane >> 4);
         const int seg = (lane & 15) ^ (row & 15);
@@ -487,8 +498,8 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a) {
       // the operands of four row tiles are read back to back, then their
       // MFMAs run; the second four only when the tile has them
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (h == 0 || mtiles > 4) {
+      for (int h = 0; h < MTMAX / 4; ++h) {
+        if (h == 0 || mtiles > 4 * h) {
           bf16x8_t av[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -547,7 +558,7 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
 
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+  for (int m = 0; m < MTMAX; ++m) {
     if (m >= mtiles) continue;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -649,15 +660,15 @@ static hipError_t launch_gemm(const GemmArgs& a0, bool large, int row_tiles, int
   const bool exw = FP4 && (a0.K / 32) % 16 == 0;
   GemmArgs a = a0;
   // large tiles: four waves of lg_tiles_per_wave 16-column MFMA tiles
-  const int cols = large ? 64 * lg_tiles_per_wave(GLU, FP4) : 16;
+  const int cols = large ? 16 * lg_waves(FP4) * lg_tiles_per_wave(GLU, FP4) : 16;
   a.n_tiles_n = (a.N + cols - 1) / cols;
   // row tiles rounded up to whole rounds of the XCDs (tile_of_block)
   const int rounds = (row_tiles + kXcds - 1) / kXcds;
   dim3 grid((unsigned)(rounds * kXcds * a.n_tiles_n), 1, (unsigned)z);
   if (large && exw)
-    hipLaunchKernelGGL((gemm_large_kernel<GLU, FP4, FP4>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_large_kernel<GLU, FP4, FP4>), grid, dim3(64 * lg_waves(FP4)), 0, s, a);
   else if (large)
-    hipLaunchKernelGGL((gemm_large_kernel<GLU, FP4, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_large_kernel<GLU, FP4, false>), grid, dim3(64 * lg_waves(FP4)), 0, s, a);
   else if (FP4 && (a0.K / 32) % 16 == 0 && a0.K / 32 <= 128)
     hipLaunchKernelGGL((gemm_small_kernel<GLU, FP4, FP4>), grid, dim3(256), 0, s, a);
   else
@@ -714,7 +725,7 @@ hipError_t launch_experts(const Plan& p, const uint16_t* x, const lmoe_weights& 
   }
   if (d.S > 0) {
     const bool sh_large = d.T > 64;
-    const int rows = sh_large ? kLargeRows : kSmallRows;
+    const int rows = sh_large ? kDenseRows : kSmallRows;
     const int row_tiles = (d.T + rows - 1) / rows;
     {  // shared gate/up + GLU
       GemmArgs a = {};
