@@ -119,13 +119,14 @@ def stage_kernel(stage: str, large: bool, sh_large: bool, d=None) -> str:
     kind = {"gate_up": ("true", "true"), "down": ("false", "true"),
             "shared_gate_up": ("true", "false"), "shared_down": ("false", "false")}[stage]
     big = sh_large if stage.startswith("shared") else large
-    if not big:
-        return f"gemm_small_kernel<{kind[0]}, {kind[1]}>"
-    # the large MXFP4 kernels read exponents through LDS when K/32 is a
-    # multiple of 16 (third template argument)
+    # the MXFP4 kernels take their exponents in whole 16-block windows when
+    # K/32 is a multiple of 16 (third template argument); the small kernel
+    # holds them in registers, so only up to 128 blocks a row
     K = None if d is None else {"gate_up": d.L, "down": d.I}.get(stage)
-    exw = "true" if (K is not None and (K // 32) % 16 == 0) else "false"
-    return f"gemm_large_kernel<{kind[0]}, {kind[1]}, {exw}>"
+    win = K is not None and (K // 32) % 16 == 0
+    if not big:
+        return f"gemm_small_kernel<{kind[0]}, {kind[1]}, {str(win and K // 32 <= 128).lower()}>"
+    return f"gemm_large_kernel<{kind[0]}, {kind[1]}, {str(win).lower()}>"
 
 
 def sources_sha() -> str:
@@ -301,10 +302,12 @@ def kernel_units(res, lm):
     """(kernel, algorithmic bytes, flops, seconds) per launched kernel."""
     d = res["w"].dims
     logits_given = res["w"].logits_given
-    _, _, sb, sf = algorithmic(d, res["D"], logits_given)
+    tb, tf, sb, sf = algorithmic(d, res["D"], logits_given)
     if lm.path_name(d, logits_given) == "fused_decode":
+        # one kernel does the whole layer: the layer's bytes (the token is
+        # read once, though three stages count it)
         sec = res["stage_ms"]["router"] * 1e-3
-        return [(FUSED_KERNEL, sum(sb.values()), sum(sf.values()), sec)]
+        return [(FUSED_KERNEL, tb, tf, sec)]
     R = d.T * d.k
     large = (R / max(1, min(d.E, R))) > 8.0
     sh_large = d.T > 64

@@ -1,0 +1,79 @@
+"""Host-side checks of bench.py's contract and work model (no GPU): the
+multi-GPU refusal, the algorithmic byte and flop counts at the Kimi-K3
+shapes against sums written out independently here, and the names under
+which the measured kernels are reported."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from workloads import get_workload  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def test_decode_algorithmic_bytes():
+    """T=1, 16 distinct experts: 16 experts' gate, up and down codes (half a
+    byte a weight) and exponents (a byte per 32), the two bf16 shared experts,
+    the bf16 router, the token in and out."""
+    d = get_workload("decode").dims
+    per_expert = 3 * 3584 * 2048 // 2 + 3 * 3584 * 2048 // 32
+    shared = 2 * 3 * 3584 * 2048 * 2
+    router = 3584 * 896 * 2
+    io = 2 * 3584 * 2
+    want = 16 * per_expert + shared + router + io
+    total_bytes, total_flops, st_bytes, _ = bench.algorithmic(d, 16, False)
+    assert want == 281_688_064
+    assert total_bytes == pytest.approx(want, rel=0, abs=0.5)
+    # the per-stage split counts the token once more in each of the router,
+    # gate/up and shared gate/up stages, which all read it
+    assert sum(st_bytes.values()) == pytest.approx(total_bytes + 2 * 2 * 3584, rel=1e-12)
+    # two flops per multiply-add: gate+up+down of 16 routes, 2 shared, router
+    assert total_flops == 2 * (16 * 3 * 3584 * 2048 + 2 * 3 * 3584 * 2048 + 3584 * 896)
+
+
+def test_prefill_algorithmic_flops():
+    d = get_workload("prefill").dims
+    _, total_flops, _, st_flops = bench.algorithmic(d, 896, False)
+    assert st_flops["gate_up"] == 4 * 4096 * 16 * 3584 * 2048 == 1_924_145_348_608
+    assert total_flops == 2 * 4096 * (16 * 3 * 3584 * 2048 + 2 * 3 * 3584 * 2048 + 3584 * 896)
+
+
+def test_reported_kernel_names_match_the_profiled_kernels():
+    """The large MXFP4 kernels carry a third template argument when the
+    exponents go through LDS (K/32 a multiple of 16): both Kimi-K3 GEMMs."""
+    d = get_workload("prefill").dims
+    assert bench.stage_kernel("gate_up", True, True, d) == "gemm_large_kernel<true, true, true>"
+    assert bench.stage_kernel("down", True, True, d) == "gemm_large_kernel<false, true, true>"
+    assert bench.stage_kernel("shared_gate_up", True, True, d) == \
+        "gemm_large_kernel<true, false, false>"
+    # small tiles hold a row's exponents in registers: up to 128 blocks (K3:
+    # 112 for gate/up, 64 for down)
+    assert bench.stage_kernel("gate_up", False, False, d) == "gemm_small_kernel<true, true, true>"
+    assert bench.stage_kernel("down", False, False, d) == "gemm_small_kernel<false, true, true>"
+    assert bench.stage_kernel("shared_down", False, False, d) == \
+        "gemm_small_kernel<false, false, false>"
+    assert bench.stage_kernel("router", True, True, d) == "router_kernel"
+
+
+def test_stale_traffic_is_not_reported(tmp_path, monkeypatch):
+    """Counter traffic taken on other kernel sources is not reported."""
+    f = tmp_path / "t.json"
+    f.write_text('{"sources_sha": "0000", "kernels": {"decode_kernel": {"traffic_bytes": 1}}}')
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.measured_traffic("decode_kernel") is None
+    f.write_text('{"sources_sha": "%s", "kernels": {"decode_kernel": {"traffic_bytes": 7}}}'
+                 % bench.sources_sha())
+    assert bench.measured_traffic("decode_kernel") == 7
+    assert bench.measured_traffic("other") is None
