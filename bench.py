@@ -209,9 +209,11 @@ def run_case(lm, hip, name, dev, steps, warmup, rotate: bool, traced_steps: int)
     import torch
     n_tok = N_TOKENS if rotate else 1
     reps = N_REPLICAS if rotate else 1
-    w, experts, dense, x_pool, logits = setup(name, dev, n_tok, reps)
+    w = __import__("workloads").get_workload(name)
+    T = w.dims.T
+    # rotating calls take T rows at a time from a pool of n_tok * T rows
+    w, experts, dense, x_pool, logits = setup(name, dev, n_tok * T, reps)
     d = w.dims
-    T = d.T
     ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
     out = torch.empty((T, d.L), dtype=torch.int16, device=dev)
     rbuf = routing_buffers(d, dev)
@@ -219,7 +221,7 @@ def run_case(lm, hip, name, dev, steps, warmup, rotate: bool, traced_steps: int)
 
     def args(i):
         if rotate:
-            xi = x_pool[i % n_tok: i % n_tok + 1]
+            xi = x_pool[(i % n_tok) * T: (i % n_tok + 1) * T]
             wi = {**experts, **dense[i % reps]}
         else:
             xi = x_pool[:T]
@@ -370,6 +372,33 @@ def cpu_baseline(max_tokens: int, budget_s: float):
                       f"+ 2 bf16 shared, float64 numpy oracle), {sec:.1f} s of oracle work"}
 
 
+# Further workloads reported on request (--extra): the other configurations of
+# the layer, the expert width the pages' per-expert size implies, and one
+# GPU's share of the layer split eight ways. Decode-sized ones are HBM-bound
+# and rotate tokens like the headline case; the rest are rated against MFMA.
+EXTRA = ("batched_decode", "skewed", "decode_i3072", "prefill_i3072", "decode_tp8")
+
+
+def extra_case(lm, hip, name, dev, steps):
+    from workloads import get_workload
+    d = get_workload(name).dims
+    hbm = d.T <= 64
+    res = run_case(lm, hip, name, dev, steps if hbm else max(3, steps // 20), 3, rotate=hbm,
+                   traced_steps=5)
+    tb, tf, _, _ = algorithmic(d, res["D"], res["w"].logits_given)
+    sec = res["ms"] * 1e-3
+    out = {"T": d.T, "L": d.L, "E": d.E, "k": d.k, "I": d.I, "S": d.S, "Is": d.Is,
+           "distinct_experts": round(res["D"], 1), "ms_per_step": round(res["ms"], 5),
+           "gb_s": round(tb / sec / 1e9, 1), "tflop_s": round(tf / sec / 1e12, 2),
+           "algorithmic_bytes": round(tb), "algorithmic_flops": round(tf),
+           "roofline": roofline_for(res, "hbm" if hbm else "mfma", lm),
+           "stage_us": {k: round(v * 1e3, 1) for k, v in res["stage_ms"].items()}}
+    out["frac_of_peak"] = round(out["gb_s"] / HBM_PEAK_GBS if hbm
+                                else out["tflop_s"] / BF16_PEAK_TFLOPS, 4)
+    log(f"{name}: {res['ms']:.4f} ms/step, {out['gb_s']} GB/s, {out['tflop_s']} TFLOP/s")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -380,6 +409,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--extra", default="",
+                    help="comma-separated further workloads to report, or 'all': "
+                         + ", ".join(EXTRA))
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this size (PMC calibration)")
     args = ap.parse_args()
@@ -450,6 +482,9 @@ def main():
             "roofline": roofline_for(pf, "mfma", lm),
             "stage_us": {k: round(v * 1e3, 1) for k, v in pf["stage_ms"].items()},
         }
+    if args.extra:
+        names = EXTRA if args.extra == "all" else tuple(args.extra.split(","))
+        result["extra"] = {n: extra_case(lm, hip, n, dev, args.steps) for n in names}
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args.cpu_tokens, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -39,8 +39,10 @@ Plan make_plan(const lmoe_dims& d) {
   const double avg = (double)p.R / (double)std::max(1, std::min(d.E, p.R));
   p.rows_per_tile = (avg <= 8.0) ? kSmallRows : kLargeRows;
   p.max_tiles = std::min(d.E, p.R) + p.R / p.rows_per_tile;
+  // every row a decode wave stages (h of one route or one shared expert) and
+  // the token itself fit its fixed-size staging
   p.fused_decode = d.T == 1 && d.L <= kDecodeMaxWidth && d.I <= kDecodeMaxWidth &&
-                   d.S * d.Is <= kDecodeMaxWidth;
+                   p.d.Is <= kDecodeMaxWidth;
   return p;
 }
 

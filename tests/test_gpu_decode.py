@@ -76,6 +76,7 @@ def _run_tokens(lm, dev, w: Workload, n_tokens: int):
     ("no_shared", Dims(T=1, L=320, E=64, k=8, I=256, S=0, Is=0), ("uniform", 118, 132)),
     ("k1", Dims(T=1, L=256, E=16, k=1, I=64, S=3, Is=64), ("uniform", 118, 132)),
     ("wide_k", Dims(T=1, L=288, E=1024, k=32, I=96, S=1, Is=4096), ("uniform", 118, 132)),
+    ("many_shared", Dims(T=1, L=320, E=40, k=4, I=160, S=3, Is=1600), ("uniform", 118, 132)),
 ])
 def test_fused_decode_shapes(lm, dev, name, dims, scales):
     _run_tokens(lm, dev, Workload(name, 40 + len(name), dims, scales=scales), 3)

@@ -302,3 +302,17 @@ def test_full_prefill(lm, dev):
 
 def test_full_skewed(lm, dev):
     _full_size(lm, dev, "skewed", 3)
+
+
+def test_full_decode_i3072(lm, dev):
+    """The expert width implied by the pages' per-expert size."""
+    _full_size(lm, dev, "decode_i3072", 1)
+
+
+def test_full_prefill_i3072(lm, dev):
+    _full_size(lm, dev, "prefill_i3072", 3)
+
+
+def test_full_decode_tp8(lm, dev):
+    """One GPU's eighth of every expert (I = Is = 256), router whole."""
+    _full_size(lm, dev, "decode_tp8", 1)

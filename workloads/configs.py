@@ -17,6 +17,16 @@ Named workloads:
   prefill         T=4096, same layer                   (seed 3)
   skewed          T=8192, same layer, logits given with a Zipf(1.2) expert
                   bias and 5% of tokens carrying a 32-way exact tie (seed 4)
+plus the same layer at the widths the pages imply or shard to:
+  decode_i3072    T=1,    I=Is=3072 (seed 1): the expert width that the
+  prefill_i3072   T=4096, I=Is=3072 (seed 3)  per-expert size the pages quote
+                  implies (17.72 MiB per NVFP4 expert: huggingface.co "Notes
+                  from an NVFP4 port of Kimi K3.1 Pro", the paragraph on
+                  per-token expert reads), here in MXFP4
+  decode_tp8      T=1,    I=Is=256  (seed 1): one GPU's share of every expert
+                  when the experts are split eight ways along the intermediate
+                  width (dev48.org "Kimi K3 on AMD Instinct GPUs with
+                  TokenSpeed", Figure 2), the router whole
 plus smaller parity shapes with ragged tails (not multiples of any tile).
 """
 from __future__ import annotations
@@ -81,6 +91,15 @@ WORKLOADS = {
     "skewed": Workload(
         "skewed", 4, Dims(T=8192, **_K3), logits_given=True,
         note="Zipf(1.2) expert bias on given logits, 5% of tokens tied over 32 experts"),
+    "decode_i3072": Workload(
+        "decode_i3072", 1, Dims(T=1, **{**_K3, "I": 3072, "Is": 3072}),
+        note="K3 decode at the expert width the pages' per-expert size implies"),
+    "prefill_i3072": Workload(
+        "prefill_i3072", 3, Dims(T=4096, **{**_K3, "I": 3072, "Is": 3072}),
+        note="prefill chunk at the expert width the pages' per-expert size implies"),
+    "decode_tp8": Workload(
+        "decode_tp8", 1, Dims(T=1, **{**_K3, "I": 256, "Is": 256}),
+        note="one GPU's eighth of every routed and shared expert, router whole"),
     # Parity shapes: several tiles plus ragged tails in every dimension.
     "ragged": Workload(
         "ragged", 10, Dims(T=37, L=416, E=48, k=6, I=352, S=2, Is=224),
