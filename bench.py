@@ -120,13 +120,14 @@ def stage_kernel(stage: str, large: bool, sh_large: bool, d=None) -> str:
             "shared_gate_up": ("true", "false"), "shared_down": ("false", "false")}[stage]
     big = sh_large if stage.startswith("shared") else large
     # the MXFP4 kernels take their exponents in whole 16-block windows when
-    # K/32 is a multiple of 16 (third template argument); the small kernel
-    # holds them in registers, so only up to 128 blocks a row
+    # K/32 is a multiple of 16 (third template argument), up to 128 blocks a
+    # row in the small kernel's registers and 112 in the large kernel's LDS
     K = None if d is None else {"gate_up": d.L, "down": d.I}.get(stage)
     win = K is not None and (K // 32) % 16 == 0
     if not big:
         return f"gemm_small_kernel<{kind[0]}, {kind[1]}, {str(win and K // 32 <= 128).lower()}>"
-    return f"gemm_large_kernel<{kind[0]}, {kind[1]}, {str(win).lower()}>"
+    # the large kernel stages whole exponent rows of up to 112 bytes
+    return f"gemm_large_kernel<{kind[0]}, {kind[1]}, {str(win and K // 32 <= 112).lower()}>"
 
 
 def sources_sha() -> str:

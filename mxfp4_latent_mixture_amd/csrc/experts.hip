@@ -307,8 +307,9 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Large groups (<= 128 rows): 128 rows x 128 (gate/up) or 256 (down)
-// columns per workgroup with MXFP4 weights, half that with bf16 ones; each
+// Large groups: up to 96 rows (MXFP4) or 256 rows (bf16, the shared
+// experts) x 128 (gate/up) or 256 (down) columns per workgroup with MXFP4
+// weights, and the same columns over eight waves with bf16 ones; each
 // wave owns two paired gate/up 16-wide MFMA tiles for the GLU, or four tiles
 // of the down projection, over all row tiles, so both kinds issue the same
 // MFMAs per chunk.
@@ -321,9 +322,14 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
 // it; two LDS buffers and one barrier per chunk. Rows are stored with their
 // 16-byte segments XOR-swizzled by the row index, so the MFMA operand reads of
 // 16 rows hit distinct banks, and the operands of four row tiles are read
-// back to back before their MFMAs. Two workgroups share a CU.
+// back to back before their MFMAs. Two MXFP4 workgroups share a CU; 96 rows
+// leave LDS room for the exponent rows (the prefill groups of the Kimi-K3
+// layer average 73 rows and rarely pass 96).
 // ---------------------------------------------------------------------------
 constexpr int kLgKc = 128;  // K values per chunk
+// Exponent bytes per weight row that the large MXFP4 kernel stages in LDS
+// (K <= 3584, the Kimi-K3 latent width).
+constexpr int kExRowMax = 112;
 
 // 16-column MFMA tiles per wave: two gate/up pairs or four down tiles; half
 // as many for bf16 weights, whose chunk takes four times the registers.
@@ -336,7 +342,7 @@ __host__ __device__ constexpr int lg_tiles_per_wave(bool glu, bool fp4) {
 template <int ROWS>
 using LgChunk = uint16_t[ROWS][kLgKc];
 
-// Routed groups (MXFP4): four waves, up to 128 rows, two workgroups per CU.
+// Routed groups (MXFP4): four waves, up to 96 rows, two workgroups per CU.
 // Shared experts (bf16, dense): eight waves and 256 rows, one workgroup per
 // CU, so each weight chunk serves twice the rows (every row tile reads all of
 // the shared weights) and each activation chunk eight waves.
@@ -350,8 +356,8 @@ __global__ __launch_bounds__(64 * lg_waves(FP4), FP4 ? 2 : 1) void gemm_large_ke
   constexpr int MTMAX = ROWS / 16;
   __shared__ __attribute__((aligned(16))) LgChunk<ROWS> sx0, sx1;
   __shared__ const uint16_t* s_arow[ROWS];
-  // EXW: each wave's exponent windows (its 64 weight rows x 16 blocks)
-  __shared__ __attribute__((aligned(16))) uint8_t s_ex[EXW ? WAVES : 1][64][16];
+  // EXW: each wave's exponent rows (its 64 weight rows, whole K range)
+  __shared__ __attribute__((aligned(16))) uint8_t s_ex[EXW ? WAVES : 1][EXW ? 64 * kExRowMax : 16];
   auto slot = [&](int r) -> LgChunk<ROWS>& { return r == 0 ? sx0 : sx1; };
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -394,37 +400,45 @@ __global__ __launch_bounds__(64 * lg_waves(FP4), FP4 ? 2 : 1) void gemm_large_ke
     }
   }
 
-  // Exponents, EXW: MX blocks 16W .. 16W + 15 of a row (window W, chunks
-  // 4W .. 4W + 3) reach LDS in one 16-byte global-to-LDS load per row, one
-  // load instruction per wave and window, instead of one byte load per lane
-  // and chunk; each wave reads only its own rows, so no barrier is needed.
-  // Lane l of the copy moves the window of row (w, mm, col) = l / 16 / NM,
-  // l / 16 % NM, l % 16 of this wave.
-  static_assert(!EXW || (FP4 && NW * NM == 4), "one copy lane per weight row of the wave");
-  const uint8_t* ex_row = nullptr;
+  // Exponents, EXW: a wave's 64 weight rows are NM runs of 16 * NW
+  // consecutive rows, so their exponents are NM contiguous runs of
+  // 16 * NW * nblk bytes. They are copied into LDS once, whole, by 16-byte
+  // global-to-LDS loads that read every byte of every line they touch (row r
+  // of the wave, r = mm * 16 * NW + w * 16 + col, at byte r * nblk). Copies
+  // of part of each row per K window read each line once per window, and the
+  // weight stream evicts it in between: for the Kimi-K3 gate/up that fetched
+  // eight times the exponent bytes. Each wave reads only its own rows, so no
+  // barrier is needed.
+  static_assert(!EXW || (FP4 && NW * NM == 4), "64 weight rows per wave");
   if constexpr (EXW) {
-    const int w = (lane >> 4) / NM, mm = (lane >> 4) % NM;
-    const int n = n0 + w * 16 + (lane & 15);
-    ex_row = (mm ? a.s1 : a.s0) + ti.e * a.s_estride + (int64_t)(n < N ? n : 0) * nblk;
+    const int bytes = 64 * nblk;  // a multiple of 1024 (nblk % 16 == 0)
+#pragma unroll
+    for (int i = 0; i < kExRowMax / 16; ++i) {
+      if (i * 1024 < bytes) {  // the same for every lane
+        const int o = i * 1024 + lane * 16;
+        const int r = o / nblk, byte = o - r * nblk;  // 16 bytes inside row r
+        const int mm = r / (16 * NW);
+        const int n = n0 + r % (16 * NW);
+        const uint8_t* src =
+            (mm ? a.s1 : a.s0) + ti.e * a.s_estride + (int64_t)(n < N ? n : 0) * nblk + byte;
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(src),
+            (__attribute__((address_space(3))) void*)(&s_ex[wave][i * 1024]), 16, 0, 0);
+      }
+    }
   }
-  const int nwin = nblk / 16;
-  auto copy_ex = [&](int win) {
-    if constexpr (EXW)
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(ex_row + 16 * min(win, nwin - 1)),
-          (__attribute__((address_space(3))) void*)(&s_ex[wave][0][0]), 16, 0, 0);
-  };
-  // the window's exponents of this lane's blocks (4c + grp for its 4 chunks),
-  // packed one byte per chunk
+  // the exponents of this lane's blocks in window win (blocks 16 win + 4j +
+  // grp, chunks 4 win + j), packed one byte per chunk
   uint32_t exw[NW][NM];
-  auto read_ex = [&]() {
+  auto read_ex = [&](int win) {
     if constexpr (EXW) {
       const uint32_t sel = (uint32_t)grp | ((uint32_t)(4 + grp) << 8) | 0x0c0c0000u;
 #pragma unroll
       for (int w = 0; w < NW; ++w)
 #pragma unroll
         for (int mm = 0; mm < NM; ++mm) {
-          const u32x4_t d = *reinterpret_cast<const u32x4_t*>(&s_ex[wave][(w * NM + mm) * 16 + col][0]);
+          const int r = mm * 16 * NW + w * 16 + col;
+          const u32x4_t d = *reinterpret_cast<const u32x4_t*>(&s_ex[wave][r * nblk + 16 * win]);
           exw[w][mm] = __builtin_amdgcn_perm(d[1], d[0], sel) |
                        (__builtin_amdgcn_perm(d[3], d[2], sel) << 16);
         }
@@ -481,6 +495,16 @@ __global__ __launch_bounds__(64 * lg_waves(FP4), FP4 ? 2 : 1) void gemm_large_ke
   };
   auto compute = [&](int c, int buf, const Bq& b) {
     const bool kv = c * 4 + grp < nblk;  // past the end: zero weights
+    // the lane's block scale per weight tile, once per chunk; zero past the
+    // end (E2M1 codes are finite, so a zero scale gives zero weights)
+    float scale[NW][NM];
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+      for (int mm = 0; mm < NM; ++mm) {
+        const uint32_t ex = !FP4 ? 127u : EXW ? (exw[w][mm] >> (8 * (c & 3))) & 0xffu : b.e[w][mm];
+        scale[w][mm] = kv ? e8m0_to_f32(ex) : 0.f;
+      }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8_t bv[NW][NM];
@@ -488,32 +512,34 @@ __global__ __launch_bounds__(64 * lg_waves(FP4), FP4 ? 2 : 1) void gemm_large_ke
       for (int w = 0; w < NW; ++w)
 #pragma unroll
         for (int mm = 0; mm < NM; ++mm) {
-          if (FP4) {
-            const uint32_t ex = EXW ? (exw[w][mm] >> (8 * (c & 3))) & 0xffu : b.e[w][mm];
-            bv[w][mm] = dequant8(kv ? b.q[w][mm][s] : 0u, e8m0_to_f32(kv ? ex : 127u));
-          }
+          if (FP4)
+            bv[w][mm] = dequant8(b.q[w][mm][s], scale[w][mm]);
           else
             bv[w][mm] = as_bf16x8(kv ? b.h[w][mm][s] : zero16());
         }
       // the operands of four row tiles are read back to back, then their
       // MFMAs run; the second four only when the tile has them
 #pragma unroll
-      for (int h = 0; h < MTMAX / 4; ++h) {
+      for (int h = 0; h < (MTMAX + 3) / 4; ++h) {
+        constexpr int kLast = MTMAX % 4 ? MTMAX % 4 : 4;  // row tiles in the last group
         if (h == 0 || mtiles > 4 * h) {
           bf16x8_t av[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int row = (4 * h + i) * 16 + col;
+            const int row = min(4 * h + i, MTMAX - 1) * 16 + col;
             const int phys = (grp * 4 + s) ^ (row & 15);
             av[i] = *reinterpret_cast<const bf16x8_t*>(&slot(buf)[row][phys * 8]);
           }
           // keeps the reads ahead of the branches below (the compiler would
           // otherwise sink each into its branch and wait for it alone)
-          asm volatile("" ::"v"(av[0]), "v"(av[1]), "v"(av[2]), "v"(av[3]));
+          if (4 * h + 4 <= MTMAX)
+            asm volatile("" ::"v"(av[0]), "v"(av[1]), "v"(av[2]), "v"(av[3]));
+          else if (kLast == 2)
+            asm volatile("" ::"v"(av[0]), "v"(av[1]));
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int m = 4 * h + i;
-            if (m < mtiles) {
+            if (m < MTMAX && m < mtiles) {
 #pragma unroll
               for (int w = 0; w < NW; ++w)
 #pragma unroll
@@ -528,7 +554,6 @@ __global__ __launch_bounds__(64 * lg_waves(FP4), FP4 ? 2 : 1) void gemm_large_ke
 
   __syncthreads();  // s_arow
   Bq bq[2];
-  copy_ex(0);
   copy_x(0, 0);
   load_b(0, bq[0]);
   // No chunk load is conditional (a branch around the loads would make the
@@ -542,12 +567,7 @@ __global__ __launch_bounds__(64 * lg_waves(FP4), FP4 ? 2 : 1) void gemm_large_ke
       // then for every thread, and every wave is done with the other buffer
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __builtin_amdgcn_s_barrier();
-      if (EXW && (c & 3) == 0) {
-        // window c / 4 into registers, then the next window into its place
-        read_ex();
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the reads are done
-        copy_ex(c / 4 + 1);
-      }
+      if (EXW && (c & 3) == 0) read_ex(min(c / 4, nblk / 16 - 1));
       copy_x(c + 1, r ^ 1);
       load_b(c + 1, bq[r ^ 1]);
       __builtin_amdgcn_sched_barrier(0);
@@ -656,8 +676,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 template <bool GLU, bool FP4>
 static hipError_t launch_gemm(const GemmArgs& a0, bool large, int row_tiles, int z,
                               hipStream_t s) {
-  // exponent windows through LDS when every row holds whole 16-block windows
-  const bool exw = FP4 && (a0.K / 32) % 16 == 0;
+  // exponent rows through LDS when they hold whole 16-block windows and fit
+  const bool exw = FP4 && (a0.K / 32) % 16 == 0 && a0.K / 32 <= kExRowMax;
   GemmArgs a = a0;
   // large tiles: four waves of lg_tiles_per_wave 16-column MFMA tiles
   const int cols = large ? 16 * lg_waves(FP4) * lg_tiles_per_wave(GLU, FP4) : 16;

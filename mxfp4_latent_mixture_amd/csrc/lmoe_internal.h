@@ -13,7 +13,7 @@ namespace lmoe {
 
 // Rows (routes) per tile of the grouped expert GEMMs.
 constexpr int kSmallRows = 16;   // one 16-row MFMA tile: decode-sized groups
-constexpr int kLargeRows = 128;  // eight 16-row MFMA tiles: prefill-sized groups
+constexpr int kLargeRows = 96;   // six 16-row MFMA tiles: prefill-sized groups
 constexpr int kDenseRows = 256;  // sixteen: the shared experts' tokens, in one group
 
 // Router: K steps of 32, split over ks partial sums when T is small so the
