@@ -349,6 +349,11 @@ using LgChunk = uint16_t[ROWS][kLgKc];
 __host__ __device__ constexpr int lg_waves(bool fp4) { return fp4 ? 4 : 8; }
 __host__ __device__ constexpr int lg_rows(bool fp4) { return fp4 ? kLargeRows : kDenseRows; }
 
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
 template <bool GLU, bool FP4, bool EXW>
 __global__ __launch_bounds__(64 * lg_waves(FP4), FP4 ? 2 : 1) void gemm_large_kernel(GemmArgs a) {
   constexpr int WAVES = lg_waves(FP4);
@@ -445,157 +450,197 @@ __global__ __launch_bounds__(64 * lg_waves(FP4), FP4 ? 2 : 1) void gemm_large_ke
     }
   };
 
-  f32x4_t acc[MTMAX][NW][NM];
+  // The rest runs with MT row tiles known at compile time for MXFP4 weights
+  // (one instantiation per count a tile can have), and with the tile's count
+  // tested at run time for bf16 ones (sixteen row tiles).
+  auto body = [&](auto mt_c) {
+    constexpr int MT = decltype(mt_c)::value;
+    f32x4_t acc[MT][NW][NM];
 #pragma unroll
-  for (int m = 0; m < MTMAX; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
+      for (int w = 0; w < NW; ++w)
 #pragma unroll
-      for (int mm = 0; mm < NM; ++mm) acc[m][w][mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int mm = 0; mm < NM; ++mm) acc[m][w][mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // copy of chunk c (clamped to the last chunk) into LDS buffer `buf`:
-  // instruction j of wave w moves rows w*32 + 4j .. +4, lane l the 16-byte
-  // segment at physical slot l % 16 of row l / 16 (logical segment slot ^ row
-  // % 16); instructions wholly past the tile's row groups are skipped
-  auto copy_x = [&](int c, int buf) {
-    const int cc = min(c, nchunks - 1);
+    // copy of chunk c (clamped to the last chunk) into LDS buffer `buf`:
+    // instruction j of wave w moves rows w*32 + 4j .. +4, lane l the 16-byte
+    // segment at physical slot l % 16 of row l / 16 (logical segment slot ^ row
+    // % 16); instructions wholly past the tile's row groups are skipped
+    auto copy_x = [&](int c, int buf) {
+      const int cc = min(c, nchunks - 1);
 #pragma unroll
-    for (int j = 0; j < ROWS / WAVES / 4; ++j) {
-      const int row0 = wave * (ROWS / WAVES) + j * 4;
-      if (row0 < mtiles * 16) {
-        const int row = row0 + (lane >> 4);
-        const int seg = (lane & 15) ^ (row & 15);
-        const int k = min(cc * kLgKc + seg * 8, K - 8);  // K % 32 == 0, so k + 8 <= K
-        __builtin_amdgcn_global_load_lds(
-            reinterpret_cast<const void*>(s_arow[row] + k),
-            (__attribute__((address_space(3))) void*)(&slot(buf)[row0][0]), 16, 0, 0);
-      }
-    }
-  };
-  // weights of chunk c for this lane: MX block c*4 + grp
-  struct Bq {
-    u32x4_t q[NW][NM];     // MXFP4: 32 codes
-    uint32_t e[NW][NM];    //        their exponent
-    u32x4_t h[NW][NM][4];  // bf16: 32 values
-  };
-  auto load_b = [&](int c, Bq& b) {
-    const int blk = min(c * 4 + grp, nblk - 1);
-#pragma unroll
-    for (int w = 0; w < NW; ++w)
-#pragma unroll
-      for (int mm = 0; mm < NM; ++mm) {
-        if (FP4) {
-          b.q[w][mm] = load16(qr[w][mm] + blk * 16);
-          if (!EXW) b.e[w][mm] = er[w][mm][blk];
-        } else {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) b.h[w][mm][s] = load16(br[w][mm] + blk * 32 + s * 8);
+      for (int j = 0; j < ROWS / WAVES / 4; ++j) {
+        const int row0 = wave * (ROWS / WAVES) + j * 4;
+        if (row0 < (FP4 ? MT : mtiles) * 16) {
+          const int row = row0 + (lane >> 4);
+          const int seg = (lane & 15) ^ (row & 15);
+          const int k = min(cc * kLgKc + seg * 8, K - 8);  // K % 32 == 0, so k + 8 <= K
+          __builtin_amdgcn_global_load_lds(
+              reinterpret_cast<const void*>(s_arow[row] + k),
+              (__attribute__((address_space(3))) void*)(&slot(buf)[row0][0]), 16, 0, 0);
         }
       }
-  };
-  auto compute = [&](int c, int buf, const Bq& b) {
-    const bool kv = c * 4 + grp < nblk;  // past the end: zero weights
-    // the lane's block scale per weight tile, once per chunk; zero past the
-    // end (E2M1 codes are finite, so a zero scale gives zero weights)
-    float scale[NW][NM];
-#pragma unroll
-    for (int w = 0; w < NW; ++w)
-#pragma unroll
-      for (int mm = 0; mm < NM; ++mm) {
-        const uint32_t ex = !FP4 ? 127u : EXW ? (exw[w][mm] >> (8 * (c & 3))) & 0xffu : b.e[w][mm];
-        scale[w][mm] = kv ? e8m0_to_f32(ex) : 0.f;
-      }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8_t bv[NW][NM];
+    };
+    // weights of chunk c for this lane: MX block c*4 + grp
+    struct Bq {
+      u32x4_t q[NW][NM];     // MXFP4: 32 codes
+      uint32_t e[NW][NM];    //        their exponent
+      u32x4_t h[NW][NM][4];  // bf16: 32 values
+    };
+    auto load_b = [&](int c, Bq& b) {
+      const int blk = min(c * 4 + grp, nblk - 1);
 #pragma unroll
       for (int w = 0; w < NW; ++w)
 #pragma unroll
         for (int mm = 0; mm < NM; ++mm) {
-          if (FP4)
-            bv[w][mm] = dequant8(b.q[w][mm][s], scale[w][mm]);
-          else
-            bv[w][mm] = as_bf16x8(kv ? b.h[w][mm][s] : zero16());
-        }
-      // the operands of four row tiles are read back to back, then their
-      // MFMAs run; the second four only when the tile has them
+          if (FP4) {
+            b.q[w][mm] = load16(qr[w][mm] + blk * 16);
+            if (!EXW) b.e[w][mm] = er[w][mm][blk];
+          } else {
 #pragma unroll
-      for (int h = 0; h < (MTMAX + 3) / 4; ++h) {
-        constexpr int kLast = MTMAX % 4 ? MTMAX % 4 : 4;  // row tiles in the last group
-        if (h == 0 || mtiles > 4 * h) {
-          bf16x8_t av[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = min(4 * h + i, MTMAX - 1) * 16 + col;
-            const int phys = (grp * 4 + s) ^ (row & 15);
-            av[i] = *reinterpret_cast<const bf16x8_t*>(&slot(buf)[row][phys * 8]);
+            for (int s = 0; s < 4; ++s) b.h[w][mm][s] = load16(br[w][mm] + blk * 32 + s * 8);
           }
-          // keeps the reads ahead of the branches below (the compiler would
-          // otherwise sink each into its branch and wait for it alone)
-          if (4 * h + 4 <= MTMAX)
-            asm volatile("" ::"v"(av[0]), "v"(av[1]), "v"(av[2]), "v"(av[3]));
-          else if (kLast == 2)
-            asm volatile("" ::"v"(av[0]), "v"(av[1]));
+        }
+    };
+    auto compute = [&](int c, int buf, const Bq& b) {
+      const bool kv = c * 4 + grp < nblk;  // past the end: zero weights
+      // the lane's block scale per weight tile, once per chunk; zero past the
+      // end (E2M1 codes are finite, so a zero scale gives zero weights)
+      float scale[NW][NM];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = 4 * h + i;
-            if (m < MTMAX && m < mtiles) {
+      for (int w = 0; w < NW; ++w)
 #pragma unroll
-              for (int w = 0; w < NW; ++w)
+        for (int mm = 0; mm < NM; ++mm) {
+          const uint32_t ex = !FP4 ? 127u : EXW ? (exw[w][mm] >> (8 * (c & 3))) & 0xffu : b.e[w][mm];
+          scale[w][mm] = kv ? e8m0_to_f32(ex) : 0.f;
+        }
+      // FP4: every row tile's operands of step s + 1 are read from LDS while
+      // step s multiplies
+      bf16x8_t av[2][FP4 ? MT : 1];
+      auto read_a = [&](int s, bf16x8_t (&dst)[FP4 ? MT : 1]) {
 #pragma unroll
-                for (int mm = 0; mm < NM; ++mm)
-                  acc[m][w][mm] = mfma16(av[i], bv[w][mm], acc[m][w][mm]);
+        for (int m = 0; m < (FP4 ? MT : 0); ++m) {
+          const int row = m * 16 + col;
+          const int phys = (grp * 4 + s) ^ (row & 15);
+          dst[m] = *reinterpret_cast<const bf16x8_t*>(&slot(buf)[row][phys * 8]);
+        }
+      };
+      read_a(0, av[0]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (s < 3) read_a(s + 1, av[(s + 1) & 1]);
+        bf16x8_t bv[NW][NM];
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+#pragma unroll
+          for (int mm = 0; mm < NM; ++mm) {
+            if (FP4)
+              bv[w][mm] = dequant8(b.q[w][mm][s], scale[w][mm]);
+            else
+              bv[w][mm] = as_bf16x8(kv ? b.h[w][mm][s] : zero16());
+          }
+        if constexpr (FP4) {
+          // MT is this tile's row-tile count: no branches, so each MFMA
+          // block can overlap the next step's operand reads
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+#pragma unroll
+              for (int mm = 0; mm < NM; ++mm)
+                acc[m][w][mm] = mfma16(av[s & 1][m], bv[w][mm], acc[m][w][mm]);
+        } else {
+        // the operands of four row tiles are read back to back, then their
+        // MFMAs run; the next four only when the tile has them
+#pragma unroll
+        for (int h = 0; h < MT / 4; ++h) {
+          if (h == 0 || mtiles > 4 * h) {
+            bf16x8_t a4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int row = (4 * h + i) * 16 + col;
+              const int phys = (grp * 4 + s) ^ (row & 15);
+              a4[i] = *reinterpret_cast<const bf16x8_t*>(&slot(buf)[row][phys * 8]);
+            }
+            // keeps the reads ahead of the branches below (the compiler would
+            // otherwise sink each into its branch and wait for it alone)
+            asm volatile("" ::"v"(a4[0]), "v"(a4[1]), "v"(a4[2]), "v"(a4[3]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int m = 4 * h + i;
+              if (m < mtiles) {
+#pragma unroll
+                for (int w = 0; w < NW; ++w)
+#pragma unroll
+                  for (int mm = 0; mm < NM; ++mm)
+                    acc[m][w][mm] = mfma16(a4[i], bv[w][mm], acc[m][w][mm]);
+              }
+            }
+          }
+        }
+        }
+      }
+    };
+
+    __syncthreads();  // s_arow
+    Bq bq[2];
+    copy_x(0, 0);
+    load_b(0, bq[0]);
+    // No chunk load is conditional (a branch around the loads would make the
+    // compiler wait for all of them): a chunk past the end multiplies zero
+    // weights.
+    for (int cb = 0; cb < nchunks; cb += 2) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int c = cb + r;
+        // chunk c (loaded during the previous step) has landed for this thread,
+        // then for every thread, and every wave is done with the other buffer
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        if (EXW && (c & 3) == 0) read_ex(min(c / 4, nblk / 16 - 1));
+        copy_x(c + 1, r ^ 1);
+        load_b(c + 1, bq[r ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(c, r, bq[r]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (!FP4 && m >= mtiles) continue;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        if (!nvalid[w]) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = m * 16 + grp * 4 + j;
+          if (r < ti.cnt) {
+            const int64_t o = out_row(a, ti, r) * a.out_stride + nrow[w];
+            if constexpr (GLU) {
+              a.h_out[o] = f32_to_bf16_bits(silu(acc[m][w][0][j]) * acc[m][w][1][j]);
+            } else {
+              a.y_out[o] = acc[m][w][0][j];
             }
           }
         }
       }
     }
   };
-
-  __syncthreads();  // s_arow
-  Bq bq[2];
-  copy_x(0, 0);
-  load_b(0, bq[0]);
-  // No chunk load is conditional (a branch around the loads would make the
-  // compiler wait for all of them): a chunk past the end multiplies zero
-  // weights.
-  for (int cb = 0; cb < nchunks; cb += 2) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int c = cb + r;
-      // chunk c (loaded during the previous step) has landed for this thread,
-      // then for every thread, and every wave is done with the other buffer
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      __builtin_amdgcn_s_barrier();
-      if (EXW && (c & 3) == 0) read_ex(min(c / 4, nblk / 16 - 1));
-      copy_x(c + 1, r ^ 1);
-      load_b(c + 1, bq[r ^ 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(c, r, bq[r]);
-      __builtin_amdgcn_sched_barrier(0);
+  if constexpr (FP4) {
+    static_assert(MTMAX == 6, "row-tile counts dispatched below");
+    switch (mtiles) {
+      case 1: body(IntC<1>{}); break;
+      case 2: body(IntC<2>{}); break;
+      case 3: body(IntC<3>{}); break;
+      case 4: body(IntC<4>{}); break;
+      case 5: body(IntC<5>{}); break;
+      default: body(IntC<6>{}); break;
     }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-
-#pragma unroll
-  for (int m = 0; m < MTMAX; ++m) {
-    if (m >= mtiles) continue;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      if (!nvalid[w]) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = m * 16 + grp * 4 + j;
-        if (r < ti.cnt) {
-          const int64_t o = out_row(a, ti, r) * a.out_stride + nrow[w];
-          if constexpr (GLU) {
-            a.h_out[o] = f32_to_bf16_bits(silu(acc[m][w][0][j]) * acc[m][w][1][j]);
-          } else {
-            a.y_out[o] = acc[m][w][0][j];
-          }
-        }
-      }
-    }
+  } else {
+    body(IntC<MTMAX>{});
   }
 }
 
