@@ -15,11 +15,23 @@
  * Conventions for every call:
  *  - Pointers marked "device" are HIP device pointers owned by the caller and
  *    must be 16-byte aligned; "host" pointers are read during the call only.
- *  - The library never allocates, frees or synchronises. Temporary storage
- *    comes from the caller's workspace (see lmoe_workspace_bytes).
+ *  - The library never allocates device memory, frees or synchronises.
+ *    Temporary storage comes from the caller's workspace (see
+ *    lmoe_workspace_bytes).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *    default stream). Arguments are validated on the host before anything is
  *    enqueued: a non-zero status means nothing was launched.
+ *  - lmoe_forward with T > 1 (or given logits) and shared experts runs the
+ *    shared experts on a second stream of the current device, which the
+ *    library creates with two events on its first such call: forked from
+ *    `stream` by an event at the start and joined back to it before the
+ *    combine, so the call is complete when `stream` has reached its end, as
+ *    if all of it ran there. That stream is shared by every call on the
+ *    device, so calls from different streams can wait on each other's
+ *    shared-expert work (never on anything else). A call under stream
+ *    capture pulls the second stream into the capture; calls on the device
+ *    must not overlap one being captured. lmoe_forward_traced keeps every
+ *    stage on `stream`.
  *  - Calls are re-entrant provided concurrent calls use distinct workspaces
  *    and outputs.
  *  - Results are deterministic: the same inputs give bit-identical outputs

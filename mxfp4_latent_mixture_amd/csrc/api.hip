@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "lmoe_internal.h"
 
@@ -223,6 +224,38 @@ extern "C" int lmoe_route(const lmoe_dims* dims, const uint16_t* x, const uint16
                    nullptr);
 }
 
+// A second stream per device, with a fork and a join event, on which the
+// shared experts run beside the routing and the routed GEMMs (they depend
+// only on x). Created on a device's first grouped call; if creation fails,
+// calls stay on the caller's stream. The mutex makes each call's fork, side
+// launches and join one unit, so concurrent callers cannot interleave their
+// event records; calls from different caller streams queue on the one side
+// stream.
+struct SideStream {
+  std::mutex mu;
+  bool tried = false;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+static SideStream* side_stream() {
+  static SideStream sides[64];
+  static std::mutex create_mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStream& st = sides[dev];
+  std::lock_guard<std::mutex> g(create_mu);
+  if (!st.tried) {
+    st.tried = true;
+    // default priority, like every stream here
+    if (hipStreamCreateWithFlags(&st.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&st.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&st.join, hipEventDisableTiming) != hipSuccess)
+      st.s = nullptr;
+  }
+  return st.s ? &st : nullptr;
+}
+
 static int forward_impl(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights* wts,
                         int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
                         size_t ws_bytes, void* stream, const hipEvent_t* ev) {
@@ -247,9 +280,28 @@ static int forward_impl(const lmoe_dims* dims, const uint16_t* x, const lmoe_wei
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.fused_decode && !logits_given) return run_fused_decode(p, wsp, x, w, r, out, s, ev);
   Routing rt;
-  st = run_route(p, wsp, x, w.router_w, logits_given, r, &rt, s, ev);
+  // Traced calls keep every stage on the caller's stream, in order, so each
+  // stage's events time it alone.
+  SideStream* side = (!ev && p.d.S > 0) ? side_stream() : nullptr;
+  if (!side) {
+    st = run_route(p, wsp, x, w.router_w, logits_given, r, &rt, s, ev);
+    if (st) return st;
+    hipError_t e = launch_experts(p, x, w, wsp, rt.perm, rt.inv, rt.w, out, s, ev);
+    return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> g(side->mu);
+  if (hipEventRecord(side->fork, s) != hipSuccess ||
+      hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess ||
+      launch_shared(p, x, w, wsp, side->s, nullptr) != hipSuccess ||
+      hipEventRecord(side->join, side->s) != hipSuccess)
+    return LMOE_ERR_HIP;
+  st = run_route(p, wsp, x, w.router_w, logits_given, r, &rt, s, nullptr);
+  hipError_t e = st ? hipSuccess : launch_routed(p, x, w, wsp, rt.perm, s, nullptr);
+  // the join is waited for on every path, so no later call on s can reuse
+  // the workspace before the shared experts are done with it
+  if (hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return LMOE_ERR_HIP;
   if (st) return st;
-  hipError_t e = launch_experts(p, x, w, wsp, rt.perm, rt.inv, rt.w, out, s, ev);
+  if (e == hipSuccess) e = launch_combine(p, wsp, rt.inv, rt.w, out, s, nullptr);
   return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
 }
 

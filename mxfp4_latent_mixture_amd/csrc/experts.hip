@@ -741,10 +741,9 @@ static hipError_t launch_gemm(const GemmArgs& a0, bool large, int row_tiles, int
   return hipGetLastError();
 }
 
-hipError_t launch_experts(const Plan& p, const uint16_t* x, const lmoe_weights& w,
-                          const Workspace& ws, const int32_t* perm, const int32_t* inv,
-                          const float* topk_w, uint16_t* out, hipStream_t s,
-                          const hipEvent_t* ev) {
+hipError_t launch_routed(const Plan& p, const uint16_t* x, const lmoe_weights& w,
+                         const Workspace& ws, const int32_t* perm, hipStream_t s,
+                         const hipEvent_t* ev) {
   const lmoe_dims& d = p.d;
   const bool large = p.rows_per_tile == kLargeRows;
   hipError_t err;
@@ -786,8 +785,15 @@ hipError_t launch_experts(const Plan& p, const uint16_t* x, const lmoe_weights& 
     a.out_stride = d.L;
     err = launch_gemm<false, true>(a, large, p.max_tiles, 1, s);
     if (err != hipSuccess) return err;
-    if ((err = record_stage(ev, LMOE_STAGE_DOWN, s)) != hipSuccess) return err;
+    err = record_stage(ev, LMOE_STAGE_DOWN, s);
   }
+  return err;
+}
+
+hipError_t launch_shared(const Plan& p, const uint16_t* x, const lmoe_weights& w,
+                         const Workspace& ws, hipStream_t s, const hipEvent_t* ev) {
+  const lmoe_dims& d = p.d;
+  hipError_t err = hipSuccess;
   if (d.S > 0) {
     const bool sh_large = d.T > 64;
     const int rows = sh_large ? kDenseRows : kSmallRows;
@@ -829,6 +835,14 @@ hipError_t launch_experts(const Plan& p, const uint16_t* x, const lmoe_weights& 
     if ((err = record_stage(ev, LMOE_STAGE_SHARED_GATEUP, s)) != hipSuccess) return err;
     if ((err = record_stage(ev, LMOE_STAGE_SHARED_DOWN, s)) != hipSuccess) return err;
   }
+  return err;
+}
+
+hipError_t launch_combine(const Plan& p, const Workspace& ws, const int32_t* inv,
+                          const float* topk_w, uint16_t* out, hipStream_t s,
+                          const hipEvent_t* ev) {
+  const lmoe_dims& d = p.d;
+  hipError_t err;
   {
     const int64_t n = (int64_t)d.T * (d.L / 4);
     const unsigned blocks = (unsigned)((n + 255) / 256);
@@ -838,6 +852,16 @@ hipError_t launch_experts(const Plan& p, const uint16_t* x, const lmoe_weights& 
     if (err != hipSuccess) return err;
     err = record_stage(ev, LMOE_STAGE_COMBINE, s);
   }
+  return err;
+}
+
+hipError_t launch_experts(const Plan& p, const uint16_t* x, const lmoe_weights& w,
+                          const Workspace& ws, const int32_t* perm, const int32_t* inv,
+                          const float* topk_w, uint16_t* out, hipStream_t s,
+                          const hipEvent_t* ev) {
+  hipError_t err = launch_routed(p, x, w, ws, perm, s, ev);
+  if (err == hipSuccess) err = launch_shared(p, x, w, ws, s, ev);
+  if (err == hipSuccess) err = launch_combine(p, ws, inv, topk_w, out, s, ev);
   return err;
 }
 

@@ -122,6 +122,16 @@ hipError_t launch_experts(const Plan& p, const uint16_t* x, const lmoe_weights& 
                           const Workspace& ws, const int32_t* perm, const int32_t* inv,
                           const float* topk_w, uint16_t* out, hipStream_t s,
                           const hipEvent_t* ev);
+// its three parts: routed gate/up and down; the shared experts (they read
+// only x, so they may run beside the routing); the combine, which needs both
+hipError_t launch_routed(const Plan& p, const uint16_t* x, const lmoe_weights& w,
+                         const Workspace& ws, const int32_t* perm, hipStream_t s,
+                         const hipEvent_t* ev);
+hipError_t launch_shared(const Plan& p, const uint16_t* x, const lmoe_weights& w,
+                         const Workspace& ws, hipStream_t s, const hipEvent_t* ev);
+hipError_t launch_combine(const Plan& p, const Workspace& ws, const int32_t* inv,
+                          const float* topk_w, uint16_t* out, hipStream_t s,
+                          const hipEvent_t* ev);
 
 inline hipError_t record_stage(const hipEvent_t* ev, int stage, hipStream_t s) {
   return ev ? hipEventRecord(ev[stage], s) : hipSuccess;

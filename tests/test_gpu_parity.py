@@ -316,3 +316,63 @@ def test_full_prefill_i3072(lm, dev):
 def test_full_decode_tp8(lm, dev):
     """One GPU's eighth of every expert (I = Is = 256), router whole."""
     _full_size(lm, dev, "decode_tp8", 1)
+
+
+# ----------------------------------------------------------------------------
+# The shared experts on the library's second stream (untraced grouped calls)
+# against the same layer with every stage on the caller's stream (traced)
+# ----------------------------------------------------------------------------
+
+def _hip_events(n):
+    import ctypes
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    evs = []
+    for _ in range(n):
+        e = ctypes.c_void_p()
+        assert lib.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    return evs
+
+
+@pytest.mark.parametrize("name", ["ragged", "ragged_prefill", "ragged_skew"])
+def test_side_stream_matches_single_stream(lm, dev, name):
+    import torch
+    w = get_workload(name)
+    d = w.dims
+    inp = gen_all(w)
+    dinp = upload(inp, dev)
+    r = {"logits": dinp["logits"]} if w.logits_given else None
+    ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
+    side = torch.empty((d.T, d.L), dtype=torch.int16, device=dev)
+    lm.forward(d, dinp["x"], dinp, w.logits_given, r, side, ws)
+    one = torch.empty_like(side)
+    lm.forward_traced(d, dinp["x"], dinp, w.logits_given, r, one, ws,
+                      _hip_events(lm.NUM_STAGE_EVENTS))
+    torch.cuda.synchronize()
+    assert np.array_equal(side.cpu().numpy(), one.cpu().numpy())
+
+
+def test_back_to_back_calls_reuse_workspace(lm, dev):
+    """Two calls on one stream and one workspace with no wait between them:
+    the second call's shared experts must not start before the first call is
+    done with the workspace."""
+    import torch
+    w = get_workload("ragged_prefill")
+    d = w.dims
+    inp = gen_all(w)
+    dinp = upload(inp, dev)
+    x2 = torch.flip(dinp["x"], dims=[0]).contiguous()
+    ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
+    ref = []
+    for x in (dinp["x"], x2):
+        o = torch.empty((d.T, d.L), dtype=torch.int16, device=dev)
+        lm.forward(d, x, dinp, False, None, o, ws)
+        torch.cuda.synchronize()
+        ref.append(o.cpu().numpy())
+    outs = [torch.empty((d.T, d.L), dtype=torch.int16, device=dev) for _ in range(4)]
+    for i, o in enumerate(outs):
+        lm.forward(d, dinp["x"] if i % 2 == 0 else x2, dinp, False, None, o, ws)
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert np.array_equal(o.cpu().numpy(), ref[i % 2]), f"call {i}"
