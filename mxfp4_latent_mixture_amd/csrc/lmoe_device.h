@@ -20,6 +20,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
 // 2^(b-127) as fp32; b = 0 is the fp32 subnormal 2^-127, b = 255 is NaN.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
   uint32_t bits = (b == 0u) ? 0x00400000u : ((b == 255u) ? 0x7FC00000u : (b << 23));

@@ -9,6 +9,7 @@
 // route of that expert (TokenSpeed section 4.1).
 #include "lmoe_device.h"
 #include "lmoe_internal.h"
+#include "lmoe_topk.h"
 
 namespace lmoe {
 
@@ -94,85 +95,45 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Top-k. Order: larger logit first, equal logits by lower expert index, NaN
-// after every number, -0 == +0. Encoded as one 64-bit key per expert:
-// high word an order-preserving image of the float, low word ~expert.
+// Top-k: one wave per token (four tokens per workgroup). Each lane sums the
+// K-split partial logits of its 16 experts (e = lane + 64 i) in a fixed order,
+// then the wave selects by threshold (lmoe_topk.h; by k rounds when the
+// largest keys crowd into fewer lanes than there are candidates) and takes
+// the softmax over the selected logits.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t order_key(float f, int e) {
-  uint32_t u = __float_as_uint(f);
-  if (f == 0.0f) u = 0u;
-  uint32_t k32;
-  if (f != f) {
-    k32 = 0u;
-  } else {
-    k32 = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  }
-  return ((uint64_t)k32 << 32) | (uint64_t)(~(uint32_t)e);
-}
+constexpr int kTopkWaves = 4;
+constexpr int kMaxE = kWave * kTopkKeysPerLane;  // experts (1024)
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+__global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(
+    const float* __restrict__ part, int ks, int T, int E, int k, float* __restrict__ logits_out,
+    int32_t* __restrict__ idx, float* __restrict__ wout) {
+  __shared__ TopkScratch scr[kTopkWaves];
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int t = blockIdx.x * kTopkWaves + wave;
+  if (t >= T) return;  // the whole wave; no workgroup barrier follows
+  float lv[kTopkKeysPerLane];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint64_t o = __shfl_xor(v, off, kWave);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
-constexpr int kMaxE = 1024;
-constexpr int kPerLane = kMaxE / kWave;  // 16
-
-// One 256-thread workgroup per token: all threads sum the K-split partials
-// into LDS, then wave 0 selects.
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ part, int ks, int T,
-                                                   int E, int k, float* __restrict__ logits_out,
-                                                   int32_t* __restrict__ idx,
-                                                   float* __restrict__ wout) {
-  __shared__ float sl[kMaxE];
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += 256) {
-    float s = 0.f;
-    // fixed summation order; unrolled so the partial loads are in flight together
-#pragma unroll 8
-    for (int i = 0; i < ks; ++i) s += part[((size_t)i * T + t) * E + e];
-    sl[e] = s;
-    if (logits_out) logits_out[(size_t)t * E + e] = s;
-  }
-  __syncthreads();
-  if (tid >= kWave) return;
-  const int lane = tid;
-
-  uint64_t key[kPerLane];
+  for (int i = 0; i < kTopkKeysPerLane; ++i) lv[i] = 0.f;
+  for (int q = 0; q < ks; ++q) {
+    const float* pq = part + ((size_t)q * T + t) * E;
 #pragma unroll
-  for (int i = 0; i < kPerLane; ++i) {
+    for (int i = 0; i < kTopkKeysPerLane; ++i) {
+      const int e = lane + kWave * i;
+      if (e < E) lv[i] = q == 0 ? pq[e] : lv[i] + pq[e];
+    }
+  }
+  uint64_t key[kTopkKeysPerLane];
+#pragma unroll
+  for (int i = 0; i < kTopkKeysPerLane; ++i) {
     const int e = lane + kWave * i;
-    key[i] = (e < E) ? order_key(sl[e], e) : 0ull;
+    key[i] = e < E ? order_key(lv[i], e) : 0ull;
+    if (logits_out && e < E) logits_out[(size_t)t * E + e] = lv[i];
   }
-  uint64_t best = 0ull;
-#pragma unroll
-  for (int i = 0; i < kPerLane; ++i) best = key[i] > best ? key[i] : best;
-
-  int my_e = 0;
-  float my_l = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const uint64_t b = wave_max_u64(best);
-    const int ew = (int)(~(uint32_t)b);
-    if (lane == j) {
-      my_e = ew;
-      my_l = sl[ew];
-    }
-    if ((ew & (kWave - 1)) == lane) {
-      const int slot = ew / kWave;
-      best = 0ull;
-#pragma unroll
-      for (int i = 0; i < kPerLane; ++i) {
-        if (i == slot) key[i] = 0ull;
-        best = key[i] > best ? key[i] : best;
-      }
-    }
-  }
+  uint64_t mine = 0ull;  // lane j: the j-th largest key
+  if (!select_by_threshold(k, key, scr[wave], mine)) select_by_rounds(k, key, mine);
   // softmax over the selected logits, relative to the largest (the first)
+  const int my_e = (int)(~(uint32_t)mine);
+  const float my_l = lane < k ? key_value(mine) : 0.f;
   const float l0 = __shfl(my_l, 0, kWave);
   const float z = (lane < k) ? expf(my_l - l0) : 0.f;
   float s = z;
@@ -385,8 +346,8 @@ hipError_t launch_router(const Plan& p, const uint16_t* x, const uint16_t* wr, f
 hipError_t launch_topk(const Plan& p, const float* part, int ks, float* logits_out,
                        int32_t* idx, float* w, hipStream_t s) {
   const lmoe_dims& d = p.d;
-  hipLaunchKernelGGL(topk_kernel, dim3(d.T), dim3(256), 0, s, part, ks, d.T, d.E, d.k,
-                     logits_out, idx, w);
+  hipLaunchKernelGGL(topk_kernel, dim3((d.T + kTopkWaves - 1) / kTopkWaves), dim3(64 * kTopkWaves),
+                     0, s, part, ks, d.T, d.E, d.k, logits_out, idx, w);
   return hipGetLastError();
 }
 
