@@ -95,31 +95,51 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Top-k: one wave per token (four tokens per workgroup). Each lane sums the
-// K-split partial logits of its 16 experts (e = lane + 64 i) in a fixed order,
-// then the wave selects by threshold (lmoe_topk.h; by k rounds when the
-// largest keys crowd into fewer lanes than there are candidates) and takes
-// the softmax over the selected logits.
+// Top-k. The logits are summed from the router's K-split partials in a fixed
+// order (split 0 first); one wave then selects by threshold (lmoe_topk.h; by k
+// rounds when the largest keys crowd into fewer lanes than there are
+// candidates) and takes the softmax over the selected logits.
+//   SPLIT = false (one partial, prefill sizes): one wave per token, four
+//     tokens per workgroup; lane l holds experts l + 64 i.
+//   SPLIT = true (many partials, small T): one workgroup per token; its 256
+//     threads sum the partials of four experts each, eight splits in flight,
+//     into LDS, and wave 0 selects.
 // ---------------------------------------------------------------------------
 constexpr int kTopkWaves = 4;
 constexpr int kMaxE = kWave * kTopkKeysPerLane;  // experts (1024)
 
+template <bool SPLIT>
 __global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(
     const float* __restrict__ part, int ks, int T, int E, int k, float* __restrict__ logits_out,
     int32_t* __restrict__ idx, float* __restrict__ wout) {
-  __shared__ TopkScratch scr[kTopkWaves];
+  __shared__ TopkScratch scr[SPLIT ? 1 : kTopkWaves];
+  __shared__ float sl[SPLIT ? kMaxE : 1];
   const int wave = threadIdx.x >> 6, lane = lane_id();
-  const int t = blockIdx.x * kTopkWaves + wave;
-  if (t >= T) return;  // the whole wave; no workgroup barrier follows
+  const int t = SPLIT ? blockIdx.x : blockIdx.x * kTopkWaves + wave;
   float lv[kTopkKeysPerLane];
-#pragma unroll
-  for (int i = 0; i < kTopkKeysPerLane; ++i) lv[i] = 0.f;
-  for (int q = 0; q < ks; ++q) {
-    const float* pq = part + ((size_t)q * T + t) * E;
+  if constexpr (SPLIT) {
+    for (int e = threadIdx.x; e < E; e += 64 * kTopkWaves) {
+      float sum = 0.f;
+#pragma unroll 8
+      for (int q = 0; q < ks; ++q) sum += part[((size_t)q * T + t) * E + e];
+      sl[e] = sum;
+      if (logits_out) logits_out[(size_t)t * E + e] = sum;
+    }
+    __syncthreads();
+    if (wave != 0) return;
 #pragma unroll
     for (int i = 0; i < kTopkKeysPerLane; ++i) {
       const int e = lane + kWave * i;
-      if (e < E) lv[i] = q == 0 ? pq[e] : lv[i] + pq[e];
+      lv[i] = e < E ? sl[e] : 0.f;
+    }
+  } else {
+    if (t >= T) return;  // the whole wave; no workgroup barrier follows
+    const float* pt = part + (size_t)t * E;
+#pragma unroll
+    for (int i = 0; i < kTopkKeysPerLane; ++i) {
+      const int e = lane + kWave * i;
+      lv[i] = e < E ? pt[e] : 0.f;
+      if (logits_out && e < E) logits_out[(size_t)t * E + e] = lv[i];
     }
   }
   uint64_t key[kTopkKeysPerLane];
@@ -127,10 +147,9 @@ __global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(
   for (int i = 0; i < kTopkKeysPerLane; ++i) {
     const int e = lane + kWave * i;
     key[i] = e < E ? order_key(lv[i], e) : 0ull;
-    if (logits_out && e < E) logits_out[(size_t)t * E + e] = lv[i];
   }
   uint64_t mine = 0ull;  // lane j: the j-th largest key
-  if (!select_by_threshold(k, key, scr[wave], mine)) select_by_rounds(k, key, mine);
+  if (!select_by_threshold(k, key, scr[SPLIT ? 0 : wave], mine)) select_by_rounds(k, key, mine);
   // softmax over the selected logits, relative to the largest (the first)
   const int my_e = (int)(~(uint32_t)mine);
   const float my_l = lane < k ? key_value(mine) : 0.f;
@@ -346,8 +365,12 @@ hipError_t launch_router(const Plan& p, const uint16_t* x, const uint16_t* wr, f
 hipError_t launch_topk(const Plan& p, const float* part, int ks, float* logits_out,
                        int32_t* idx, float* w, hipStream_t s) {
   const lmoe_dims& d = p.d;
-  hipLaunchKernelGGL(topk_kernel, dim3((d.T + kTopkWaves - 1) / kTopkWaves), dim3(64 * kTopkWaves),
-                     0, s, part, ks, d.T, d.E, d.k, logits_out, idx, w);
+  if (ks == 1)
+    hipLaunchKernelGGL(topk_kernel<false>, dim3((d.T + kTopkWaves - 1) / kTopkWaves),
+                       dim3(64 * kTopkWaves), 0, s, part, ks, d.T, d.E, d.k, logits_out, idx, w);
+  else
+    hipLaunchKernelGGL(topk_kernel<true>, dim3(d.T), dim3(64 * kTopkWaves), 0, s, part, ks, d.T,
+                       d.E, d.k, logits_out, idx, w);
   return hipGetLastError();
 }
 
