@@ -113,7 +113,15 @@ STAGE_KERNEL = {
 }
 
 
-def stage_kernel(stage: str, large: bool, sh_large: bool, d=None) -> str:
+def stage_kernel(stage: str, large: bool, sh_large: bool, d=None, logits_given=False) -> str:
+    if stage == "topk" and d is not None:
+        # one wave per token when the router leaves one partial sum per
+        # logit, one workgroup per token when it splits K (small T)
+        tiles = -(-d.E // 64) * -(-d.T // 64)
+        ks = 1 if logits_given else max(1, min(d.L // 32, -(-512 // tiles)))
+        return f"topk_kernel<{'false' if ks == 1 else 'true'}>"
+    if stage == "permute" and d is not None and d.T > 512:
+        return "chunk_scan_kernel"
     if stage in STAGE_KERNEL:
         return STAGE_KERNEL[stage]
     kind = {"gate_up": ("true", "true"), "down": ("false", "true"),
@@ -314,7 +322,8 @@ def kernel_units(res, lm):
     R = d.T * d.k
     large = (R / max(1, min(d.E, R))) > 8.0
     sh_large = d.T > 64
-    return [(stage_kernel(s, large, sh_large, d), sb[s], sf[s], res["stage_ms"][s] * 1e-3)
+    return [(stage_kernel(s, large, sh_large, d, logits_given), sb[s], sf[s],
+             res["stage_ms"][s] * 1e-3)
             for s in sb if res["stage_ms"][s] > 0]
 
 

@@ -65,6 +65,12 @@ def test_reported_kernel_names_match_the_profiled_kernels():
     assert bench.stage_kernel("shared_down", False, False, d) == \
         "gemm_small_kernel<false, false, false>"
     assert bench.stage_kernel("router", True, True, d) == "router_kernel"
+    # the router splits K over workgroups only when its tiles are few
+    assert bench.stage_kernel("topk", True, True, d) == "topk_kernel<false>"
+    assert bench.stage_kernel("topk", False, False, get_workload("batched_decode").dims) == \
+        "topk_kernel<true>"
+    assert bench.stage_kernel("topk", True, True, get_workload("skewed").dims, True) == \
+        "topk_kernel<false>"
 
 
 def test_stale_traffic_is_not_reported(tmp_path, monkeypatch):
