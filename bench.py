@@ -117,8 +117,10 @@ def stage_kernel(stage: str, large: bool, sh_large: bool, d=None, logits_given=F
     if stage == "topk" and d is not None:
         # one wave per token when the router leaves one partial sum per
         # logit, one workgroup per token when it splits K (small T)
-        tiles = -(-d.E // 64) * -(-d.T // 64)
-        ks = 1 if logits_given else max(1, min(d.L // 32, -(-512 // tiles)))
+        tok = 128 if d.T > 512 else 64
+        tiles = -(-d.E // 64) * -(-d.T // tok)
+        target = 256 if tok == 128 else 512
+        ks = 1 if logits_given else max(1, min(d.L // 32, -(-target // tiles)))
         return f"topk_kernel<{'false' if ks == 1 else 'true'}>"
     if stage == "permute" and d is not None and d.T > 512:
         return "chunk_scan_kernel"

@@ -28,10 +28,14 @@ Plan make_plan(const lmoe_dims& d) {
   p.d = d;
   if (p.d.S == 0) p.d.Is = 0;
   p.R = d.T * d.k;
-  // Router: enough (tile x split) workgroups to spread the weight stream.
+  // Router: enough (tile x split) workgroups to spread the weight stream;
+  // 128-token tiles beyond 512 tokens (each router row read once per 128
+  // tokens), and no K split once they alone fill the chip.
   const int nsteps = d.L / 32;
-  const int tiles = ((d.E + 63) / 64) * ((d.T + 63) / 64);
-  int ks = std::max(1, std::min(nsteps, (512 + tiles - 1) / std::max(1, tiles)));
+  p.router.tok = d.T > 512 ? 128 : 64;
+  const int tiles = ((d.E + 63) / 64) * ((d.T + p.router.tok - 1) / p.router.tok);
+  const int target = p.router.tok == 128 ? 256 : 512;
+  int ks = std::max(1, std::min(nsteps, (target + tiles - 1) / std::max(1, tiles)));
   int per = (nsteps + ks - 1) / ks;
   ks = (nsteps + per - 1) / per;
   p.router.ks = ks;

@@ -21,6 +21,7 @@ constexpr int kDenseRows = 256;  // sixteen: the shared experts' tokens, in one 
 struct RouterPlan {
   int ks;          // number of K splits (partial sums)
   int steps_per;   // 32-wide K steps per split
+  int tok;         // tokens per router tile (64, or 128 beyond 512 tokens)
 };
 
 // Counter block at the start of every workspace (int32 slots, each counter on

@@ -15,83 +15,103 @@ namespace lmoe {
 
 // ---------------------------------------------------------------------------
 // Router: part[split][t][e] = sum over the split's K range of x[t][k] W[e][k].
-// Tile: 64 tokens x 64 experts per 256-thread workgroup; each wave owns 16
-// tokens and four 16-expert MFMA tiles. K runs in chunks of 128 values (four
+// Tile: TOK tokens (64, or 128 for prefill sizes) x 64 experts per
+// 256-thread workgroup; each wave owns TOK/4 tokens (one or two 16-token MFMA
+// tiles) and four 16-expert MFMA tiles, so a 128-token tile reads each
+// router row once for twice the tokens. K runs in chunks of 128 values (four
 // MFMA steps per pair of barriers); the next chunk is loaded into registers
 // while the current one is multiplied from LDS. A split's range is whole
 // 32-value steps; values past it are loaded as zeros.
 // ---------------------------------------------------------------------------
-constexpr int kRtTok = 64;
 constexpr int kRtExp = 64;
 constexpr int kRtKc = 128;             // K values per chunk
 constexpr int kRtPad = kRtKc + 8;      // LDS row length in bf16: rows 272 bytes apart
-constexpr int kRtVec = kRtKc / 8 / 4;  // 16-byte pieces per thread and matrix (4)
+constexpr int kRtPieces = kRtKc / 8;   // 16-byte pieces per chunk row (16)
 
+template <int TOK>
 __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ wr,
                                                      float* __restrict__ part, int T, int L,
                                                      int E, int steps_per) {
-  __shared__ __attribute__((aligned(16))) uint16_t sx[kRtTok][kRtPad];
+  constexpr int MT = TOK / 64;              // 16-token MFMA tiles per wave
+  constexpr int XTPR = 256 / TOK;           // threads per token row of a chunk
+  constexpr int XV = kRtPieces / XTPR;      // their 16-byte pieces each
+  constexpr int WV = kRtPieces / 4;         // four threads per router row
+  __shared__ __attribute__((aligned(16))) uint16_t sx[TOK][kRtPad];
   __shared__ __attribute__((aligned(16))) uint16_t sw[kRtExp][kRtPad];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
   const int e0 = blockIdx.x * kRtExp;
-  const int t0 = blockIdx.y * kRtTok;
+  const int t0 = blockIdx.y * TOK;
   const int split = blockIdx.z;
   const int nsteps = L / 32;
   const int k0 = split * steps_per * 32;
   const int k1 = min(nsteps, (split + 1) * steps_per) * 32;
 
-  // thread tid moves row tid / 4, 16-byte pieces (tid % 4) + 4 i of a chunk row
-  const int row = tid >> 2, q = tid & 3;
-  const int t = t0 + row, e = e0 + row;
+  // token row tid / XTPR, pieces tid % XTPR + XTPR i; router row tid / 4,
+  // pieces tid % 4 + 4 i
+  const int xrow = tid / XTPR, xq = tid % XTPR;
+  const int wrow = tid >> 2, wq = tid & 3;
+  const int t = t0 + xrow, e = e0 + wrow;
   const uint16_t* xr = x + (size_t)min(t, T - 1) * L;
   const uint16_t* wrr = wr + (size_t)min(e, E - 1) * L;
-  u32x4_t vx[kRtVec], vw[kRtVec];
+  u32x4_t vx[XV], vw[WV];
   auto load = [&](int kc) {
 #pragma unroll
-    for (int i = 0; i < kRtVec; ++i) {
-      const int k = kc + (q + 4 * i) * 8;
-      const bool ok = k < k1;
-      vx[i] = (ok && t < T) ? load16(xr + k) : zero16();
-      vw[i] = (ok && e < E) ? load16(wrr + k) : zero16();
+    for (int i = 0; i < XV; ++i) {
+      const int k = kc + (xq + XTPR * i) * 8;
+      vx[i] = (k < k1 && t < T) ? load16(xr + k) : zero16();
+    }
+#pragma unroll
+    for (int i = 0; i < WV; ++i) {
+      const int k = kc + (wq + 4 * i) * 8;
+      vw[i] = (k < k1 && e < E) ? load16(wrr + k) : zero16();
     }
   };
 
-  f32x4_t acc[4];
+  f32x4_t acc[MT][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[m][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   load(k0);
   for (int kc = k0; kc < k1; kc += kRtKc) {
     __syncthreads();  // every wave is done with the previous chunk
 #pragma unroll
-    for (int i = 0; i < kRtVec; ++i) {
-      *reinterpret_cast<u32x4_t*>(&sx[row][(q + 4 * i) * 8]) = vx[i];
-      *reinterpret_cast<u32x4_t*>(&sw[row][(q + 4 * i) * 8]) = vw[i];
-    }
+    for (int i = 0; i < XV; ++i)
+      *reinterpret_cast<u32x4_t*>(&sx[xrow][(xq + XTPR * i) * 8]) = vx[i];
+#pragma unroll
+    for (int i = 0; i < WV; ++i)
+      *reinterpret_cast<u32x4_t*>(&sw[wrow][(wq + 4 * i) * 8]) = vw[i];
     __syncthreads();
     load(kc + kRtKc);  // in flight while this chunk is multiplied
 #pragma unroll
     for (int s = 0; s < kRtKc / 32; ++s) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sx[wave * 16 + col][s * 32 + grp * 8]);
+      bf16x8_t a[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        a[m] = *reinterpret_cast<const bf16x8_t*>(&sx[wave * 16 * MT + m * 16 + col][s * 32 + grp * 8]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(&sw[nt * 16 + col][s * 32 + grp * 8]);
-        acc[nt] = mfma16(a, b, acc[nt]);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m][nt] = mfma16(a[m], b, acc[m][nt]);
       }
     }
   }
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int ee = e0 + nt * 16 + col;
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tt = t0 + wave * 16 + grp * 4 + j;
-      if (tt < T && ee < E) part[((size_t)split * T + tt) * E + ee] = acc[nt][j];
+    for (int nt = 0; nt < 4; ++nt) {
+      const int ee = e0 + nt * 16 + col;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tt = t0 + wave * 16 * MT + m * 16 + grp * 4 + j;
+        if (tt < T && ee < E) part[((size_t)split * T + tt) * E + ee] = acc[m][nt][j];
+      }
     }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -356,9 +376,14 @@ __global__ __launch_bounds__(256) void chunk_scatter_kernel(const int32_t* __res
 hipError_t launch_router(const Plan& p, const uint16_t* x, const uint16_t* wr, float* part,
                          hipStream_t s) {
   const lmoe_dims& d = p.d;
-  dim3 grid((d.E + kRtExp - 1) / kRtExp, (d.T + kRtTok - 1) / kRtTok, p.router.ks);
-  hipLaunchKernelGGL(router_kernel, grid, dim3(256), 0, s, x, wr, part, d.T, d.L, d.E,
-                     p.router.steps_per);
+  const int tok = p.router.tok;
+  dim3 grid((d.E + kRtExp - 1) / kRtExp, (d.T + tok - 1) / tok, p.router.ks);
+  if (tok == 128)
+    hipLaunchKernelGGL(router_kernel<128>, grid, dim3(256), 0, s, x, wr, part, d.T, d.L, d.E,
+                       p.router.steps_per);
+  else
+    hipLaunchKernelGGL(router_kernel<64>, grid, dim3(256), 0, s, x, wr, part, d.T, d.L, d.E,
+                       p.router.steps_per);
   return hipGetLastError();
 }
 
