@@ -140,10 +140,29 @@ def stage_kernel(stage: str, large: bool, sh_large: bool, d=None, logits_given=F
     return f"gemm_large_kernel<{kind[0]}, {kind[1]}, {str(win and K // 32 <= 112).lower()}>"
 
 
-def sources_sha() -> str:
-    h = hashlib.sha256()
+# The source files a kernel is compiled from: its own file and the headers
+# every kernel file includes. Counter traffic is kept per kernel, keyed to a
+# hash of these files, so a change elsewhere does not discard it.
+KERNEL_SOURCES = {
+    "decode_kernel": "decode.hip",
+    "gemm_": "experts.hip",
+    "router_kernel": "route.hip",
+    "topk_kernel": "route.hip",
+    "chunk_": "route.hip",
+    "permute_kernel": "route.hip",
+    "combine_kernel": "experts.hip",
+}
+
+
+def sources_sha(kernel: str = None) -> str:
+    """Hash of the kernel's source files (all of csrc when kernel is None)."""
     csrc = os.path.join(ROOT, "mxfp4_latent_mixture_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    names = sorted(os.listdir(csrc))
+    if kernel is not None:
+        own = [f for k, f in KERNEL_SOURCES.items() if kernel.startswith(k)]
+        names = [n for n in names if n.endswith(".h") or n in own]
+    h = hashlib.sha256()
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -151,16 +170,16 @@ def sources_sha() -> str:
 
 def measured_traffic(kernel: str):
     """HBM bytes per launch of `kernel` from the committed PMC summary, or None
-    when absent or taken on different kernel sources."""
+    when absent or taken on different sources of that kernel."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("sources_sha") != sources_sha():
-        return None
     k = t.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("traffic_bytes")
+    if k is None or k.get("sources_sha") != sources_sha(kernel):
+        return None
+    return k.get("traffic_bytes")
 
 
 # ---------------------------------------------------------------------------

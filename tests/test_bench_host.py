@@ -74,12 +74,23 @@ def test_reported_kernel_names_match_the_profiled_kernels():
 
 
 def test_stale_traffic_is_not_reported(tmp_path, monkeypatch):
-    """Counter traffic taken on other kernel sources is not reported."""
+    """Counter traffic taken on other sources of a kernel is not reported;
+    traffic of a kernel whose sources are unchanged is."""
     f = tmp_path / "t.json"
-    f.write_text('{"sources_sha": "0000", "kernels": {"decode_kernel": {"traffic_bytes": 1}}}')
+    f.write_text('{"kernels": {"decode_kernel": {"sources_sha": "0000", "traffic_bytes": 1}}}')
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
     assert bench.measured_traffic("decode_kernel") is None
-    f.write_text('{"sources_sha": "%s", "kernels": {"decode_kernel": {"traffic_bytes": 7}}}'
-                 % bench.sources_sha())
+    f.write_text('{"kernels": {"decode_kernel": {"sources_sha": "%s", "traffic_bytes": 7}}}'
+                 % bench.sources_sha("decode_kernel"))
     assert bench.measured_traffic("decode_kernel") == 7
     assert bench.measured_traffic("other") is None
+
+
+def test_kernel_sources_hash_only_their_files():
+    """The decode kernel's hash covers decode.hip and the headers, not the
+    grouped path's files; the grouped GEMMs' covers experts.hip."""
+    assert bench.sources_sha("decode_kernel") != bench.sources_sha("gemm_large_kernel<true, true, true>")
+    assert bench.sources_sha("gemm_large_kernel<true, true, true>") == \
+        bench.sources_sha("gemm_small_kernel<true, true, true>")
+    assert bench.sources_sha() not in (bench.sources_sha("decode_kernel"),
+                                       bench.sources_sha("gemm_large_kernel<true, true, true>"))
