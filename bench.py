@@ -124,20 +124,20 @@ def stage_kernel(stage: str, large: bool, sh_large: bool, d=None, logits_given=F
         return f"topk_kernel<{'false' if ks == 1 else 'true'}>"
     if stage == "permute" and d is not None and d.T > 512:
         return "chunk_scan_kernel"
+    if stage == "router" and d is not None:
+        return f"router_kernel<{128 if d.T > 512 else 64}>"
     if stage in STAGE_KERNEL:
         return STAGE_KERNEL[stage]
     kind = {"gate_up": ("true", "true"), "down": ("false", "true"),
             "shared_gate_up": ("true", "false"), "shared_down": ("false", "false")}[stage]
-    big = sh_large if stage.startswith("shared") else large
-    # the MXFP4 kernels take their exponents in whole 16-block windows when
-    # K/32 is a multiple of 16 (third template argument), up to 128 blocks a
-    # row in the small kernel's registers and 112 in the large kernel's LDS
+    if stage.startswith("shared") and not sh_large:
+        # bf16 16-row tiles for the shared experts of up to 64 tokens
+        return f"gemm_small_kernel<{kind[0]}>"
+    # the large MXFP4 kernel stages whole exponent rows in LDS when K/32 is a
+    # multiple of 16 and at most 112 (third template argument)
     K = None if d is None else {"gate_up": d.L, "down": d.I}.get(stage)
-    win = K is not None and (K // 32) % 16 == 0
-    if not big:
-        return f"gemm_small_kernel<{kind[0]}, {kind[1]}, {str(win and K // 32 <= 128).lower()}>"
-    # the large kernel stages whole exponent rows of up to 112 bytes
-    return f"gemm_large_kernel<{kind[0]}, {kind[1]}, {str(win and K // 32 <= 112).lower()}>"
+    win = K is not None and (K // 32) % 16 == 0 and K // 32 <= 112
+    return f"gemm_large_kernel<{kind[0]}, {kind[1]}, {str(win).lower()}>"
 
 
 # The source files a kernel is compiled from: its own file and the headers
@@ -340,8 +340,7 @@ def kernel_units(res, lm):
         # read once, though three stages count it)
         sec = res["stage_ms"]["router"] * 1e-3
         return [(FUSED_KERNEL, tb, tf, sec)]
-    R = d.T * d.k
-    large = (R / max(1, min(d.E, R))) > 8.0
+    large = True  # routed groups of every size take the large kernel
     sh_large = d.T > 64
     return [(stage_kernel(s, large, sh_large, d, logits_given), sb[s], sf[s],
              res["stage_ms"][s] * 1e-3)

@@ -192,12 +192,12 @@ const char* lmoe_stage_name(int stage);
 
 /* Which implementation lmoe_forward uses for these dimensions (static
  * string): "fused_decode" (T == 1 with computed logits and L, I, Is at most
- * 4096: the whole layer in one persistent kernel), "grouped_small" (expert groups of at most 16 rows)
- * or "grouped_large" (groups of up to 96 rows), "invalid" for bad dims.
- * Decode streams the active weights once per token (infervisor.ai "Bringing
- * up Kimi-K3 on day zero", "The roofline"); the grouped forms follow the
- * expert-sorted tiling of dev48.org "Kimi K3 on AMD Instinct GPUs with
- * TokenSpeed", section 4.1. */
+ * 4096: the whole layer in one persistent kernel), "grouped" (routing
+ * kernels, then grouped GEMMs over expert groups of up to 96 rows, then the
+ * combine), "invalid" for bad dims. Decode streams the active weights once
+ * per token (infervisor.ai "Bringing up Kimi-K3 on day zero", "The
+ * roofline"); the grouped form follows the expert-sorted tiling of dev48.org
+ * "Kimi K3 on AMD Instinct GPUs with TokenSpeed", section 4.1. */
 const char* lmoe_path_name(const lmoe_dims* dims, int logits_given);
 
 /* Test hook: dequantise an MXFP4 matrix with the same device routine the

@@ -96,44 +96,22 @@ __device__ __forceinline__ int64_t out_row(const GemmArgs& a, const TileInfo& ti
 }
 
 // ---------------------------------------------------------------------------
-// Small groups (<= 16 rows): one 16-row x 16-column output tile per
-// workgroup, K split over the four waves in contiguous quarters. In a wave
-// iteration the four lane groups take adjacent runs of U MX blocks, so one
-// wave-wide load covers 4*U*16 contiguous bytes of every weight row it touches
-// (whole cache lines, nothing fetched twice). The next iteration's weight
-// loads are issued before the current iteration's MFMAs. The four waves'
-// partial tiles are added in LDS in a fixed order.
+// Small dense tiles (bf16 weights, <= 16 rows: the shared experts for up to
+// 64 tokens): one 16-row x 16-column output tile per workgroup, K split over
+// the four waves in contiguous quarters, so the few rows still give a
+// workgroup per 16 columns. In a wave iteration lane group g reads values
+// 8 g .. 8 g + 7 of each 32-value step, 64 contiguous bytes of every weight
+// row per load; the next iteration's weights are loaded before the current
+// iteration's MFMAs. The four waves' partial tiles are added in LDS in a
+// fixed order. (MXFP4 groups of any size go to the large kernel: for 1-5
+// routes per expert it streams the weights faster than these tiles did.)
 // ---------------------------------------------------------------------------
-template <bool FP4>
-struct SmallOps;
-
-template <>
-struct SmallOps<true> {  // two MX blocks of codes and their exponents per matrix
-  u32x4_t c0[2], c1[2];
-  uint32_t s0[2], s1[2];
-};
-
-template <>
-struct SmallOps<false> {  // one 32-value block of bf16 weights per matrix
+struct SmallOps {  // one 32-value block of bf16 weights per matrix
   u32x4_t b0[4], b1[4];
 };
 
-// A buffer resource over `bytes` bytes at `base`, a pointer that is the same
-// for every lane: said so, so the resource stays in scalar registers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int64_t bytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  const uint64_t u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p) |
-                     ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) << 32);
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0,
-                                           __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
-}
-
-// EXR: the MX exponents of a wave's whole K range sit in registers, loaded
-// once (K/32 a multiple of 16 and at most 128: at most 32 bytes per row).
-template <bool GLU, bool FP4, bool EXR>
+template <bool GLU>
 __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
-  constexpr int U = FP4 ? 2 : 1;   // MX blocks per lane per iteration
-  constexpr int SPAN = 4 * U;      // blocks per wave iteration
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
@@ -147,132 +125,46 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
   const int nblk = K / 32;
   const int bw_lo = (wave * nblk) / 4;
   const int bw_hi = ((wave + 1) * nblk) / 4;
-  const int iters = (bw_hi - bw_lo + SPAN - 1) / SPAN;
+  const int iters = (bw_hi - bw_lo + 3) / 4;
 
   const bool mvalid = col < ti.cnt;
   const uint16_t* ap = mvalid ? act_row(a, ti, col) : a.act;
   const int n = n0 + col;
   const bool nvalid = n < N;
   const int nn = nvalid ? n : 0;
+  const uint16_t* b0r = a.b0 + ti.e * a.b_estride + (int64_t)nn * K;
+  const uint16_t* b1r = GLU ? a.b1 + ti.e * a.b_estride + (int64_t)nn * K : nullptr;
 
-  const uint8_t* q0r = nullptr;
-  const uint8_t* s0r = nullptr;
-  const uint8_t* q1r = nullptr;
-  const uint8_t* s1r = nullptr;
-  const uint16_t* b0r = nullptr;
-  const uint16_t* b1r = nullptr;
-  if (FP4) {
-    q0r = a.q0 + ti.e * a.q_estride + (int64_t)nn * (K / 2);
-    s0r = a.s0 + ti.e * a.s_estride + (int64_t)nn * (K / 32);
-    if (GLU) {
-      q1r = a.q1 + ti.e * a.q_estride + (int64_t)nn * (K / 2);
-      s1r = a.s1 + ti.e * a.s_estride + (int64_t)nn * (K / 32);
-    }
-  } else {
-    b0r = a.b0 + ti.e * a.b_estride + (int64_t)nn * K;
-    if (GLU) b1r = a.b1 + ti.e * a.b_estride + (int64_t)nn * K;
-  }
-
-  // first block of this lane in iteration it
-  auto first_blk = [&](int it) { return bw_lo + it * SPAN + grp * U; };
-
-  // EXR: exponents of blocks bw_lo .. bw_lo + 31 of the lane's row, one
-  // aligned 16-byte buffer load per half (past the matrix the range check
-  // returns zeros, in whole words: its N * K / 32 bytes are a multiple of 16);
-  // iteration it reads words 0 and 1 (blocks 8 it .. 8 it + 7), then the
-  // window moves on by two words
-  static_assert(!EXR || (FP4 && U == 2 && SPAN == 8), "eight blocks per iteration");
-  uint32_t ex[2][8];
-  if constexpr (EXR) {
+  // block of this lane in iteration it
+  auto blk_of = [&](int it) { return bw_lo + it * 4 + grp; };
+  auto load_ops = [&](int it, SmallOps& o) {
+    const int blk = blk_of(it);
+    const bool ok = nvalid && it < iters && blk < bw_hi;
 #pragma unroll
-    for (int mm = 0; mm < (GLU ? 2 : 1); ++mm) {
-      const auto r = uniform_rsrc((mm ? a.s1 : a.s0) + ti.e * a.s_estride, (int64_t)N * nblk);
-      const int off = nn * nblk + bw_lo;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4_t v = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * h, 0, 0));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ex[mm][4 * h + j] = v[j];
-      }
-    }
-  }
-
-  auto load_ops = [&](int it, SmallOps<FP4>& o) {
-    const int b0 = first_blk(it);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int blk = b0 + u;
-      const bool ok = nvalid && it < iters && blk < bw_hi;
-      if constexpr (FP4) {
-        o.c0[u] = ok ? load16(q0r + blk * 16) : zero16();
-        if (!EXR) o.s0[u] = ok ? (uint32_t)s0r[blk] : 127u;
-        if (GLU) {
-          o.c1[u] = ok ? load16(q1r + blk * 16) : zero16();
-          if (!EXR) o.s1[u] = ok ? (uint32_t)s1r[blk] : 127u;
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          o.b0[q] = ok ? load16(b0r + blk * 32 + q * 8) : zero16();
-          if (GLU) o.b1[q] = ok ? load16(b1r + blk * 32 + q * 8) : zero16();
-        }
-      }
+    for (int q = 0; q < 4; ++q) {
+      o.b0[q] = ok ? load16(b0r + blk * 32 + q * 8) : zero16();
+      if (GLU) o.b1[q] = ok ? load16(b1r + blk * 32 + q * 8) : zero16();
     }
   };
 
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f};
   f32x4_t acc1 = {0.f, 0.f, 0.f, 0.f};
-  SmallOps<FP4> cur, nxt;
+  SmallOps cur, nxt;
   load_ops(0, cur);
   for (int it = 0; it < iters; ++it) {
     load_ops(it + 1, nxt);
-    const int b0 = first_blk(it);
+    const int blk = blk_of(it);
+    const bool aok = mvalid && blk < bw_hi;
+    u32x4_t xv[4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int blk = b0 + u;
-      const bool aok = mvalid && blk < bw_hi;
-      u32x4_t xv[4];
+    for (int q = 0; q < 4; ++q) xv[q] = aok ? load16(ap + blk * 32 + q * 8) : zero16();
 #pragma unroll
-      for (int q = 0; q < 4; ++q) xv[q] = aok ? load16(ap + blk * 32 + q * 8) : zero16();
-      float sc0 = 1.f, sc1 = 1.f;
-      if constexpr (EXR) {
-        // block 8 it + 2 grp + u of the window: word grp / 2, byte 2 (grp % 2) + u;
-        // blocks past the range keep 127 (their codes are zero)
-        const bool ok = nvalid && blk < bw_hi;
-        const int sh = 8 * (2 * (grp & 1) + u);
-        const uint32_t e0 = ((grp & 2) ? ex[0][1] : ex[0][0]) >> sh;
-        sc0 = e8m0_to_f32(ok ? e0 & 0xffu : 127u);
-        if (GLU) {
-          const uint32_t e1 = ((grp & 2) ? ex[1][1] : ex[1][0]) >> sh;
-          sc1 = e8m0_to_f32(ok ? e1 & 0xffu : 127u);
-        }
-      } else if constexpr (FP4) {
-        sc0 = e8m0_to_f32(cur.s0[u]);
-        if (GLU) sc1 = e8m0_to_f32(cur.s1[u]);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bf16x8_t bv0, bv1;
-        if constexpr (FP4) {
-          bv0 = dequant8(cur.c0[u][q], sc0);
-          if (GLU) bv1 = dequant8(cur.c1[u][q], sc1);
-        } else {
-          bv0 = as_bf16x8(cur.b0[q]);
-          if (GLU) bv1 = as_bf16x8(cur.b1[q]);
-        }
-        const bf16x8_t av = as_bf16x8(xv[q]);
-        acc0 = mfma16(av, bv0, acc0);
-        if (GLU) acc1 = mfma16(av, bv1, acc1);
-      }
+    for (int q = 0; q < 4; ++q) {
+      const bf16x8_t av = as_bf16x8(xv[q]);
+      acc0 = mfma16(av, as_bf16x8(cur.b0[q]), acc0);
+      if (GLU) acc1 = mfma16(av, as_bf16x8(cur.b1[q]), acc1);
     }
     cur = nxt;
-    if constexpr (EXR) {
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-        for (int j = 0; j < 6; ++j) ex[mm][j] = ex[mm][j + 2];
-    }
   }
 
   __shared__ f32x4_t red[2][4][64];
@@ -734,10 +626,10 @@ static hipError_t launch_gemm(const GemmArgs& a0, bool large, int row_tiles, int
     hipLaunchKernelGGL((gemm_large_kernel<GLU, FP4, FP4>), grid, dim3(64 * lg_waves(FP4)), 0, s, a);
   else if (large)
     hipLaunchKernelGGL((gemm_large_kernel<GLU, FP4, false>), grid, dim3(64 * lg_waves(FP4)), 0, s, a);
-  else if (FP4 && (a0.K / 32) % 16 == 0 && a0.K / 32 <= 128)
-    hipLaunchKernelGGL((gemm_small_kernel<GLU, FP4, FP4>), grid, dim3(256), 0, s, a);
+  else if constexpr (!FP4)
+    hipLaunchKernelGGL((gemm_small_kernel<GLU>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_small_kernel<GLU, FP4, false>), grid, dim3(256), 0, s, a);
+    return hipErrorInvalidValue;  // MXFP4 groups always take the large kernel
   return hipGetLastError();
 }
 
@@ -745,7 +637,7 @@ hipError_t launch_routed(const Plan& p, const uint16_t* x, const lmoe_weights& w
                          const Workspace& ws, const int32_t* perm, hipStream_t s,
                          const hipEvent_t* ev) {
   const lmoe_dims& d = p.d;
-  const bool large = p.rows_per_tile == kLargeRows;
+  const bool large = true;  // MXFP4 groups of every size (see the small tiles)
   hipError_t err;
   {  // routed gate/up + GLU
     GemmArgs a = {};

@@ -12,7 +12,7 @@
 namespace lmoe {
 
 // Rows (routes) per tile of the grouped expert GEMMs.
-constexpr int kSmallRows = 16;   // one 16-row MFMA tile: decode-sized groups
+constexpr int kSmallRows = 16;   // one 16-row MFMA tile: shared-expert tiles up to 64 tokens
 constexpr int kLargeRows = 96;   // six 16-row MFMA tiles: prefill-sized groups
 constexpr int kDenseRows = 256;  // sixteen: the shared experts' tokens, in one group
 
@@ -48,7 +48,7 @@ struct Plan {
   bool fused_decode;  // T == 1: the whole layer in one persistent kernel
   int R;              // T * k routes
   RouterPlan router;
-  int rows_per_tile;  // kSmallRows or kLargeRows
+  int rows_per_tile;  // routed group tiles: kLargeRows
   int max_tiles;      // upper bound on routed tiles
 };
 

@@ -55,14 +55,14 @@ def test_traced_forward_rejects_missing_events(lm):
 
 def test_path_names(lm):
     assert lm.path_name(K3) == "fused_decode"
-    assert lm.path_name(K3, True) == "grouped_small"
-    assert lm.path_name((64,) + K3[1:]) == "grouped_small"
-    assert lm.path_name((4096,) + K3[1:]) == "grouped_large"
-    assert lm.path_name((1, 8192, 896, 16, 2048, 2, 2048)) == "grouped_small"  # L too wide
+    assert lm.path_name(K3, True) == "grouped"
+    assert lm.path_name((64,) + K3[1:]) == "grouped"
+    assert lm.path_name((4096,) + K3[1:]) == "grouped"
+    assert lm.path_name((1, 8192, 896, 16, 2048, 2, 2048)) == "grouped"  # L too wide
     # per-expert widths up to 4096 decode in one kernel, whatever S * Is
     assert lm.path_name((1, 3584, 896, 16, 3072, 2, 3072)) == "fused_decode"
     assert lm.path_name((1, 3584, 896, 16, 256, 8, 4096)) == "fused_decode"
-    assert lm.path_name((1, 3584, 896, 16, 2048, 2, 4128)) == "grouped_small"
+    assert lm.path_name((1, 3584, 896, 16, 2048, 2, 4128)) == "grouped"
     assert lm.path_name((1, 3583, 896, 16, 2048, 2, 2048)) == "invalid"
 
 

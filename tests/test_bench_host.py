@@ -51,23 +51,23 @@ def test_prefill_algorithmic_flops():
 
 
 def test_reported_kernel_names_match_the_profiled_kernels():
-    """The large MXFP4 kernels carry a third template argument when the
-    exponents go through LDS (K/32 a multiple of 16): both Kimi-K3 GEMMs."""
+    """The large MXFP4 kernel carries a third template argument when it
+    stages the exponent rows in LDS (K/32 a multiple of 16, at most 112): both
+    Kimi-K3 GEMMs. Shared experts of up to 64 tokens use 16-row bf16 tiles."""
     d = get_workload("prefill").dims
     assert bench.stage_kernel("gate_up", True, True, d) == "gemm_large_kernel<true, true, true>"
     assert bench.stage_kernel("down", True, True, d) == "gemm_large_kernel<false, true, true>"
     assert bench.stage_kernel("shared_gate_up", True, True, d) == \
         "gemm_large_kernel<true, false, false>"
-    # small tiles hold a row's exponents in registers: up to 128 blocks (K3:
-    # 112 for gate/up, 64 for down)
-    assert bench.stage_kernel("gate_up", False, False, d) == "gemm_small_kernel<true, true, true>"
-    assert bench.stage_kernel("down", False, False, d) == "gemm_small_kernel<false, true, true>"
-    assert bench.stage_kernel("shared_down", False, False, d) == \
-        "gemm_small_kernel<false, false, false>"
-    assert bench.stage_kernel("router", True, True, d) == "router_kernel"
+    assert bench.stage_kernel("shared_down", True, False, d) == "gemm_small_kernel<false>"
+    wide = get_workload("prefill").dims.__class__(**{**get_workload("prefill").dims.__dict__, "L": 4096})
+    assert bench.stage_kernel("gate_up", True, True, wide) == "gemm_large_kernel<true, true, false>"
+    assert bench.stage_kernel("router", True, True, d) == "router_kernel<128>"
+    assert bench.stage_kernel("router", True, False, get_workload("batched_decode").dims) == \
+        "router_kernel<64>"
     # the router splits K over workgroups only when its tiles are few
     assert bench.stage_kernel("topk", True, True, d) == "topk_kernel<false>"
-    assert bench.stage_kernel("topk", False, False, get_workload("batched_decode").dims) == \
+    assert bench.stage_kernel("topk", True, False, get_workload("batched_decode").dims) == \
         "topk_kernel<true>"
     assert bench.stage_kernel("topk", True, True, get_workload("skewed").dims, True) == \
         "topk_kernel<false>"

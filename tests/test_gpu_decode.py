@@ -184,7 +184,7 @@ def test_single_token_with_given_logits_uses_grouped_path(lm, dev):
     w = Workload("given1", 51, Dims(T=1, L=256, E=32, k=4, I=128, S=2, Is=128),
                  scales=("uniform", 120, 130), logits_given=True)
     d = w.dims
-    assert lm.path_name(d, True) == "grouped_small"
+    assert lm.path_name(d, True) == "grouped"
     inp = gen_all(w)
     dinp = upload(inp, dev)
     r = alloc_routing(d, dev)
