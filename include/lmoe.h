@@ -21,7 +21,7 @@
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *    default stream). Arguments are validated on the host before anything is
  *    enqueued: a non-zero status means nothing was launched.
- *  - lmoe_forward with T > 1 (or given logits) and shared experts runs the
+ *  - lmoe_forward with T > 4 (or given logits) and shared experts runs the
  *    shared experts on a second stream of the current device, which the
  *    library creates with two events on its first such call: forked from
  *    `stream` by an event at the start and joined back to it before the
@@ -191,8 +191,9 @@ int lmoe_forward_traced(const lmoe_dims* dims, const uint16_t* x, const lmoe_wei
 const char* lmoe_stage_name(int stage);
 
 /* Which implementation lmoe_forward uses for these dimensions (static
- * string): "fused_decode" (T == 1 with computed logits and L, I, Is at most
- * 4096: the whole layer in one persistent kernel), "grouped" (routing
+ * string): "fused_decode" (1 <= T <= 4 with computed logits and L, I, Is at
+ * most 4096: the whole layer in one persistent kernel, launched once per
+ * token, then the grouping of all routes), "grouped" (routing
  * kernels, then grouped GEMMs over expert groups of up to 96 rows, then the
  * combine), "invalid" for bad dims. Decode streams the active weights once
  * per token (infervisor.ai "Bringing up Kimi-K3 on day zero", "The
