@@ -21,7 +21,7 @@
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *    default stream). Arguments are validated on the host before anything is
  *    enqueued: a non-zero status means nothing was launched.
- *  - lmoe_forward with T > 4 (or given logits) and shared experts runs the
+ *  - lmoe_forward on the grouped path (lmoe_path_name) with shared experts runs the
  *    shared experts on a second stream of the current device, which the
  *    library creates with two events on its first such call: forked from
  *    `stream` by an event at the start and joined back to it before the
