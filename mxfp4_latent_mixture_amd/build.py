@@ -34,6 +34,9 @@ def build(verbose: bool = False) -> str:
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed-fp32 VALU forms are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # single-lane atomics stay as written: the atomic optimizer would turn
+        # a ticket draw into one whose result is read back at once
+        "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
         "-I", INCLUDE, "-o", tmp,
     ] + [os.path.join(CSRC, s) for s in SOURCES]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -702,12 +702,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   const int q = gw % kQueues;
   int* ticket = a.ctr + kCtrTicket + 16 * q;
   WaveState st{-1};
+  // The drawn ticket stays in lane 0's register until the next item starts:
+  // reading it into a scalar at once would wait out the atomic's round trip
+  // before every item.
   auto draw = [&]() {
-    int t = 0;
-    if (lane_id() == 0) t = q + kQueues * add_dev(ticket, 1);
-    return __builtin_amdgcn_readfirstlane(t);
+    int v = 0;
+    if (lane_id() == 0) v = add_dev(ticket, 1);
+    return v;
   };
-  int t = draw();
+  auto ticket_of = [&](int v) { return q + kQueues * __builtin_amdgcn_readfirstlane(v); };
+  int t = ticket_of(draw());
   while (t < a.t_total) {
     const int next = draw();  // in flight while this item runs
     if (t < a.t_shgu) {
@@ -721,7 +725,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       shared_dn_item(a, t - a.t_shd, arow, st, tk);
     else
       routed_dn_item(a, t - a.t_dn, arow, st, tk);
-    t = next;
+    t = ticket_of(next);
   }
   if (blockIdx.x == 0 && wave == 0) {
     ensure_topk(a, tk);
