@@ -46,6 +46,8 @@
 // invalidate is issued. Counters and flagged logits sit in the first 32 KiB
 // of the workspace, are zero when a launch starts and are zeroed again by its
 // last wave to leave.
+#include <atomic>
+
 #include "lmoe_device.h"
 #include "lmoe_internal.h"
 #include "lmoe_topk.h"
@@ -755,11 +757,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
 // Host side
 // ---------------------------------------------------------------------------
 static int decode_grid(size_t lds_bytes) {
-  static int cached[64] = {0};
-  static size_t cached_lds[64] = {0};
+  // per device: the grid in the low half, the LDS size it was computed for in
+  // the high half, so concurrent callers see a consistent pair
+  static std::atomic<uint64_t> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] > 0 && cached_lds[dev] == lds_bytes) return cached[dev];
+  const uint64_t c = cached[dev].load(std::memory_order_relaxed);
+  if ((uint32_t)c > 0 && (c >> 32) == lds_bytes) return (int)(uint32_t)c;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
@@ -768,9 +772,9 @@ static int decode_grid(size_t lds_bytes) {
           hipSuccess ||
       per_cu <= 0)
     per_cu = 1;
-  cached[dev] = cus * std::min(per_cu, kWgPerCu);
-  cached_lds[dev] = lds_bytes;
-  return cached[dev];
+  const int grid = cus * std::min(per_cu, kWgPerCu);
+  cached[dev].store(((uint64_t)lds_bytes << 32) | (uint32_t)grid, std::memory_order_relaxed);
+  return grid;
 }
 
 void make_decode_args(const Plan& p, DecodeArgs& a) {
