@@ -115,8 +115,12 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
-  int tile, nt;
-  tile_of_block(a.n_tiles_n, &tile, &nt);
+  // Column tiles in consecutive workgroups, which run on different XCDs: with
+  // the few row tiles of these sizes, dealing each row tile to one XCD would
+  // leave the other seven idle, and the at most 16 activation rows (a few KB
+  // per K range) are cheap to fetch into every L2.
+  const int nt = (int)(blockIdx.x % a.n_tiles_n);
+  const int tile = (int)(blockIdx.x / a.n_tiles_n);
   TileInfo ti;
   if (!resolve_tile(a, tile, kSmallRows, &ti)) return;
 
@@ -619,9 +623,10 @@ static hipError_t launch_gemm(const GemmArgs& a0, bool large, int row_tiles, int
   // large tiles: four waves of lg_tiles_per_wave 16-column MFMA tiles
   const int cols = large ? 16 * lg_waves(FP4) * lg_tiles_per_wave(GLU, FP4) : 16;
   a.n_tiles_n = (a.N + cols - 1) / cols;
-  // row tiles rounded up to whole rounds of the XCDs (tile_of_block)
+  // large tiles: row tiles rounded up to whole rounds of the XCDs
+  // (tile_of_block); small tiles: one workgroup per (row tile, column tile)
   const int rounds = (row_tiles + kXcds - 1) / kXcds;
-  dim3 grid((unsigned)(rounds * kXcds * a.n_tiles_n), 1, (unsigned)z);
+  dim3 grid((unsigned)((large ? rounds * kXcds : row_tiles) * a.n_tiles_n), 1, (unsigned)z);
   if (large && exw)
     hipLaunchKernelGGL((gemm_large_kernel<GLU, FP4, FP4>), grid, dim3(64 * lg_waves(FP4)), 0, s, a);
   else if (large)
