@@ -263,8 +263,16 @@ __global__ __launch_bounds__(64 * lg_waves(FP4), FP4 ? 2 : 1) void gemm_large_ke
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
+  // Fewer dense row tiles than XCDs (the shared experts below 8 x 256 tokens):
+  // column tiles in consecutive workgroups, over every XCD, as the small
+  // tiles do; otherwise each row tile on one XCD.
   int tile, nt;
-  tile_of_block(a.n_tiles_n, &tile, &nt);
+  if (!a.tiles && (a.dense_rows + ROWS - 1) / ROWS < kXcds) {
+    nt = (int)(blockIdx.x % a.n_tiles_n);
+    tile = (int)(blockIdx.x / a.n_tiles_n);
+  } else {
+    tile_of_block(a.n_tiles_n, &tile, &nt);
+  }
   TileInfo ti;
   if (!resolve_tile(a, tile, ROWS, &ti)) return;
   constexpr int NW = lg_tiles_per_wave(GLU, FP4);  // 16-column tiles per wave
@@ -623,10 +631,12 @@ static hipError_t launch_gemm(const GemmArgs& a0, bool large, int row_tiles, int
   // large tiles: four waves of lg_tiles_per_wave 16-column MFMA tiles
   const int cols = large ? 16 * lg_waves(FP4) * lg_tiles_per_wave(GLU, FP4) : 16;
   a.n_tiles_n = (a.N + cols - 1) / cols;
-  // large tiles: row tiles rounded up to whole rounds of the XCDs
-  // (tile_of_block); small tiles: one workgroup per (row tile, column tile)
+  // row tiles dealt to the XCDs (tile_of_block): rounded up to whole rounds
+  // of them; spread over the XCDs by column tile (small tiles, and fewer
+  // dense row tiles than XCDs): one workgroup per (row tile, column tile)
   const int rounds = (row_tiles + kXcds - 1) / kXcds;
-  dim3 grid((unsigned)((large ? rounds * kXcds : row_tiles) * a.n_tiles_n), 1, (unsigned)z);
+  const bool spread = !large || (!a.tiles && row_tiles < kXcds);
+  dim3 grid((unsigned)((spread ? row_tiles : rounds * kXcds) * a.n_tiles_n), 1, (unsigned)z);
   if (large && exw)
     hipLaunchKernelGGL((gemm_large_kernel<GLU, FP4, FP4>), grid, dim3(64 * lg_waves(FP4)), 0, s, a);
   else if (large)
