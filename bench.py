@@ -337,13 +337,11 @@ def kernel_units(res, lm):
     tb, tf, sb, sf = algorithmic(d, res["D"], logits_given)
     if lm.path_name(d, logits_given) == "fused_decode":
         # one kernel does the whole layer: the layer's bytes (the token is
-        # read once, though three stages count it). At T=1 every timed step is
-        # one launch of it, back to back, so the events around the timed
+        # read once, though three stages count it). It runs one token: every
+        # timed step is one launch of it, back to back, so the events around the timed
         # region give its average launch; the events a traced call records
         # around the kernel add 2-5 us of their own.
-        if d.T == 1:
-            return [(FUSED_KERNEL, tb, tf, res["ms"] * 1e-3)]
-        return [(FUSED_KERNEL, tb, tf, res["stage_ms"]["router"] * 1e-3)]
+        return [(FUSED_KERNEL, tb, tf, res["ms"] * 1e-3)]
     large = True  # routed groups of every size take the large kernel
     sh_large = d.T > 64
     return [(stage_kernel(s, large, sh_large, d, logits_given), sb[s], sf[s],

@@ -191,9 +191,8 @@ int lmoe_forward_traced(const lmoe_dims* dims, const uint16_t* x, const lmoe_wei
 const char* lmoe_stage_name(int stage);
 
 /* Which implementation lmoe_forward uses for these dimensions (static
- * string): "fused_decode" (1 <= T <= 4 with computed logits and L, I, Is at
- * most 4096: the whole layer in one persistent kernel, launched once per
- * token, then the grouping of all routes), "grouped" (routing
+ * string): "fused_decode" (T == 1 with computed logits and L, I, Is at
+ * most 4096: the whole layer in one persistent kernel), "grouped" (routing
  * kernels, then grouped GEMMs over expert groups of up to 96 rows, then the
  * combine), "invalid" for bad dims. Decode streams the active weights once
  * per token (infervisor.ai "Bringing up Kimi-K3 on day zero", "The

@@ -46,12 +46,12 @@ Plan make_plan(const lmoe_dims& d) {
   // per expert (T = 2 .. 384).
   p.rows_per_tile = kLargeRows;
   p.max_tiles = std::min(d.E, p.R) + p.R / p.rows_per_tile;
-  // every row a decode wave stages (h of one route or one shared expert) and
-  // the token itself fit its fixed-size staging; a few tokens run it once
-  // each (for T <= kDecodeTokens that beats the grouped path, whose fixed
-  // costs a few tokens do not amortise)
-  p.fused_decode = d.T >= 1 && d.T <= kDecodeTokens && d.L <= kDecodeMaxWidth &&
-                   d.I <= kDecodeMaxWidth && p.d.Is <= kDecodeMaxWidth;
+  // One token, when every row a decode wave stages (h of one route or one
+  // shared expert) and the token itself fit its fixed-size staging. From two
+  // tokens the grouped path is faster on the Kimi-K3 layer (T = 2: 131 us
+  // against 145 us for one decode launch per token).
+  p.fused_decode = d.T == 1 && d.L <= kDecodeMaxWidth && d.I <= kDecodeMaxWidth &&
+                   p.d.Is <= kDecodeMaxWidth;
   return p;
 }
 
@@ -81,17 +81,6 @@ Workspace carve_workspace(const Plan& p, void* base) {
   w.h_sh = reinterpret_cast<uint16_t*>(take(S * T * Is * 2));
   w.y = reinterpret_cast<float*>(take(R * L * 4));
   w.y_sh = reinterpret_cast<float*>(take(S * T * L * 4));
-  if (p.fused_decode) {
-    // one-token grouping scratch of the per-token launches (T > 1)
-    w.dcounts = reinterpret_cast<int32_t*>(take(E * 4));
-    w.doffsets = reinterpret_cast<int32_t*>(take((E + 1) * 4));
-    w.dperm = reinterpret_cast<int32_t*>(take((size_t)d.k * 4));
-    w.dinv = reinterpret_cast<int32_t*>(take((size_t)d.k * 4));
-    w.dh = reinterpret_cast<uint16_t*>(take((size_t)d.k * I * 2));
-    w.dhsh = reinterpret_cast<uint16_t*>(take(S * Is * 2));
-    w.dy = reinterpret_cast<float*>(take((size_t)d.k * L * 4));
-    w.dysh = reinterpret_cast<float*>(take(S * L * 4));
-  }
   w.bytes = off;
   return w;
 }
@@ -155,7 +144,6 @@ static int run_route(const Plan& p, const Workspace& ws, const uint16_t* x, cons
 static int run_fused_decode(const Plan& p, const Workspace& ws, const uint16_t* x,
                             const lmoe_weights& w, const lmoe_routing* r, uint16_t* out,
                             hipStream_t s, const hipEvent_t* ev) {
-  const lmoe_dims& d = p.d;
   DecodeArgs a;
   make_decode_args(p, a);
   a.x = x;
@@ -176,46 +164,19 @@ static int run_fused_decode(const Plan& p, const Workspace& ws, const uint16_t* 
   int32_t* perm = (r && r->perm) ? r->perm : ws.perm;
   int32_t* inv = (r && r->inv_perm) ? r->inv_perm : ws.inv;
   a.ctr = ws.ctr;
-  a.h = ws.dh;
-  a.hsh = ws.dhsh;
-  a.y = ws.dy;
-  a.ysh = ws.dysh;
-  if (d.T == 1) {
-    a.x = x;
-    a.out = out;
-    a.logits_out = r ? r->logits : nullptr;
-    a.idx = idx;
-    a.w = wt;
-    a.counts = counts;
-    a.offsets = offsets;
-    a.perm = perm;
-    a.inv = inv;
-    return launch_decode(a, s, ev) == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
-  }
-  // A few tokens: one launch per token, in order on the stream (each leaves
-  // the workspace counters zeroed for the next). Each writes its own selection
-  // and weights and its one-token grouping into scratch; the grouping of all
-  // T * k routes is then built from the selections. Every stage's time lands
-  // on the router stage, as for one token.
-  if (record_stage(ev, LMOE_STAGE_BEGIN, s) != hipSuccess) return LMOE_ERR_HIP;
-  for (int t = 0; t < d.T; ++t) {
-    a.x = x + (size_t)t * d.L;
-    a.out = out + (size_t)t * d.L;
-    a.logits_out = (r && r->logits) ? r->logits + (size_t)t * d.E : nullptr;
-    a.idx = idx + (size_t)t * d.k;
-    a.w = wt + (size_t)t * d.k;
-    a.counts = ws.dcounts;
-    a.offsets = ws.doffsets;
-    a.perm = ws.dperm;
-    a.inv = ws.dinv;
-    if (launch_decode(a, s, nullptr) != hipSuccess) return LMOE_ERR_HIP;
-  }
-  if (launch_permute(p, idx, counts, offsets, perm, inv, ws.tiles, ws.ntiles, ws.chunk_base,
-                     s) != hipSuccess)
-    return LMOE_ERR_HIP;
-  for (int i = LMOE_STAGE_ROUTER; i < LMOE_NUM_STAGE_EVENTS; ++i)
-    if (record_stage(ev, i, s) != hipSuccess) return LMOE_ERR_HIP;
-  return LMOE_OK;
+  a.h = ws.h;
+  a.hsh = ws.h_sh;
+  a.y = ws.y;
+  a.ysh = ws.y_sh;
+  a.out = out;
+  a.logits_out = r ? r->logits : nullptr;
+  a.idx = idx;
+  a.w = wt;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.perm = perm;
+  a.inv = inv;
+  return launch_decode(a, s, ev) == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
 }
 
 static int check_routing(const lmoe_routing* r, int logits_given) {

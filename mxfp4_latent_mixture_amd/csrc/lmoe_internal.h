@@ -41,12 +41,11 @@ constexpr int kCtrShared = 2592;    // + 16 * shared expert (< 8): gate/up items
 constexpr int kCtrLogit = 4096;
 constexpr size_t kCtrBytes = 32768;
 // The single-token decode kernel keeps the token and one A row in LDS.
-constexpr int kDecodeTokens = 4;      // tokens per call that run the fused decode kernel
 constexpr int kDecodeMaxWidth = 4096;
 
 struct Plan {
   lmoe_dims d;
-  bool fused_decode;  // T <= kDecodeTokens: the whole layer in one persistent kernel per token
+  bool fused_decode;  // T == 1: the whole layer in one persistent kernel
   int R;              // T * k routes
   RouterPlan router;
   int rows_per_tile;  // routed group tiles: kLargeRows
@@ -70,14 +69,6 @@ struct Workspace {
   float* y;           // [R][L] fp32 route partials, sorted route order
   float* y_sh;        // [S][T][L] fp32
   // fused decode (one launch per token)
-  int32_t* dcounts;   // [E]    one-token grouping, scratch when T > 1
-  int32_t* doffsets;  // [E+1]
-  int32_t* dperm;     // [k]
-  int32_t* dinv;      // [k]
-  uint16_t* dh;       // [k][I] bf16
-  uint16_t* dhsh;     // [S][Is] bf16
-  float* dy;          // [k][L]
-  float* dysh;        // [S][L]
   size_t bytes;       // total bytes needed
 };
 
