@@ -292,6 +292,17 @@ def test_full_decode(lm, dev):
     _full_size(lm, dev, "decode", 1)
 
 
+def test_full_decode_three_tokens(lm, dev):
+    """Three K3 decode tokens in one call (seed 1's inputs): from two tokens
+    the grouped path runs, with the shared experts in small tiles spread over
+    every XCD. Every token is checked."""
+    from workloads import configs
+    name = "decode_t3"
+    configs.WORKLOADS.setdefault(name, get_workload("decode").with_T(3, name))
+    assert lm.path_name(configs.WORKLOADS[name].dims) == "grouped"
+    _full_size(lm, dev, name, 3)
+
+
 def test_full_batched_decode(lm, dev):
     _full_size(lm, dev, "batched_decode", 3)
 
