@@ -136,6 +136,12 @@ size_t lmoe_workspace_bytes(const lmoe_dims* dims);
 
 /* Routing only: router logits (unless logits_given), top-k selection with
  * softmax weights, and the expert grouping (counts, offsets, perm, inv_perm).
+ * The router scores every expert from the MoE input in one projection
+ * (dev48.org "Kimi K3 on AMD Instinct GPUs with TokenSpeed", section 4.3; here
+ * from the latent x), each token keeps its k best of E (k = 16 of 896 in
+ * infervisor.ai "Bringing up Kimi-K3 on day zero", "The model we hadn't run"),
+ * and routes are grouped by expert, stable in route order, so that one weight
+ * panel serves every route of an expert (TokenSpeed section 4.1).
  *   dims      host; x bf16 [T][L] device (may be NULL if logits_given)
  *   router_w  bf16 [E][L] device (ignored if logits_given)
  *   r         host struct of device pointers (may be NULL: nothing returned)
@@ -145,16 +151,65 @@ int lmoe_route(const lmoe_dims* dims, const uint16_t* x, const uint16_t* router_
                int logits_given, const lmoe_routing* r, void* ws, size_t ws_bytes,
                void* stream);
 
-/* The whole layer: routing, routed experts, shared experts and combine.
+/* The whole layer: routing, routed experts, shared experts and combine: the
+ * Latent MoE of dev48.org "Kimi K3 on AMD Instinct GPUs with TokenSpeed",
+ * section 4 (k of E routed MXFP4 experts plus S always-on shared experts in
+ * the latent width), with route partials kept and summed in FP32 (section
+ * 4.3) and the MXFP4 format of infervisor.ai "Bringing up Kimi-K3 on day
+ * zero", "The model we hadn't run".
  *   x    bf16 [T][L] device;  w  host struct of device weight pointers
  *   r    optional routing outputs (see lmoe_routing); when logits_given,
  *        r->logits is the input logits and r must not be NULL
  *   out  bf16 [T][L] device, written with the combined output
  *   ws   device workspace of ws_bytes >= lmoe_workspace_bytes(dims)
+ * On the grouped path with S > 0 the shared experts run on the library's
+ * per-device second stream (see the conventions above); lmoe_forward_ex lets
+ * the caller choose.
  * Errors: LMOE_ERR_NULL, _SHAPE, _ALIGN, _WORKSPACE, _HIP. */
 int lmoe_forward(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights* w,
                  int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
                  size_t ws_bytes, void* stream);
+
+/* Where lmoe_forward_ex runs the shared experts. They read only x, so on the
+ * grouped path they can run beside the routing and the routed GEMMs.
+ *   side_stream  hipStream_t for the shared experts, or NULL: every stage on
+ *                the call's stream
+ *   fork_event   hipEvent_t (created by the caller, timing may be disabled):
+ *                recorded on the call's stream at the start; side_stream waits
+ *                for it before the shared experts
+ *   join_event   hipEvent_t: recorded on side_stream after the shared
+ *                experts; the call's stream waits for it before the combine
+ * The events are re-recorded by every call that names them: calls sharing
+ * them must not be enqueued concurrently from different host threads. The
+ * call is complete when its own stream has reached its end. */
+typedef struct lmoe_exec {
+  void* side_stream;
+  void* fork_event;
+  void* join_event;
+} lmoe_exec;
+
+/* lmoe_forward with the shared experts' stream chosen by the caller instead
+ * of the library's per-device second stream: exec NULL (or its side_stream
+ * NULL) runs every stage on `stream`, and the library then creates no stream
+ * or event of its own. The single-token path (lmoe_path_name
+ * "fused_decode") is one kernel on `stream` whatever exec says. Same
+ * arguments, results and errors as lmoe_forward, plus LMOE_ERR_NULL when
+ * exec->side_stream is set and an event is missing. */
+int lmoe_forward_ex(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights* w,
+                    int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
+                    size_t ws_bytes, void* stream, const lmoe_exec* exec);
+
+/* The single-token kernel resolves its dependencies with bounded waits on
+ * device counters in the workspace; a wait that outlives its bound (about a
+ * quarter of a second: a producer that never ran) is abandoned and counted in
+ * the workspace, and that call's output is then not valid. This enqueues on
+ * `stream` a copy of that count into *count (int32 device, 4-byte aligned)
+ * and resets it to zero, with no host synchronisation: a caller that reads 0
+ * after its calls knows no wait was abandoned in them. The count accumulates
+ * over calls on one workspace until read.
+ *   ws  the workspace of those calls (ws_bytes >= 32 KiB)
+ * Errors: LMOE_ERR_NULL, _ALIGN, _WORKSPACE, _HIP. */
+int lmoe_wait_errors(void* ws, size_t ws_bytes, int32_t* count, void* stream);
 
 /* Stage boundaries recorded by lmoe_forward_traced. Event i is recorded on
  * the stream right after stage i has been enqueued (event 0 before the first

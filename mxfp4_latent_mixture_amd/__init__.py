@@ -9,6 +9,9 @@ Functions mirror the C ABI in include/lmoe.h:
   workspace_bytes(dims)
   route(dims, x, router_w, logits_given, routing, ws)
   forward(dims, x, weights, logits_given, routing, out, ws)
+  forward_ex(dims, x, weights, logits_given, routing, out, ws, side_stream, fork_event,
+             join_event)
+  wait_errors(ws, count)
   debug_dequant_mxfp4(q, s, rows, K, out)
   status_string(code)
 `dims` is a Dims-like object (attributes T, L, E, k, I, S, Is) or a tuple in
@@ -32,9 +35,9 @@ LMOE_ERR_ALIGN = 3
 LMOE_ERR_WORKSPACE = 4
 LMOE_ERR_HIP = 5
 
-EXPORTS = ("lmoe_workspace_bytes", "lmoe_route", "lmoe_forward", "lmoe_forward_traced",
-           "lmoe_stage_name", "lmoe_path_name", "lmoe_debug_dequant_mxfp4",
-           "lmoe_status_string")
+EXPORTS = ("lmoe_workspace_bytes", "lmoe_route", "lmoe_forward", "lmoe_forward_ex",
+           "lmoe_forward_traced", "lmoe_wait_errors", "lmoe_stage_name", "lmoe_path_name",
+           "lmoe_debug_dequant_mxfp4", "lmoe_status_string")
 
 # Stage boundaries recorded by forward_traced (LMOE_STAGE_* in lmoe.h).
 STAGES = ("begin", "router", "topk", "permute", "gate_up", "down", "shared_gate_up",
@@ -55,6 +58,10 @@ class lmoe_weights(ctypes.Structure):
 class lmoe_routing(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "topk_idx", "topk_w", "counts", "offsets", "perm", "inv_perm")]
+
+
+class lmoe_exec(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("side_stream", "fork_event", "join_event")]
 
 
 class LmoeError(RuntimeError):
@@ -78,6 +85,12 @@ def _load() -> ctypes.CDLL:
     lib.lmoe_forward.argtypes = [dp, vp, ctypes.POINTER(lmoe_weights), ctypes.c_int,
                                  ctypes.POINTER(lmoe_routing), vp, vp, sz, vp]
     lib.lmoe_forward.restype = ctypes.c_int
+    lib.lmoe_forward_ex.argtypes = [dp, vp, ctypes.POINTER(lmoe_weights), ctypes.c_int,
+                                    ctypes.POINTER(lmoe_routing), vp, vp, sz, vp,
+                                    ctypes.POINTER(lmoe_exec)]
+    lib.lmoe_forward_ex.restype = ctypes.c_int
+    lib.lmoe_wait_errors.argtypes = [vp, sz, vp, vp]
+    lib.lmoe_wait_errors.restype = ctypes.c_int
     lib.lmoe_forward_traced.argtypes = [dp, vp, ctypes.POINTER(lmoe_weights), ctypes.c_int,
                                         ctypes.POINTER(lmoe_routing), vp, vp, sz, vp,
                                         ctypes.POINTER(vp)]
@@ -168,6 +181,34 @@ def forward(dims, x, weights: Mapping, logits_given: bool, routing: Optional[Map
                              ws.numel() * ws.element_size() if ws is not None else 0,
                              _stream(stream))
     _check("lmoe_forward", code)
+
+
+def forward_ex(dims, x, weights: Mapping, logits_given: bool, routing: Optional[Mapping], out,
+               ws, side_stream=None, fork_event=None, join_event=None, stream=None) -> None:
+    """forward() with the shared experts on the caller's side_stream (an int
+    hipStream_t), forked and joined by the caller's fork_event / join_event
+    (int hipEvent_t); side_stream None runs every stage on `stream`."""
+    d = _dims(dims)
+    r = _routing(routing)
+    w = _weights(weights)
+    ex = None
+    if side_stream is not None:
+        ex = lmoe_exec(int(side_stream), fork_event and int(fork_event),
+                       join_event and int(join_event))
+    code = _lib.lmoe_forward_ex(ctypes.byref(d), _ptr(x), ctypes.byref(w),
+                                int(bool(logits_given)),
+                                ctypes.byref(r) if r is not None else None, _ptr(out), _ptr(ws),
+                                ws.numel() * ws.element_size() if ws is not None else 0,
+                                _stream(stream), ctypes.byref(ex) if ex is not None else None)
+    _check("lmoe_forward_ex", code)
+
+
+def wait_errors(ws, count, stream=None) -> None:
+    """Enqueue a copy of the workspace's abandoned-wait count into the int32
+    device tensor `count` and reset it."""
+    code = _lib.lmoe_wait_errors(_ptr(ws), ws.numel() * ws.element_size() if ws is not None
+                                 else 0, _ptr(count), _stream(stream))
+    _check("lmoe_wait_errors", code)
 
 
 def forward_traced(dims, x, weights: Mapping, logits_given: bool, routing: Optional[Mapping], out,

@@ -264,13 +264,28 @@ static SideStream* side_stream() {
   return st.s ? &st : nullptr;
 }
 
+// Where one call runs its shared experts: the caller's stream (s == nullptr),
+// the library's per-device second stream (under its mutex), or the caller's
+// stream and events (lmoe_forward_ex).
+struct SideExec {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex* mu = nullptr;
+};
+
+enum class SideMode { kLibrary, kCaller };
+
 static int forward_impl(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights* wts,
                         int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
-                        size_t ws_bytes, void* stream, const hipEvent_t* ev) {
+                        size_t ws_bytes, void* stream, const hipEvent_t* ev, SideMode mode,
+                        const lmoe_exec* exec) {
   if (!dims || !wts) return LMOE_ERR_NULL;
   if (!dims_ok(*dims)) return LMOE_ERR_SHAPE;
   int st = check_routing(r, logits_given);
   if (st) return st;
+  if (mode == SideMode::kCaller && exec && exec->side_stream &&
+      (!exec->fork_event || !exec->join_event))
+    return LMOE_ERR_NULL;
   if (dims->T == 0) return LMOE_OK;
   const lmoe_weights& w = *wts;
   if (!x || !out || !ws) return LMOE_ERR_NULL;
@@ -290,24 +305,39 @@ static int forward_impl(const lmoe_dims* dims, const uint16_t* x, const lmoe_wei
   Routing rt;
   // Traced calls keep every stage on the caller's stream, in order, so each
   // stage's events time it alone.
-  SideStream* side = (!ev && p.d.S > 0) ? side_stream() : nullptr;
-  if (!side) {
+  SideExec side;
+  if (!ev && p.d.S > 0) {
+    if (mode == SideMode::kLibrary) {
+      if (SideStream* lib = side_stream()) {
+        side.s = lib->s;
+        side.fork = lib->fork;
+        side.join = lib->join;
+        side.mu = &lib->mu;
+      }
+    } else if (exec && exec->side_stream) {
+      side.s = static_cast<hipStream_t>(exec->side_stream);
+      side.fork = static_cast<hipEvent_t>(exec->fork_event);
+      side.join = static_cast<hipEvent_t>(exec->join_event);
+    }
+  }
+  if (!side.s) {
     st = run_route(p, wsp, x, w.router_w, logits_given, r, &rt, s, ev);
     if (st) return st;
     hipError_t e = launch_experts(p, x, w, wsp, rt.perm, rt.inv, rt.w, out, s, ev);
     return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
   }
-  std::lock_guard<std::mutex> g(side->mu);
-  if (hipEventRecord(side->fork, s) != hipSuccess ||
-      hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess ||
-      launch_shared(p, x, w, wsp, side->s, nullptr) != hipSuccess ||
-      hipEventRecord(side->join, side->s) != hipSuccess)
+  std::unique_lock<std::mutex> g;
+  if (side.mu) g = std::unique_lock<std::mutex>(*side.mu);
+  if (hipEventRecord(side.fork, s) != hipSuccess ||
+      hipStreamWaitEvent(side.s, side.fork, 0) != hipSuccess ||
+      launch_shared(p, x, w, wsp, side.s, nullptr) != hipSuccess ||
+      hipEventRecord(side.join, side.s) != hipSuccess)
     return LMOE_ERR_HIP;
   st = run_route(p, wsp, x, w.router_w, logits_given, r, &rt, s, nullptr);
   hipError_t e = st ? hipSuccess : launch_routed(p, x, w, wsp, rt.perm, s, nullptr);
   // the join is waited for on every path, so no later call on s can reuse
   // the workspace before the shared experts are done with it
-  if (hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return LMOE_ERR_HIP;
+  if (hipStreamWaitEvent(s, side.join, 0) != hipSuccess) return LMOE_ERR_HIP;
   if (st) return st;
   if (e == hipSuccess) e = launch_combine(p, wsp, rt.inv, rt.w, out, s, nullptr);
   return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
@@ -316,7 +346,24 @@ static int forward_impl(const lmoe_dims* dims, const uint16_t* x, const lmoe_wei
 extern "C" int lmoe_forward(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights* wts,
                             int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
                             size_t ws_bytes, void* stream) {
-  return forward_impl(dims, x, wts, logits_given, r, out, ws, ws_bytes, stream, nullptr);
+  return forward_impl(dims, x, wts, logits_given, r, out, ws, ws_bytes, stream, nullptr,
+                      SideMode::kLibrary, nullptr);
+}
+
+extern "C" int lmoe_forward_ex(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights* wts,
+                               int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
+                               size_t ws_bytes, void* stream, const lmoe_exec* exec) {
+  return forward_impl(dims, x, wts, logits_given, r, out, ws, ws_bytes, stream, nullptr,
+                      SideMode::kCaller, exec);
+}
+
+extern "C" int lmoe_wait_errors(void* ws, size_t ws_bytes, int32_t* count, void* stream) {
+  if (!ws || !count) return LMOE_ERR_NULL;
+  if (!aligned16(ws) || (reinterpret_cast<uintptr_t>(count) & 3u)) return LMOE_ERR_ALIGN;
+  if (ws_bytes < kCtrBytes) return LMOE_ERR_WORKSPACE;
+  hipError_t e = launch_read_errors(static_cast<int32_t*>(ws), count,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
 }
 
 extern "C" int lmoe_forward_traced(const lmoe_dims* dims, const uint16_t* x,
@@ -329,7 +376,8 @@ extern "C" int lmoe_forward_traced(const lmoe_dims* dims, const uint16_t* x,
     if (!events[i]) return LMOE_ERR_NULL;
     ev[i] = static_cast<hipEvent_t>(events[i]);
   }
-  return forward_impl(dims, x, wts, logits_given, r, out, ws, ws_bytes, stream, ev);
+  return forward_impl(dims, x, wts, logits_given, r, out, ws, ws_bytes, stream, ev,
+                      SideMode::kLibrary, nullptr);
 }
 
 extern "C" const char* lmoe_path_name(const lmoe_dims* dims, int logits_given) {

@@ -98,6 +98,11 @@ __device__ __forceinline__ u32x4_t ld16_dev(const void* p) {
 // All of this wave's stores have completed; then lane 0 bumps the counter.
 // Returns the previous value (uniform) when `want_old`.
 __device__ __forceinline__ int publish(int* ctr, bool want_old) {
+  // The data stores above are device-scope (coherent in every L2 partition)
+  // and complete before the counter bump once the wait returns. The fence
+  // keeps the compiler from moving a store past that point: the waitcnt
+  // builtin alone touches no memory in the compiler's model.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   int old = 0;
   if (lane_id() == 0) {
@@ -121,7 +126,11 @@ __device__ __forceinline__ void wait_geq(const int* ctr, int target, int* err, i
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off, kWave);
     s = __builtin_amdgcn_readfirstlane(s);
-    if (s >= target) break;
+    if (s >= target) {
+      // the dependent loads that follow stay after the counter was seen
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      break;
+    }
     if (++it > kSpinLimit) {
       if (lane_id() == 0) add_dev(err, 1);
       break;
@@ -486,7 +495,10 @@ __device__ void compute_topk(const DecodeArgs& a, TopkLds& tk) {
       in = in && (w[i] >> 32) != 0;
       lv[i] = __uint_as_float((uint32_t)w[i]);
     }
-    if (__builtin_amdgcn_ballot_w64(!in) == 0) break;
+    if (__builtin_amdgcn_ballot_w64(!in) == 0) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      break;
+    }
     if (it > kSpinLimit) {  // a broken producer: counted, and the wait abandoned
       if (lane == 0) add_dev(a.ctr + kCtrError, 1);
       break;
@@ -802,6 +814,16 @@ void make_decode_args(const Plan& p, DecodeArgs& a) {
   // per-wave A row: h of one route or of one shared expert
   a.a_region = std::max(d.I, d.S > 0 ? d.Is : 0);
   a.lds_bytes = (size_t)(((d.L + 7) & ~7) + 4 * a.a_region) * 2;
+}
+
+__global__ __launch_bounds__(64) void read_errors_kernel(int32_t* ctr, int32_t* count) {
+  if (threadIdx.x == 0)
+    *count = __hip_atomic_exchange(ctr + kCtrError, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_read_errors(int32_t* ctr, int32_t* count, hipStream_t s) {
+  hipLaunchKernelGGL(read_errors_kernel, dim3(1), dim3(64), 0, s, ctr, count);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, const hipEvent_t* ev) {

@@ -136,6 +136,9 @@ inline hipError_t record_stage(const hipEvent_t* ev, int stage, hipStream_t s) {
 // ---- single-token decode (decode.hip) ----
 void make_decode_args(const Plan& p, DecodeArgs& a);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, const hipEvent_t* ev);
+// copies the abandoned-wait count of a workspace's counter block to *count
+// and resets it
+hipError_t launch_read_errors(int32_t* ctr, int32_t* count, hipStream_t s);
 
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* sc, int rows, int K, uint16_t* out,
                           hipStream_t s);

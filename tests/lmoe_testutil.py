@@ -4,7 +4,7 @@ from __future__ import annotations
 
 import sys
 import time
-from typing import Dict, Optional
+from typing import Callable, Dict, Optional
 
 import numpy as np
 
@@ -79,15 +79,101 @@ def out_bound(ref64: np.ndarray, rms: Optional[float] = None) -> np.ndarray:
     return tol + np.ldexp(1.0, e - 8)
 
 
-def check_out(got_bits: np.ndarray, ref64: np.ndarray, what: str, rms: Optional[float] = None):
+# Model of the kernels' fp32 evaluation of a GLU input, g = sum_l x_l W_l over
+# K values: |g_fp32 - g| <= H_ACC * 2^-24 * sum_l |x_l W_l|. The kernels add
+# K/32 exact block sums into an fp32 accumulator; on the workloads that
+# ordering stays below 4 * 2^-24 * sum |x W| (fp32 emulation on the host), so
+# 16 leaves a margin of four. A larger H_ACC widens the allowance below, a
+# smaller one can only make the check stricter.
+H_ACC = 16.0
+
+
+def h_flip_allowance(x64: np.ndarray, gate: np.ndarray, up: np.ndarray, down: np.ndarray):
+    """Allowance for one expert's GLU, per row of x64 and output column:
+    where fp32 g and u may round h = bf16(silu(g) u) to the other side of a
+    bf16 rounding midpoint than the float64 oracle does, the two h differ by
+    one bf16 ulp, and output l moves by that ulp times |down[l, i]|. An h
+    element is counted when the distance of the float64 silu(g) u to its
+    nearest rounding midpoint is at most the propagated evaluation error
+    (H_ACC model for g and u, 8 fp32 ulp for silu and the product); each
+    counted element adds twice its bf16 spacing (covering the spacing change
+    at a power of two) times |down[l, i]|. Returns [rows][L]."""
+    g = x64 @ gate.T
+    u = x64 @ up.T
+    ax = np.abs(x64)
+    dg = H_ACC * 2.0 ** -24 * (ax @ np.abs(gate).T)
+    du = H_ACC * 2.0 ** -24 * (ax @ np.abs(up).T)
+    with np.errstate(over="ignore", invalid="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-g))
+        s = g * sig
+        ds_dg = sig * (1.0 + g * (1.0 - sig))
+    v = s * u
+    dv = np.abs(ds_dg * u) * dg + np.abs(s) * du + 8 * 2.0 ** -24 * np.abs(v)
+    h = O.f64_from_bf16(O.bf16_from_f64(v))
+    av = np.abs(v)
+    e = np.floor(np.log2(np.where(av > 0, av, 1.0)))
+    half = np.ldexp(1.0, (e - 8).astype(np.int64))       # half the bf16 spacing at |v|
+    near = (av > 0) & (np.abs(np.abs(v - h) - half) <= dv)
+    flip = np.where(near, 4.0 * half, 0.0)               # twice the spacing
+    return flip @ np.abs(down).T
+
+
+def flip_allowance_fn(x_bits: np.ndarray, idx: np.ndarray, w: np.ndarray,
+                      get_expert: Callable[[int], Dict[str, np.ndarray]],
+                      shared: Optional[Dict[str, np.ndarray]], L: int, I: int,
+                      experts: Optional[set] = None):
+    """fn(rows) -> [len(rows)][L]: the h-rounding allowance of those rows of
+    x (h_flip_allowance of each selected expert, weighted by the token's
+    softmax weight as in the combine, plus each shared expert with weight 1).
+    `experts` restricts the routed experts counted (the others contribute
+    nothing, e.g. silenced experts)."""
+    def fn(rows):
+        rows = np.asarray(rows, np.int64)
+        x64 = O.f64_from_bf16(np.asarray(x_bits)[rows])
+        sel = np.asarray(idx)[rows]
+        acc = np.zeros((rows.size, L), np.float64)
+        for e in np.unique(sel):
+            if experts is not None and int(e) not in experts:
+                continue
+            rr, jj = np.nonzero(sel == e)
+            ex = get_expert(int(e))
+            gate = O.dequant_mxfp4(ex["gate_q"], ex["gate_s"], I, L)
+            up = O.dequant_mxfp4(ex["up_q"], ex["up_s"], I, L)
+            down = O.dequant_mxfp4(ex["down_q"], ex["down_s"], L, I)
+            a = h_flip_allowance(x64[rr], gate, up, down)
+            acc[rr] += np.asarray(w, np.float64)[rows[rr], jj][:, None] * a
+        if shared is not None:
+            for sidx in range(shared["sh_gate"].shape[0]):
+                acc += h_flip_allowance(x64, O.f64_from_bf16(shared["sh_gate"][sidx]),
+                                        O.f64_from_bf16(shared["sh_up"][sidx]),
+                                        O.f64_from_bf16(shared["sh_down"][sidx]))
+        return acc
+    return fn
+
+
+def check_out(got_bits: np.ndarray, ref64: np.ndarray, what: str, rms: Optional[float] = None,
+              allowance_fn=None, rows: Optional[np.ndarray] = None):
+    """Outputs [n][L] within out_bound of the float64 reference. Where that
+    fails and `allowance_fn` is given, the failing rows are checked again with
+    their h-rounding allowance added (allowance_fn(token ids) with the token
+    ids `rows` of the compared rows, default 0..n-1)."""
     got = O.f64_from_bf16(got_bits)
     if rms is None:
         rms = float(np.sqrt(np.mean(ref64 ** 2)))
     bound = out_bound(ref64, rms)
     err = np.abs(got - ref64)
+    n_flip = 0
+    if allowance_fn is not None and not np.all(err <= bound):
+        fail = np.nonzero(np.any(~(err <= bound), axis=1))[0]
+        tok = (np.arange(got.shape[0]) if rows is None else np.asarray(rows))[fail]
+        n_flip = int(np.sum(~(err[fail] <= bound[fail])))
+        bound = bound.copy()
+        bound[fail] += allowance_fn(tok)
     bad = np.nonzero(~(err <= bound))
     rel_rms = float(np.sqrt(np.mean((got - ref64) ** 2)) / rms)
-    log(f"{what}: max|err|/rms={err.max() / rms:.3e} rms(err)/rms={rel_rms:.3e}")
+    log(f"{what}: max|err|/rms={err.max() / rms:.3e} rms(err)/rms={rel_rms:.3e}"
+        + (f"; {n_flip} of {err.size} outputs within the h-rounding allowance only"
+           if n_flip else ""))
     assert bad[0].size == 0, (
         f"{what}: {bad[0].size} outputs out of bound; first at {tuple(b[0] for b in bad)}: "
         f"got {got[bad][0]!r} ref {ref64[bad][0]!r} bound {bound[bad][0]!r}")
@@ -104,6 +190,62 @@ def logits_bound(x_bits: np.ndarray, wr_bits: np.ndarray) -> np.ndarray:
     L = ax.shape[1]
     s = ax @ aw.T
     return (L + 2) * 2.0 ** -24 * s + 2.0 ** -24 * s
+
+
+def topk_w_bound(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Bound on |w_gpu - w_oracle| for the softmax over the selected logits,
+    per selected route, for the kernels' evaluation: d_j = fl(l_j - l_0) in
+    fp32, z_j = expf(d_j), s = fp32 sum of the k terms in some order,
+    w_j = z_j / s correctly rounded. With u = 2^-24 (half an fp32 ulp) and an
+    expf error of at most 2 ulp (<= 8u relative), to first order:
+      rounding of d_j, carried through exp      |d_j| u
+      expf                                      8u
+      the same two in every term of s           max_i |d_i| u + 8u
+      summing k positive terms                  (k - 1) u
+      the division, the oracle's own rounding   2u
+    so |w_gpu - w_ref| <= (|d_j| + max_i |d_i| + k + 17) u w_ref, and 1% more
+    for second-order terms."""
+    lg = np.asarray(logits, np.float32).astype(np.float64)
+    sel = np.take_along_axis(lg, np.asarray(idx, np.int64), axis=1)
+    with np.errstate(invalid="ignore"):
+        d = np.abs(sel - sel[:, :1])
+        w = O.softmax_selected(logits, idx).astype(np.float64)
+    # a -inf logit below a finite first one has weight exactly 0 on both
+    # sides (expf(-inf) = 0): bound 0 there; rows with NaN weights are not
+    # compared
+    fin = np.isfinite(d)
+    d = np.where(fin, d, 0.0)
+    k = sel.shape[1]
+    rel = (d + d.max(axis=1, keepdims=True) + k + 17) * 2.0 ** -24 * 1.01
+    return np.where(fin, rel * np.abs(np.nan_to_num(w)), 0.0)
+
+
+def check_routing_exact(res: Dict[str, np.ndarray], logits: np.ndarray, k: int, what: str):
+    """The routing outputs of one call against the oracle's routing steps on
+    the same logits (given logits, or the GPU's own computed ones): indices,
+    counts, offsets, perm and inv_perm bit for bit; weights within
+    topk_w_bound. Returns the largest weight error in fp32 ulps."""
+    E = logits.shape[1]
+    idx = O.topk_select(logits, k)
+    with np.errstate(invalid="ignore"):
+        w = O.softmax_selected(logits, idx)
+    counts, offsets, perm, inv = O.permute_routes(idx, E)
+    bad = np.nonzero(np.any(res["topk_idx"] != idx, axis=1))[0]
+    assert bad.size == 0, (f"{what}: top-k indices differ on {bad.size} tokens, first {bad[0]}: "
+                           f"got {res['topk_idx'][bad[0]].tolist()} want {idx[bad[0]].tolist()}")
+    fin = np.isfinite(w)
+    err = np.abs(res["topk_w"].astype(np.float64) - w.astype(np.float64))
+    bound = topk_w_bound(logits, idx)
+    assert np.all(err[fin] <= bound[fin]), f"{what}: weights differ beyond the bound"
+    ulp = np.spacing(np.abs(w[fin]).astype(np.float32)).astype(np.float64)
+    max_ulp = float((err[fin] / ulp).max()) if fin.any() else 0.0
+    assert np.array_equal(res["counts"], counts), f"{what}: counts differ"
+    assert np.array_equal(res["offsets"], offsets), f"{what}: offsets differ"
+    assert np.array_equal(res["perm"], perm), f"{what}: perm differs"
+    assert np.array_equal(res["inv_perm"], inv), f"{what}: inv_perm differs"
+    log(f"{what}: routing bit-exact ({logits.shape[0]} tokens, E={E}, k={k}); "
+        f"weights within {max_ulp:.1f} ulp")
+    return max_ulp
 
 
 def check_routing_against_oracle(gpu_idx: np.ndarray, gpu_logits: np.ndarray,

@@ -26,7 +26,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     assert names == sorted(["lmoe_workspace_bytes", "lmoe_route", "lmoe_forward",
-                            "lmoe_forward_traced", "lmoe_stage_name", "lmoe_path_name",
+                            "lmoe_forward_ex", "lmoe_forward_traced", "lmoe_wait_errors",
+                            "lmoe_stage_name", "lmoe_path_name",
                             "lmoe_debug_dequant_mxfp4", "lmoe_status_string"]), names
 
 
@@ -170,6 +171,40 @@ def test_dequant_hook_rejects_bad_arguments(lm):
     assert f(None, 0x2000, 4, 64, 0x3000, None) == lm.LMOE_ERR_NULL
     assert f(0x1008, 0x2000, 4, 64, 0x3000, None) == lm.LMOE_ERR_ALIGN
     assert f(0x1000, 0x2000, 0, 64, 0x3000, None) == lm.LMOE_OK
+
+
+def test_forward_ex_rejects_bad_arguments(lm):
+    d = lm._dims(K3)
+    w = _weights(lm)
+    f = lm._lib.lmoe_forward_ex
+    # a side stream without its fork or join event
+    for ex in (lm.lmoe_exec(0x1000, None, 0x3000), lm.lmoe_exec(0x1000, 0x2000, None)):
+        assert f(ctypes.byref(d), 0x20000000, ctypes.byref(w), 0, None, 0x30000000, 0x40000000,
+                 1 << 40, None, ctypes.byref(ex)) == lm.LMOE_ERR_NULL
+        d0 = lm._dims((0,) + K3[1:])
+        assert f(ctypes.byref(d0), None, ctypes.byref(w), 0, None, None, None, 0, None,
+                 ctypes.byref(ex)) == lm.LMOE_ERR_NULL
+    # the same argument checks as lmoe_forward
+    assert f(None, 0, None, 0, None, 0, 0, 0, None, None) == lm.LMOE_ERR_NULL
+    bad = lm._dims((1, 3583, 896, 16, 2048, 2, 2048))
+    assert f(ctypes.byref(bad), 0x20000000, ctypes.byref(w), 0, None, 0x30000000, 0x40000000,
+             1 << 40, None, None) == lm.LMOE_ERR_SHAPE
+    assert f(ctypes.byref(d), 0x20000008, ctypes.byref(w), 0, None, 0x30000000, 0x40000000,
+             1 << 40, None, None) == lm.LMOE_ERR_ALIGN
+    assert f(ctypes.byref(d), 0x20000000, ctypes.byref(w), 0, None, 0x30000000, 0x40000000,
+             lm.workspace_bytes(K3) - 1, None, None) == lm.LMOE_ERR_WORKSPACE
+    d0 = lm._dims((0,) + K3[1:])
+    assert f(ctypes.byref(d0), None, ctypes.byref(lm.lmoe_weights()), 0, None, None, None, 0,
+             None, None) == lm.LMOE_OK
+
+
+def test_wait_errors_rejects_bad_arguments(lm):
+    f = lm._lib.lmoe_wait_errors
+    assert f(None, 1 << 20, 0x2000, None) == lm.LMOE_ERR_NULL
+    assert f(0x40000000, 1 << 20, None, None) == lm.LMOE_ERR_NULL
+    assert f(0x40000008, 1 << 20, 0x2000, None) == lm.LMOE_ERR_ALIGN
+    assert f(0x40000000, 1 << 20, 0x2002, None) == lm.LMOE_ERR_ALIGN
+    assert f(0x40000000, 32767, 0x2000, None) == lm.LMOE_ERR_WORKSPACE
 
 
 def test_binding_rejects_host_tensors(lm):

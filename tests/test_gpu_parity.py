@@ -16,7 +16,8 @@ from workloads import get_workload, gen_all, gen_logits, gen_expert, gen_x, gen_
 from workloads.configs import Dims, Workload
 
 from lmoe_testutil import (log, to_dev, upload, alloc_routing, run_forward, check_out,
-                           logits_bound, check_routing_against_oracle)
+                           logits_bound, check_routing_against_oracle, check_routing_exact,
+                           flip_allowance_fn)
 
 pytestmark = pytest.mark.gpu
 
@@ -94,19 +95,7 @@ def _route_given(lm, dev, logits: np.ndarray, k: int):
 
 
 def _check_route_exact(res, logits, k, what):
-    E = logits.shape[1]
-    idx = O.topk_select(logits, k)
-    w = O.softmax_selected(logits, idx)
-    counts, offsets, perm, inv = O.permute_routes(idx, E)
-    assert np.array_equal(res["topk_idx"], idx), f"{what}: top-k indices differ"
-    fin = np.isfinite(w)
-    assert np.all(np.abs(res["topk_w"][fin] - w[fin]) <= 4e-6 * np.abs(w[fin]) + 1e-12), \
-        f"{what}: weights differ"
-    assert np.array_equal(res["counts"], counts), f"{what}: counts differ"
-    assert np.array_equal(res["offsets"], offsets), f"{what}: offsets differ"
-    assert np.array_equal(res["perm"], perm), f"{what}: perm differs"
-    assert np.array_equal(res["inv_perm"], inv), f"{what}: inv_perm differs"
-    log(f"{what}: routing bit-exact ({logits.shape[0]} tokens, E={E}, k={k})")
+    check_routing_exact(res, logits, k, what)
 
 
 @pytest.mark.parametrize("E,k", [(8, 1), (8, 8), (40, 16), (33, 5), (1024, 32), (896, 16)])
@@ -142,26 +131,29 @@ def test_route_given_logits_skewed_full(lm, dev):
 # ----------------------------------------------------------------------------
 
 def _full_small(lm, dev, w: Workload):
+    """Every token of a layer small enough for the whole oracle. Outputs are
+    compared with the oracle run on the routing the GPU took: the given
+    logits, or the GPU's own computed logits once they are shown within the
+    summation bound and the oracle's routing on them equals the GPU's."""
     d = w.dims
     inp = gen_all(w)
     dinp = upload(inp, dev)
     got, r = run_forward(lm, w, dinp)
-    ref = O.forward(inp["x"], inp["router_w"], inp, inp, d.k,
-                    logits=inp.get("logits"))
     if w.logits_given:
-        assert np.array_equal(r["topk_idx"], ref["idx"])
-        same = np.ones(d.T, bool)
+        lg = inp["logits"]
+        check_routing_exact(r, lg, d.k, w.name)
     else:
-        same = check_routing_against_oracle(r["topk_idx"], r["logits"], ref["logits"],
+        ref_lg = O.router_logits(inp["x"], inp["router_w"])
+        same = check_routing_against_oracle(r["topk_idx"], r["logits"], ref_lg,
                                             logits_bound(inp["x"], inp["router_w"]), d.k, w.name)
         assert same.mean() >= 0.9
-    if same.all():
-        assert np.array_equal(r["counts"], ref["counts"])
-        assert np.array_equal(r["offsets"], ref["offsets"])
-        assert np.array_equal(r["perm"], ref["perm"])
-        assert np.array_equal(r["inv_perm"], ref["inv"])
-    rms = float(np.sqrt(np.mean(ref["out64"] ** 2)))
-    check_out(got[same], ref["out64"][same], f"{w.name} T={d.T}", rms)
+        lg = r["logits"]
+        check_routing_exact(r, lg, d.k, f"{w.name} (on the GPU logits)")
+    ref = O.forward(inp["x"], None, inp, inp, d.k, logits=lg)
+    get = lambda e: {key: inp[key][e] for key in ("gate_q", "gate_s", "up_q", "up_s",
+                                                   "down_q", "down_s")}
+    check_out(got, ref["out64"], f"{w.name} T={d.T}",
+              allowance_fn=flip_allowance_fn(inp["x"], ref["idx"], ref["w"], get, inp, d.L, d.I))
     return got
 
 
@@ -242,91 +234,185 @@ def test_zero_tokens_is_noop(lm, dev):
 
 
 # ----------------------------------------------------------------------------
-# Full K3-sized workloads: routing on every token, outputs on sampled tokens
+# Full K3-sized workloads. Routing on every token: with given logits the
+# oracle's selection, weights and grouping must match bit for bit (weights
+# within the derived softmax bound); with computed logits the GPU logits must
+# lie within the fp32 summation bound of the oracle's, the oracle's selection
+# and grouping applied to the GPU's own logits must match bit for bit, and the
+# selected sets must agree wherever the boundary gap is clear. Outputs: on
+# sampled tokens with the workload's real experts, and on every token with all
+# but a few experts silenced (below).
 # ----------------------------------------------------------------------------
 
-def _full_size(lm, dev, name, n_sample):
-    import torch
-    w = get_workload(name)
+def _check_full_routing(w: Workload, inp, r):
+    """Routing checks of a full-size call; returns (idx, weights) the outputs
+    are compared with and the mask of tokens whose sets agree with the
+    oracle's logits."""
     d = w.dims
-    log(f"{name}: generating inputs (T={d.T}, E={d.E}, L={d.L}, I={d.I})")
+    if w.logits_given:
+        lg = inp["logits"]
+        check_routing_exact(r, lg, d.k, w.name)
+        same = np.ones(d.T, bool)
+    else:
+        log(f"{w.name}: oracle logits")
+        ref_lg = O.router_logits(inp["x"], inp["router_w"])
+        same = check_routing_against_oracle(r["topk_idx"], r["logits"], ref_lg,
+                                            logits_bound(inp["x"], inp["router_w"]), d.k,
+                                            w.name)
+        assert same.mean() >= 0.99
+        # the oracle's routing steps on the GPU's own logits: bit-exact
+        lg = r["logits"]
+        check_routing_exact(r, lg, d.k, f"{w.name} (on the GPU logits)")
+    idx = O.topk_select(lg, d.k)
+    return idx, O.softmax_selected(lg, idx), same
+
+
+def _full_size(lm, dev, w: Workload, n_sample):
+    import torch
+    d = w.dims
+    log(f"{w.name}: generating inputs (T={d.T}, E={d.E}, L={d.L}, I={d.I})")
     inp = gen_all(w)
     dinp = upload(inp, dev)
     for key in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s"):
         del inp[key]                      # experts are regenerated per expert below
-    log(f"{name}: running lmoe_forward")
+    log(f"{w.name}: running lmoe_forward")
     got, r = run_forward(lm, w, dinp)
     del dinp
     torch.cuda.empty_cache()
-    if w.logits_given:
-        lg = inp["logits"]
-        _check_route_exact({"topk_idx": r["topk_idx"], "topk_w": r["topk_w"],
-                            "counts": r["counts"], "offsets": r["offsets"], "perm": r["perm"],
-                            "inv_perm": r["inv_perm"]}, lg, d.k, name)
-        same = np.ones(d.T, bool)
-        ref_lg = lg
-    else:
-        log(f"{name}: oracle logits")
-        ref_lg = O.router_logits(inp["x"], inp["router_w"])
-        same = check_routing_against_oracle(r["topk_idx"], r["logits"], ref_lg,
-                                            logits_bound(inp["x"], inp["router_w"]), d.k, name)
-        assert same.mean() >= 0.99
-    ref_idx = O.topk_select(ref_lg, d.k)
-    ref_w = O.softmax_selected(ref_lg, ref_idx)
+    idx, wts, same = _check_full_routing(w, inp, r)
     rng = np.random.default_rng(99)
     cand = np.nonzero(same)[0]
     toks = list(rng.choice(cand, size=min(n_sample, cand.size), replace=False))
     if w.logits_given:
-        tied = [t for t in cand if (ref_lg[t] == ref_lg[t].max()).sum() > d.k]
-        hot = int(np.argmax(r["counts"]))
-        hot_tok = [t for t in cand if hot in ref_idx[t]]
-        toks = sorted(set(toks[: max(1, n_sample - 2)]) | {tied[0], hot_tok[-1]})
+        tied = [t for t in cand if (inp["logits"][t] == inp["logits"][t].max()).sum() > d.k]
+        toks = sorted(set(toks[: max(1, n_sample - 1)]) | {tied[0]})
     toks = sorted(int(t) for t in toks)
-    log(f"{name}: oracle on tokens {toks}")
-    o64, _ = O.forward_tokens(inp["x"], ref_idx, ref_w, lambda e: gen_expert(w, e), inp,
-                              d.L, d.I, toks)
-    check_out(got[toks], o64, f"{name} sampled tokens")
+    log(f"{w.name}: oracle on tokens {toks}")
+    get = lambda e: gen_expert(w, e)
+    o64, _ = O.forward_tokens(inp["x"], idx, wts, get, inp, d.L, d.I, toks)
+    check_out(got[toks], o64, f"{w.name} sampled tokens", rows=np.array(toks),
+              allowance_fn=flip_allowance_fn(inp["x"], idx, wts, get, inp, d.L, d.I))
 
 
 def test_full_decode(lm, dev):
-    _full_size(lm, dev, "decode", 1)
+    _full_size(lm, dev, get_workload("decode"), 1)
 
 
 def test_full_decode_three_tokens(lm, dev):
     """Three K3 decode tokens in one call (seed 1's inputs): from two tokens
     the grouped path runs, with the shared experts in small tiles spread over
     every XCD. Every token is checked."""
-    from workloads import configs
-    name = "decode_t3"
-    configs.WORKLOADS.setdefault(name, get_workload("decode").with_T(3, name))
-    assert lm.path_name(configs.WORKLOADS[name].dims) == "grouped"
-    _full_size(lm, dev, name, 3)
+    w = get_workload("decode").with_T(3, "decode_t3")
+    assert lm.path_name(w.dims) == "grouped"
+    _full_size(lm, dev, w, 3)
 
 
 def test_full_batched_decode(lm, dev):
-    _full_size(lm, dev, "batched_decode", 3)
+    _full_size(lm, dev, get_workload("batched_decode"), 3)
 
 
 def test_full_prefill(lm, dev):
-    _full_size(lm, dev, "prefill", 3)
+    _full_size(lm, dev, get_workload("prefill"), 3)
 
 
 def test_full_skewed(lm, dev):
-    _full_size(lm, dev, "skewed", 3)
+    _full_size(lm, dev, get_workload("skewed"), 3)
 
 
 def test_full_decode_i3072(lm, dev):
     """The expert width implied by the pages' per-expert size."""
-    _full_size(lm, dev, "decode_i3072", 1)
+    _full_size(lm, dev, get_workload("decode_i3072"), 1)
 
 
 def test_full_prefill_i3072(lm, dev):
-    _full_size(lm, dev, "prefill_i3072", 3)
+    _full_size(lm, dev, get_workload("prefill_i3072"), 3)
 
 
 def test_full_decode_tp8(lm, dev):
     """One GPU's eighth of every expert (I = Is = 256), router whole."""
-    _full_size(lm, dev, "decode_tp8", 1)
+    _full_size(lm, dev, get_workload("decode_tp8"), 1)
+
+
+# ----------------------------------------------------------------------------
+# Every token at full size. The workload runs with its real router, routing and
+# shapes, but every expert outside a kept set has all gate codes zero, so its
+# routes give h = bf16(silu(0) u) = 0 and y = 0: each output is then the kept
+# experts' weighted partials plus the shared experts, which the oracle computes
+# for all T tokens at the cost of the kept experts alone. Kept: the hottest
+# expert (every one of its tokens checked, over all of its row tiles), the
+# coldest non-empty one, and one whose group just passes a 96-row tile.
+# ----------------------------------------------------------------------------
+
+def _every_token_isolated(lm, dev, w: Workload):
+    import torch
+    d = w.dims
+    log(f"{w.name}: generating inputs (T={d.T}, E={d.E}, L={d.L}, I={d.I})")
+    inp = gen_all(w)
+    dinp = upload(inp, dev)
+    for key in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s"):
+        del inp[key]
+    # routing first (it does not read the expert weights)
+    r0 = alloc_routing(d, dev)
+    if w.logits_given:
+        r0["logits"] = dinp["logits"]
+    ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
+    lm.route(d, dinp["x"], dinp["router_w"], w.logits_given, r0, ws)
+    torch.cuda.synchronize()
+    counts = r0["counts"].cpu().numpy()
+    order = np.argsort(-counts, kind="stable")
+    hot = int(order[0])
+    cold = int(order[np.nonzero(counts[order] > 0)[0][-1]])
+    past = np.nonzero((counts > 96) & (counts <= 120))[0]
+    keep = sorted({hot, cold} | ({int(past[0])} if past.size else set()))
+    log(f"{w.name}: kept experts {keep} with {counts[keep].tolist()} routes")
+    mask = torch.ones(d.E, dtype=torch.bool, device=dev)
+    mask[keep] = False
+    dinp["gate_q"].view(d.E, -1)[mask] = 0
+    got, r = run_forward(lm, w, dinp)
+    del dinp, ws
+    torch.cuda.empty_cache()
+    assert np.array_equal(r["topk_idx"], r0["topk_idx"].cpu().numpy())
+    idx, wts, _ = _check_full_routing(w, inp, r)
+    x64 = O.f64_from_bf16(inp["x"])
+    y = np.zeros((d.T, d.k, d.L), np.float64)
+    for e in keep:
+        ex = gen_expert(w, e)
+        rows, slots = np.nonzero(idx == e)
+        gate = O.dequant_mxfp4(ex["gate_q"], ex["gate_s"], d.I, d.L)
+        up = O.dequant_mxfp4(ex["up_q"], ex["up_s"], d.I, d.L)
+        down = O.dequant_mxfp4(ex["down_q"], ex["down_s"], d.L, d.I)
+        _, y[rows, slots] = O.glu_ffn(x64[rows], gate, up, down)
+    ysh = np.stack([O.glu_ffn(x64, O.f64_from_bf16(inp["sh_gate"][s]),
+                              O.f64_from_bf16(inp["sh_up"][s]),
+                              O.f64_from_bf16(inp["sh_down"][s]))[1] for s in range(d.S)])
+    o64, _ = O.combine(y, wts, ysh)
+    del y
+    check_out(got, o64, f"{w.name} every token ({len(keep)} experts kept)",
+              allowance_fn=flip_allowance_fn(inp["x"], idx, wts, lambda e: gen_expert(w, e), inp,
+                                             d.L, d.I, experts=set(keep)))
+
+
+@pytest.mark.parametrize("name", ["prefill", "skewed", "batched_decode"])
+def test_full_every_token_isolated(lm, dev, name):
+    _every_token_isolated(lm, dev, get_workload(name))
+
+
+# ----------------------------------------------------------------------------
+# The Kimi-K3 widths (L = 3584, I = Is = 2048, k = 16) with few experts, so the
+# oracle runs the whole layer on every token: computed logits with 2-4 row
+# tiles per group, and given Zipf-skewed logits with groups of 1 to 16 row
+# tiles. Both use the whole-exponent-row path of the grouped kernels.
+# ----------------------------------------------------------------------------
+
+K3W = dict(L=3584, k=16, I=2048, S=2, Is=2048)
+
+
+@pytest.mark.parametrize("w", [
+    Workload("k3w_e64_t1024", 31, Dims(T=1024, E=64, **K3W)),
+    Workload("k3w_e48_t1536_skew", 32, Dims(T=1536, E=48, **K3W), logits_given=True),
+], ids=lambda w: w.name)
+def test_k3_width_every_token(lm, dev, w):
+    _full_small(lm, dev, w)
 
 
 # ----------------------------------------------------------------------------
@@ -362,6 +448,33 @@ def test_side_stream_matches_single_stream(lm, dev, name):
                       _hip_events(lm.NUM_STAGE_EVENTS))
     torch.cuda.synchronize()
     assert np.array_equal(side.cpu().numpy(), one.cpu().numpy())
+
+
+@pytest.mark.parametrize("name", ["ragged_prefill", "ragged_skew"])
+def test_forward_ex_side_stream_choices(lm, dev, name):
+    """lmoe_forward_ex with the shared experts on a caller stream forked and
+    joined by caller events, and with every stage on one stream: both equal
+    lmoe_forward bit for bit."""
+    import torch
+    w = get_workload(name)
+    d = w.dims
+    inp = gen_all(w)
+    dinp = upload(inp, dev)
+    r = {"logits": dinp["logits"]} if w.logits_given else None
+    ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
+    ref = torch.empty((d.T, d.L), dtype=torch.int16, device=dev)
+    lm.forward(d, dinp["x"], dinp, w.logits_given, r, ref, ws)
+    side = torch.cuda.Stream()
+    fork, join = _hip_events(2)
+    for use_side in (True, False, True):
+        out = torch.empty_like(ref)
+        if use_side:
+            lm.forward_ex(d, dinp["x"], dinp, w.logits_given, r, out, ws, side.cuda_stream,
+                          fork, join)
+        else:
+            lm.forward_ex(d, dinp["x"], dinp, w.logits_given, r, out, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref.cpu().numpy()), f"side={use_side}"
 
 
 def test_back_to_back_calls_reuse_workspace(lm, dev):
