@@ -211,6 +211,27 @@ int lmoe_forward_ex(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights
  * Errors: LMOE_ERR_NULL, _ALIGN, _WORKSPACE, _HIP. */
 int lmoe_wait_errors(void* ws, size_t ws_bytes, int32_t* count, void* stream);
 
+/* Size of the device scratch lmoe_forward_noalloc uses: one static array per
+ * GPU, held from the library's first such call on that GPU until the process
+ * ends. */
+#define LMOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* lmoe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same layer and results, with the workspace taken from a static device array
+ * of LMOE_NOALLOC_SCRATCH_BYTES on the current GPU instead of a caller
+ * buffer. The call allocates nothing (no hipMalloc, hipFree, stream or event
+ * creation; every stage runs on `stream`); its first call on a GPU looks up
+ * that GPU's array and clears the part that must start at zero.
+ * Every call on one GPU shares that array, which keeps the last call's
+ * contents: calls that overlap on one GPU (different streams or threads)
+ * race and must be serialised by the caller.
+ * Arguments, results and errors as lmoe_forward, plus LMOE_ERR_WORKSPACE when
+ * lmoe_workspace_bytes(dims) exceeds LMOE_NOALLOC_SCRATCH_BYTES (at the
+ * Kimi-K3 widths: up to about 150 tokens). */
+int lmoe_forward_noalloc(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights* w,
+                         int logits_given, const lmoe_routing* r, uint16_t* out, void* stream);
+
 /* Stage boundaries recorded by lmoe_forward_traced. Event i is recorded on
  * the stream right after stage i has been enqueued (event 0 before the first
  * one); a stage that does not run for these arguments (the router when logits

@@ -12,6 +12,7 @@ Functions mirror the C ABI in include/lmoe.h:
   forward_ex(dims, x, weights, logits_given, routing, out, ws, side_stream, fork_event,
              join_event)
   wait_errors(ws, count)
+  forward_noalloc(dims, x, weights, logits_given, routing, out)
   debug_dequant_mxfp4(q, s, rows, K, out)
   status_string(code)
 `dims` is a Dims-like object (attributes T, L, E, k, I, S, Is) or a tuple in
@@ -34,9 +35,11 @@ LMOE_ERR_SHAPE = 2
 LMOE_ERR_ALIGN = 3
 LMOE_ERR_WORKSPACE = 4
 LMOE_ERR_HIP = 5
+# scratch of lmoe_forward_noalloc per GPU (LMOE_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("lmoe_workspace_bytes", "lmoe_route", "lmoe_forward", "lmoe_forward_ex",
-           "lmoe_forward_traced", "lmoe_wait_errors", "lmoe_stage_name", "lmoe_path_name",
+           "lmoe_forward_traced", "lmoe_wait_errors", "lmoe_forward_noalloc", "lmoe_stage_name", "lmoe_path_name",
            "lmoe_debug_dequant_mxfp4", "lmoe_status_string")
 
 # Stage boundaries recorded by forward_traced (LMOE_STAGE_* in lmoe.h).
@@ -89,6 +92,9 @@ def _load() -> ctypes.CDLL:
                                     ctypes.POINTER(lmoe_routing), vp, vp, sz, vp,
                                     ctypes.POINTER(lmoe_exec)]
     lib.lmoe_forward_ex.restype = ctypes.c_int
+    lib.lmoe_forward_noalloc.argtypes = [dp, vp, ctypes.POINTER(lmoe_weights), ctypes.c_int,
+                                         ctypes.POINTER(lmoe_routing), vp, vp]
+    lib.lmoe_forward_noalloc.restype = ctypes.c_int
     lib.lmoe_wait_errors.argtypes = [vp, sz, vp, vp]
     lib.lmoe_wait_errors.restype = ctypes.c_int
     lib.lmoe_forward_traced.argtypes = [dp, vp, ctypes.POINTER(lmoe_weights), ctypes.c_int,
@@ -201,6 +207,20 @@ def forward_ex(dims, x, weights: Mapping, logits_given: bool, routing: Optional[
                                 ws.numel() * ws.element_size() if ws is not None else 0,
                                 _stream(stream), ctypes.byref(ex) if ex is not None else None)
     _check("lmoe_forward_ex", code)
+
+
+def forward_noalloc(dims, x, weights: Mapping, logits_given: bool, routing: Optional[Mapping],
+                    out, stream=None) -> None:
+    """forward() with the library's static per-GPU scratch as workspace: no
+    device allocation; calls that overlap on one GPU race."""
+    d = _dims(dims)
+    r = _routing(routing)
+    w = _weights(weights)
+    code = _lib.lmoe_forward_noalloc(ctypes.byref(d), _ptr(x), ctypes.byref(w),
+                                     int(bool(logits_given)),
+                                     ctypes.byref(r) if r is not None else None, _ptr(out),
+                                     _stream(stream))
+    _check("lmoe_forward_noalloc", code)
 
 
 def wait_errors(ws, count, stream=None) -> None:

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <mutex>
 
@@ -355,6 +356,75 @@ extern "C" int lmoe_forward_ex(const lmoe_dims* dims, const uint16_t* x, const l
                                size_t ws_bytes, void* stream, const lmoe_exec* exec) {
   return forward_impl(dims, x, wts, logits_given, r, out, ws, ws_bytes, stream, nullptr,
                       SideMode::kCaller, exec);
+}
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Scratch of lmoe_forward_noalloc: one array per GPU (each device holds its
+// own copy at its own address). In host code `scratch` names a host-side
+// stand-in, never the device memory: its device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[LMOE_NOALLOC_SCRATCH_BYTES];
+
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+struct ScratchSlot {
+  std::once_flag once;
+  hipError_t err = hipErrorNotInitialized;
+  void* ptr = nullptr;
+};
+
+// The device address of this device's scratch (nullptr on failure).
+static void* scratch_ptr(int dev) {
+  static ScratchSlot slots[64];
+  if (dev < 0 || dev >= 64) return nullptr;
+  ScratchSlot& sl = slots[dev];
+  std::call_once(sl.once, [&] {
+    void* p = nullptr;
+    sl.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    sl.ptr = sl.err == hipSuccess ? p : nullptr;
+  });
+  return sl.ptr;
+}
+
+// True from the second time it is asked for a device on: the first caller
+// clears the counter block.
+static bool scratch_cleared_once(int dev) {
+  static std::atomic<bool> cleared[64];
+  return cleared[dev].exchange(true);
+}
+
+}  // namespace
+
+extern "C" int lmoe_forward_noalloc(const lmoe_dims* dims, const uint16_t* x,
+                                    const lmoe_weights* wts, int logits_given,
+                                    const lmoe_routing* r, uint16_t* out, void* stream) {
+  if (!dims || !wts) return LMOE_ERR_NULL;
+  if (!dims_ok(*dims)) return LMOE_ERR_SHAPE;
+  const size_t need = carve_workspace(make_plan(*dims), nullptr).bytes;
+  if (need > LMOE_NOALLOC_SCRATCH_BYTES) return LMOE_ERR_WORKSPACE;
+  if (dims->T == 0) return forward_impl(dims, x, wts, logits_given, r, out, nullptr, 0, stream,
+                                        nullptr, SideMode::kCaller, nullptr);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LMOE_ERR_HIP;
+  void* ws = scratch_ptr(dev);
+  if (!ws) return LMOE_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!scratch_cleared_once(dev)) {
+    // the counter block must be zero before the first call; every call
+    // leaves it zero (a fill kernel, not a memset, so capture is safe)
+    const int n = (int)(kCtrBytes / 4);
+    hipLaunchKernelGGL(zero_kernel, dim3((n + 255) / 256), dim3(256), 0, s,
+                       static_cast<uint32_t*>(ws), n);
+    if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
+  }
+  return forward_impl(dims, x, wts, logits_given, r, out, ws, LMOE_NOALLOC_SCRATCH_BYTES, stream,
+                      nullptr, SideMode::kCaller, nullptr);
 }
 
 extern "C" int lmoe_wait_errors(void* ws, size_t ws_bytes, int32_t* count, void* stream) {

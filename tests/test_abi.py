@@ -27,6 +27,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     assert names == sorted(["lmoe_workspace_bytes", "lmoe_route", "lmoe_forward",
                             "lmoe_forward_ex", "lmoe_forward_traced", "lmoe_wait_errors",
+                            "lmoe_forward_noalloc",
                             "lmoe_stage_name", "lmoe_path_name",
                             "lmoe_debug_dequant_mxfp4", "lmoe_status_string"]), names
 
@@ -196,6 +197,33 @@ def test_forward_ex_rejects_bad_arguments(lm):
     d0 = lm._dims((0,) + K3[1:])
     assert f(ctypes.byref(d0), None, ctypes.byref(lm.lmoe_weights()), 0, None, None, None, 0,
              None, None) == lm.LMOE_OK
+
+
+def test_forward_noalloc_rejects_on_the_host(lm):
+    """Rejections that return before the device is touched."""
+    f = lm._lib.lmoe_forward_noalloc
+    w = _weights(lm)
+    assert f(None, 0x20000000, ctypes.byref(w), 0, None, 0x30000000, None) == lm.LMOE_ERR_NULL
+    bad = lm._dims((1, 3583, 896, 16, 2048, 2, 2048))
+    assert f(ctypes.byref(bad), 0x20000000, ctypes.byref(w), 0, None, 0x30000000,
+             None) == lm.LMOE_ERR_SHAPE
+    # the scratch holds the workspace of up to about 150 Kimi-K3 tokens
+    for T in (1, 64, 128):
+        assert lm.workspace_bytes((T,) + K3[1:]) <= lm.NOALLOC_SCRATCH_BYTES, T
+    big = (4096,) + K3[1:]
+    assert lm.workspace_bytes(big) > lm.NOALLOC_SCRATCH_BYTES
+    d = lm._dims(big)
+    assert f(ctypes.byref(d), 0x20000000, ctypes.byref(w), 0, None, 0x30000000,
+             None) == lm.LMOE_ERR_WORKSPACE
+    d0 = lm._dims((0,) + K3[1:])
+    assert f(ctypes.byref(d0), None, ctypes.byref(lm.lmoe_weights()), 0, None, None,
+             None) == lm.LMOE_OK
+
+
+def test_header_scratch_size_matches_binding(lm):
+    text = open(HEADER).read()
+    m = re.search(r"#define LMOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == lm.NOALLOC_SCRATCH_BYTES
 
 
 def test_wait_errors_rejects_bad_arguments(lm):
