@@ -193,13 +193,22 @@ def upload(a: np.ndarray, dev):
     return torch.from_numpy(a).to(dev)
 
 
-def setup(name: str, dev, n_tokens: int = 1, replicas: int = 1):
+def setup(name: str, dev, n_tokens: int = 1, replicas: int = 1, lm=None, packed=False):
+    """Inputs resident on the device. packed: the routed experts repacked once
+    by lmoe_pack_weights (as at model load; not part of any timed step)."""
+    import torch
     from workloads import get_workload, gen_x, gen_router, gen_experts, gen_shared, gen_logits
     w = get_workload(name)
     t0 = time.time()
     ex = gen_experts(w)
     weights = {k: upload(v, dev) for k, v in ex.items()}
     del ex
+    if packed:
+        pk = {k: torch.empty(n, dtype=torch.uint8, device=dev)
+              for k, n in lm.packed_sizes(w.dims).items()}
+        lm.pack_weights(w.dims, weights, pk)
+        torch.cuda.synchronize()
+        weights = pk
     dense = []
     rw = upload(gen_router(w), dev)
     sh = {k: upload(v, dev) for k, v in gen_shared(w).items()}
@@ -234,15 +243,30 @@ def routing_buffers(d, dev):
     }
 
 
-def run_case(lm, hip, name, dev, steps, warmup, rotate: bool, traced_steps: int):
-    """Time `steps` layer calls; returns a dict of measurements."""
+def run_case(lm, hip, name, dev, steps, warmup, rotate: bool, traced_steps: int,
+             packed: bool = False):
+    """Time `steps` layer calls; returns a dict of measurements. packed: the
+    tile-packed routed experts and lmoe_forward_packed (shared experts on a
+    second stream of the bench's own)."""
     import torch
     n_tok = N_TOKENS if rotate else 1
     reps = N_REPLICAS if rotate else 1
     w = __import__("workloads").get_workload(name)
     T = w.dims.T
     # rotating calls take T rows at a time from a pool of n_tok * T rows
-    w, experts, dense, x_pool, logits = setup(name, dev, n_tok * T, reps)
+    w, experts, dense, x_pool, logits = setup(name, dev, n_tok * T, reps, lm, packed)
+    side = torch.cuda.Stream() if packed else None
+    fork, join = (hip.event(), hip.event()) if packed else (None, None)
+
+    def fwd(d, xi, wi, lg, r, out, ws, events=None):
+        if packed and events is not None:
+            lm.forward_packed(d, xi, wi, lg, r, out, ws, stage_events=events)
+        elif packed:
+            lm.forward_packed(d, xi, wi, lg, r, out, ws, side.cuda_stream, fork, join)
+        elif events is not None:
+            lm.forward_traced(d, xi, wi, lg, r, out, ws, events)
+        else:
+            lm.forward(d, xi, wi, lg, r, out, ws)
     d = w.dims
     ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
     out = torch.empty((T, d.L), dtype=torch.int16, device=dev)
@@ -266,14 +290,14 @@ def run_case(lm, hip, name, dev, steps, warmup, rotate: bool, traced_steps: int)
         rr = dict(rbuf)
         if r:
             rr.update(r)
-        lm.forward(d, xi, wi, w.logits_given, rr, out, ws)
+        fwd(d, xi, wi, w.logits_given, rr, out, ws)
         D.append(int((rbuf["counts"] > 0).sum().item()))
     D_mean = float(np.mean(D))
 
     pre = [args(i) for i in range(max(steps, warmup, traced_steps, 1))]
     for i in range(warmup):
         xi, wi, r = pre[i % len(pre)]
-        lm.forward(d, xi, wi, w.logits_given, r, out, ws)
+        fwd(d, xi, wi, w.logits_given, r, out, ws)
     torch.cuda.synchronize()
 
     # The GPU is held in a spin kernel while the host enqueues, so the timed
@@ -294,7 +318,7 @@ def run_case(lm, hip, name, dev, steps, warmup, rotate: bool, traced_steps: int)
 
     def call(i):
         xi, wi, r = pre[i]
-        return lambda: lm.forward(d, xi, wi, w.logits_given, r, out, ws)
+        return lambda: fwd(d, xi, wi, w.logits_given, r, out, ws)
 
     tot_ms, enq_ms = timed([call(i) for i in range(steps)])
     ms = tot_ms / steps
@@ -310,7 +334,7 @@ def run_case(lm, hip, name, dev, steps, warmup, rotate: bool, traced_steps: int)
 
     def traced(i):
         xi, wi, r = pre[i]
-        return lambda: lm.forward_traced(d, xi, wi, w.logits_given, r, out, ws, evs[i])
+        return lambda: fwd(d, xi, wi, w.logits_given, r, out, ws, evs[i])
 
     timed([traced(i) for i in range(traced_steps)])
     stage_ms = {s: 0.0 for s in lm.STAGES[1:]}
@@ -322,7 +346,7 @@ def run_case(lm, hip, name, dev, steps, warmup, rotate: bool, traced_steps: int)
     del experts, dense, x_pool, ws, out
     torch.cuda.empty_cache()
     return {"w": w, "D": D_mean, "ms": ms, "enqueue_ms": enq_ms / steps, "warm_ms": warm_ms,
-            "stage_ms": stage_ms, "traced_ms": traced_total}
+            "stage_ms": stage_ms, "traced_ms": traced_total, "packed": packed}
 
 
 # The single-token path is one kernel; the library records every stage event
@@ -344,7 +368,9 @@ def kernel_units(res, lm):
         return [(FUSED_KERNEL, tb, tf, res["ms"] * 1e-3)]
     large = True  # routed groups of every size take the large kernel
     sh_large = d.T > 64
-    return [(stage_kernel(s, large, sh_large, d, logits_given), sb[s], sf[s],
+    packed_kernel = {"gate_up": "gemm_packed_kernel<true>", "down": "gemm_packed_kernel<false>"}
+    return [((packed_kernel.get(s) if res.get("packed") else None)
+             or stage_kernel(s, large, sh_large, d, logits_given), sb[s], sf[s],
              res["stage_ms"][s] * 1e-3)
             for s in sb if res["stage_ms"][s] > 0]
 
@@ -499,18 +525,21 @@ EXTRA = ("batched_decode", "skewed", "decode_i3072", "prefill_i3072", "decode_tp
 DEFAULT_EXTRA = "batched_decode,skewed,decode_i3072"
 
 
-def extra_case(lm, hip, name, dev, steps):
+def extra_case(lm, hip, name, dev, steps, packed: bool):
     from workloads import get_workload
     d = get_workload(name).dims
     hbm = d.T <= 64
+    # single tokens take the one-kernel path on row-major experts
+    packed = packed and d.T > 1
     res = run_case(lm, hip, name, dev, steps if hbm else max(3, steps // 20), 3, rotate=hbm,
-                   traced_steps=5)
+                   traced_steps=5, packed=packed)
     tb, tf, _, _ = algorithmic(d, res["D"], res["w"].logits_given)
     sec = res["ms"] * 1e-3
     out = {"T": d.T, "L": d.L, "E": d.E, "k": d.k, "I": d.I, "S": d.S, "Is": d.Is,
            "distinct_experts": round(res["D"], 1), "ms_per_step": round(res["ms"], 5),
            "gb_s": round(tb / sec / 1e9, 1), "tflop_s": round(tf / sec / 1e12, 2),
            "algorithmic_bytes": round(tb), "algorithmic_flops": round(tf),
+           "layout": "packed" if packed else "row-major",
            "roofline": roofline_for(res, "hbm" if hbm else "mfma", lm),
            "stage_us": stage_us(res, lm)}
     out["frac_of_peak"] = round(out["gb_s"] / HBM_PEAK_GBS if hbm
@@ -534,6 +563,9 @@ def main():
     ap.add_argument("--extra", default=DEFAULT_EXTRA,
                     help="comma-separated further workloads to report, 'all', or 'none': "
                          + ", ".join(EXTRA))
+    ap.add_argument("--layout", default="packed", choices=("packed", "row-major"),
+                    help="routed-expert layout of the multi-token cases (single tokens run "
+                         "the one-kernel path on row-major experts)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this size (PMC calibration)")
     args = ap.parse_args()
@@ -589,7 +621,7 @@ def main():
     }
     if not args.no_prefill:
         pf = run_case(lm, hip, "prefill", dev, args.prefill_steps, 2, rotate=False,
-                      traced_steps=min(args.prefill_steps, 5))
+                      traced_steps=min(args.prefill_steps, 5), packed=args.layout == "packed")
         pd = pf["w"].dims
         ptb, ptf, _, _ = algorithmic(pd, pf["D"], False)
         tfl = ptf / (pf["ms"] * 1e-3) / 1e12
@@ -600,12 +632,20 @@ def main():
             "steps": args.prefill_steps, "frac_of_peak": round(tfl / BF16_PEAK_TFLOPS, 4),
             "gb_s": round(ptb / (pf["ms"] * 1e-3) / 1e9, 1),
             "workload": "K3 LatentMoE prefill chunk: T=4096, same layer, seed 3",
+            "layout": args.layout,
             "roofline": roofline_for(pf, "mfma", lm),
             "stage_us": stage_us(pf, lm),
         }
     if args.extra and args.extra != "none":
         names = EXTRA if args.extra == "all" else tuple(args.extra.split(","))
-        result["extra"] = {n: extra_case(lm, hip, n, dev, args.steps) for n in names}
+        result["extra"] = {}
+        for n in names:
+            packed = args.layout == "packed"
+            if n.endswith("_rowmajor"):
+                n, packed = n[: -len("_rowmajor")], False
+                result["extra"][n + "_rowmajor"] = extra_case(lm, hip, n, dev, args.steps, False)
+            else:
+                result["extra"][n] = extra_case(lm, hip, n, dev, args.steps, packed)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args.cpu_tokens, args.cpu_seconds)
         if "prefill" in result:

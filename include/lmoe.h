@@ -186,6 +186,10 @@ typedef struct lmoe_exec {
   void* side_stream;
   void* fork_event;
   void* join_event;
+  /* NULL, or LMOE_NUM_STAGE_EVENTS caller-created hipEvent_t recorded at the
+   * stage boundaries as lmoe_forward_traced does; every stage then runs on
+   * the call's stream and side_stream is not used */
+  void* const* stage_events;
 } lmoe_exec;
 
 /* lmoe_forward with the shared experts' stream chosen by the caller instead
@@ -210,6 +214,69 @@ int lmoe_forward_ex(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights
  *   ws  the workspace of those calls (ws_bytes >= 32 KiB)
  * Errors: LMOE_ERR_NULL, _ALIGN, _WORKSPACE, _HIP. */
 int lmoe_wait_errors(void* ws, size_t ws_bytes, int32_t* count, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Tile-packed routed experts. The checkpoint's MXFP4 matrices, repacked once
+ * (as the MXFP4 experts are repacked at load time in huggingface.co "Notes
+ * from an NVFP4 port of Kimi K3.1 Pro", introduction) into the order the
+ * grouped 32x32x16-MFMA GEMMs read: every 64-lane load instruction then reads
+ * 1 KB contiguous. Codes and exponents are the same bytes, reordered, so the
+ * layer's results are the same as from the row-major layout.
+ *
+ * A packed matrix of N rows and K values per row (K % 32 == 0) has
+ * N32 = ceil(N/32) tiles of 32 rows, K128 = ceil(K/128) chunks and
+ * K512 = ceil(K/512) exponent windows; per expert, in that order:
+ *   codes      [N32][K128][2][64][16] bytes: the 16 bytes of lane l, half j
+ *              of chunk c of tile n are the codes of row 32n + l%32, MX block
+ *              4c + 2(l/32) + j (32 values, element 2m in the low nibble of
+ *              byte m)
+ *   exponents  [N32][K512][64][8] bytes: byte b of lane l in window w of tile
+ *              n is the E8M0 exponent of row 32n + l%32, block
+ *              4(4w + b/2) + 2(l/32) + b%2
+ * Rows and blocks past the matrix hold code 0 and exponent 127.
+ * gu: the gate and up matrices of an expert as one matrix of N = 2I rows and
+ *     K = L: tile n holds gate rows 16n .. 16n+15, then up rows 16n .. 16n+15.
+ * down: the down matrix, N = L, K = I.
+ * --------------------------------------------------------------------------- */
+typedef struct lmoe_packed_sizes {
+  size_t gu_q, gu_s, down_q, down_s;  /* bytes over all E experts */
+} lmoe_packed_sizes;
+
+/* Bytes of each packed array for these dims (host).
+ * Errors: LMOE_ERR_NULL, _SHAPE. */
+int lmoe_packed_sizes_of(const lmoe_dims* dims, lmoe_packed_sizes* sizes);
+
+/* Repack the routed experts of w (row-major, as lmoe_weights; router and
+ * shared pointers are not read) into the caller's device arrays gu_q, gu_s,
+ * down_q, down_s of lmoe_packed_sizes_of bytes. Asynchronous on `stream`;
+ * the sources must stay valid until it completes.
+ * Errors: LMOE_ERR_NULL, _SHAPE, _ALIGN, _HIP. */
+int lmoe_pack_weights(const lmoe_dims* dims, const lmoe_weights* w, uint8_t* gu_q,
+                      uint8_t* gu_s, uint8_t* down_q, uint8_t* down_s, void* stream);
+
+/* The layer's weights with the routed experts tile-packed. */
+typedef struct lmoe_packed_weights {
+  const uint16_t* router_w;  /* bf16 [E][L], as lmoe_weights */
+  const uint8_t* gu_q;       /* packed gate/up codes and exponents */
+  const uint8_t* gu_s;
+  const uint8_t* down_q;     /* packed down codes and exponents */
+  const uint8_t* down_s;
+  const uint16_t* sh_gate;   /* as lmoe_weights */
+  const uint16_t* sh_up;
+  const uint16_t* sh_down;
+} lmoe_packed_weights;
+
+/* lmoe_forward_ex on tile-packed routed experts: the same layer and results
+ * (up to the order of fp32 sums), with the routed GEMMs on 32x32x16 bf16
+ * MFMA over expert groups of up to 128 routes. Every token count runs the
+ * grouped path (routing kernels, grouped GEMMs, combine). exec as in
+ * lmoe_forward_ex (NULL: every stage on `stream`). The workspace is the one
+ * lmoe_workspace_bytes gives. T * L and T * k * I must stay below 2^32
+ * (LMOE_ERR_SHAPE otherwise; 131072 tokens at the Kimi-K3 widths).
+ * Errors: as lmoe_forward_ex. */
+int lmoe_forward_packed(const lmoe_dims* dims, const uint16_t* x, const lmoe_packed_weights* w,
+                        int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
+                        size_t ws_bytes, void* stream, const lmoe_exec* exec);
 
 /* Size of the device scratch lmoe_forward_noalloc uses: one static array per
  * GPU, held from the library's first such call on that GPU until the process

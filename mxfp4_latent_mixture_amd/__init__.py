@@ -13,6 +13,10 @@ Functions mirror the C ABI in include/lmoe.h:
              join_event)
   wait_errors(ws, count)
   forward_noalloc(dims, x, weights, logits_given, routing, out)
+  packed_sizes(dims)
+  pack_weights(dims, weights, packed)
+  forward_packed(dims, x, weights, logits_given, routing, out, ws, side_stream, fork_event,
+                 join_event)
   debug_dequant_mxfp4(q, s, rows, K, out)
   status_string(code)
 `dims` is a Dims-like object (attributes T, L, E, k, I, S, Is) or a tuple in
@@ -40,7 +44,10 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("lmoe_workspace_bytes", "lmoe_route", "lmoe_forward", "lmoe_forward_ex",
            "lmoe_forward_traced", "lmoe_wait_errors", "lmoe_forward_noalloc", "lmoe_stage_name", "lmoe_path_name",
-           "lmoe_debug_dequant_mxfp4", "lmoe_status_string")
+           "lmoe_debug_dequant_mxfp4", "lmoe_status_string", "lmoe_packed_sizes_of",
+           "lmoe_pack_weights", "lmoe_forward_packed")
+# members of lmoe_packed_sizes / the packed routed-expert arrays
+PACKED_KEYS = ("gu_q", "gu_s", "down_q", "down_s")
 
 # Stage boundaries recorded by forward_traced (LMOE_STAGE_* in lmoe.h).
 STAGES = ("begin", "router", "topk", "permute", "gate_up", "down", "shared_gate_up",
@@ -64,7 +71,31 @@ class lmoe_routing(ctypes.Structure):
 
 
 class lmoe_exec(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("side_stream", "fork_event", "join_event")]
+    _fields_ = [("side_stream", ctypes.c_void_p), ("fork_event", ctypes.c_void_p),
+                ("join_event", ctypes.c_void_p), ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
+
+
+def _exec(side_stream, fork_event, join_event, stage_events):
+    if side_stream is None and stage_events is None:
+        return None
+    ex = lmoe_exec(side_stream and int(side_stream), fork_event and int(fork_event),
+                   join_event and int(join_event), None)
+    if stage_events is not None:
+        if len(stage_events) != NUM_STAGE_EVENTS:
+            raise ValueError(f"need {NUM_STAGE_EVENTS} events")
+        arr = (ctypes.c_void_p * NUM_STAGE_EVENTS)(*[int(e) for e in stage_events])
+        ex.stage_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        ex._keep = arr
+    return ex
+
+
+class lmoe_packed_sizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("gu_q", "gu_s", "down_q", "down_s")]
+
+
+class lmoe_packed_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "router_w", "gu_q", "gu_s", "down_q", "down_s", "sh_gate", "sh_up", "sh_down")]
 
 
 class LmoeError(RuntimeError):
@@ -78,6 +109,13 @@ def _load() -> ctypes.CDLL:
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python mxfp4_latent_mixture_amd/build.py` "
             "(hipcc, gfx950). There is no CPU fallback.")
+    # torch ships its own HIP runtime under the same soname as the system's:
+    # loading torch first makes this library bind to the runtime that
+    # allocates the tensors it is handed (one runtime per process)
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
     dp = ctypes.POINTER(lmoe_dims)
@@ -95,6 +133,14 @@ def _load() -> ctypes.CDLL:
     lib.lmoe_forward_noalloc.argtypes = [dp, vp, ctypes.POINTER(lmoe_weights), ctypes.c_int,
                                          ctypes.POINTER(lmoe_routing), vp, vp]
     lib.lmoe_forward_noalloc.restype = ctypes.c_int
+    lib.lmoe_packed_sizes_of.argtypes = [dp, ctypes.POINTER(lmoe_packed_sizes)]
+    lib.lmoe_packed_sizes_of.restype = ctypes.c_int
+    lib.lmoe_pack_weights.argtypes = [dp, ctypes.POINTER(lmoe_weights), vp, vp, vp, vp, vp]
+    lib.lmoe_pack_weights.restype = ctypes.c_int
+    lib.lmoe_forward_packed.argtypes = [dp, vp, ctypes.POINTER(lmoe_packed_weights), ctypes.c_int,
+                                        ctypes.POINTER(lmoe_routing), vp, vp, sz, vp,
+                                        ctypes.POINTER(lmoe_exec)]
+    lib.lmoe_forward_packed.restype = ctypes.c_int
     lib.lmoe_wait_errors.argtypes = [vp, sz, vp, vp]
     lib.lmoe_wait_errors.restype = ctypes.c_int
     lib.lmoe_forward_traced.argtypes = [dp, vp, ctypes.POINTER(lmoe_weights), ctypes.c_int,
@@ -190,17 +236,17 @@ def forward(dims, x, weights: Mapping, logits_given: bool, routing: Optional[Map
 
 
 def forward_ex(dims, x, weights: Mapping, logits_given: bool, routing: Optional[Mapping], out,
-               ws, side_stream=None, fork_event=None, join_event=None, stream=None) -> None:
+               ws, side_stream=None, fork_event=None, join_event=None, stream=None,
+               stage_events=None) -> None:
     """forward() with the shared experts on the caller's side_stream (an int
     hipStream_t), forked and joined by the caller's fork_event / join_event
-    (int hipEvent_t); side_stream None runs every stage on `stream`."""
+    (int hipEvent_t); side_stream None runs every stage on `stream`.
+    stage_events: NUM_STAGE_EVENTS hipEvent_t recorded at the stage
+    boundaries (every stage on `stream`)."""
     d = _dims(dims)
     r = _routing(routing)
     w = _weights(weights)
-    ex = None
-    if side_stream is not None:
-        ex = lmoe_exec(int(side_stream), fork_event and int(fork_event),
-                       join_event and int(join_event))
+    ex = _exec(side_stream, fork_event, join_event, stage_events)
     code = _lib.lmoe_forward_ex(ctypes.byref(d), _ptr(x), ctypes.byref(w),
                                 int(bool(logits_given)),
                                 ctypes.byref(r) if r is not None else None, _ptr(out), _ptr(ws),
@@ -221,6 +267,42 @@ def forward_noalloc(dims, x, weights: Mapping, logits_given: bool, routing: Opti
                                      ctypes.byref(r) if r is not None else None, _ptr(out),
                                      _stream(stream))
     _check("lmoe_forward_noalloc", code)
+
+
+def packed_sizes(dims) -> dict:
+    """Bytes of each tile-packed routed-expert array (PACKED_KEYS)."""
+    d = _dims(dims)
+    z = lmoe_packed_sizes()
+    _check("lmoe_packed_sizes_of", _lib.lmoe_packed_sizes_of(ctypes.byref(d), ctypes.byref(z)))
+    return {k: int(getattr(z, k)) for k in PACKED_KEYS}
+
+
+def pack_weights(dims, weights: Mapping, packed: Mapping, stream=None) -> None:
+    """Repack the routed experts of `weights` (row-major) into the uint8
+    device tensors packed[k] for k in PACKED_KEYS (packed_sizes bytes)."""
+    d = _dims(dims)
+    w = _weights(weights)
+    code = _lib.lmoe_pack_weights(ctypes.byref(d), ctypes.byref(w),
+                                  *[_ptr(packed[k]) for k in PACKED_KEYS], _stream(stream))
+    _check("lmoe_pack_weights", code)
+
+
+def forward_packed(dims, x, weights: Mapping, logits_given: bool, routing: Optional[Mapping],
+                   out, ws, side_stream=None, fork_event=None, join_event=None,
+                   stream=None, stage_events=None) -> None:
+    """forward_ex() on tile-packed routed experts: `weights` holds router_w,
+    the PACKED_KEYS arrays and the shared-expert tensors."""
+    d = _dims(dims)
+    r = _routing(routing)
+    w = lmoe_packed_weights(*[_ptr(weights.get(n)) for n, _ in lmoe_packed_weights._fields_])
+    ex = _exec(side_stream, fork_event, join_event, stage_events)
+    code = _lib.lmoe_forward_packed(ctypes.byref(d), _ptr(x), ctypes.byref(w),
+                                    int(bool(logits_given)),
+                                    ctypes.byref(r) if r is not None else None, _ptr(out),
+                                    _ptr(ws), ws.numel() * ws.element_size() if ws is not None
+                                    else 0, _stream(stream),
+                                    ctypes.byref(ex) if ex is not None else None)
+    _check("lmoe_forward_packed", code)
 
 
 def wait_errors(ws, count, stream=None) -> None:

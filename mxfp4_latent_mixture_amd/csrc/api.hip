@@ -56,6 +56,14 @@ Plan make_plan(const lmoe_dims& d) {
   return p;
 }
 
+Plan make_packed_plan(const lmoe_dims& d) {
+  Plan p = make_plan(d);
+  p.rows_per_tile = kPackedRows;
+  p.max_tiles = std::min(d.E, p.R) + p.R / p.rows_per_tile;
+  p.fused_decode = false;
+  return p;
+}
+
 Workspace carve_workspace(const Plan& p, void* base) {
   const lmoe_dims& d = p.d;
   Workspace w = {};
@@ -276,29 +284,50 @@ struct SideExec {
 
 enum class SideMode { kLibrary, kCaller };
 
+// pk: the tile-packed routed weights (lmoe_forward_packed), whose gate/up
+// and down pointers replace wts' (which then carries router and shared ones).
 static int forward_impl(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights* wts,
                         int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
                         size_t ws_bytes, void* stream, const hipEvent_t* ev, SideMode mode,
-                        const lmoe_exec* exec) {
+                        const lmoe_exec* exec, const PackedWeights* pk = nullptr) {
   if (!dims || !wts) return LMOE_ERR_NULL;
   if (!dims_ok(*dims)) return LMOE_ERR_SHAPE;
   int st = check_routing(r, logits_given);
   if (st) return st;
-  if (mode == SideMode::kCaller && exec && exec->side_stream &&
-      (!exec->fork_event || !exec->join_event))
+  hipEvent_t exec_ev[LMOE_NUM_STAGE_EVENTS];
+  if (mode == SideMode::kCaller && exec && exec->stage_events) {
+    if (ev) return LMOE_ERR_NULL;
+    for (int i = 0; i < LMOE_NUM_STAGE_EVENTS; ++i) {
+      if (!exec->stage_events[i]) return LMOE_ERR_NULL;
+      exec_ev[i] = static_cast<hipEvent_t>(exec->stage_events[i]);
+    }
+    ev = exec_ev;
+  } else if (mode == SideMode::kCaller && exec && exec->side_stream &&
+             (!exec->fork_event || !exec->join_event)) {
     return LMOE_ERR_NULL;
+  }
   if (dims->T == 0) return LMOE_OK;
   const lmoe_weights& w = *wts;
   if (!x || !out || !ws) return LMOE_ERR_NULL;
   if (!logits_given && !w.router_w) return LMOE_ERR_NULL;
-  if (!w.gate_q || !w.gate_s || !w.up_q || !w.up_s || !w.down_q || !w.down_s)
+  if (pk) {
+    if (!pk->gu_q || !pk->gu_s || !pk->down_q || !pk->down_s) return LMOE_ERR_NULL;
+    const void* pp[] = {pk->gu_q, pk->gu_s, pk->down_q, pk->down_s};
+    for (const void* q : pp)
+      if (check_opt_ptr(q)) return LMOE_ERR_ALIGN;
+  } else if (!w.gate_q || !w.gate_s || !w.up_q || !w.up_s || !w.down_q || !w.down_s) {
     return LMOE_ERR_NULL;
+  }
   if (dims->S > 0 && (!w.sh_gate || !w.sh_up || !w.sh_down)) return LMOE_ERR_NULL;
   const void* ptrs[] = {x, out, ws, w.router_w, w.gate_q, w.gate_s, w.up_q,
                         w.up_s, w.down_q, w.down_s, w.sh_gate, w.sh_up, w.sh_down};
   for (const void* q : ptrs)
     if (check_opt_ptr(q)) return LMOE_ERR_ALIGN;
-  Plan p = make_plan(*dims);
+  // the packed GEMMs address activation rows with 32-bit element offsets
+  if (pk && ((int64_t)dims->T * dims->L >= (int64_t(1) << 32) ||
+             (int64_t)dims->T * dims->k * dims->I >= (int64_t(1) << 32)))
+    return LMOE_ERR_SHAPE;
+  Plan p = pk ? make_packed_plan(*dims) : make_plan(*dims);
   Workspace wsp = carve_workspace(p, ws);
   if (ws_bytes < wsp.bytes) return LMOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -321,10 +350,16 @@ static int forward_impl(const lmoe_dims* dims, const uint16_t* x, const lmoe_wei
       side.join = static_cast<hipEvent_t>(exec->join_event);
     }
   }
+  auto routed = [&](hipStream_t rs, const hipEvent_t* rev) {
+    return pk ? launch_routed_packed(p, x, *pk, wsp, rt.perm, rs, rev)
+              : launch_routed(p, x, w, wsp, rt.perm, rs, rev);
+  };
   if (!side.s) {
     st = run_route(p, wsp, x, w.router_w, logits_given, r, &rt, s, ev);
     if (st) return st;
-    hipError_t e = launch_experts(p, x, w, wsp, rt.perm, rt.inv, rt.w, out, s, ev);
+    hipError_t e = routed(s, ev);
+    if (e == hipSuccess) e = launch_shared(p, x, w, wsp, s, ev);
+    if (e == hipSuccess) e = launch_combine(p, wsp, rt.inv, rt.w, out, s, ev);
     return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
   }
   std::unique_lock<std::mutex> g;
@@ -335,7 +370,7 @@ static int forward_impl(const lmoe_dims* dims, const uint16_t* x, const lmoe_wei
       hipEventRecord(side.join, side.s) != hipSuccess)
     return LMOE_ERR_HIP;
   st = run_route(p, wsp, x, w.router_w, logits_given, r, &rt, s, nullptr);
-  hipError_t e = st ? hipSuccess : launch_routed(p, x, w, wsp, rt.perm, s, nullptr);
+  hipError_t e = st ? hipSuccess : routed(s, nullptr);
   // the join is waited for on every path, so no later call on s can reuse
   // the workspace before the shared experts are done with it
   if (hipStreamWaitEvent(s, side.join, 0) != hipSuccess) return LMOE_ERR_HIP;
@@ -434,6 +469,48 @@ extern "C" int lmoe_wait_errors(void* ws, size_t ws_bytes, int32_t* count, void*
   hipError_t e = launch_read_errors(static_cast<int32_t*>(ws), count,
                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
+}
+
+extern "C" int lmoe_packed_sizes_of(const lmoe_dims* dims, lmoe_packed_sizes* sizes) {
+  if (!dims || !sizes) return LMOE_ERR_NULL;
+  if (!dims_ok(*dims)) return LMOE_ERR_SHAPE;
+  const PackedSizes z = packed_sizes(*dims);
+  sizes->gu_q = z.gu_q;
+  sizes->gu_s = z.gu_s;
+  sizes->down_q = z.down_q;
+  sizes->down_s = z.down_s;
+  return LMOE_OK;
+}
+
+extern "C" int lmoe_pack_weights(const lmoe_dims* dims, const lmoe_weights* w, uint8_t* gu_q,
+                                 uint8_t* gu_s, uint8_t* down_q, uint8_t* down_s, void* stream) {
+  if (!dims || !w) return LMOE_ERR_NULL;
+  if (!dims_ok(*dims)) return LMOE_ERR_SHAPE;
+  if (!w->gate_q || !w->gate_s || !w->up_q || !w->up_s || !w->down_q || !w->down_s || !gu_q ||
+      !gu_s || !down_q || !down_s)
+    return LMOE_ERR_NULL;
+  const void* ptrs[] = {w->gate_q, w->gate_s, w->up_q, w->up_s, w->down_q, w->down_s,
+                        gu_q,      gu_s,      down_q,  down_s};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return LMOE_ERR_ALIGN;
+  hipError_t e = launch_pack(*dims, *w, gu_q, gu_s, down_q, down_s,
+                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
+}
+
+extern "C" int lmoe_forward_packed(const lmoe_dims* dims, const uint16_t* x,
+                                   const lmoe_packed_weights* w, int logits_given,
+                                   const lmoe_routing* r, uint16_t* out, void* ws,
+                                   size_t ws_bytes, void* stream, const lmoe_exec* exec) {
+  if (!w) return LMOE_ERR_NULL;
+  lmoe_weights cw = {};
+  cw.router_w = w->router_w;
+  cw.sh_gate = w->sh_gate;
+  cw.sh_up = w->sh_up;
+  cw.sh_down = w->sh_down;
+  PackedWeights pk = {w->gu_q, w->gu_s, w->down_q, w->down_s};
+  return forward_impl(dims, x, &cw, logits_given, r, out, ws, ws_bytes, stream, nullptr,
+                      SideMode::kCaller, exec, &pk);
 }
 
 extern "C" int lmoe_forward_traced(const lmoe_dims* dims, const uint16_t* x,

@@ -762,16 +762,6 @@ hipError_t launch_combine(const Plan& p, const Workspace& ws, const int32_t* inv
   return err;
 }
 
-hipError_t launch_experts(const Plan& p, const uint16_t* x, const lmoe_weights& w,
-                          const Workspace& ws, const int32_t* perm, const int32_t* inv,
-                          const float* topk_w, uint16_t* out, hipStream_t s,
-                          const hipEvent_t* ev) {
-  hipError_t err = launch_routed(p, x, w, ws, perm, s, ev);
-  if (err == hipSuccess) err = launch_shared(p, x, w, ws, s, ev);
-  if (err == hipSuccess) err = launch_combine(p, ws, inv, topk_w, out, s, ev);
-  return err;
-}
-
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* sc, int rows, int K, uint16_t* out,
                           hipStream_t s) {
   const int64_t n = (int64_t)rows * (K / 8);

@@ -96,7 +96,19 @@ struct DecodeArgs {
   size_t lds_bytes;    // dynamic LDS per workgroup
 };
 
+// Tile-packed routed weights (lmoe_pack_weights).
+struct PackedWeights {
+  const uint8_t *gu_q, *gu_s, *down_q, *down_s;
+};
+struct PackedSizes {
+  size_t gu_q, gu_s, down_q, down_s;
+};
+// Routes per row tile of the packed GEMMs (three 32-row MFMA tiles).
+constexpr int kPackedRows = 96;
+
 Plan make_plan(const lmoe_dims& d);
+// The plan of the packed path: 128-route row tiles.
+Plan make_packed_plan(const lmoe_dims& d);
 Workspace carve_workspace(const Plan& p, void* base);
 
 // ---- kernel launchers (route.hip) ----
@@ -115,10 +127,6 @@ hipError_t launch_permute(const Plan& p, const int32_t* idx, int32_t* counts, in
 // ---- kernel launchers (experts.hip) ----
 // ev: optional stage events (LMOE_NUM_STAGE_EVENTS entries), recorded after
 // each stage.
-hipError_t launch_experts(const Plan& p, const uint16_t* x, const lmoe_weights& w,
-                          const Workspace& ws, const int32_t* perm, const int32_t* inv,
-                          const float* topk_w, uint16_t* out, hipStream_t s,
-                          const hipEvent_t* ev);
 // its three parts: routed gate/up and down; the shared experts (they read
 // only x, so they may run beside the routing); the combine, which needs both
 hipError_t launch_routed(const Plan& p, const uint16_t* x, const lmoe_weights& w,
@@ -133,6 +141,14 @@ hipError_t launch_combine(const Plan& p, const Workspace& ws, const int32_t* inv
 inline hipError_t record_stage(const hipEvent_t* ev, int stage, hipStream_t s) {
   return ev ? hipEventRecord(ev[stage], s) : hipSuccess;
 }
+// ---- tile-packed experts (packed.hip) ----
+PackedSizes packed_sizes(const lmoe_dims& d);
+hipError_t launch_pack(const lmoe_dims& d, const lmoe_weights& w, uint8_t* gu_q, uint8_t* gu_s,
+                       uint8_t* dn_q, uint8_t* dn_s, hipStream_t s);
+hipError_t launch_routed_packed(const Plan& p, const uint16_t* x, const PackedWeights& w,
+                                const Workspace& ws, const int32_t* perm, hipStream_t s,
+                                const hipEvent_t* ev);
+
 // ---- single-token decode (decode.hip) ----
 void make_decode_args(const Plan& p, DecodeArgs& a);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, const hipEvent_t* ev);

@@ -1,0 +1,487 @@
+// Tile-packed MXFP4 experts: a one-time repack of the checkpoint's MXFP4
+// matrices into the order in which the grouped GEMMs read them, and those
+// GEMMs on 32x32x16 bf16 MFMA.
+//
+// The checkpoint keeps each expert matrix row-major with the E8M0 exponent
+// running along K (huggingface.co "Notes from an NVFP4 port of Kimi K3.1 Pro",
+// introduction, which likewise repacks the experts once at load time). A wave
+// of the GEMMs multiplies a 32-row weight tile: lane l supplies row l % 32 and
+// the K values 8 (l / 32) .. +7 of each MFMA step. Read from the row-major
+// layout, one 16-byte load per lane then touches 32 rows per instruction;
+// packed, every load instruction reads 1 KB contiguous and every exponent
+// load 512 bytes contiguous. The values are untouched: the same E2M1 codes
+// and E8M0 bytes, reordered (layout in include/lmoe.h, lmoe_pack_weights).
+//
+// Gate and up are interleaved in one packed matrix GU of 2I rows: packed
+// tile n holds gate rows 16n .. 16n+15 then up rows 16n .. 16n+15, so an
+// MFMA output tile carries g in columns 0..15 and u in columns 16..31 for the
+// same 16 intermediate columns, and the GLU needs one lane exchange.
+//
+// Per expert e and route r of token t (dev48.org "Kimi K3 on AMD Instinct GPUs
+// with TokenSpeed", section 4): h_r = bf16(silu(x_t Gq_e^T) * (x_t Uq_e^T)),
+// y_r = h_r Dq_e^T in fp32 (route partials summed in FP32, section 4.3).
+#include "lmoe_device.h"
+#include "lmoe_internal.h"
+
+namespace lmoe {
+
+// ---------------------------------------------------------------------------
+// Pack kernels
+// ---------------------------------------------------------------------------
+struct PackSrc {
+  const uint8_t* q0;  // matrix rows [N0][K/2]; GU: gate
+  const uint8_t* s0;  //             [N0][K/32]
+  const uint8_t* q1;  // GU: up (nullptr for a plain matrix)
+  const uint8_t* s1;
+  int64_t q_estride, s_estride;  // bytes per expert of q0 / s0 (and q1 / s1)
+  int N;                         // packed rows (GU: 2 I)
+  int K;
+  bool gu;
+};
+
+// Source row of packed row p: plain p; GU tile n = p / 32 holds gate rows
+// 16 n .. 16 n + 15, then up rows 16 n .. 16 n + 15.
+__device__ __forceinline__ void packed_source(const PackSrc& a, int e, int p, const uint8_t** q,
+                                              const uint8_t** s) {
+  int row = p, m = 0;
+  if (a.gu) {
+    const int n = p >> 5, r = p & 31;
+    m = r >> 4;
+    row = 16 * n + (r & 15);
+  }
+  const int64_t qrow = (int64_t)row * (a.K / 2), srow = (int64_t)row * (a.K / 32);
+  *q = (m ? a.q1 : a.q0) + e * a.q_estride + qrow;
+  *s = (m ? a.s1 : a.s0) + e * a.s_estride + srow;
+}
+
+// One thread per 16 bytes of packed codes: expert e, tile n, chunk c, half j,
+// lane l <- codes of packed row 32 n + l % 32, MX block 4 c + 2 (l / 32) + j.
+__global__ __launch_bounds__(256) void pack_codes_kernel(PackSrc a, int E, uint8_t* __restrict__ dst) {
+  const int N32 = (a.N + 31) / 32, K128 = (a.K + 127) / 128, nblk = a.K / 32;
+  const int64_t units = (int64_t)E * N32 * K128 * 128;
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int l = (int)(u & 63);
+  const int j = (int)((u >> 6) & 1);
+  int64_t rest = u >> 7;
+  const int c = (int)(rest % K128);
+  rest /= K128;
+  const int n = (int)(rest % N32);
+  const int e = (int)(rest / N32);
+  const int p = 32 * n + (l & 31);
+  const int blk = 4 * c + 2 * (l >> 5) + j;
+  u32x4_t v = zero16();
+  if (p < a.N && blk < nblk) {
+    const uint8_t *q, *s;
+    packed_source(a, e, p, &q, &s);
+    v = load16(q + blk * 16);
+  }
+  *reinterpret_cast<u32x4_t*>(dst + u * 16) = v;
+}
+
+// One thread per 8 bytes of packed exponents: expert e, tile n, window w of
+// four chunks, lane l <- byte b = exponent of packed row 32 n + l % 32, block
+// 4 (4 w + b / 2) + 2 (l / 32) + b % 2; 127 (a scale of 1) past the end.
+__global__ __launch_bounds__(256) void pack_scales_kernel(PackSrc a, int E, uint8_t* __restrict__ dst) {
+  const int N32 = (a.N + 31) / 32, K512 = (a.K + 511) / 512, nblk = a.K / 32;
+  const int64_t units = (int64_t)E * N32 * K512 * 64;
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int l = (int)(u & 63);
+  int64_t rest = u >> 6;
+  const int w = (int)(rest % K512);
+  rest /= K512;
+  const int n = (int)(rest % N32);
+  const int e = (int)(rest / N32);
+  const int p = 32 * n + (l & 31);
+  uint32_t lo = 0, hi = 0;
+  const uint8_t *q = nullptr, *s = nullptr;
+  if (p < a.N) packed_source(a, e, p, &q, &s);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int blk = 4 * (4 * w + b / 2) + 2 * (l >> 5) + (b & 1);
+    const uint32_t v = (p < a.N && blk < nblk) ? s[blk] : 127u;
+    if (b < 4)
+      lo |= v << (8 * b);
+    else
+      hi |= v << (8 * (b - 4));
+  }
+  *reinterpret_cast<uint2*>(dst + u * 8) = make_uint2(lo, hi);
+}
+
+PackedSizes packed_sizes(const lmoe_dims& d) {
+  PackedSizes z;
+  const int64_t gu32 = (2 * (int64_t)d.I + 31) / 32, dn32 = ((int64_t)d.L + 31) / 32;
+  z.gu_q = (size_t)d.E * gu32 * ((d.L + 127) / 128) * 2048;
+  z.gu_s = (size_t)d.E * gu32 * ((d.L + 511) / 512) * 512;
+  z.down_q = (size_t)d.E * dn32 * ((d.I + 127) / 128) * 2048;
+  z.down_s = (size_t)d.E * dn32 * ((d.I + 511) / 512) * 512;
+  return z;
+}
+
+hipError_t launch_pack(const lmoe_dims& d, const lmoe_weights& w, uint8_t* gu_q, uint8_t* gu_s,
+                       uint8_t* dn_q, uint8_t* dn_s, hipStream_t st) {
+  PackSrc g = {};
+  g.q0 = w.gate_q;
+  g.s0 = w.gate_s;
+  g.q1 = w.up_q;
+  g.s1 = w.up_s;
+  g.q_estride = (int64_t)d.I * d.L / 2;
+  g.s_estride = (int64_t)d.I * d.L / 32;
+  g.N = 2 * d.I;
+  g.K = d.L;
+  g.gu = true;
+  PackSrc dn = {};
+  dn.q0 = w.down_q;
+  dn.s0 = w.down_s;
+  dn.q_estride = (int64_t)d.L * d.I / 2;
+  dn.s_estride = (int64_t)d.L * d.I / 32;
+  dn.N = d.L;
+  dn.K = d.I;
+  dn.gu = false;
+  const PackSrc* srcs[2] = {&g, &dn};
+  uint8_t* qd[2] = {gu_q, dn_q};
+  uint8_t* sd[2] = {gu_s, dn_s};
+  for (int i = 0; i < 2; ++i) {
+    const PackSrc& a = *srcs[i];
+    const int64_t N32 = (a.N + 31) / 32;
+    const int64_t cu = (int64_t)d.E * N32 * ((a.K + 127) / 128) * 128;
+    hipLaunchKernelGGL(pack_codes_kernel, dim3((unsigned)((cu + 255) / 256)), dim3(256), 0, st, a,
+                       d.E, qd[i]);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t su = (int64_t)d.E * N32 * ((a.K + 511) / 512) * 64;
+    hipLaunchKernelGGL(pack_scales_kernel, dim3((unsigned)((su + 255) / 256)), dim3(256), 0, st,
+                       a, d.E, sd[i]);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM over packed weights: 32x32x16 bf16 MFMA.
+//
+// A workgroup covers one row tile of up to 96 routes of one expert (three
+// 32-row MFMA tiles) and eight packed 32-row weight tiles: gate/up 128
+// intermediate columns, down 256 output columns. Each of its four waves owns
+// two weight tiles over every row tile. K runs in chunks of 128 values: the
+// chunk's activation rows are copied into LDS by 16-byte global-to-LDS loads
+// (no registers), segments XOR-swizzled by row so the MFMA operand reads of
+// 16 rows hit distinct banks; the chunk's weights (two 1 KB loads per tile)
+// are loaded into registers one chunk ahead; two LDS buffers and one barrier
+// per chunk. Lane (r, h) = (l % 32, l / 32) takes, in chunk c, MX blocks
+// 4c + 2h and 4c + 2h + 1 (the packed order), so the A operand of MFMA step
+// (j, m) is activation segment 8h + 4j + m of the chunk row. Exponents come
+// one 8-byte load per tile per four chunks.
+// ---------------------------------------------------------------------------
+struct PkArgs {
+  const uint16_t* act;  // bf16 rows; row of sorted position p: gather ? gather[p] / div : p
+  int64_t act_stride;
+  const int32_t* gather;
+  int gather_div;
+  const int32_t* tiles;  // (expert, first sorted position, rows)
+  const int32_t* ntiles;
+  const uint8_t* q;      // packed codes / exponents of expert 0
+  const uint8_t* s;
+  int64_t q_estride, s_estride;
+  int N32;               // packed weight tiles per expert
+  int K, K128, K512;
+  int N;                 // output columns: GLU I, plain N rows
+  uint16_t* h_out;       // GLU: bf16 [rows][N]
+  float* y_out;          // plain: fp32 [rows][N]
+  int64_t out_stride;
+  int n_tiles_n;         // column workgroups per row tile
+};
+
+constexpr int kPkRows = 96;    // routes per row tile (three 32-row MFMA tiles)
+constexpr int kPkKc = 128;     // K values per chunk
+constexpr int kPkWaves = 4;    // waves per workgroup (two workgroups per CU)
+constexpr int kPkThreads = 64 * kPkWaves;
+constexpr int kPkNB = 2;       // weight tiles per wave
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// One array per LDS buffer: the compiler then tells a global-to-LDS copy into
+// one buffer from the MFMA operand reads of the other, and does not wait for
+// the copy before every read.
+template <int R>
+using PkChunk = uint16_t[R][kPkKc];
+
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <bool GLU, int MT>
+__device__ __forceinline__ void pk_body(const PkArgs& a, int e, int p0, int cnt, int nt,
+                                        PkChunk<kPkRows>& sx0, PkChunk<kPkRows>& sx1,
+                                        PkChunk<kPkRows>& sx2, const uint32_t* s_arow) {
+  auto slot = [&](int r) -> PkChunk<kPkRows>& { return r == 0 ? sx0 : r == 1 ? sx1 : sx2; };
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int r32 = lane & 31, hh = lane >> 5;
+  // this wave's weight tiles (clamped: tiles past the matrix read the last
+  // one, their columns are never stored)
+  int bt[kPkNB];
+  const uint8_t* qb[kPkNB];
+  const uint8_t* sb[kPkNB];
+#pragma unroll
+  for (int t = 0; t < kPkNB; ++t) {
+    bt[t] = (nt * kPkWaves + wave) * kPkNB + t;
+    const int btc = min(bt[t], a.N32 - 1);
+    qb[t] = a.q + e * a.q_estride + (int64_t)btc * a.K128 * 2048 + lane * 16;
+    sb[t] = a.s + e * a.s_estride + (int64_t)btc * a.K512 * 512 + lane * 8;
+  }
+  f32x16_t acc[MT][kPkNB];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int t = 0; t < kPkNB; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][t][i] = 0.f;
+
+  constexpr int kCopies = MT * 32 / 4 / kPkWaves;  // copy instructions per wave and chunk
+  static_assert(kCopies * 4 * kPkWaves == MT * 32, "rows shared evenly by the waves");
+  // activation chunk c (clamped to the last) into LDS buffer `buf`: the
+  // MT * 32 rows are shared by the waves, four rows per instruction (every
+  // wave issues the same number, so the waits below count the same loads in
+  // every wave); lane l moves the 16-byte segment at physical slot l % 16 of
+  // row l / 16, which holds logical segment (l % 16) ^ (row % 16)
+  auto copy_x = [&](int c, int buf) {
+    const int cc = min(c, a.K128 - 1);
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) {
+      const int row0 = wave * kCopies * 4 + i * 4;
+      const int row = row0 + (lane >> 4);
+      const int seg = (lane & 15) ^ (row & 15);
+      const int k = min(cc * kPkKc + seg * 8, a.K - 8);
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(a.act + s_arow[row] + k),
+          (__attribute__((address_space(3))) void*)(&slot(buf)[row0][0]), 16, 0, 0);
+    }
+  };
+  struct Bq {
+    u32x4_t q[kPkNB][2];
+  };
+  auto load_b = [&](int c, Bq& b) {
+    const int cc = min(c, a.K128 - 1);
+#pragma unroll
+    for (int t = 0; t < kPkNB; ++t)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b.q[t][j] = load16(qb[t] + (int64_t)cc * 2048 + j * 1024);
+  };
+  // the exponents of chunk c: the dword of its window (four chunks) that
+  // holds them, bytes 2 (c % 2) + j
+  auto load_ex = [&](int c, uint32_t (&dst)[kPkNB]) {
+    const int cc = min(c, a.K128 - 1);
+#pragma unroll
+    for (int t = 0; t < kPkNB; ++t)
+      dst[t] = *reinterpret_cast<const uint32_t*>(sb[t] + (cc / 4) * 512 + 4 * ((cc >> 1) & 1));
+  };
+  auto compute = [&](int c, int buf, const Bq& b, const uint32_t (&ex)[kPkNB]) {
+    // blocks past K are packed as zero codes with exponent 127: zeros
+    float scale[kPkNB][2];
+#pragma unroll
+    for (int t = 0; t < kPkNB; ++t)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        scale[t][j] = e8m0_to_f32((ex[t] >> (8 * (2 * (c & 1) + j))) & 0xffu);
+    // step st = 4 j + m of the chunk; the operands of step st + 1 (LDS
+    // reads and dequantisation) are prepared while step st multiplies
+    bf16x8_t av[2][MT], bv[2][kPkNB];
+    auto prep = [&](int st, bf16x8_t (&a_)[MT], bf16x8_t (&b_)[kPkNB]) {
+      const int j = st >> 2, m = st & 3;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = mt * 32 + r32;
+        const int phys = (8 * hh + 4 * j + m) ^ (row & 15);
+        a_[mt] = *reinterpret_cast<const bf16x8_t*>(&slot(buf)[row][phys * 8]);
+      }
+#pragma unroll
+      for (int t = 0; t < kPkNB; ++t) b_[t] = dequant8(b.q[t][j][m], scale[t][j]);
+    };
+    // Each step's MFMAs are issued first; the next step's reads and
+    // conversions follow in their shadow (the scheduling barriers keep the
+    // compiler from moving each read next to its first use, which exposed
+    // the LDS latency).
+    prep(0, av[0], bv[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < kPkNB; ++t)
+          acc[mt][t] = mfma32(av[st & 1][mt], bv[st & 1][t], acc[mt][t]);
+      if (st < 7) prep(st + 1, av[(st + 1) & 1], bv[(st + 1) & 1]);
+      // interleave: after each of the first MT MFMAs one operand read of the
+      // next step, after each of the others a share of its conversions
+#pragma unroll
+      for (int i = 0; i < MT * kPkNB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if (i < MT)
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        else
+          __builtin_amdgcn_sched_group_barrier(0x002, (8 * kPkNB / 2 + MT - 1) / MT, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Activations (in a ring of three LDS buffers) and weights (in a ring of
+  // three register buffers) stay two chunks ahead, the exponents one. In
+  // chunk c the loads are issued in the order exponents (c + 1), activations
+  // (c + 2), weights (c + 2); so at the top of chunk c + 1, waiting until at
+  // most the loads of chunk c + 2 are outstanding (vector memory
+  // loads complete in issue order) leaves everything chunk c + 1 needs
+  // landed while the next chunk's loads stay in flight across the barrier.
+  // Groups of three chunks are unrolled so ring slots are fixed registers and
+  // buffers; the first group runs before the loop (both edges into the loop
+  // then carry the same loads in flight, which keeps the compiler's waits
+  // exact) and a last, partial group after it.
+  constexpr int U = 3;
+  constexpr int kAhead = kCopies + 2 * kPkNB;        // loads of chunk c + 2
+  constexpr int kWaitAhead = 0x0F70 | kAhead;        // vmcnt(kAhead)
+  static_assert(kAhead < 16, "vmcnt field");
+  __syncthreads();  // s_arow
+  Bq bq[U];
+  uint32_t ex[kPkNB], ex_next[kPkNB];
+  load_ex(0, ex_next);
+  copy_x(0, 0);
+  load_b(0, bq[0]);
+  copy_x(1, 1);
+  load_b(1, bq[1]);
+  auto group = [&](int cb, bool last) {
+#pragma unroll
+    for (int r = 0; r < U; ++r) {
+      const int c = cb + r;
+      __builtin_amdgcn_s_waitcnt(kWaitAhead);
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int t = 0; t < kPkNB; ++t) ex[t] = ex_next[t];
+      load_ex(c + 1, ex_next);
+      copy_x(c + 2, (r + 2) % U);
+      load_b(c + 2, bq[(r + 2) % U]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (!last || c < a.K128) compute(c, r, bq[r], ex);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const int full = a.K128 / U;  // whole groups
+  if (full > 0) group(0, false);
+  for (int g = 1; g < full; ++g) group(g * U, false);
+  if (a.K128 % U) group(full * U, true);
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // output slot i of lane l: row 8 (i / 4) + 4 (l / 32) + i % 4 of the MFMA
+  // tile, column l % 32
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < kPkNB; ++t) {
+      if (bt[t] >= a.N32) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = mt * 32 + 8 * (i / 4) + 4 * hh + (i & 3);
+        const float v = acc[mt][t][i];
+        if constexpr (GLU) {
+          // column c < 16: gate of intermediate column 16 bt + c; up from
+          // lane + 16
+          const float u = __shfl_down(v, 16, kWave);
+          const int col = bt[t] * 16 + r32;
+          if (r32 < 16 && row < cnt && col < a.N)
+            a.h_out[(int64_t)(p0 + row) * a.out_stride + col] = f32_to_bf16_bits(silu(v) * u);
+        } else {
+          const int col = bt[t] * 32 + r32;
+          if (row < cnt && col < a.N) a.y_out[(int64_t)(p0 + row) * a.out_stride + col] = v;
+        }
+      }
+    }
+}
+
+template <bool GLU>
+__global__ __launch_bounds__(kPkThreads, 8 / kPkWaves) void gemm_packed_kernel(PkArgs a) {
+  __shared__ __attribute__((aligned(16))) PkChunk<kPkRows> sx0, sx1, sx2;
+  __shared__ uint32_t s_arow[kPkRows];  // element offset of each row in act
+  // XCD-aware order: workgroup i runs on XCD i % 8; the column workgroups of
+  // one row tile go to one XCD, so its activation rows are fetched into that
+  // L2 once
+  const int b = blockIdx.x;
+  const int s = b / 8;
+  const int nt = s % a.n_tiles_n;
+  const int tile = (s / a.n_tiles_n) * 8 + b % 8;
+  if (tile >= *a.ntiles) return;
+  const int e = __builtin_amdgcn_readfirstlane(a.tiles[3 * tile + 0]);
+  const int p0 = __builtin_amdgcn_readfirstlane(a.tiles[3 * tile + 1]);
+  const int cnt = __builtin_amdgcn_readfirstlane(a.tiles[3 * tile + 2]);
+  // rows past the tile repeat its last row: finite values, never stored
+  for (int r = threadIdx.x; r < kPkRows; r += kPkThreads) {
+    const int p = p0 + min(r, cnt - 1);
+    const int64_t row = a.gather ? (int64_t)(a.gather[p] / a.gather_div) : (int64_t)p;
+    s_arow[r] = (uint32_t)(row * a.act_stride);  // < 2^32: checked on the host
+  }
+  switch ((cnt + 31) / 32) {
+    case 1: pk_body<GLU, 1>(a, e, p0, cnt, nt, sx0, sx1, sx2, s_arow); break;
+    case 2: pk_body<GLU, 2>(a, e, p0, cnt, nt, sx0, sx1, sx2, s_arow); break;
+    default: pk_body<GLU, 3>(a, e, p0, cnt, nt, sx0, sx1, sx2, s_arow); break;
+  }
+}
+
+hipError_t launch_routed_packed(const Plan& p, const uint16_t* x, const PackedWeights& w,
+                                const Workspace& ws, const int32_t* perm, hipStream_t s,
+                                const hipEvent_t* ev) {
+  const lmoe_dims& d = p.d;
+  const int rounds = (p.max_tiles + 7) / 8;
+  hipError_t err;
+  {  // gate/up + GLU
+    PkArgs a = {};
+    a.act = x;
+    a.act_stride = d.L;
+    a.gather = perm;
+    a.gather_div = d.k;
+    a.tiles = ws.tiles;
+    a.ntiles = ws.ntiles;
+    a.q = w.gu_q;
+    a.s = w.gu_s;
+    a.N32 = (2 * d.I + 31) / 32;
+    a.K = d.L;
+    a.K128 = (d.L + 127) / 128;
+    a.K512 = (d.L + 511) / 512;
+    a.q_estride = (int64_t)a.N32 * a.K128 * 2048;
+    a.s_estride = (int64_t)a.N32 * a.K512 * 512;
+    a.N = d.I;
+    a.h_out = ws.h;
+    a.out_stride = d.I;
+    a.n_tiles_n = (a.N32 + kPkWaves * kPkNB - 1) / (kPkWaves * kPkNB);
+    hipLaunchKernelGGL(gemm_packed_kernel<true>, dim3((unsigned)(rounds * 8 * a.n_tiles_n)),
+                       dim3(kPkThreads), 0, s, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = record_stage(ev, LMOE_STAGE_GATEUP, s)) != hipSuccess) return err;
+  }
+  {  // down
+    PkArgs a = {};
+    a.act = ws.h;
+    a.act_stride = d.I;
+    a.tiles = ws.tiles;
+    a.ntiles = ws.ntiles;
+    a.q = w.down_q;
+    a.s = w.down_s;
+    a.N32 = (d.L + 31) / 32;
+    a.K = d.I;
+    a.K128 = (d.I + 127) / 128;
+    a.K512 = (d.I + 511) / 512;
+    a.q_estride = (int64_t)a.N32 * a.K128 * 2048;
+    a.s_estride = (int64_t)a.N32 * a.K512 * 512;
+    a.N = d.L;
+    a.y_out = ws.y;
+    a.out_stride = d.L;
+    a.n_tiles_n = (a.N32 + kPkWaves * kPkNB - 1) / (kPkWaves * kPkNB);
+    hipLaunchKernelGGL(gemm_packed_kernel<false>, dim3((unsigned)(rounds * 8 * a.n_tiles_n)),
+                       dim3(kPkThreads), 0, s, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    err = record_stage(ev, LMOE_STAGE_DOWN, s);
+  }
+  return err;
+}
+
+}  // namespace lmoe

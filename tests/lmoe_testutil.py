@@ -50,8 +50,21 @@ def alloc_routing(d, dev) -> Dict[str, object]:
     }
 
 
-def run_forward(lm, w: Workload, dev_inp: Dict[str, object], routing: Optional[dict] = None):
-    """Run lmoe_forward; returns (out bf16 bits numpy, routing dict of numpy)."""
+def pack_on_device(lm, d, dev_inp: Dict[str, object]) -> Dict[str, object]:
+    """The routed experts of dev_inp repacked by lmoe_pack_weights."""
+    import torch
+    dev = dev_inp["x"].device
+    pk = {k: torch.empty(n, dtype=torch.uint8, device=dev)
+          for k, n in lm.packed_sizes(d).items()}
+    lm.pack_weights(d, dev_inp, pk)
+    return pk
+
+
+def run_forward(lm, w: Workload, dev_inp: Dict[str, object], routing: Optional[dict] = None,
+                packed: bool = False):
+    """Run lmoe_forward (or, packed, lmoe_pack_weights then
+    lmoe_forward_packed); returns (out bf16 bits numpy, routing dict of
+    numpy)."""
     import torch
     d = w.dims
     dev = dev_inp["x"].device
@@ -61,7 +74,11 @@ def run_forward(lm, w: Workload, dev_inp: Dict[str, object], routing: Optional[d
         routing["logits"] = dev_inp["logits"]
     out = torch.empty((d.T, d.L), dtype=torch.int16, device=dev)
     ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
-    lm.forward(d, dev_inp["x"], dev_inp, w.logits_given, routing, out, ws)
+    if packed:
+        pk = pack_on_device(lm, d, dev_inp)
+        lm.forward_packed(d, dev_inp["x"], {**dev_inp, **pk}, w.logits_given, routing, out, ws)
+    else:
+        lm.forward(d, dev_inp["x"], dev_inp, w.logits_given, routing, out, ws)
     torch.cuda.synchronize()
     res = {k: v.cpu().numpy() for k, v in routing.items()}
     return out.cpu().numpy().view(np.uint16), res

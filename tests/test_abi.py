@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
     names = _declared()
     assert names == sorted(["lmoe_workspace_bytes", "lmoe_route", "lmoe_forward",
                             "lmoe_forward_ex", "lmoe_forward_traced", "lmoe_wait_errors",
-                            "lmoe_forward_noalloc",
+                            "lmoe_forward_noalloc", "lmoe_packed_sizes_of",
+                            "lmoe_pack_weights", "lmoe_forward_packed",
                             "lmoe_stage_name", "lmoe_path_name",
                             "lmoe_debug_dequant_mxfp4", "lmoe_status_string"]), names
 
@@ -178,8 +179,10 @@ def test_forward_ex_rejects_bad_arguments(lm):
     d = lm._dims(K3)
     w = _weights(lm)
     f = lm._lib.lmoe_forward_ex
-    # a side stream without its fork or join event
-    for ex in (lm.lmoe_exec(0x1000, None, 0x3000), lm.lmoe_exec(0x1000, 0x2000, None)):
+    # a side stream without its fork or join event; a missing stage event
+    ev = (ctypes.c_void_p * lm.NUM_STAGE_EVENTS)(*([0x1000] * (lm.NUM_STAGE_EVENTS - 1) + [0]))
+    traced = lm.lmoe_exec(None, None, None, ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)))
+    for ex in (lm.lmoe_exec(0x1000, None, 0x3000), lm.lmoe_exec(0x1000, 0x2000, None), traced):
         assert f(ctypes.byref(d), 0x20000000, ctypes.byref(w), 0, None, 0x30000000, 0x40000000,
                  1 << 40, None, ctypes.byref(ex)) == lm.LMOE_ERR_NULL
         d0 = lm._dims((0,) + K3[1:])
@@ -224,6 +227,50 @@ def test_header_scratch_size_matches_binding(lm):
     text = open(HEADER).read()
     m = re.search(r"#define LMOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == lm.NOALLOC_SCRATCH_BYTES
+
+
+def test_packed_sizes(lm):
+    z = lm.packed_sizes(K3)
+    # Kimi-K3 widths need no padding: the packed arrays hold exactly the
+    # row-major bytes
+    assert z["gu_q"] == 896 * 2 * 2048 * 3584 // 2
+    assert z["down_q"] == 896 * 3584 * 2048 // 2
+    assert z["gu_s"] == 896 * 2 * 2048 * 3584 // 32
+    assert z["down_s"] == 896 * 3584 * 2048 // 32
+    # ragged widths pad rows to 32 and K to 128 (codes) / 512 (exponents)
+    z = lm.packed_sizes((1, 416, 48, 6, 352, 2, 224))
+    assert z["gu_q"] == 48 * (704 // 32) * 4 * 2048
+    assert z["down_q"] == 48 * 13 * 3 * 2048
+    with pytest.raises(lm.LmoeError):
+        lm.packed_sizes((1, 3583, 896, 16, 2048, 2, 2048))
+
+
+def test_pack_and_forward_packed_reject_bad_arguments(lm):
+    d = lm._dims(K3)
+    w = _weights(lm)
+    f = lm._lib.lmoe_pack_weights
+    P = (0x50000000, 0x51000000, 0x52000000, 0x53000000)
+    assert f(None, ctypes.byref(w), *P, None) == lm.LMOE_ERR_NULL
+    assert f(ctypes.byref(d), ctypes.byref(w), None, *P[1:], None) == lm.LMOE_ERR_NULL
+    assert f(ctypes.byref(d), ctypes.byref(w), P[0] + 8, *P[1:], None) == lm.LMOE_ERR_ALIGN
+    bad = lm._dims((1, 3583, 896, 16, 2048, 2, 2048))
+    assert f(ctypes.byref(bad), ctypes.byref(w), *P, None) == lm.LMOE_ERR_SHAPE
+    g = lm._lib.lmoe_forward_packed
+    pw = lm.lmoe_packed_weights(0x10000000, *P, 0x11000000, 0x12000000, 0x13000000)
+    assert g(ctypes.byref(d), 0x20000000, None, 0, None, 0x30000000, 0x40000000, 1 << 40,
+             None, None) == lm.LMOE_ERR_NULL
+    pw0 = lm.lmoe_packed_weights(0x10000000, None, *P[1:], 0x11000000, 0x12000000, 0x13000000)
+    assert g(ctypes.byref(d), 0x20000000, ctypes.byref(pw0), 0, None, 0x30000000, 0x40000000,
+             1 << 40, None, None) == lm.LMOE_ERR_NULL
+    pw1 = lm.lmoe_packed_weights(0x10000000, P[0] + 4, *P[1:], 0x11000000, 0x12000000,
+                                 0x13000000)
+    assert g(ctypes.byref(d), 0x20000000, ctypes.byref(pw1), 0, None, 0x30000000, 0x40000000,
+             1 << 40, None, None) == lm.LMOE_ERR_ALIGN
+    assert g(ctypes.byref(d), 0x20000000, ctypes.byref(pw), 0, None, 0x30000000, 0x40000000,
+             lm.workspace_bytes(K3) - 1, None, None) == lm.LMOE_ERR_WORKSPACE
+    d0 = lm._dims((0,) + K3[1:])
+    assert g(ctypes.byref(d0), None, ctypes.byref(pw), 0, None, None, None, 0, None,
+             None) == lm.LMOE_OK
 
 
 def test_wait_errors_rejects_bad_arguments(lm):

@@ -18,6 +18,8 @@ from workloads.configs import Dims, Workload
 from lmoe_testutil import (log, to_dev, upload, alloc_routing, run_forward, check_out,
                            logits_bound, check_routing_against_oracle, check_routing_exact,
                            flip_allowance_fn)
+from lmoe_layer_checks import full_small as _full_small, full_size as _full_size, \
+    every_token_isolated as _every_token_isolated
 
 pytestmark = pytest.mark.gpu
 
@@ -130,33 +132,6 @@ def test_route_given_logits_skewed_full(lm, dev):
 # Whole layer on small shapes: every token
 # ----------------------------------------------------------------------------
 
-def _full_small(lm, dev, w: Workload):
-    """Every token of a layer small enough for the whole oracle. Outputs are
-    compared with the oracle run on the routing the GPU took: the given
-    logits, or the GPU's own computed logits once they are shown within the
-    summation bound and the oracle's routing on them equals the GPU's."""
-    d = w.dims
-    inp = gen_all(w)
-    dinp = upload(inp, dev)
-    got, r = run_forward(lm, w, dinp)
-    if w.logits_given:
-        lg = inp["logits"]
-        check_routing_exact(r, lg, d.k, w.name)
-    else:
-        ref_lg = O.router_logits(inp["x"], inp["router_w"])
-        same = check_routing_against_oracle(r["topk_idx"], r["logits"], ref_lg,
-                                            logits_bound(inp["x"], inp["router_w"]), d.k, w.name)
-        assert same.mean() >= 0.9
-        lg = r["logits"]
-        check_routing_exact(r, lg, d.k, f"{w.name} (on the GPU logits)")
-    ref = O.forward(inp["x"], None, inp, inp, d.k, logits=lg)
-    get = lambda e: {key: inp[key][e] for key in ("gate_q", "gate_s", "up_q", "up_s",
-                                                   "down_q", "down_s")}
-    check_out(got, ref["out64"], f"{w.name} T={d.T}",
-              allowance_fn=flip_allowance_fn(inp["x"], ref["idx"], ref["w"], get, inp, d.L, d.I))
-    return got
-
-
 @pytest.mark.parametrize("name", ["tiny", "ragged", "ragged_prefill", "ragged_skew"])
 def test_forward_small_workloads(lm, dev, name):
     _full_small(lm, dev, get_workload(name))
@@ -244,56 +219,6 @@ def test_zero_tokens_is_noop(lm, dev):
 # but a few experts silenced (below).
 # ----------------------------------------------------------------------------
 
-def _check_full_routing(w: Workload, inp, r):
-    """Routing checks of a full-size call; returns (idx, weights) the outputs
-    are compared with and the mask of tokens whose sets agree with the
-    oracle's logits."""
-    d = w.dims
-    if w.logits_given:
-        lg = inp["logits"]
-        check_routing_exact(r, lg, d.k, w.name)
-        same = np.ones(d.T, bool)
-    else:
-        log(f"{w.name}: oracle logits")
-        ref_lg = O.router_logits(inp["x"], inp["router_w"])
-        same = check_routing_against_oracle(r["topk_idx"], r["logits"], ref_lg,
-                                            logits_bound(inp["x"], inp["router_w"]), d.k,
-                                            w.name)
-        assert same.mean() >= 0.99
-        # the oracle's routing steps on the GPU's own logits: bit-exact
-        lg = r["logits"]
-        check_routing_exact(r, lg, d.k, f"{w.name} (on the GPU logits)")
-    idx = O.topk_select(lg, d.k)
-    return idx, O.softmax_selected(lg, idx), same
-
-
-def _full_size(lm, dev, w: Workload, n_sample):
-    import torch
-    d = w.dims
-    log(f"{w.name}: generating inputs (T={d.T}, E={d.E}, L={d.L}, I={d.I})")
-    inp = gen_all(w)
-    dinp = upload(inp, dev)
-    for key in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s"):
-        del inp[key]                      # experts are regenerated per expert below
-    log(f"{w.name}: running lmoe_forward")
-    got, r = run_forward(lm, w, dinp)
-    del dinp
-    torch.cuda.empty_cache()
-    idx, wts, same = _check_full_routing(w, inp, r)
-    rng = np.random.default_rng(99)
-    cand = np.nonzero(same)[0]
-    toks = list(rng.choice(cand, size=min(n_sample, cand.size), replace=False))
-    if w.logits_given:
-        tied = [t for t in cand if (inp["logits"][t] == inp["logits"][t].max()).sum() > d.k]
-        toks = sorted(set(toks[: max(1, n_sample - 1)]) | {tied[0]})
-    toks = sorted(int(t) for t in toks)
-    log(f"{w.name}: oracle on tokens {toks}")
-    get = lambda e: gen_expert(w, e)
-    o64, _ = O.forward_tokens(inp["x"], idx, wts, get, inp, d.L, d.I, toks)
-    check_out(got[toks], o64, f"{w.name} sampled tokens", rows=np.array(toks),
-              allowance_fn=flip_allowance_fn(inp["x"], idx, wts, get, inp, d.L, d.I))
-
-
 def test_full_decode(lm, dev):
     _full_size(lm, dev, get_workload("decode"), 1)
 
@@ -342,55 +267,6 @@ def test_full_decode_tp8(lm, dev):
 # expert (every one of its tokens checked, over all of its row tiles), the
 # coldest non-empty one, and one whose group just passes a 96-row tile.
 # ----------------------------------------------------------------------------
-
-def _every_token_isolated(lm, dev, w: Workload):
-    import torch
-    d = w.dims
-    log(f"{w.name}: generating inputs (T={d.T}, E={d.E}, L={d.L}, I={d.I})")
-    inp = gen_all(w)
-    dinp = upload(inp, dev)
-    for key in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s"):
-        del inp[key]
-    # routing first (it does not read the expert weights)
-    r0 = alloc_routing(d, dev)
-    if w.logits_given:
-        r0["logits"] = dinp["logits"]
-    ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
-    lm.route(d, dinp["x"], dinp["router_w"], w.logits_given, r0, ws)
-    torch.cuda.synchronize()
-    counts = r0["counts"].cpu().numpy()
-    order = np.argsort(-counts, kind="stable")
-    hot = int(order[0])
-    cold = int(order[np.nonzero(counts[order] > 0)[0][-1]])
-    past = np.nonzero((counts > 96) & (counts <= 120))[0]
-    keep = sorted({hot, cold} | ({int(past[0])} if past.size else set()))
-    log(f"{w.name}: kept experts {keep} with {counts[keep].tolist()} routes")
-    mask = torch.ones(d.E, dtype=torch.bool, device=dev)
-    mask[keep] = False
-    dinp["gate_q"].view(d.E, -1)[mask] = 0
-    got, r = run_forward(lm, w, dinp)
-    del dinp, ws
-    torch.cuda.empty_cache()
-    assert np.array_equal(r["topk_idx"], r0["topk_idx"].cpu().numpy())
-    idx, wts, _ = _check_full_routing(w, inp, r)
-    x64 = O.f64_from_bf16(inp["x"])
-    y = np.zeros((d.T, d.k, d.L), np.float64)
-    for e in keep:
-        ex = gen_expert(w, e)
-        rows, slots = np.nonzero(idx == e)
-        gate = O.dequant_mxfp4(ex["gate_q"], ex["gate_s"], d.I, d.L)
-        up = O.dequant_mxfp4(ex["up_q"], ex["up_s"], d.I, d.L)
-        down = O.dequant_mxfp4(ex["down_q"], ex["down_s"], d.L, d.I)
-        _, y[rows, slots] = O.glu_ffn(x64[rows], gate, up, down)
-    ysh = np.stack([O.glu_ffn(x64, O.f64_from_bf16(inp["sh_gate"][s]),
-                              O.f64_from_bf16(inp["sh_up"][s]),
-                              O.f64_from_bf16(inp["sh_down"][s]))[1] for s in range(d.S)])
-    o64, _ = O.combine(y, wts, ysh)
-    del y
-    check_out(got, o64, f"{w.name} every token ({len(keep)} experts kept)",
-              allowance_fn=flip_allowance_fn(inp["x"], idx, wts, lambda e: gen_expert(w, e), inp,
-                                             d.L, d.I, experts=set(keep)))
-
 
 @pytest.mark.parametrize("name", ["prefill", "skewed", "batched_decode"])
 def test_full_every_token_isolated(lm, dev, name):
