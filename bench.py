@@ -145,7 +145,11 @@ def stage_kernel(stage: str, large: bool, sh_large: bool, d=None, logits_given=F
 # hash of these files, so a change elsewhere does not discard it.
 KERNEL_SOURCES = {
     "decode_kernel": "decode.hip",
-    "gemm_": "experts.hip",
+    "gemm_packed": "packed.hip",
+    "pack_": "packed.hip",
+    "read_stream": "experts.hip",
+    "gemm_large": "experts.hip",
+    "gemm_small": "experts.hip",
     "router_kernel": "route.hip",
     "topk_kernel": "route.hip",
     "chunk_": "route.hip",
@@ -168,15 +172,72 @@ def sources_sha(kernel: str = None) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed PMC summary, or None
-    when absent or taken on different sources of that kernel."""
+def kernel_short_name(name: str) -> str:
+    """rocprofv3's kernel name without 'void', namespace and arguments."""
+    return name.replace("void ", "").replace("lmoe::", "").split("(")[0]
+
+
+def traffic_from(pmc_dir: str, workload: str) -> dict:
+    """Merge into profiles/pmc_traffic.json the HBM bytes per dispatch of the
+    kernels in two rocprofv3 --pmc runs of this bench with --calib-copy-mib
+    1024: <pmc_dir>/fetch (FETCH_SIZE) and <pmc_dir>/write (WRITE_SIZE), each
+    holding a *_counter_collection.csv. Each kernel's figure is its mean
+    FETCH_SIZE and WRITE_SIZE (KiB) scaled by what the same counters read for
+    the 1 GiB device copy, filed under `workload` (the single-token kernel
+    always under decode), and keyed to a hash of the kernel's sources."""
+    import csv
+    import glob
+
+    def read(tag):
+        acc = {}
+        for path in glob.glob(os.path.join(pmc_dir, tag, "*counter_collection.csv")):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    acc.setdefault(kernel_short_name(r["Kernel_Name"]), []).append(
+                        float(r["Counter_Value"]))
+        return acc
+
+    f, w = read("fetch"), read("write")
+    copy = [k for k in f if "copyBuffer" in k]
+    if not copy:
+        raise SystemExit("no device copy in the counter runs: run the bench with "
+                         "--calib-copy-mib 1024")
+    cal_f, cal_w = max(f[copy[0]]), max(w[copy[0]])
+    fs, ws = round(1048576.0 / cal_f, 4), round(1048576.0 / cal_w, 4)
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            out = json.load(fh)
+    except (OSError, ValueError):
+        out = {}
+    out["calibration"] = {"copy_bytes_each_way": 1 << 30, "fetch_kib": cal_f,
+                          "write_kib": cal_w, "fetch_scale": fs, "write_scale": ws}
+    kernels = out.setdefault("kernels", {})
+    for k in sorted(f):
+        if not any(k.startswith(p) for p in KERNEL_SOURCES) or k not in w:
+            continue
+        fk = sum(f[k]) / len(f[k])
+        wk = sum(w[k]) / len(w[k])
+        tag = "decode" if k == FUSED_KERNEL else workload
+        if not isinstance(kernels.get(k), dict) or "traffic_bytes" in kernels.get(k, {}):
+            kernels[k] = {}
+        kernels[k][tag] = {"sources_sha": sources_sha(k), "dispatches": len(f[k]),
+                           "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                           "traffic_bytes": int(round((fk * fs + wk * ws) * 1024))}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1, sort_keys=True)
+    return out
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` in `workload` from the committed PMC
+    summary, or None when absent or taken on different sources of that
+    kernel."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    k = t.get("kernels", {}).get(kernel)
+    k = t.get("kernels", {}).get(kernel, {}).get(workload)
     if k is None or k.get("sources_sha") != sources_sha(kernel):
         return None
     return k.get("traffic_bytes")
@@ -375,6 +436,34 @@ def kernel_units(res, lm):
             for s in sb if res["stage_ms"][s] > 0]
 
 
+def read_ceiling(lm, hip, dev, gib: int = 4, reps: int = 10):
+    """The plain HBM read rate of this GPU: lmoe_debug_read_stream over a
+    `gib` GiB buffer (every byte read once with 16-byte loads), best over a
+    few grid sizes, median of `reps` timed reads each."""
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    buf = torch.zeros(gib << 30, dtype=torch.uint8, device=dev)
+    best = None
+    for blocks in (1024, 2048, 4096, 8192):
+        sink = torch.empty(blocks, dtype=torch.int32, device=dev)
+        lm.debug_read_stream(buf, sink, blocks)
+        times = []
+        for _ in range(reps):
+            e0, e1 = hip.event(), hip.event()
+            hip.record(e0, stream)
+            lm.debug_read_stream(buf, sink, blocks)
+            hip.record(e1, stream)
+            times.append(hip.elapsed_ms(e0, e1))
+        ms = float(np.median(times))
+        gbs = buf.numel() / (ms * 1e-3) / 1e9
+        if best is None or gbs > best["gb_s"]:
+            best = {"gb_s": round(gbs, 1), "workgroups": blocks, "bytes": buf.numel(),
+                    "kernel": "read_stream_kernel"}
+    del buf
+    torch.cuda.empty_cache()
+    return best
+
+
 def stage_us(res, lm):
     """Per-stage times in us from the traced calls; on the single-token path
     one kernel runs every stage, so only that kernel's average launch (the
@@ -394,7 +483,8 @@ def roofline_for(res, bound: str, lm):
     else:
         achieved, peak, unit = flops / sec / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": measured_traffic(kernel),
+            "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(kernel, res["w"].name),
             "kernel": kernel, "kernel_us": round(sec * 1e6, 2),
             "algorithmic_bytes": round(nbytes), "algorithmic_flops": round(flops)}
 
@@ -566,9 +656,23 @@ def main():
     ap.add_argument("--layout", default="packed", choices=("packed", "row-major"),
                     help="routed-expert layout of the multi-token cases (single tokens run "
                          "the one-kernel path on row-major experts)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the plain HBM read ceiling measurement")
+    ap.add_argument("--traffic-from", default="",
+                    help="merge into profiles/pmc_traffic.json the FETCH_SIZE / WRITE_SIZE "
+                         "counter runs in this directory (subfolders fetch/ and write/) and exit")
+    ap.add_argument("--traffic-workload", default="prefill",
+                    help="workload the --traffic-from runs measured (the single-token "
+                         "kernel is always filed under decode)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this size (PMC calibration)")
     args = ap.parse_args()
+    if args.traffic_from:
+        out = traffic_from(args.traffic_from, args.traffic_workload)
+        for k, v in out["kernels"].items():
+            for wl, e in v.items():
+                print(f"{k} [{wl}]: {e['traffic_bytes']} bytes per dispatch")
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this layer is measured on a single MI355X "
               f"(asked for --gpus {args.gpus}); multi-GPU sharding is not built.",
@@ -589,6 +693,10 @@ def main():
         log(f"calibration copy of {n} bytes done")
         del a, b
 
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = read_ceiling(lm, hip, dev)
+        log(f"plain HBM read ceiling: {ceiling['gb_s']} GB/s ({ceiling['workgroups']} workgroups)")
     dec = run_case(lm, hip, "decode", dev, args.steps, args.warmup, rotate=True,
                    traced_steps=min(args.steps, 50))
     d = dec["w"].dims
@@ -614,7 +722,11 @@ def main():
                                "64 rotating tokens, 4 rotating copies of router+shared weights",
                    "tokens": d.T, "latent": d.L, "experts": d.E, "top_k": d.k,
                    "intermediate": d.I, "shared": d.S},
-        "roofline": roofline_for(dec, "hbm", lm),
+        "roofline": {**roofline_for(dec, "hbm", lm),
+                     **({"read_ceiling_gb_s": ceiling["gb_s"],
+                         "frac_of_read_ceiling": round(value / ceiling["gb_s"], 4)}
+                        if ceiling else {})},
+        "hbm_read_ceiling": ceiling,
         "algorithmic_bytes_per_step": round(tb),
         "warm_gb_s": round(tb / (dec["warm_ms"] * 1e-3) / 1e9, 2),
         "stage_us": stage_us(dec, lm),

@@ -351,6 +351,17 @@ const char* lmoe_path_name(const lmoe_dims* dims, int logits_given);
 int lmoe_debug_dequant_mxfp4(const uint8_t* q, const uint8_t* s, int32_t rows, int32_t K,
                              uint16_t* out, void* stream);
 
+/* Measurement hook: read every byte of p (device, 16-byte aligned, bytes a
+ * multiple of 16) once with 16-byte loads from `blocks` workgroups of 256
+ * threads striding over it, and write one word per workgroup to sink
+ * (uint32 [blocks] device). The plain HBM read rate this reaches is the
+ * ceiling the HBM-bound decode kernel is measured against (infervisor.ai
+ * "Bringing up Kimi-K3 on day zero", "The roofline": batch-1 decode is bound
+ * by weight bytes). Errors: LMOE_ERR_NULL, _SHAPE (blocks outside 1..65536),
+ * _ALIGN, _HIP. */
+int lmoe_debug_read_stream(const void* p, size_t bytes, uint32_t* sink, int32_t blocks,
+                           void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* lmoe_status_string(int status);
 

@@ -45,7 +45,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("lmoe_workspace_bytes", "lmoe_route", "lmoe_forward", "lmoe_forward_ex",
            "lmoe_forward_traced", "lmoe_wait_errors", "lmoe_forward_noalloc", "lmoe_stage_name", "lmoe_path_name",
            "lmoe_debug_dequant_mxfp4", "lmoe_status_string", "lmoe_packed_sizes_of",
-           "lmoe_pack_weights", "lmoe_forward_packed")
+           "lmoe_pack_weights", "lmoe_forward_packed", "lmoe_debug_read_stream")
 # members of lmoe_packed_sizes / the packed routed-expert arrays
 PACKED_KEYS = ("gu_q", "gu_s", "down_q", "down_s")
 
@@ -151,6 +151,8 @@ def _load() -> ctypes.CDLL:
     lib.lmoe_path_name.restype = ctypes.c_char_p
     lib.lmoe_stage_name.argtypes = [ctypes.c_int]
     lib.lmoe_stage_name.restype = ctypes.c_char_p
+    lib.lmoe_debug_read_stream.argtypes = [vp, sz, vp, i32, vp]
+    lib.lmoe_debug_read_stream.restype = ctypes.c_int
     lib.lmoe_debug_dequant_mxfp4.argtypes = [vp, vp, i32, i32, vp, vp]
     lib.lmoe_debug_dequant_mxfp4.restype = ctypes.c_int
     lib.lmoe_status_string.argtypes = [ctypes.c_int]
@@ -338,6 +340,14 @@ def path_name(dims, logits_given: bool = False) -> str:
 
 def stage_name(i: int) -> str:
     return _lib.lmoe_stage_name(int(i)).decode()
+
+
+def debug_read_stream(buf, sink, blocks: int, stream=None) -> None:
+    """Read every byte of the device tensor buf once (the plain HBM read
+    rate); one word per workgroup lands in the int32 device tensor sink."""
+    code = _lib.lmoe_debug_read_stream(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                       int(blocks), _stream(stream))
+    _check("lmoe_debug_read_stream", code)
 
 
 def debug_dequant_mxfp4(q, s, rows: int, K: int, out, stream=None) -> None:

@@ -541,6 +541,16 @@ extern "C" const char* lmoe_stage_name(int stage) {
   return (stage >= 0 && stage < LMOE_NUM_STAGE_EVENTS) ? names[stage] : "?";
 }
 
+extern "C" int lmoe_debug_read_stream(const void* p, size_t bytes, uint32_t* sink,
+                                     int32_t blocks, void* stream) {
+  if (!p || !sink) return LMOE_ERR_NULL;
+  if (bytes % 16 || blocks < 1 || blocks > 65536) return LMOE_ERR_SHAPE;
+  if (!aligned16(p) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return LMOE_ERR_ALIGN;
+  if (bytes == 0) return LMOE_OK;
+  hipError_t e = launch_read_stream(p, bytes, sink, blocks, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
+}
+
 extern "C" int lmoe_debug_dequant_mxfp4(const uint8_t* q, const uint8_t* s, int32_t rows,
                                         int32_t K, uint16_t* out, void* stream) {
   if (rows < 0 || K <= 0 || K % 32) return LMOE_ERR_SHAPE;

@@ -620,6 +620,41 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Measurement hook: the plain HBM read rate the decode kernel is held
+// against. Every byte of the buffer is read once with 16-byte loads, four in
+// flight per thread, the workgroups striding over the buffer; each workgroup
+// folds what it read into one word (so no load is dead).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void read_stream_kernel(const u32x4_t* __restrict__ p,
+                                                          int64_t n16, uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  uint32_t x = 0;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4_t a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    x ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3];
+    x ^= c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^ d[3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4_t a = p[i];
+    x ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x ^= __shfl_xor(x, off, kWave);
+  __shared__ uint32_t red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+hipError_t launch_read_stream(const void* p, size_t bytes, uint32_t* sink, int blocks,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(read_stream_kernel, dim3(blocks), dim3(256), 0, s,
+                     static_cast<const u32x4_t*>(p), (int64_t)(bytes / 16), sink);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 template <bool GLU, bool FP4>

@@ -156,6 +156,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, const hipEvent_t* e
 // and resets it
 hipError_t launch_read_errors(int32_t* ctr, int32_t* count, hipStream_t s);
 
+hipError_t launch_read_stream(const void* p, size_t bytes, uint32_t* sink, int blocks,
+                              hipStream_t s);
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* sc, int rows, int K, uint16_t* out,
                           hipStream_t s);
 

@@ -29,6 +29,7 @@ def test_header_declares_the_boundary():
                             "lmoe_forward_ex", "lmoe_forward_traced", "lmoe_wait_errors",
                             "lmoe_forward_noalloc", "lmoe_packed_sizes_of",
                             "lmoe_pack_weights", "lmoe_forward_packed",
+                            "lmoe_debug_read_stream",
                             "lmoe_stage_name", "lmoe_path_name",
                             "lmoe_debug_dequant_mxfp4", "lmoe_status_string"]), names
 
@@ -280,6 +281,18 @@ def test_wait_errors_rejects_bad_arguments(lm):
     assert f(0x40000008, 1 << 20, 0x2000, None) == lm.LMOE_ERR_ALIGN
     assert f(0x40000000, 1 << 20, 0x2002, None) == lm.LMOE_ERR_ALIGN
     assert f(0x40000000, 32767, 0x2000, None) == lm.LMOE_ERR_WORKSPACE
+
+
+def test_read_stream_rejects_bad_arguments(lm):
+    f = lm._lib.lmoe_debug_read_stream
+    assert f(None, 1024, 0x2000, 4, None) == lm.LMOE_ERR_NULL
+    assert f(0x1000, 1024, None, 4, None) == lm.LMOE_ERR_NULL
+    assert f(0x1000, 1000, 0x2000, 4, None) == lm.LMOE_ERR_SHAPE
+    assert f(0x1000, 1024, 0x2000, 0, None) == lm.LMOE_ERR_SHAPE
+    assert f(0x1000, 1024, 0x2000, 65537, None) == lm.LMOE_ERR_SHAPE
+    assert f(0x1008, 1024, 0x2000, 4, None) == lm.LMOE_ERR_ALIGN
+    assert f(0x1000, 1024, 0x2002, 4, None) == lm.LMOE_ERR_ALIGN
+    assert f(0x1000, 0, 0x2000, 4, None) == lm.LMOE_OK
 
 
 def test_binding_rejects_host_tensors(lm):

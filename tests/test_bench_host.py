@@ -74,16 +74,20 @@ def test_reported_kernel_names_match_the_profiled_kernels():
 
 
 def test_stale_traffic_is_not_reported(tmp_path, monkeypatch):
-    """Counter traffic taken on other sources of a kernel is not reported;
-    traffic of a kernel whose sources are unchanged is."""
+    """Counter traffic taken on other sources of a kernel, or in another
+    workload, is not reported; traffic of a kernel whose sources are
+    unchanged is, for the workload it was taken in."""
     f = tmp_path / "t.json"
-    f.write_text('{"kernels": {"decode_kernel": {"sources_sha": "0000", "traffic_bytes": 1}}}')
+    f.write_text('{"kernels": {"decode_kernel": {"decode": '
+                 '{"sources_sha": "0000", "traffic_bytes": 1}}}}')
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    assert bench.measured_traffic("decode_kernel") is None
-    f.write_text('{"kernels": {"decode_kernel": {"sources_sha": "%s", "traffic_bytes": 7}}}'
+    assert bench.measured_traffic("decode_kernel", "decode") is None
+    f.write_text('{"kernels": {"decode_kernel": {"decode": '
+                 '{"sources_sha": "%s", "traffic_bytes": 7}}}}'
                  % bench.sources_sha("decode_kernel"))
-    assert bench.measured_traffic("decode_kernel") == 7
-    assert bench.measured_traffic("other") is None
+    assert bench.measured_traffic("decode_kernel", "decode") == 7
+    assert bench.measured_traffic("decode_kernel", "prefill") is None
+    assert bench.measured_traffic("other", "decode") is None
 
 
 def test_kernel_sources_hash_only_their_files():
