@@ -145,6 +145,7 @@ def stage_kernel(stage: str, large: bool, sh_large: bool, d=None, logits_given=F
 # hash of these files, so a change elsewhere does not discard it.
 KERNEL_SOURCES = {
     "decode_kernel": "decode.hip",
+    "decode_multi_kernel": "decode_multi.hip",
     "gemm_packed": "packed.hip",
     "pack_": "packed.hip",
     "read_stream": "experts.hip",
@@ -411,8 +412,10 @@ def run_case(lm, hip, name, dev, steps, warmup, rotate: bool, traced_steps: int,
 
 
 # The single-token path is one kernel; the library records every stage event
-# right after it, so its whole time lands on the first stage.
+# right after it, so its whole time lands on the first stage. So is the path
+# of 2..16 tokens.
 FUSED_KERNEL = "decode_kernel"
+FUSED_KERNELS = {"fused_decode": FUSED_KERNEL, "fused_multi": "decode_multi_kernel"}
 
 
 def kernel_units(res, lm):
@@ -420,13 +423,14 @@ def kernel_units(res, lm):
     d = res["w"].dims
     logits_given = res["w"].logits_given
     tb, tf, sb, sf = algorithmic(d, res["D"], logits_given)
-    if lm.path_name(d, logits_given) == "fused_decode":
-        # one kernel does the whole layer: the layer's bytes (the token is
-        # read once, though three stages count it). It runs one token: every
-        # timed step is one launch of it, back to back, so the events around the timed
-        # region give its average launch; the events a traced call records
-        # around the kernel add 2-5 us of their own.
-        return [(FUSED_KERNEL, tb, tf, res["ms"] * 1e-3)]
+    path = lm.path_name(d, logits_given)
+    if path in FUSED_KERNELS and not res.get("packed"):
+        # one kernel does the whole layer: the layer's bytes (the tokens are
+        # read once, though three stages count them). Every timed step is one
+        # launch of it, back to back, so the events around the timed region
+        # give its average launch; the events a traced call records around
+        # the kernel add 2-5 us of their own.
+        return [(FUSED_KERNELS[path], tb, tf, res["ms"] * 1e-3)]
     large = True  # routed groups of every size take the large kernel
     sh_large = d.T > 64
     packed_kernel = {"gate_up": "gemm_packed_kernel<true>", "down": "gemm_packed_kernel<false>"}
@@ -469,8 +473,9 @@ def stage_us(res, lm):
     one kernel runs every stage, so only that kernel's average launch (the
     untraced timed region) is reported."""
     w = res["w"]
-    if lm.path_name(w.dims, w.logits_given) == "fused_decode":
-        return {FUSED_KERNEL: round(res["ms"] * 1e3, 2)}
+    path = lm.path_name(w.dims, w.logits_given)
+    if path in FUSED_KERNELS and not res.get("packed"):
+        return {FUSED_KERNELS[path]: round(res["ms"] * 1e3, 2)}
     return {k: round(v * 1e3, 1) for k, v in res["stage_ms"].items()}
 
 
@@ -638,6 +643,28 @@ def extra_case(lm, hip, name, dev, steps, packed: bool):
     return out
 
 
+# Decode of a few tokens per call: the fused kernel (row-major experts,
+# lmoe_forward) against the grouped path (tile-packed experts,
+# lmoe_forward_packed) at each T; both stream the D distinct experts' weights.
+SMALL_T = (2, 4, 8, 16)
+
+
+def small_t_sweep(lm, hip, dev, steps):
+    out = {}
+    cross = None
+    for T in SMALL_T:
+        name = f"decode_t{T}"
+        fused = extra_case(lm, hip, name, dev, steps, False)
+        grouped = extra_case(lm, hip, name, dev, steps, True)
+        out[name] = {"fused": fused, "grouped_packed": grouped,
+                     "faster": "fused" if fused["ms_per_step"] <= grouped["ms_per_step"]
+                     else "grouped_packed"}
+        if cross is None and out[name]["faster"] != "fused":
+            cross = T
+    out["first_T_grouped_faster"] = cross
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -653,6 +680,9 @@ def main():
     ap.add_argument("--extra", default=DEFAULT_EXTRA,
                     help="comma-separated further workloads to report, 'all', or 'none': "
                          + ", ".join(EXTRA))
+    ap.add_argument("--no-small-t", action="store_true",
+                    help="skip the 2..16-token decode sweep (fused kernel against the "
+                         "grouped path)")
     ap.add_argument("--layout", default="packed", choices=("packed", "row-major"),
                     help="routed-expert layout of the multi-token cases (single tokens run "
                          "the one-kernel path on row-major experts)")
@@ -758,6 +788,8 @@ def main():
                 result["extra"][n + "_rowmajor"] = extra_case(lm, hip, n, dev, args.steps, False)
             else:
                 result["extra"][n] = extra_case(lm, hip, n, dev, args.steps, packed)
+    if not args.no_small_t:
+        result["decode_small_t"] = small_t_sweep(lm, hip, dev, max(20, args.steps // 2))
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args.cpu_tokens, args.cpu_seconds)
         if "prefill" in result:

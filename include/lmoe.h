@@ -127,11 +127,16 @@ typedef struct lmoe_routing {
   int32_t* inv_perm;
 } lmoe_routing;
 
+/* Size of the counter block at the start of every workspace: the dependency
+ * counters of the persistent decode kernels (1 to 16 tokens). */
+#define LMOE_COUNTER_BYTES ((size_t)256 << 10)
+
 /* Bytes of device workspace lmoe_route / lmoe_forward need for these
  * dimensions (the same value serves both). Returns 0 for invalid dims.
  * The workspace must be zero-filled before its first use; every call leaves
- * its first 32 KiB (the single-token decode kernel's dependency counters)
- * zeroed again, so a workspace can be reused across calls and dimensions. */
+ * its first LMOE_COUNTER_BYTES (the decode kernels' dependency counters)
+ * zeroed again, so a workspace can be reused across calls and dimensions.
+ * After lmoe_wait_errors reports an abandoned wait, zero that block again. */
 size_t lmoe_workspace_bytes(const lmoe_dims* dims);
 
 /* Routing only: router logits (unless logits_given), top-k selection with
@@ -195,23 +200,24 @@ typedef struct lmoe_exec {
 /* lmoe_forward with the shared experts' stream chosen by the caller instead
  * of the library's per-device second stream: exec NULL (or its side_stream
  * NULL) runs every stage on `stream`, and the library then creates no stream
- * or event of its own. The single-token path (lmoe_path_name
- * "fused_decode") is one kernel on `stream` whatever exec says. Same
+ * or event of its own. The decode paths (lmoe_path_name "fused_decode"
+ * and "fused_multi") are one kernel on `stream` whatever exec says. Same
  * arguments, results and errors as lmoe_forward, plus LMOE_ERR_NULL when
  * exec->side_stream is set and an event is missing. */
 int lmoe_forward_ex(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights* w,
                     int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
                     size_t ws_bytes, void* stream, const lmoe_exec* exec);
 
-/* The single-token kernel resolves its dependencies with bounded waits on
- * device counters in the workspace; a wait that outlives its bound (about a
- * quarter of a second: a producer that never ran) is abandoned and counted in
- * the workspace, and that call's output is then not valid. This enqueues on
+/* The decode kernels (1 to 16 tokens) resolve their dependencies with bounded
+ * waits on device counters in the workspace; a wait that outlives its bound
+ * (about a quarter of a second: a producer that never ran) is abandoned and
+ * counted in the workspace, and that call's output is then not valid. This
+ * enqueues on
  * `stream` a copy of that count into *count (int32 device, 4-byte aligned)
  * and resets it to zero, with no host synchronisation: a caller that reads 0
  * after its calls knows no wait was abandoned in them. The count accumulates
  * over calls on one workspace until read.
- *   ws  the workspace of those calls (ws_bytes >= 32 KiB)
+ *   ws  the workspace of those calls (ws_bytes >= LMOE_COUNTER_BYTES)
  * Errors: LMOE_ERR_NULL, _ALIGN, _WORKSPACE, _HIP. */
 int lmoe_wait_errors(void* ws, size_t ws_bytes, int32_t* count, void* stream);
 
@@ -335,12 +341,17 @@ const char* lmoe_stage_name(int stage);
 
 /* Which implementation lmoe_forward uses for these dimensions (static
  * string): "fused_decode" (T == 1 with computed logits and L, I, Is at
- * most 4096: the whole layer in one persistent kernel), "grouped" (routing
+ * most 4096: the whole layer in one persistent kernel), "fused_multi"
+ * (2 <= T <= 16 with computed logits, T * k <= 256 and the same widths: one
+ * persistent kernel with one token per MFMA row, each selected expert
+ * streamed once for all the tokens that chose it), "grouped" (routing
  * kernels, then grouped GEMMs over expert groups of up to 96 rows, then the
  * combine), "invalid" for bad dims. Decode streams the active weights once
- * per token (infervisor.ai "Bringing up Kimi-K3 on day zero", "The
- * roofline"); the grouped form follows the expert-sorted tiling of dev48.org
- * "Kimi K3 on AMD Instinct GPUs with TokenSpeed", section 4.1. */
+ * per step (infervisor.ai "Bringing up Kimi-K3 on day zero", "The
+ * roofline"); small batches walk their tokens' routes directly and the
+ * grouped form follows the expert-sorted tiling of dev48.org "Kimi K3 on AMD
+ * Instinct GPUs with TokenSpeed", section 4.1. lmoe_forward_packed always
+ * takes the grouped form. */
 const char* lmoe_path_name(const lmoe_dims* dims, int logits_given);
 
 /* Test hook: dequantise an MXFP4 matrix with the same device routine the

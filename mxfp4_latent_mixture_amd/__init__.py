@@ -41,6 +41,8 @@ LMOE_ERR_WORKSPACE = 4
 LMOE_ERR_HIP = 5
 # scratch of lmoe_forward_noalloc per GPU (LMOE_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 64 << 20
+# the decode kernels' counter block at the start of a workspace (LMOE_COUNTER_BYTES)
+COUNTER_BYTES = 256 << 10
 
 EXPORTS = ("lmoe_workspace_bytes", "lmoe_route", "lmoe_forward", "lmoe_forward_ex",
            "lmoe_forward_traced", "lmoe_wait_errors", "lmoe_forward_noalloc", "lmoe_stage_name", "lmoe_path_name",

@@ -48,11 +48,14 @@ Plan make_plan(const lmoe_dims& d) {
   p.rows_per_tile = kLargeRows;
   p.max_tiles = std::min(d.E, p.R) + p.R / p.rows_per_tile;
   // One token, when every row a decode wave stages (h of one route or one
-  // shared expert) and the token itself fit its fixed-size staging. From two
-  // tokens the grouped path is faster on the Kimi-K3 layer (T = 2: 131 us
-  // against 145 us for one decode launch per token).
-  p.fused_decode = d.T == 1 && d.L <= kDecodeMaxWidth && d.I <= kDecodeMaxWidth &&
-                   p.d.Is <= kDecodeMaxWidth;
+  // shared expert) and the token itself fit its fixed-size staging.
+  const bool widths_ok =
+      d.L <= kDecodeMaxWidth && d.I <= kDecodeMaxWidth && p.d.Is <= kDecodeMaxWidth;
+  p.fused_decode = d.T == 1 && widths_ok;
+  // 2..16 tokens: one per MFMA row, when the routes fit the grouping tables
+  // and the tokens fit the LDS.
+  p.fused_multi = d.T >= 2 && d.T <= kMultiMaxT && d.T * d.k <= kMultiMaxRoutes && widths_ok &&
+                  decode_multi_lds_bytes(d) <= kLdsBytes;
   return p;
 }
 
@@ -61,6 +64,7 @@ Plan make_packed_plan(const lmoe_dims& d) {
   p.rows_per_tile = kPackedRows;
   p.max_tiles = std::min(d.E, p.R) + p.R / p.rows_per_tile;
   p.fused_decode = false;
+  p.fused_multi = false;
   return p;
 }
 
@@ -148,13 +152,16 @@ static int run_route(const Plan& p, const Workspace& ws, const uint16_t* x, cons
   return LMOE_OK;
 }
 
-// T == 1: the whole layer as one persistent kernel. Stage events: the
-// kernel's time lands on the router stage.
+// T == 1, or 2..16 tokens: the whole layer as one persistent kernel. Stage
+// events: the kernel's time lands on the router stage.
 static int run_fused_decode(const Plan& p, const Workspace& ws, const uint16_t* x,
                             const lmoe_weights& w, const lmoe_routing* r, uint16_t* out,
                             hipStream_t s, const hipEvent_t* ev) {
   DecodeArgs a;
-  make_decode_args(p, a);
+  if (p.fused_multi)
+    make_decode_multi_args(p, a);
+  else
+    make_decode_args(p, a);
   a.x = x;
   a.wr = w.router_w;
   a.gq = w.gate_q;
@@ -185,7 +192,8 @@ static int run_fused_decode(const Plan& p, const Workspace& ws, const uint16_t* 
   a.offsets = offsets;
   a.perm = perm;
   a.inv = inv;
-  return launch_decode(a, s, ev) == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
+  const hipError_t e = p.fused_multi ? launch_decode_multi(a, s, ev) : launch_decode(a, s, ev);
+  return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
 }
 
 static int check_routing(const lmoe_routing* r, int logits_given) {
@@ -331,7 +339,8 @@ static int forward_impl(const lmoe_dims* dims, const uint16_t* x, const lmoe_wei
   Workspace wsp = carve_workspace(p, ws);
   if (ws_bytes < wsp.bytes) return LMOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p.fused_decode && !logits_given) return run_fused_decode(p, wsp, x, w, r, out, s, ev);
+  if ((p.fused_decode || p.fused_multi) && !logits_given)
+    return run_fused_decode(p, wsp, x, w, r, out, s, ev);
   Routing rt;
   // Traced calls keep every stage on the caller's stream, in order, so each
   // stage's events time it alone.
@@ -531,6 +540,7 @@ extern "C" const char* lmoe_path_name(const lmoe_dims* dims, int logits_given) {
   if (!dims || !dims_ok(*dims)) return "invalid";
   Plan p = make_plan(*dims);
   if (p.fused_decode && !logits_given) return "fused_decode";
+  if (p.fused_multi && !logits_given) return "fused_multi";
   return "grouped";
 }
 

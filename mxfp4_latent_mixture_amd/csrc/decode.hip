@@ -43,20 +43,19 @@
 // before it bumps a counter. A logit needs no counter: its flag and value are
 // one aligned 64-bit word, so a reader that sees the flag sees the value,
 // which saves the selecting wave one round trip. No L2 writeback or
-// invalidate is issued. Counters and flagged logits sit in the first 32 KiB
-// of the workspace, are zero when a launch starts and are zeroed again by its
+// invalidate is issued. Counters and flagged logits sit in the workspace's
+// counter block, are zero when a launch starts and are zeroed again by its
 // last wave to leave.
 #include <atomic>
 
-#include "lmoe_device.h"
 #include "lmoe_internal.h"
+#include "lmoe_stream.h"
 #include "lmoe_topk.h"
 
 namespace lmoe {
 
 namespace {
 
-constexpr long kSpinLimit = 1l << 22;
 constexpr int kMaxK = kTopkMaxK;  // routes per token on this path
 constexpr int kKeysPerLane = kTopkKeysPerLane;
 constexpr int kMaxShared = 8;     // shared experts
@@ -64,80 +63,6 @@ constexpr int kDepth = 1;         // bursts of weights in flight ahead of the MF
 // Workgroups per compute unit. Four streaming waves per CU keep enough bytes
 // in flight; more concurrent items only lengthen each item and the tail.
 constexpr int kWgPerCu = 1;
-
-__device__ __forceinline__ int ld_dev(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int add_dev(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev_f32(float* p, float v) {
-  st_dev(reinterpret_cast<uint32_t*>(p), __float_as_uint(v));
-}
-__device__ __forceinline__ float ld_dev_f32(const float* p) {
-  return __uint_as_float(ld_dev(reinterpret_cast<const uint32_t*>(p)));
-}
-// 16 bytes written by another wave of this launch
-__device__ __forceinline__ u32x4_t ld16_dev(const void* p) {
-  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
-  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  u32x4_t r = {(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
-  return r;
-}
-
-// All of this wave's stores have completed; then lane 0 bumps the counter.
-// Returns the previous value (uniform) when `want_old`.
-__device__ __forceinline__ int publish(int* ctr, bool want_old) {
-  // The data stores above are device-scope (coherent in every L2 partition)
-  // and complete before the counter bump once the wait returns. The fence
-  // keeps the compiler from moving a store past that point: the waitcnt
-  // builtin alone touches no memory in the compiler's model.
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  int old = 0;
-  if (lane_id() == 0) {
-    if (want_old)
-      old = add_dev(ctr, 1);
-    else
-      __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  return __builtin_amdgcn_readfirstlane(old);
-}
-
-// Waits until the sum of n (<= 64) counters spaced `stride` ints apart reaches
-// target. A wait that outlives the spin limit (a broken producer) is counted in
-// the error slot and abandoned.
-__device__ __forceinline__ void wait_geq(const int* ctr, int target, int* err, int n = 1,
-                                         int stride = 0) {
-  long it = 0;
-  for (;;) {
-    int s = 0;
-    if (lane_id() < n) s = ld_dev(ctr + stride * lane_id());
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off, kWave);
-    s = __builtin_amdgcn_readfirstlane(s);
-    if (s >= target) {
-      // the dependent loads that follow stay after the counter was seen
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      break;
-    }
-    if (++it > kSpinLimit) {
-      if (lane_id() == 0) add_dev(err, 1);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-}
 
 // Per-wave state kept across items.
 struct WaveState {
@@ -153,237 +78,6 @@ struct TopkLds {
 };
 
 }  // namespace
-
-// ---------------------------------------------------------------------------
-// Weight streaming. Weights are read through buffer resources: an offset past
-// the end of the matrix returns zeros, so padding rows and past-the-end blocks
-// need no branches around loads, and each burst of loads is issued as a group
-// (pinned by scheduling barriers) one burst ahead of the MFMAs that consume
-// it.
-//
-// Every lane of a lane group reads the same A values (an LDS broadcast), so
-// all 16 rows of each MFMA result equal the token's row; lanes 0..15 of
-// acc[t][0] hold the tile's 16 results.
-//
-// MXFP4 rows (16 bytes of codes per 32-value block): in iteration it, lane
-// group g takes blocks 8 it + 2 g + u (u = 0, 1), so the four groups read 128
-// contiguous bytes of every row per iteration. Each 64-block window's 64
-// exponent bytes are fetched with dword-aligned loads (the range check of a
-// buffer load zeroes a whole dword that reaches past the end), realigned,
-// reduced to the 16 bytes the lane uses, and prefetched one window ahead.
-//
-// bf16 rows: in iteration it, instruction j, lane group g reads values
-// 128 it + 32 j + 8 g .. +8, so each instruction reads 64 contiguous bytes of
-// every row.
-// ---------------------------------------------------------------------------
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int kOob = 0x40000000;  // an offset past the end of every matrix
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-__device__ __forceinline__ u32x4_t bload16(rsrc_t r, int off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ uint32_t bload4(rsrc_t r, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-
-// One tile of 16 weight rows: the lane's row starts at byte `row` of its
-// resource(s) (kOob for a padding row).
-struct Tile4 {
-  rsrc_t codes, scales;
-  int code_row, scale_row;
-};
-struct Tile16 {
-  rsrc_t w;
-  int row;
-};
-
-// D bursts are kept in flight ahead of the one being computed, in a ring of
-// RING buffers. `pre` runs once the first bursts are in flight and before arow
-// is first read: a dependency wait and the staging of arow overlap those loads.
-template <int NT, int IPB, int D, typename Pre>
-__device__ __forceinline__ void gemv_fp4(const uint16_t* arow, int nblk, const Tile4 (&tl)[NT],
-                                         f32x4_t (&acc)[NT], Pre&& pre) {
-  constexpr int BPW = 8 / IPB;  // bursts per 64-block window
-  constexpr int RING = D == 1 ? 2 : 4;
-  static_assert(8 % IPB == 0 && BPW % RING == 0 && D < RING, "the ring must tile a window");
-  const int grp = lane_id() >> 4;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int nwin = (nblk + 63) / 64;
-
-  // raw exponent window: 17 dwords from the dword at or below the window start
-  struct Raw {
-    u32x4_t q[4];
-    uint32_t tail;
-  };
-  Raw raw[NT];
-  uint32_t ex[NT][4];  // the lane's 16 exponent bytes of the current window
-  uint32_t shift[NT];
-  auto load_exps = [&](int w) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int off = 64 * w < nblk ? tl[t].scale_row + 64 * w : kOob;
-      const int sh = off & 3;
-      const int a0 = off - sh;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) raw[t].q[j] = bload16(tl[t].scales, a0 + 16 * j);
-      raw[t].tail = bload4(tl[t].scales, sh ? a0 + 64 : kOob);
-      shift[t] = (uint32_t)sh;
-    }
-  };
-  // exponent of block 8 p + 2 g + u of the window is byte 2 p + u of ex:
-  // the lane's two bytes of iteration p are halfword g of window bytes 8p..8p+7
-  auto take_exps = [&]() {
-    const uint32_t gs = 16u * (uint32_t)grp;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      uint32_t d[17];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) d[4 * j + c] = raw[t].q[j][c];
-      d[16] = raw[t].tail;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) d[i] = __builtin_amdgcn_alignbyte(d[i + 1], d[i], shift[t]);
-      uint32_t hw[8];
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const uint64_t v = ((uint64_t)d[2 * p + 1] << 32) | d[2 * p];
-        hw[p] = (uint32_t)(v >> gs) & 0xFFFFu;
-      }
-#pragma unroll
-      for (int p = 0; p < 8; p += 2) ex[t][p >> 1] = hw[p] | (hw[p + 1] << 16);
-    }
-  };
-  struct Buf {
-    u32x4_t c[IPB][NT][2];
-  };
-  // bp is a compile-time constant at every call
-  auto load = [&](int w, const int bp, Buf& b) {
-#pragma unroll
-    for (int c = 0; c < IPB; ++c) {
-      const int it = w * 8 + bp * IPB + c;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int blk = 8 * it + 2 * grp + u;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          b.c[c][t][u] = bload16(tl[t].codes, blk < nblk ? tl[t].code_row + blk * 16 : kOob);
-      }
-    }
-  };
-  auto compute = [&](int w, const int bp, const Buf& b) {
-#pragma unroll
-    for (int c = 0; c < IPB; ++c) {
-      const int p = bp * IPB + c;  // iteration within the window
-      const int it = w * 8 + p;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int blk = 8 * it + 2 * grp + u;
-        const bool ok = blk < nblk;
-        // past-the-end blocks carry zero codes and exponent 2^0 (never NaN);
-        // their A reads stay inside the row
-        const int ablk = ok ? blk : nblk - 1;
-        float scale[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const uint32_t e8 = (ex[t][p >> 1] >> (8 * (2 * (p & 1) + u))) & 0xFFu;
-          scale[t] = e8m0_to_f32(ok ? e8 : 127u);
-        }
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(arow + ablk * 32 + qq * 8);
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-            acc[t] = mfma16(av, dequant8(b.c[c][t][u][qq], scale[t]), acc[t]);
-        }
-      }
-    }
-  };
-  Buf buf[RING];
-  load_exps(0);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int b = 0; b < D; ++b) load(0, b, buf[b]);
-  __builtin_amdgcn_sched_barrier(0);
-  pre();
-  take_exps();
-  for (int w = 0; w < nwin; ++w) {
-#pragma unroll
-    for (int bp = 0; bp < BPW; ++bp) {
-      // the burst D ahead (in the next window near the end of this one)
-      if (bp + D < BPW)
-        load(w, bp + D, buf[(bp + D) % RING]);
-      else
-        load(w + 1, bp + D - BPW, buf[(bp + D) % RING]);
-      if (bp == 0) load_exps(w + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(w, bp, buf[bp % RING]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    take_exps();
-  }
-}
-
-template <int NT, int IPB, int D, typename Pre>
-__device__ __forceinline__ void gemv_bf16(const uint16_t* arow, int nblk, const Tile16 (&tl)[NT],
-                                          f32x4_t (&acc)[NT], Pre&& pre) {
-  constexpr int RING = D == 1 ? 2 : 4;
-  static_assert(D < RING, "the ring holds the bursts in flight");
-  const int grp = lane_id() >> 4;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int iters = (nblk + 3) / 4;  // 4 blocks of 32 values per iteration
-  const int bursts = (iters + IPB - 1) / IPB;
-  struct Buf {
-    u32x4_t b[IPB][NT][4];
-  };
-  auto load = [&](int burst, Buf& w) {
-#pragma unroll
-    for (int c = 0; c < IPB; ++c) {
-      const int it = burst * IPB + c;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int blk = 4 * it + j;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          w.b[c][t][j] = bload16(tl[t].w, blk < nblk ? tl[t].row + blk * 64 + grp * 16 : kOob);
-      }
-    }
-  };
-  auto compute = [&](int burst, const Buf& w) {
-#pragma unroll
-    for (int c = 0; c < IPB; ++c) {
-      const int it = burst * IPB + c;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int blk = min(4 * it + j, nblk - 1);
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(arow + blk * 32 + grp * 8);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = mfma16(av, as_bf16x8(w.b[c][t][j]), acc[t]);
-      }
-    }
-  };
-  // no load is conditional: bursts past the end read out of bounds (zeros)
-  Buf buf[RING];
-#pragma unroll
-  for (int b = 0; b < D; ++b) load(b, buf[b]);
-  __builtin_amdgcn_sched_barrier(0);
-  pre();
-  for (int b = 0; b < bursts; b += RING) {
-#pragma unroll
-    for (int r = 0; r < RING; ++r) {
-      load(b + r + D, buf[(r + D) % RING]);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(b + r, buf[r]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-}
 
 // Copy n (<= kDecodeMaxWidth, a multiple of 8) bf16 values written by other
 // waves of this launch into the wave's LDS row. Every load is issued before
@@ -577,7 +271,7 @@ __device__ void shared_gu_item(const DecodeArgs& a, int item, const uint16_t* xs
   tl[0].w = make_rsrc((col < 8 ? a.shg : a.shu) + (size_t)s * a.Is * a.L, mbytes);
   tl[0].row = i < a.Is ? i * a.L * 2 : kOob;
   f32x4_t acc[1];
-  gemv_bf16<1, 2, kDepth>(xs, a.L / 32, tl, acc, [] {});
+  gemv_bf16<1, 2, kDepth>(ALds{xs}, a.L / 32, tl, acc, [] {});
   // g in lanes 0..7, u in lanes 8..15
   store_glu(a.hsh + (size_t)s * a.Is + i0, acc[0][0], acc[0][0], 8, 8, a.Is - i0);
   publish(a.ctr + kCtrShared + 16 * s, false);
@@ -601,7 +295,7 @@ __device__ void routed_gu_item(const DecodeArgs& a, int item, const uint16_t* xs
   tl[0].code_row = tl[1].code_row = i < a.I ? i * (a.L / 2) : kOob;
   tl[0].scale_row = tl[1].scale_row = i < a.I ? i * (a.L / 32) : kOob;
   f32x4_t acc[2];
-  gemv_fp4<2, 2, kDepth>(xs, a.L / 32, tl, acc, [] {});
+  gemv_fp4<2, 2, kDepth>(ALds{xs}, a.L / 32, tl, acc, [] {});
   // g in lanes 0..15 of tile 0, u in lanes 0..15 of tile 1
   store_glu(a.h + (size_t)j * a.I + i0, acc[0][0], acc[1][0], 16, 0, a.I - i0);
   publish(a.ctr + kCtrRoute + 16 * j, false);
@@ -648,7 +342,7 @@ __device__ void shared_dn_item(const DecodeArgs& a, int item, uint16_t* arow, Wa
   tl[0].w = make_rsrc(a.shd + (size_t)s * a.L * a.Is, (uint32_t)a.L * a.Is * 2);
   tl[0].row = l < a.L ? l * a.Is * 2 : kOob;
   f32x4_t acc[1];
-  gemv_bf16<1, 2, kDepth>(arow, a.Is / 32, tl, acc, [&] {
+  gemv_bf16<1, 2, kDepth>(ALds{arow}, a.Is / 32, tl, acc, [&] {
     if (st.staged != 1000 + s) {
       wait_geq(a.ctr + kCtrShared + 16 * s, a.shgu_per_expert, a.ctr + kCtrError);
       stage_row(arow, a.hsh + (size_t)s * a.Is, a.Is);
@@ -679,7 +373,7 @@ __device__ void routed_dn_item(const DecodeArgs& a, int item, uint16_t* arow, Wa
     tl[t].scale_row = l < a.L ? l * (a.I / 32) : kOob;
   }
   f32x4_t acc[2];
-  gemv_fp4<2, 2, kDepth>(arow, a.I / 32, tl, acc, [&] {
+  gemv_fp4<2, 2, kDepth>(ALds{arow}, a.I / 32, tl, acc, [&] {
     if (st.staged != j) {
       wait_geq(a.ctr + kCtrRoute + 16 * j, a.gu_per_route, a.ctr + kCtrError);
       stage_row(arow, a.h + (size_t)j * a.I, a.I);
@@ -791,6 +485,7 @@ static int decode_grid(size_t lds_bytes) {
 
 void make_decode_args(const Plan& p, DecodeArgs& a) {
   const lmoe_dims& d = p.d;
+  a.T = 1;
   a.L = d.L;
   a.E = d.E;
   a.k = d.k;
@@ -798,6 +493,8 @@ void make_decode_args(const Plan& p, DecodeArgs& a) {
   a.S = d.S;
   a.Is = d.Is;
   a.n_router = d.E;
+  a.n_groups = d.k;
+  a.xstride = d.L;
   a.shgu_per_expert = d.S > 0 ? (d.Is + 7) / 8 : 0;
   a.n_shgu = d.S * a.shgu_per_expert;
   a.gu_per_route = (d.I + 15) / 16;
@@ -806,7 +503,7 @@ void make_decode_args(const Plan& p, DecodeArgs& a) {
   a.n_shd = d.S * a.shd_per_expert;
   a.dn_per_route = (d.L + 31) / 32;
   a.n_dn = d.k * a.dn_per_route;
-  a.t_shgu = a.n_router;
+  a.t_topk = a.t_shgu = a.n_router;
   a.t_gu = a.t_shgu + a.n_shgu;
   a.t_shd = a.t_gu + a.n_gu;
   a.t_dn = a.t_shd + a.n_shd;

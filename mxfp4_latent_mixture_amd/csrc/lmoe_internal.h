@@ -26,12 +26,14 @@ struct RouterPlan {
 
 // Counter block at the start of every workspace (int32 slots, each counter on
 // its own 64-byte line; device-scope atomics on one address serialise, so
-// heavily bumped counts are spread over several slots). Only the single-token decode kernel uses it;
-// it must be zero when that kernel starts and is left zeroed when it ends.
+// heavily bumped counts are spread over several slots). Only the persistent
+// decode kernels use it; it must be zero when one starts and is left zeroed
+// when it ends. Slots common to both decode kernels:
 constexpr int kQueues = 32;         // ticket queues: item i is in queue i % kQueues
 constexpr int kCtrTicket = 0;       // + 16 * queue
 constexpr int kCtrExit = 1024;      // waves that have left
 constexpr int kCtrError = 1040;     // dependency waits abandoned at the spin limit
+// single token:
 constexpr int kCtrRoute = 1056;     // + 16 * route (< 32): gate/up items done
 constexpr int kCtrBlock = 1568;     // + 16 * block (< 64): parts of a 64-row output block done
 constexpr int kCtrShared = 2592;    // + 16 * shared expert (< 8): gate/up items done
@@ -39,13 +41,28 @@ constexpr int kCtrShared = 2592;    // + 16 * shared expert (< 8): gate/up items
 // in the low half and 1 in the high half once written, so a reader sees
 // every logit and whether it is in with one load, without a done count.
 constexpr int kCtrLogit = 4096;
-constexpr size_t kCtrBytes = 32768;
+// 2..16 tokens:
+constexpr int kMcTopk = 1056;       // tokens whose top-k is published
+constexpr int kMcShared = 1072;     // + 16 * shared expert (< 8): gate/up items done
+constexpr int kMcGroup = 2048;      // + 16 * expert group (< 256): gate/up items done
+constexpr int kMcPart = 8192;       // + 16 * (64 * token + block): inputs of a 64-row block done
+constexpr int kMcLogit = 32768;     // 64-bit flagged logits [token][expert], E <= 1024
+constexpr size_t kCtrBytes = LMOE_COUNTER_BYTES;
+static_assert((size_t)kMcLogit * 4 + 16 * 1024 * 8 <= kCtrBytes, "counter block");
+static_assert((size_t)kCtrLogit * 4 + 1024 * 8 <= kCtrBytes, "counter block");
 // The single-token decode kernel keeps the token and one A row in LDS.
 constexpr int kDecodeMaxWidth = 4096;
+
+// The multi-token decode kernel: one token per MFMA row, the routes of all
+// tokens grouped by expert inside the launch.
+constexpr int kMultiMaxT = 16;
+constexpr int kMultiMaxRoutes = 256;  // T * k
+constexpr size_t kLdsBytes = 160 * 1024;  // LDS of one workgroup on gfx950
 
 struct Plan {
   lmoe_dims d;
   bool fused_decode;  // T == 1: the whole layer in one persistent kernel
+  bool fused_multi;   // 2 <= T <= kMultiMaxT: likewise, one token per MFMA row
   int R;              // T * k routes
   RouterPlan router;
   int rows_per_tile;  // routed group tiles: kLargeRows
@@ -73,24 +90,27 @@ struct Workspace {
 };
 
 struct DecodeArgs {
-  const uint16_t* x;   // [L] bf16
+  const uint16_t* x;   // [T][L] bf16
   const uint16_t* wr;  // [E][L] bf16
   const uint8_t *gq, *gs, *uq, *us, *dq, *ds;
   const uint16_t *shg, *shu, *shd;
-  int L, E, k, I, S, Is;
-  float* logits_out;   // optional
+  int T, L, E, k, I, S, Is;
+  float* logits_out;   // optional [T][E]
   int32_t* idx;
   float* w;
   int32_t *counts, *offsets, *perm, *inv;
   uint16_t* out;
   int32_t* ctr;
-  uint16_t* h;         // [k][I] bf16
-  uint16_t* hsh;       // [S][Is] bf16
-  float* y;            // [k][L] routed down outputs
-  float* ysh;          // [S][L] shared down outputs
-  // work items by kind, in ticket order, and where each kind starts
+  uint16_t* h;         // [T * k][I] bf16, by route t * k + j
+  uint16_t* hsh;       // [S][T][Is] bf16
+  float* y;            // [T * k][L] routed down outputs
+  float* ysh;          // [S][T][L] shared down outputs
+  // work items by kind, in ticket order, and where each kind starts (the
+  // single-token kernel has no top-k items: t_topk == t_shgu)
   int n_router, n_shgu, n_gu, n_shd, n_dn;
-  int t_shgu, t_gu, t_shd, t_dn, t_total;
+  int t_topk, t_shgu, t_gu, t_shd, t_dn, t_total;
+  int n_groups;        // multi-token: expert group slots, min(E, T * k)
+  int xstride;         // multi-token: LDS row stride of the tokens, bf16 elements
   int shgu_per_expert, gu_per_route, dn_per_route, shd_per_expert;
   int a_region;        // per-wave LDS A row, bf16 elements
   size_t lds_bytes;    // dynamic LDS per workgroup
@@ -152,6 +172,11 @@ hipError_t launch_routed_packed(const Plan& p, const uint16_t* x, const PackedWe
 // ---- single-token decode (decode.hip) ----
 void make_decode_args(const Plan& p, DecodeArgs& a);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, const hipEvent_t* ev);
+// ---- 2..16-token decode (decode_multi.hip) ----
+void make_decode_multi_args(const Plan& p, DecodeArgs& a);
+// LDS bytes the multi-token kernel needs (tokens and grouping tables)
+size_t decode_multi_lds_bytes(const lmoe_dims& d);
+hipError_t launch_decode_multi(const DecodeArgs& a, hipStream_t s, const hipEvent_t* ev);
 // copies the abandoned-wait count of a workspace's counter block to *count
 // and resets it
 hipError_t launch_read_errors(int32_t* ctr, int32_t* count, hipStream_t s);

@@ -60,9 +60,11 @@ def test_traced_forward_rejects_missing_events(lm):
 def test_path_names(lm):
     assert lm.path_name(K3) == "fused_decode"
     assert lm.path_name(K3, True) == "grouped"
-    # from two tokens the grouped path is faster
-    for T in (2, 3, 4, 5):
-        assert lm.path_name((T,) + K3[1:]) == "grouped"
+    # 2..16 tokens: one kernel, one token per MFMA row
+    for T in (2, 3, 4, 5, 16):
+        assert lm.path_name((T,) + K3[1:]) == "fused_multi"
+        assert lm.path_name((T,) + K3[1:], True) == "grouped"
+    assert lm.path_name((17,) + K3[1:]) == "grouped"
     assert lm.path_name((64,) + K3[1:]) == "grouped"
     assert lm.path_name((4096,) + K3[1:]) == "grouped"
     assert lm.path_name((1, 8192, 896, 16, 2048, 2, 2048)) == "grouped"  # L too wide

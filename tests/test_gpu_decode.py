@@ -14,7 +14,7 @@ from lmoe_testutil import (log, upload, alloc_routing, check_out, logits_bound,
 
 pytestmark = pytest.mark.gpu
 
-CTR_INTS = 32768 // 4
+CTR_BYTES = 256 << 10  # LMOE_COUNTER_BYTES
 ERROR_SLOT = 1040  # int32 slot of the abandoned-wait count
 
 
@@ -66,7 +66,7 @@ def _run_tokens(lm, dev, w: Workload, n_tokens: int):
         check_out(got, ref["out64"], f"{w.name} token {t}",
                   allowance_fn=flip_allowance_fn(xs[t:t + 1], ref["idx"], ref["w"],
                                                  lambda e: _expert(inp, e), inp, d.L, d.I))
-    ctr = ws[:32768].view(torch.int32).cpu().numpy()
+    ctr = ws[:CTR_BYTES].view(torch.int32).cpu().numpy()
     assert ctr[ERROR_SLOT] == 0, "a dependency wait timed out"
     assert not ctr.any(), f"counters left non-zero at {np.nonzero(ctr)[0][:8]}"
     # the same count through the C ABI's readout
@@ -133,7 +133,7 @@ def test_fused_decode_router_ties_and_nan(lm, dev):
     check_out(out.cpu().numpy().view(np.uint16), ref["out64"], "ties1",
               allowance_fn=flip_allowance_fn(inp["x"], ref["idx"], ref["w"],
                                              lambda e: _expert(inp, e), inp, d.L, d.I))
-    assert not ws[:32768].view(torch.int32).cpu().numpy().any()
+    assert not ws[:CTR_BYTES].view(torch.int32).cpu().numpy().any()
 
 
 def _crowded_router(inp, d):
@@ -179,7 +179,7 @@ def test_fused_decode_router_crowded_lanes(lm, dev):
     check_out(out.cpu().numpy().view(np.uint16), ref["out64"], "crowd1",
               allowance_fn=flip_allowance_fn(x, ref["idx"], ref["w"],
                                              lambda e: _expert(inp, e), inp, d.L, d.I))
-    assert not ws[:32768].view(torch.int32).cpu().numpy().any()
+    assert not ws[:CTR_BYTES].view(torch.int32).cpu().numpy().any()
 
 
 def test_fused_decode_k3_back_to_back(lm, dev):

@@ -224,11 +224,10 @@ def test_full_decode(lm, dev):
 
 
 def test_full_decode_three_tokens(lm, dev):
-    """Three K3 decode tokens in one call (seed 1's inputs): from two tokens
-    the grouped path runs, with the shared experts in small tiles spread over
-    every XCD. Every token is checked."""
+    """Three K3 decode tokens in one call (seed 1's inputs) on the fused
+    multi-token kernel. Every token is checked."""
     w = get_workload("decode").with_T(3, "decode_t3")
-    assert lm.path_name(w.dims) == "grouped"
+    assert lm.path_name(w.dims) == "fused_multi"
     _full_size(lm, dev, w, 3)
 
 

@@ -91,6 +91,11 @@ WORKLOADS = {
     "skewed": Workload(
         "skewed", 4, Dims(T=8192, **_K3), logits_given=True,
         note="Zipf(1.2) expert bias on given logits, 5% of tokens tied over 32 experts"),
+    # a few decode tokens per call (speculative or concurrent decode), from
+    # the decode configuration's token stream
+    **{f"decode_t{T}": Workload(
+        f"decode_t{T}", 1, Dims(T=T, **_K3),
+        note=f"{T} decode tokens per call, the decode layer") for T in (2, 4, 8, 16)},
     "decode_i3072": Workload(
         "decode_i3072", 1, Dims(T=1, **{**_K3, "I": 3072, "Is": 3072}),
         note="K3 decode at the expert width the pages' per-expert size implies"),
