@@ -306,10 +306,11 @@ def routing_buffers(d, dev):
 
 
 def run_case(lm, hip, name, dev, steps, warmup, rotate: bool, traced_steps: int,
-             packed: bool = False):
+             packed: bool = False, path=None):
     """Time `steps` layer calls; returns a dict of measurements. packed: the
     tile-packed routed experts and lmoe_forward_packed (shared experts on a
-    second stream of the bench's own)."""
+    second stream of the bench's own). path: lmoe_forward_ex with that path
+    choice (PATH_GROUPED or PATH_FUSED), likewise with the bench's stream."""
     import torch
     n_tok = N_TOKENS if rotate else 1
     reps = N_REPLICAS if rotate else 1
@@ -317,14 +318,19 @@ def run_case(lm, hip, name, dev, steps, warmup, rotate: bool, traced_steps: int,
     T = w.dims.T
     # rotating calls take T rows at a time from a pool of n_tok * T rows
     w, experts, dense, x_pool, logits = setup(name, dev, n_tok * T, reps, lm, packed)
-    side = torch.cuda.Stream() if packed else None
-    fork, join = (hip.event(), hip.event()) if packed else (None, None)
+    own = packed or path is not None
+    side = torch.cuda.Stream() if own else None
+    fork, join = (hip.event(), hip.event()) if own else (None, None)
 
     def fwd(d, xi, wi, lg, r, out, ws, events=None):
         if packed and events is not None:
             lm.forward_packed(d, xi, wi, lg, r, out, ws, stage_events=events)
         elif packed:
             lm.forward_packed(d, xi, wi, lg, r, out, ws, side.cuda_stream, fork, join)
+        elif path is not None and events is not None:
+            lm.forward_ex(d, xi, wi, lg, r, out, ws, stage_events=events, path=path)
+        elif path is not None:
+            lm.forward_ex(d, xi, wi, lg, r, out, ws, side.cuda_stream, fork, join, path=path)
         elif events is not None:
             lm.forward_traced(d, xi, wi, lg, r, out, ws, events)
         else:
@@ -408,7 +414,7 @@ def run_case(lm, hip, name, dev, steps, warmup, rotate: bool, traced_steps: int,
     del experts, dense, x_pool, ws, out
     torch.cuda.empty_cache()
     return {"w": w, "D": D_mean, "ms": ms, "enqueue_ms": enq_ms / steps, "warm_ms": warm_ms,
-            "stage_ms": stage_ms, "traced_ms": traced_total, "packed": packed}
+            "stage_ms": stage_ms, "traced_ms": traced_total, "packed": packed, "path": path}
 
 
 # The single-token path is one kernel; the library records every stage event
@@ -418,13 +424,27 @@ FUSED_KERNEL = "decode_kernel"
 FUSED_KERNELS = {"fused_decode": FUSED_KERNEL, "fused_multi": "decode_multi_kernel"}
 
 
+def taken_path(res, lm) -> str:
+    """The implementation a measured call took."""
+    w = res["w"]
+    d = w.dims
+    if res.get("packed") or res.get("path") == lm.PATH_GROUPED:
+        return "grouped"
+    if res.get("path") == lm.PATH_FUSED and not w.logits_given:
+        if d.T == 1:
+            return lm.path_name(d, False)
+        if 2 <= d.T <= 16 and d.T * d.k <= 256 and max(d.L, d.I, d.Is) <= 4096:
+            return "fused_multi"
+    return lm.path_name(d, w.logits_given)
+
+
 def kernel_units(res, lm):
     """(kernel, algorithmic bytes, flops, seconds) per launched kernel."""
     d = res["w"].dims
     logits_given = res["w"].logits_given
     tb, tf, sb, sf = algorithmic(d, res["D"], logits_given)
-    path = lm.path_name(d, logits_given)
-    if path in FUSED_KERNELS and not res.get("packed"):
+    path = taken_path(res, lm)
+    if path in FUSED_KERNELS:
         # one kernel does the whole layer: the layer's bytes (the tokens are
         # read once, though three stages count them). Every timed step is one
         # launch of it, back to back, so the events around the timed region
@@ -472,9 +492,8 @@ def stage_us(res, lm):
     """Per-stage times in us from the traced calls; on the single-token path
     one kernel runs every stage, so only that kernel's average launch (the
     untraced timed region) is reported."""
-    w = res["w"]
-    path = lm.path_name(w.dims, w.logits_given)
-    if path in FUSED_KERNELS and not res.get("packed"):
+    path = taken_path(res, lm)
+    if path in FUSED_KERNELS:
         return {FUSED_KERNELS[path]: round(res["ms"] * 1e3, 2)}
     return {k: round(v * 1e3, 1) for k, v in res["stage_ms"].items()}
 
@@ -620,14 +639,14 @@ EXTRA = ("batched_decode", "skewed", "decode_i3072", "prefill_i3072", "decode_tp
 DEFAULT_EXTRA = "batched_decode,skewed,decode_i3072"
 
 
-def extra_case(lm, hip, name, dev, steps, packed: bool):
+def extra_case(lm, hip, name, dev, steps, packed: bool, path=None):
     from workloads import get_workload
     d = get_workload(name).dims
     hbm = d.T <= 64
     # single tokens take the one-kernel path on row-major experts
-    packed = packed and d.T > 1
+    packed = packed and d.T > 1 and path is None
     res = run_case(lm, hip, name, dev, steps if hbm else max(3, steps // 20), 3, rotate=hbm,
-                   traced_steps=5, packed=packed)
+                   traced_steps=5, packed=packed, path=path)
     tb, tf, _, _ = algorithmic(d, res["D"], res["w"].logits_given)
     sec = res["ms"] * 1e-3
     out = {"T": d.T, "L": d.L, "E": d.E, "k": d.k, "I": d.I, "S": d.S, "Is": d.Is,
@@ -635,6 +654,7 @@ def extra_case(lm, hip, name, dev, steps, packed: bool):
            "gb_s": round(tb / sec / 1e9, 1), "tflop_s": round(tf / sec / 1e12, 2),
            "algorithmic_bytes": round(tb), "algorithmic_flops": round(tf),
            "layout": "packed" if packed else "row-major",
+           "path": taken_path(res, lm),
            "roofline": roofline_for(res, "hbm" if hbm else "mfma", lm),
            "stage_us": stage_us(res, lm)}
     out["frac_of_peak"] = round(out["gb_s"] / HBM_PEAK_GBS if hbm
@@ -643,23 +663,27 @@ def extra_case(lm, hip, name, dev, steps, packed: bool):
     return out
 
 
-# Decode of a few tokens per call: the fused kernel (row-major experts,
-# lmoe_forward) against the grouped path (tile-packed experts,
-# lmoe_forward_packed) at each T; both stream the D distinct experts' weights.
+# Decode of a few tokens per call: the fused multi-token kernel against the
+# grouped kernels on the same row-major experts (lmoe_forward_ex with each
+# path choice) and on tile-packed experts (lmoe_forward_packed), at each T;
+# all stream the D distinct experts' weights. `auto` is what lmoe_forward
+# takes for that shape.
 SMALL_T = (2, 4, 8, 16)
 
 
 def small_t_sweep(lm, hip, dev, steps):
+    from workloads import get_workload
     out = {}
     cross = None
     for T in SMALL_T:
         name = f"decode_t{T}"
-        fused = extra_case(lm, hip, name, dev, steps, False)
-        grouped = extra_case(lm, hip, name, dev, steps, True)
-        out[name] = {"fused": fused, "grouped_packed": grouped,
-                     "faster": "fused" if fused["ms_per_step"] <= grouped["ms_per_step"]
-                     else "grouped_packed"}
-        if cross is None and out[name]["faster"] != "fused":
+        legs = {"fused": extra_case(lm, hip, name, dev, steps, False, lm.PATH_FUSED),
+                "grouped": extra_case(lm, hip, name, dev, steps, False, lm.PATH_GROUPED),
+                "grouped_packed": extra_case(lm, hip, name, dev, steps, True)}
+        faster = min(legs, key=lambda k: legs[k]["ms_per_step"])
+        out[name] = {**legs, "faster": faster,
+                     "auto": lm.path_name(get_workload(name).dims, False)}
+        if cross is None and legs["grouped"]["ms_per_step"] < legs["fused"]["ms_per_step"]:
             cross = T
     out["first_T_grouped_faster"] = cross
     return out

@@ -131,6 +131,12 @@ typedef struct lmoe_routing {
  * counters of the persistent decode kernels (1 to 16 tokens). */
 #define LMOE_COUNTER_BYTES ((size_t)256 << 10)
 
+/* Largest weight stream (bytes of min(E, T k) routed experts plus the shared
+ * experts and router) for which lmoe_forward takes the fused multi-token
+ * kernel; measured on the Kimi-K3 layer, the fused kernel is faster at
+ * T = 2 (374 MB) and even at T = 4 (836 MB), slower from T = 8. */
+#define LMOE_FUSED_MULTI_BYTES ((size_t)800 << 20)
+
 /* Bytes of device workspace lmoe_route / lmoe_forward need for these
  * dimensions (the same value serves both). Returns 0 for invalid dims.
  * The workspace must be zero-filled before its first use; every call leaves
@@ -195,7 +201,14 @@ typedef struct lmoe_exec {
    * stage boundaries as lmoe_forward_traced does; every stage then runs on
    * the call's stream and side_stream is not used */
   void* const* stage_events;
+  /* LMOE_PATH_AUTO (0): the implementation lmoe_path_name reports;
+   * LMOE_PATH_GROUPED: the grouped kernels whatever T;
+   * LMOE_PATH_FUSED: a fused decode kernel wherever its limits allow one
+   * (lmoe_path_name's conditions without the byte threshold), else grouped */
+  int32_t path;
 } lmoe_exec;
+
+enum { LMOE_PATH_AUTO = 0, LMOE_PATH_GROUPED = 1, LMOE_PATH_FUSED = 2 };
 
 /* lmoe_forward with the shared experts' stream chosen by the caller instead
  * of the library's per-device second stream: exec NULL (or its side_stream
@@ -342,11 +355,13 @@ const char* lmoe_stage_name(int stage);
 /* Which implementation lmoe_forward uses for these dimensions (static
  * string): "fused_decode" (T == 1 with computed logits and L, I, Is at
  * most 4096: the whole layer in one persistent kernel), "fused_multi"
- * (2 <= T <= 16 with computed logits, T * k <= 256 and the same widths: one
- * persistent kernel with one token per MFMA row, each selected expert
- * streamed once for all the tokens that chose it), "grouped" (routing
- * kernels, then grouped GEMMs over expert groups of up to 96 rows, then the
- * combine), "invalid" for bad dims. Decode streams the active weights once
+ * (2 <= T <= 16 with computed logits, T * k <= 256, the same widths, and at
+ * most LMOE_FUSED_MULTI_BYTES of weights for min(E, T k) experts plus the
+ * shared ones: one persistent kernel with one token per MFMA row, each
+ * selected expert streamed once for all the tokens that chose it; beyond
+ * that size the grouped kernels stream the weights faster), "grouped"
+ * (routing kernels, then grouped GEMMs over expert groups of up to 96 rows,
+ * then the combine), "invalid" for bad dims. Decode streams the active weights once
  * per step (infervisor.ai "Bringing up Kimi-K3 on day zero", "The
  * roofline"); small batches walk their tokens' routes directly and the
  * grouped form follows the expert-sorted tiling of dev48.org "Kimi K3 on AMD

@@ -74,14 +74,19 @@ class lmoe_routing(ctypes.Structure):
 
 class lmoe_exec(ctypes.Structure):
     _fields_ = [("side_stream", ctypes.c_void_p), ("fork_event", ctypes.c_void_p),
-                ("join_event", ctypes.c_void_p), ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
+                ("join_event", ctypes.c_void_p), ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
+                ("path", ctypes.c_int32)]
 
 
-def _exec(side_stream, fork_event, join_event, stage_events):
-    if side_stream is None and stage_events is None:
+# lmoe_exec.path
+PATH_AUTO, PATH_GROUPED, PATH_FUSED = 0, 1, 2
+
+
+def _exec(side_stream, fork_event, join_event, stage_events, path=PATH_AUTO):
+    if side_stream is None and stage_events is None and path == PATH_AUTO:
         return None
     ex = lmoe_exec(side_stream and int(side_stream), fork_event and int(fork_event),
-                   join_event and int(join_event), None)
+                   join_event and int(join_event), None, int(path))
     if stage_events is not None:
         if len(stage_events) != NUM_STAGE_EVENTS:
             raise ValueError(f"need {NUM_STAGE_EVENTS} events")
@@ -241,16 +246,17 @@ def forward(dims, x, weights: Mapping, logits_given: bool, routing: Optional[Map
 
 def forward_ex(dims, x, weights: Mapping, logits_given: bool, routing: Optional[Mapping], out,
                ws, side_stream=None, fork_event=None, join_event=None, stream=None,
-               stage_events=None) -> None:
+               stage_events=None, path=PATH_AUTO) -> None:
     """forward() with the shared experts on the caller's side_stream (an int
     hipStream_t), forked and joined by the caller's fork_event / join_event
     (int hipEvent_t); side_stream None runs every stage on `stream`.
     stage_events: NUM_STAGE_EVENTS hipEvent_t recorded at the stage
-    boundaries (every stage on `stream`)."""
+    boundaries (every stage on `stream`). path: PATH_AUTO, PATH_GROUPED or
+    PATH_FUSED (lmoe_exec.path)."""
     d = _dims(dims)
     r = _routing(routing)
     w = _weights(weights)
-    ex = _exec(side_stream, fork_event, join_event, stage_events)
+    ex = _exec(side_stream, fork_event, join_event, stage_events, path)
     code = _lib.lmoe_forward_ex(ctypes.byref(d), _ptr(x), ctypes.byref(w),
                                 int(bool(logits_given)),
                                 ctypes.byref(r) if r is not None else None, _ptr(out), _ptr(ws),

@@ -53,9 +53,14 @@ Plan make_plan(const lmoe_dims& d) {
       d.L <= kDecodeMaxWidth && d.I <= kDecodeMaxWidth && p.d.Is <= kDecodeMaxWidth;
   p.fused_decode = d.T == 1 && widths_ok;
   // 2..16 tokens: one per MFMA row, when the routes fit the grouping tables
-  // and the tokens fit the LDS.
-  p.fused_multi = d.T >= 2 && d.T <= kMultiMaxT && d.T * d.k <= kMultiMaxRoutes && widths_ok &&
-                  decode_multi_lds_bytes(d) <= kLdsBytes;
+  // and the tokens fit the LDS; taken while the weight stream is small
+  // enough that the grouped path's fixed costs outweigh its faster stream.
+  p.multi_ok = d.T >= 2 && d.T <= kMultiMaxT && d.T * d.k <= kMultiMaxRoutes && widths_ok &&
+               decode_multi_lds_bytes(d) <= kLdsBytes;
+  const double fp4_row = 17.0 / 32.0;
+  const double stream = (double)std::min(d.E, d.T * d.k) * 3.0 * d.L * d.I * fp4_row +
+                        (double)p.d.S * 3.0 * d.L * p.d.Is * 2.0 + 2.0 * d.L * d.E;
+  p.fused_multi = p.multi_ok && stream <= (double)LMOE_FUSED_MULTI_BYTES;
   return p;
 }
 
@@ -65,6 +70,7 @@ Plan make_packed_plan(const lmoe_dims& d) {
   p.max_tiles = std::min(d.E, p.R) + p.R / p.rows_per_tile;
   p.fused_decode = false;
   p.fused_multi = false;
+  p.multi_ok = false;
   return p;
 }
 
@@ -336,6 +342,15 @@ static int forward_impl(const lmoe_dims* dims, const uint16_t* x, const lmoe_wei
              (int64_t)dims->T * dims->k * dims->I >= (int64_t(1) << 32)))
     return LMOE_ERR_SHAPE;
   Plan p = pk ? make_packed_plan(*dims) : make_plan(*dims);
+  if (mode == SideMode::kCaller && exec) {
+    if (exec->path == LMOE_PATH_GROUPED) {
+      p.fused_decode = p.fused_multi = false;
+    } else if (exec->path == LMOE_PATH_FUSED) {
+      p.fused_multi = p.multi_ok;
+    } else if (exec->path != LMOE_PATH_AUTO) {
+      return LMOE_ERR_SHAPE;
+    }
+  }
   Workspace wsp = carve_workspace(p, ws);
   if (ws_bytes < wsp.bytes) return LMOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -63,6 +63,7 @@ struct Plan {
   lmoe_dims d;
   bool fused_decode;  // T == 1: the whole layer in one persistent kernel
   bool fused_multi;   // 2 <= T <= kMultiMaxT: likewise, one token per MFMA row
+  bool multi_ok;      // the fused multi-token kernel could run this shape
   int R;              // T * k routes
   RouterPlan router;
   int rows_per_tile;  // routed group tiles: kLargeRows

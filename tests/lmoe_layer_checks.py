@@ -99,7 +99,7 @@ def full_size(lm, dev, w: Workload, n_sample, packed: bool = False):
               allowance_fn=flip_allowance_fn(inp["x"], idx, wts, get, inp, d.L, d.I))
 
 
-def every_token_isolated(lm, dev, w: Workload, packed: bool = False):
+def every_token_isolated(lm, dev, w: Workload, packed: bool = False, path=None):
     """Every token at full size. The workload runs with its real router,
     routing and shapes, but every expert outside a kept set has all gate codes
     zero, so its routes give h = bf16(silu(0) u) = 0 and y = 0: each output is
@@ -134,11 +134,11 @@ def every_token_isolated(lm, dev, w: Workload, packed: bool = False):
     mask = torch.ones(d.E, dtype=torch.bool, device=dev)
     mask[keep] = False
     dinp["gate_q"].view(d.E, -1)[mask] = 0
-    got, r = run_forward(lm, w, dinp, packed=packed)
+    got, r = run_forward(lm, w, dinp, packed=packed, path=path)
     del dinp, ws
     torch.cuda.empty_cache()
     idx0 = r0["topk_idx"].cpu().numpy()
-    if lm.path_name(d, w.logits_given) == "grouped":
+    if lm.path_name(d, w.logits_given) == "grouped" and path in (None, lm.PATH_GROUPED):
         assert np.array_equal(r["topk_idx"], idx0)
     else:
         # the fused decode kernels compute the logits in another order: the

@@ -61,10 +61,10 @@ def pack_on_device(lm, d, dev_inp: Dict[str, object]) -> Dict[str, object]:
 
 
 def run_forward(lm, w: Workload, dev_inp: Dict[str, object], routing: Optional[dict] = None,
-                packed: bool = False):
+                packed: bool = False, path: Optional[int] = None):
     """Run lmoe_forward (or, packed, lmoe_pack_weights then
-    lmoe_forward_packed); returns (out bf16 bits numpy, routing dict of
-    numpy)."""
+    lmoe_forward_packed; or, with `path`, lmoe_forward_ex on that path);
+    returns (out bf16 bits numpy, routing dict of numpy)."""
     import torch
     d = w.dims
     dev = dev_inp["x"].device
@@ -77,6 +77,8 @@ def run_forward(lm, w: Workload, dev_inp: Dict[str, object], routing: Optional[d
     if packed:
         pk = pack_on_device(lm, d, dev_inp)
         lm.forward_packed(d, dev_inp["x"], {**dev_inp, **pk}, w.logits_given, routing, out, ws)
+    elif path is not None:
+        lm.forward_ex(d, dev_inp["x"], dev_inp, w.logits_given, routing, out, ws, path=path)
     else:
         lm.forward(d, dev_inp["x"], dev_inp, w.logits_given, routing, out, ws)
     torch.cuda.synchronize()

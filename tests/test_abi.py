@@ -60,11 +60,13 @@ def test_traced_forward_rejects_missing_events(lm):
 def test_path_names(lm):
     assert lm.path_name(K3) == "fused_decode"
     assert lm.path_name(K3, True) == "grouped"
-    # 2..16 tokens: one kernel, one token per MFMA row
-    for T in (2, 3, 4, 5, 16):
+    # two and three K3 tokens: one kernel, one token per MFMA row; from four
+    # the grouped kernels stream the weights faster
+    for T in (2, 3):
         assert lm.path_name((T,) + K3[1:]) == "fused_multi"
         assert lm.path_name((T,) + K3[1:], True) == "grouped"
-    assert lm.path_name((17,) + K3[1:]) == "grouped"
+    for T in (4, 5, 16, 17):
+        assert lm.path_name((T,) + K3[1:]) == "grouped"
     assert lm.path_name((64,) + K3[1:]) == "grouped"
     assert lm.path_name((4096,) + K3[1:]) == "grouped"
     assert lm.path_name((1, 8192, 896, 16, 2048, 2, 2048)) == "grouped"  # L too wide
@@ -191,6 +193,10 @@ def test_forward_ex_rejects_bad_arguments(lm):
         d0 = lm._dims((0,) + K3[1:])
         assert f(ctypes.byref(d0), None, ctypes.byref(w), 0, None, None, None, 0, None,
                  ctypes.byref(ex)) == lm.LMOE_ERR_NULL
+    # an unknown path choice
+    odd = lm.lmoe_exec(None, None, None, None, 7)
+    assert f(ctypes.byref(d), 0x20000000, ctypes.byref(w), 0, None, 0x30000000, 0x40000000,
+             1 << 40, None, ctypes.byref(odd)) == lm.LMOE_ERR_SHAPE
     # the same argument checks as lmoe_forward
     assert f(None, 0, None, 0, None, 0, 0, 0, None, None) == lm.LMOE_ERR_NULL
     bad = lm._dims((1, 3583, 896, 16, 2048, 2, 2048))

@@ -203,27 +203,36 @@ def test_multi_decode_router_crowded_lanes(lm, dev):
 
 
 def test_multi_decode_path_limits(lm):
-    """The fused multi-token path runs from 2 to 16 tokens while T * k <= 256
-    and the widths fit; beyond, the grouped path."""
+    """The fused multi-token kernel can run from 2 to 16 tokens while T * k
+    <= 256 and the widths fit; lmoe_forward takes it while the weight stream
+    of min(E, T k) experts stays under LMOE_FUSED_MULTI_BYTES (Kimi-K3: two
+    and three tokens), the grouped path beyond."""
     K3 = (3584, 896, 16, 2048, 2, 2048)
-    for T in (2, 5, 16):
+    for T in (2, 3):
         assert lm.path_name((T,) + K3) == "fused_multi"
+    for T in (4, 5, 16, 17):
+        assert lm.path_name((T,) + K3) == "grouped"
+    for T in (2, 16):
         assert lm.path_name((T,) + K3, True) == "grouped"
-    assert lm.path_name((17,) + K3) == "grouped"
-    assert lm.path_name((9, 3584, 896, 32, 2048, 2, 2048)) == "grouped"   # T * k > 256
-    assert lm.path_name((8, 3584, 896, 32, 2048, 2, 2048)) == "fused_multi"
-    assert lm.path_name((4, 8192, 896, 16, 2048, 2, 2048)) == "grouped"   # L too wide
-    assert lm.path_name((4, 3584, 896, 16, 4128, 2, 2048)) == "grouped"   # I too wide
+    small = (256, 32, 4, 128, 2, 128)
+    for T in (2, 9, 16):
+        assert lm.path_name((T,) + small) == "fused_multi"
+    assert lm.path_name((17,) + small) == "grouped"
+    assert lm.path_name((9, 288, 1024, 32, 96, 1, 96)) == "grouped"      # T * k > 256
+    assert lm.path_name((8, 288, 1024, 32, 96, 1, 96)) == "fused_multi"
+    assert lm.path_name((2, 8192, 896, 16, 2048, 2, 2048)) == "grouped"  # L too wide
+    assert lm.path_name((2, 3584, 896, 16, 4128, 2, 2048)) == "grouped"  # I too wide
 
 
 @pytest.mark.parametrize("T", [2, 4])
 def test_full_multi_decode(lm, dev, T):
-    """K3 decode with T tokens in one call (seed 1's first T tokens): routing
-    on every token, and every token's output with the real experts."""
+    """K3 decode with T tokens in one call on the fused kernel (seed 1's first
+    T tokens; T = 4 through lmoe_forward_ex's path choice): routing on every
+    token, and every token's output with the real experts."""
     import torch
     w = get_workload("decode").with_T(T, f"decode_t{T}")
     d = w.dims
-    assert lm.path_name(d) == "fused_multi"
+    assert lm.path_name(d) == ("fused_multi" if T == 2 else "grouped")
     log(f"{w.name}: generating inputs")
     inp = gen_all(w)
     dinp = upload(inp, dev)
@@ -232,7 +241,7 @@ def test_full_multi_decode(lm, dev, T):
     r = alloc_routing(d, dev)
     out = torch.empty((d.T, d.L), dtype=torch.int16, device=dev)
     ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
-    lm.forward(d, dinp["x"], dinp, False, r, out, ws)
+    lm.forward_ex(d, dinp["x"], dinp, False, r, out, ws, path=lm.PATH_FUSED)
     torch.cuda.synchronize()
     got = out.cpu().numpy().view(np.uint16)
     res = {k: v.cpu().numpy() for k, v in r.items()}
@@ -250,9 +259,9 @@ def test_full_multi_decode(lm, dev, T):
 
 @pytest.mark.parametrize("T", [8, 16])
 def test_full_multi_decode_every_token_isolated(lm, dev, T):
-    """K3 decode with 8 and 16 tokens: every token's output with all but a
-    few experts silenced (their gate codes zero), so the oracle covers every
-    token at the cost of the kept experts."""
+    """K3 decode with 8 and 16 tokens on the fused kernel (chosen through
+    lmoe_forward_ex): every token's output with all but a few experts
+    silenced (their gate codes zero), so the oracle covers every token at
+    the cost of the kept experts."""
     w = get_workload("decode").with_T(T, f"decode_t{T}")
-    assert lm.path_name(w.dims) == "fused_multi"
-    every_token_isolated(lm, dev, w)
+    every_token_isolated(lm, dev, w, path=lm.PATH_FUSED)
