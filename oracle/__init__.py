@@ -23,4 +23,12 @@ from .lmoe_oracle import (  # noqa: F401
     combine,
     forward,
     forward_tokens,
+    ACT_FORMATS,
+    ACT_EMAX,
+    e4m3_table,
+    round_to_format,
+    format_values,
+    mx_quantize,
+    mx_dequant,
+    act_values,
 )

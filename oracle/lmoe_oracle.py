@@ -43,6 +43,21 @@ byte m; E8M0 byte 255 is NaN; NaN logits rank below -inf, equal NaNs by index;
 Every product x*w is exact in float64 (bf16 times a 2-significant-bit E2M1
 value times a power of two), so the only deviation from exact arithmetic is
 float64 summation and the stated bf16/fp32 roundings.
+
+Quantised activations (optional, routed experts only). The pages list the
+routed-expert GEMMs of their MI355X engine as FP8 activations with MXFP4
+weights for small decode and MXFP4 activations with MXFP4 weights for prefill
+(TokenSpeed, the precision table, row "Routed-expert GEMMs"); the shared
+experts and the router stay bf16 (same table). The pages give no scale
+granularity for the activations. Reading taken: the MX scheme the weights
+already use, one E8M0 power-of-two scale per 32 consecutive values along K
+for both element formats (FP8 E4M3 and FP4 E2M1). A block's scale exponent is
+floor(log2(max |v|)) minus the element format's largest exponent (8 for E4M3,
+2 for E2M1), clamped to the E8M0 range; a block of zeros takes 2^0. Each
+element is v / 2^X rounded to the nearest representable value, ties to the
+even code, saturating at the format's largest finite value (448, 6). The
+gate/up input is the token's bf16 row; the down input is h after its bf16
+rounding.
 """
 from __future__ import annotations
 
@@ -205,6 +220,101 @@ def permute_routes(idx: np.ndarray, E: int):
 
 
 # ----------------------------------------------------------------------------
+# Quantised activations (the reading in the module docstring)
+# ----------------------------------------------------------------------------
+
+ACT_FORMATS = ("bf16", "e4m3", "e2m1")
+# largest exponent of a finite element value: E4M3 448 = 1.75 * 2^8, E2M1 6 = 1.5 * 2^2
+ACT_EMAX = {"e4m3": 8, "e2m1": 2}
+
+
+def e4m3_table() -> np.ndarray:
+    """Value of each of the 256 FP8 E4M3 codes (float64): sign bit 7,
+    exponent bits 6..3 with bias 7, mantissa bits 2..0; exponent 0 holds the
+    subnormals m/8 * 2^-6; no infinities, and S.1111.111 is NaN."""
+    t = np.empty(256, np.float64)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 0xF, c & 7
+        if e == 15 and m == 7:
+            t[c] = np.nan
+        elif e == 0:
+            t[c] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            t[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return t
+
+
+def _magnitudes(fmt: str) -> np.ndarray:
+    """Non-negative finite values of a format, indexed by magnitude code."""
+    if fmt == "e2m1":
+        return np.asarray(E2M1_MAGNITUDES, np.float64)
+    return e4m3_table()[:127]          # codes 0..126: 0 .. 448
+
+
+def round_to_format(q: np.ndarray, fmt: str) -> np.ndarray:
+    """Codes of the values q (float64, finite) in an element format: the
+    nearest representable magnitude, a tie to the even magnitude code,
+    beyond the largest finite value that value; the sign bit from q's sign
+    (so -0 and small negatives keep it). E2M1 codes are 4-bit (sign bit 3),
+    E4M3 codes 8-bit (sign bit 7)."""
+    q = np.asarray(q, np.float64)
+    mags = _magnitudes(fmt)
+    a = np.abs(q)
+    # index of the largest grid value <= a (a >= 0 = mags[0])
+    lo = np.clip(np.searchsorted(mags, a, side="right") - 1, 0, mags.size - 1)
+    hi = np.minimum(lo + 1, mags.size - 1)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
+    code = np.where(take_hi, hi, lo)
+    code = np.where(a >= mags[-1], mags.size - 1, code)       # saturation
+    sign_bit = 0x8 if fmt == "e2m1" else 0x80
+    return (code | np.where(np.signbit(q), sign_bit, 0)).astype(np.uint8)
+
+
+def format_values(codes: np.ndarray, fmt: str) -> np.ndarray:
+    """Values (float64) of element codes."""
+    table = e2m1_table() if fmt == "e2m1" else e4m3_table()
+    return table[np.asarray(codes, np.int64)]
+
+
+def mx_quantize(v: np.ndarray, fmt: str):
+    """Quantise values v [..., K] (float64, finite, K a multiple of 32) per
+    32-value block along the last axis. Returns (codes uint8 [..., K],
+    exponent bytes uint8 [..., K/32])."""
+    v = np.asarray(v, np.float64)
+    K = v.shape[-1]
+    blocks = v.reshape(v.shape[:-1] + (K // 32, 32))
+    amax = np.abs(blocks).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - ACT_EMAX[fmt],
+                     0.0)
+    byte = np.clip(X + E8M0_BIAS, 0, 254).astype(np.int64)
+    q = blocks / np.ldexp(1.0, byte - E8M0_BIAS)[..., None]    # exact: a power of two
+    codes = round_to_format(q, fmt).reshape(v.shape)
+    return codes, byte.astype(np.uint8)
+
+
+def mx_dequant(codes: np.ndarray, exps: np.ndarray, fmt: str) -> np.ndarray:
+    """Values of MX-quantised activations (inverse of the layout of
+    mx_quantize), float64."""
+    vals = format_values(codes, fmt)
+    K = vals.shape[-1]
+    scale = np.repeat(e8m0_scale(exps), 32, axis=-1).reshape(vals.shape[:-1] + (K,))
+    return vals * scale
+
+
+def act_values(v: np.ndarray, act: str) -> np.ndarray:
+    """The activation values a routed GEMM consumes: v itself for bf16,
+    else v quantised per the reading above and dequantised."""
+    if act == "bf16":
+        return np.asarray(v, np.float64)
+    if act not in ACT_EMAX:
+        raise ValueError(f"unknown activation format {act!r}")
+    return mx_dequant(*mx_quantize(v, act), act)
+
+
+# ----------------------------------------------------------------------------
 # Experts
 # ----------------------------------------------------------------------------
 
@@ -213,17 +323,21 @@ def silu(z: np.ndarray) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
-def glu_ffn(xs: np.ndarray, gate: np.ndarray, up: np.ndarray, down: np.ndarray):
+def glu_ffn(xs: np.ndarray, gate: np.ndarray, up: np.ndarray, down: np.ndarray,
+            act: str = "bf16"):
     """One expert on the rows xs [m][L] (float64 values).
 
     gate, up: [I][L]; down: [L][I] (float64 values).
     Returns (h_bits uint16 [m][I], y float64 [m][L]) with
-    h = bf16(silu(xs gate^T) * (xs up^T)) and y = h down^T.
+    h = bf16(silu(a(xs) gate^T) * (a(xs) up^T)) and y = a(h) down^T, where a
+    is the identity for bf16 activations and the quantisation of act_values
+    otherwise.
     """
-    g = xs @ gate.T
-    u = xs @ up.T
+    xa = act_values(xs, act)
+    g = xa @ gate.T
+    u = xa @ up.T
     h_bits = bf16_from_f64(silu(g) * u)
-    y = f64_from_bf16(h_bits) @ down.T
+    y = act_values(f64_from_bf16(h_bits), act) @ down.T
     return h_bits, y
 
 
@@ -266,13 +380,15 @@ def _shared_outputs(x64: np.ndarray, shared: Mapping[str, np.ndarray]):
 def forward_tokens(x_bits: np.ndarray, idx: np.ndarray, w: np.ndarray,
                    get_expert: Callable[[int], Mapping[str, np.ndarray]],
                    shared: Mapping[str, np.ndarray], L: int, I: int,
-                   tokens: Optional[Sequence[int]] = None):
+                   tokens: Optional[Sequence[int]] = None, act: str = "bf16"):
     """Routed + shared FFN and combine for the listed tokens (all by default),
     given their routing (idx [T][k], w [T][k]).
 
     get_expert(e) returns expert e's codes and scales (the generator's layout).
     Experts are visited once each, serving every listed route that selects
-    them. Returns (out float64 [n][L], out bf16 bits [n][L]).
+    them. act: the routed experts' activation format (ACT_FORMATS); the
+    shared experts stay bf16. Returns (out float64 [n][L], out bf16 bits
+    [n][L]).
     """
     T, k = idx.shape
     toks = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
@@ -283,7 +399,7 @@ def forward_tokens(x_bits: np.ndarray, idx: np.ndarray, w: np.ndarray,
     for e in np.unique(sel):
         rows, slots = np.nonzero(sel == e)
         gate, up, down = _expert_values(get_expert(int(e)), L, I)
-        _, y = glu_ffn(x64[rows], gate, up, down)
+        _, y = glu_ffn(x64[rows], gate, up, down, act)
         y_routed[rows, slots] = y
     y_sh = _shared_outputs(x64, shared)
     return combine(y_routed, np.asarray(w)[toks], y_sh)
@@ -291,11 +407,13 @@ def forward_tokens(x_bits: np.ndarray, idx: np.ndarray, w: np.ndarray,
 
 def forward(x_bits: np.ndarray, router_bits: Optional[np.ndarray],
             experts: Mapping[str, np.ndarray], shared: Mapping[str, np.ndarray],
-            k: int, logits: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+            k: int, logits: Optional[np.ndarray] = None,
+            act: str = "bf16") -> Dict[str, np.ndarray]:
     """The whole layer on every token.
 
     experts holds stacked [E][...] codes and scales; logits, when given, replace
-    the router step. Returns every intermediate the layer exposes.
+    the router step; act is the routed experts' activation format. Returns
+    every intermediate the layer exposes.
     """
     T, L = np.asarray(x_bits).shape
     E, I = experts["gate_q"].shape[0], experts["gate_q"].shape[1]
@@ -310,7 +428,7 @@ def forward(x_bits: np.ndarray, router_bits: Optional[np.ndarray],
         return {key: experts[key][e] for key in
                 ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")}
 
-    out64, out_bits = forward_tokens(x_bits, idx, w, get, shared, L, I)
+    out64, out_bits = forward_tokens(x_bits, idx, w, get, shared, L, I, act=act)
     return {"logits": logits, "idx": idx, "w": w, "counts": counts,
             "offsets": offsets, "perm": perm, "inv": inv,
             "out64": out64, "out": out_bits}

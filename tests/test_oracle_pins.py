@@ -1,10 +1,10 @@
 """Pins of the CPU oracle against facts that do not come from the oracle itself.
 
 Each test checks the oracle against one of: the format definition of E2M1 /
-E8M0 written out with exact rationals, hand-worked fixtures under
+E8M0 / E4M3 written out with exact rationals, hand-worked fixtures under
 tests/golden/, brute force on tiny inputs, independent library routines
-(numpy sorting and counting, scipy's softmax, torch's float32->bfloat16
-conversion), closed-form special cases of the GLU FFN, and invariants of the
+(numpy sorting and counting, scipy's softmax, torch's float32->bfloat16 and
+float32->float8_e4m3fn conversions), closed-form special cases of the GLU FFN, and invariants of the
 layer (expert relabelling, identical experts, token permutation, scaling of
 the down projection). Each is chosen so that a plausible slip in the oracle
 (a swapped nibble, a dropped shared expert, a transposed weight, a reversed
@@ -488,3 +488,196 @@ def test_forward_tokens_subset_matches_full_forward():
     ref = full["out64"][toks]
     assert np.max(np.abs(o64 - ref)) <= 1e-12 * np.max(np.abs(ref))
     assert np.mean(ob == full["out"][toks]) > 0.999
+
+
+# ----------------------------------------------------------------------------
+# Quantised activations (E4M3 / E2M1 elements, one E8M0 scale per 32)
+# ----------------------------------------------------------------------------
+
+def _e4m3_from_bits(c: int):
+    """E4M3 by its bit fields, exact; None for the NaN codes."""
+    s, e, m = (c >> 7) & 1, (c >> 3) & 15, c & 7
+    if e == 15 and m == 7:
+        return None
+    mag = Fraction(m, 8) * Fraction(1, 64) if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+    return -mag if s else mag
+
+
+def test_e4m3_table_matches_bit_fields_and_torch():
+    import torch
+    t = O.e4m3_table()
+    for c in range(256):
+        ref = _e4m3_from_bits(c)
+        if ref is None:
+            assert np.isnan(t[c])
+        else:
+            assert t[c] == float(ref) and math.copysign(1, t[c]) == (-1 if c & 0x80 else 1)
+    via_torch = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    tt = via_torch.to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(tt), np.isnan(t))
+    assert np.array_equal(tt[~np.isnan(tt)], t[~np.isnan(t)])
+    assert t[0x7E] == 448.0 and t[0x01] == 2.0 ** -9
+
+
+def _brute_round(q: float, fmt: str) -> int:
+    """Nearest grid magnitude by exhaustive comparison, ties to the even
+    code, saturating; the sign bit from q's sign."""
+    mags = [_e2m1_from_bits(c) for c in range(8)] if fmt == "e2m1" else \
+        [_e4m3_from_bits(c) for c in range(127)]
+    a = abs(Fraction(q))
+    if a >= mags[-1]:
+        code = len(mags) - 1
+    else:
+        best = min(abs(m - a) for m in mags)
+        near = [i for i, m in enumerate(mags) if abs(m - a) == best]
+        code = near[0] if len(near) == 1 else [i for i in near if i % 2 == 0][0]
+    sign = (0x8 if fmt == "e2m1" else 0x80) if math.copysign(1, q) < 0 else 0
+    return code | sign
+
+
+@pytest.mark.parametrize("fmt", ["e2m1", "e4m3"])
+def test_round_to_format_brute_force(fmt):
+    rng = np.random.default_rng(5)
+    mags = np.array([float(_e2m1_from_bits(c)) for c in range(8)]) if fmt == "e2m1" else \
+        O.e4m3_table()[:127]
+    mids = (mags[:-1] + mags[1:]) / 2
+    top = mags[-1]
+    q = np.concatenate([mids, -mids, mags, -mags, [0.0, -0.0, top * 1.01, -top * 3, top * 100],
+                        rng.normal(size=200) * top / 3, rng.uniform(-top, top, size=200),
+                        np.ldexp(rng.uniform(1, 2, size=60), rng.integers(-12, 2, size=60))])
+    got = O.round_to_format(q, fmt)
+    want = np.array([_brute_round(float(v), fmt) for v in q], np.uint8)
+    assert np.array_equal(got, want)
+
+
+def test_round_to_format_e4m3_matches_torch_cast():
+    import torch
+    rng = np.random.default_rng(6)
+    q = np.concatenate([rng.uniform(-448, 448, size=4000), rng.normal(size=4000) * 0.01,
+                        (O.e4m3_table()[:126] + O.e4m3_table()[1:127]) / 2])
+    q32 = q.astype(np.float32)
+    ref = torch.from_numpy(q32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.round_to_format(q32.astype(np.float64), "e4m3"), ref)
+
+
+def test_mx_quantize_golden_cases():
+    with open(os.path.join(GOLDEN, "mx_act_cases.txt")) as f:
+        lines = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    assert len(lines) == 8
+    for fmt, byte, *pairs in lines:
+        vals = [float(p.split(":")[0]) for p in pairs]
+        codes = [int(p.split(":")[1]) for p in pairs]
+        block = np.zeros((1, 32))
+        block[0, :len(vals)] = vals
+        c, e = O.mx_quantize(block, fmt)
+        assert int(e[0, 0]) == int(byte), (fmt, byte, e)
+        assert c[0, :len(codes)].tolist() == codes, (fmt, pairs, c[0, :len(codes)])
+        assert not c[0, len(codes):].any()
+
+
+@pytest.mark.parametrize("fmt", ["e2m1", "e4m3"])
+def test_mx_quantize_properties(fmt):
+    """Scale exponent by exhaustive search (the largest element lands in the
+    top binade of the element grid), error within half a grid step of the
+    scaled value, and quantising the dequantised values reproduces them."""
+    rng = np.random.default_rng(7)
+    v = rng.normal(size=(40, 64)) * np.ldexp(1.0, rng.integers(-20, 20, size=(40, 1)))
+    v[3] = 0.0
+    v = O.f64_from_bf16(O.bf16_from_f64(v))
+    codes, exps = O.mx_quantize(v, fmt)
+    emax = O.ACT_EMAX[fmt]
+    top = 6.0 if fmt == "e2m1" else 448.0
+    for r in range(v.shape[0]):
+        for b in range(2):
+            blk = v[r, 32 * b:32 * b + 32]
+            amax = np.abs(blk).max()
+            X = int(exps[r, b]) - 127
+            if amax == 0:
+                assert X == 0
+                continue
+            # the one X with 2^emax <= amax / 2^X < 2^(emax+1)
+            cands = [x for x in range(-160, 160) if 2.0 ** emax <= amax / 2.0 ** x < 2.0 ** (emax + 1)]
+            assert cands == [X]
+    deq = O.mx_dequant(codes, exps, fmt)
+    c2, e2 = O.mx_quantize(deq, fmt)
+    assert np.array_equal(c2, codes) and np.array_equal(e2, exps)
+    scale = np.repeat(O.e8m0_scale(exps), 32, axis=1)
+    q = v / scale
+    mags = np.sort(np.abs(O.format_values(np.arange(16 if fmt == "e2m1" else 127), fmt)))
+    mags = np.unique(mags)
+    # half the local grid step around each value (saturated values excepted)
+    idx = np.clip(np.searchsorted(mags, np.abs(q)), 1, mags.size - 1)
+    step = mags[idx] - mags[idx - 1]
+    inside = np.abs(q) <= top
+    assert np.all(np.abs(deq / scale - q)[inside] <= step[inside] / 2 + 1e-300)
+
+
+def test_forward_e4m3_matches_torch_float8_layer():
+    """The layer with E4M3 activations against an independent float64 torch
+    statement that quantises through torch's float8_e4m3fn cast (per-block
+    scale 2^(floor(log2 amax) - 8), values clamped to +-448 before the
+    cast)."""
+    import torch
+    w = get_workload("tiny")
+    d = w.dims
+    inp = gen_all(w)
+    ref = O.forward(inp["x"], inp["router_w"], inp, inp, d.k, act="e4m3")
+
+    def q8(v):  # [m][K] float64 torch
+        blk = v.reshape(v.shape[0], -1, 32)
+        amax = blk.abs().amax(dim=2, keepdim=True)
+        X = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)))) - 8,
+                        torch.zeros_like(amax))
+        sc = torch.pow(2.0, X)
+        e = (blk / sc).clamp(-448, 448).to(torch.float32).to(torch.float8_e4m3fn)
+        return (e.to(torch.float64) * sc).reshape(v.shape)
+
+    x = torch.from_numpy(O.f64_from_bf16(inp["x"]))
+    out = torch.zeros(d.T, d.L, dtype=torch.float64)
+    idx, wts = ref["idx"], ref["w"].astype(np.float64)
+    for t in range(d.T):
+        for j in range(d.k):
+            e = int(idx[t, j])
+            ex = gen_expert(w, e)
+            G = torch.from_numpy(O.dequant_mxfp4(ex["gate_q"], ex["gate_s"], d.I, d.L))
+            U = torch.from_numpy(O.dequant_mxfp4(ex["up_q"], ex["up_s"], d.I, d.L))
+            D = torch.from_numpy(O.dequant_mxfp4(ex["down_q"], ex["down_s"], d.L, d.I))
+            xa = q8(x[t:t + 1])
+            g, u = xa @ G.T, xa @ U.T
+            hh = (g * torch.sigmoid(g) * u).to(torch.bfloat16).to(torch.float64)
+            out[t] += wts[t, j] * (q8(hh) @ D.T)[0]
+        for sidx in range(d.S):
+            G = torch.from_numpy(O.f64_from_bf16(inp["sh_gate"][sidx]))
+            U = torch.from_numpy(O.f64_from_bf16(inp["sh_up"][sidx]))
+            D = torch.from_numpy(O.f64_from_bf16(inp["sh_down"][sidx]))
+            g, u = x[t:t + 1] @ G.T, x[t:t + 1] @ U.T
+            hh = (g * torch.sigmoid(g) * u).to(torch.bfloat16).to(torch.float64)
+            out[t] += (hh @ D.T)[0]
+    assert np.allclose(ref["out64"], out.numpy(), rtol=1e-12, atol=1e-12)
+    # and the quantisation did something: the bf16 layer differs
+    plain = O.forward(inp["x"], inp["router_w"], inp, inp, d.k)
+    assert not np.allclose(plain["out64"], ref["out64"], rtol=1e-6, atol=0)
+
+
+def test_forward_activation_formats_reduce_when_representable():
+    """Tokens whose every 32-block is already an E2M1 block (grid values times
+    a power of two, the block maximum in the top binade) give the same gate
+    and up products in every activation format; zero-gate experts then leave
+    the quantised layer equal to the plain one."""
+    w = get_workload("tiny")
+    d = w.dims
+    inp = gen_all(w)
+    rng = np.random.default_rng(9)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6.0])
+    v = rng.choice(grid, size=(d.T, d.L)) * rng.choice([-1, 1], size=(d.T, d.L))
+    v[:, ::32] = 6.0
+    v = v * np.ldexp(1.0, rng.integers(-3, 3, size=(d.T, d.L // 32))).repeat(32, axis=1)
+    x = O.bf16_from_f64(v)
+    for fmt in ("e2m1", "e4m3"):
+        assert np.array_equal(O.act_values(O.f64_from_bf16(x), fmt), O.f64_from_bf16(x))
+    zero = dict(inp)
+    zero["gate_q"] = np.zeros_like(inp["gate_q"])
+    a = O.forward(x, inp["router_w"], zero, inp, d.k)
+    for fmt in ("e2m1", "e4m3"):
+        b = O.forward(x, inp["router_w"], zero, inp, d.k, act=fmt)
+        assert np.array_equal(a["out"], b["out"])
