@@ -34,6 +34,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0     # dense fp8 MFMA (an FP8 x FP4 product runs at the fp8 rate)
+FP4_PEAK_TFLOPS = 10100.0    # dense fp4 MFMA
+# quantised activations of the routed experts (lmoe_exec.act_format):
+# workload-name suffix -> (act format name, MFMA peak of its routed GEMMs)
+ACT_SUFFIX = {"_a8": ("e4m3", FP8_PEAK_TFLOPS), "_a4": ("e2m1", FP4_PEAK_TFLOPS)}
 N_TOKENS = 64
 N_REPLICAS = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
@@ -148,6 +153,7 @@ KERNEL_SOURCES = {
     "decode_multi_kernel": "decode_multi.hip",
     "gemm_packed": "packed.hip",
     "pack_": "packed.hip",
+    "quantize_act": "packed.hip",
     "read_stream": "experts.hip",
     "gemm_large": "experts.hip",
     "gemm_small": "experts.hip",
@@ -306,7 +312,7 @@ def routing_buffers(d, dev):
 
 
 def run_case(lm, hip, name, dev, steps, warmup, rotate: bool, traced_steps: int,
-             packed: bool = False, path=None):
+             packed: bool = False, path=None, act: str = "bf16"):
     """Time `steps` layer calls; returns a dict of measurements. packed: the
     tile-packed routed experts and lmoe_forward_packed (shared experts on a
     second stream of the bench's own). path: lmoe_forward_ex with that path
@@ -322,11 +328,14 @@ def run_case(lm, hip, name, dev, steps, warmup, rotate: bool, traced_steps: int,
     side = torch.cuda.Stream() if own else None
     fork, join = (hip.event(), hip.event()) if own else (None, None)
 
+    act_code = {"bf16": lm.ACT_BF16, "e4m3": lm.ACT_E4M3, "e2m1": lm.ACT_E2M1}[act]
+
     def fwd(d, xi, wi, lg, r, out, ws, events=None):
         if packed and events is not None:
-            lm.forward_packed(d, xi, wi, lg, r, out, ws, stage_events=events)
+            lm.forward_packed(d, xi, wi, lg, r, out, ws, stage_events=events, act=act_code)
         elif packed:
-            lm.forward_packed(d, xi, wi, lg, r, out, ws, side.cuda_stream, fork, join)
+            lm.forward_packed(d, xi, wi, lg, r, out, ws, side.cuda_stream, fork, join,
+                              act=act_code)
         elif path is not None and events is not None:
             lm.forward_ex(d, xi, wi, lg, r, out, ws, stage_events=events, path=path)
         elif path is not None:
@@ -414,7 +423,8 @@ def run_case(lm, hip, name, dev, steps, warmup, rotate: bool, traced_steps: int,
     del experts, dense, x_pool, ws, out
     torch.cuda.empty_cache()
     return {"w": w, "D": D_mean, "ms": ms, "enqueue_ms": enq_ms / steps, "warm_ms": warm_ms,
-            "stage_ms": stage_ms, "traced_ms": traced_total, "packed": packed, "path": path}
+            "stage_ms": stage_ms, "traced_ms": traced_total, "packed": packed, "path": path,
+            "act": act}
 
 
 # The single-token path is one kernel; the library records every stage event
@@ -453,7 +463,13 @@ def kernel_units(res, lm):
         return [(FUSED_KERNELS[path], tb, tf, res["ms"] * 1e-3)]
     large = True  # routed groups of every size take the large kernel
     sh_large = d.T > 64
-    packed_kernel = {"gate_up": "gemm_packed_kernel<true>", "down": "gemm_packed_kernel<false>"}
+    act = res.get("act", "bf16")
+    if act == "bf16":
+        packed_kernel = {"gate_up": "gemm_packed_kernel<true>", "down": "gemm_packed_kernel<false>"}
+    else:
+        f8 = "true" if act == "e4m3" else "false"
+        packed_kernel = {"gate_up": f"gemm_packed_q_kernel<true, {f8}>",
+                         "down": f"gemm_packed_q_kernel<false, {f8}>"}
     return [((packed_kernel.get(s) if res.get("packed") else None)
              or stage_kernel(s, large, sh_large, d, logits_given), sb[s], sf[s],
              res["stage_ms"][s] * 1e-3)
@@ -505,7 +521,11 @@ def roofline_for(res, bound: str, lm):
     if bound == "hbm":
         achieved, peak, unit = nbytes / sec / 1e9, HBM_PEAK_GBS, "GB/s"
     else:
-        achieved, peak, unit = flops / sec / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+        mfma_peak = {"bf16": BF16_PEAK_TFLOPS, "e4m3": FP8_PEAK_TFLOPS,
+                     "e2m1": FP4_PEAK_TFLOPS}[res.get("act", "bf16")]
+        if not kernel.startswith("gemm_packed"):   # the bf16 kernels of the same layer
+            mfma_peak = BF16_PEAK_TFLOPS
+        achieved, peak, unit = flops / sec / 1e12, mfma_peak, "TFLOP/s"
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4),
             "traffic": measured_traffic(kernel, res["w"].name),
@@ -633,32 +653,44 @@ def cpu_baseline_prefill(n_experts: int, n_tokens: int):
 # the layer, the expert width the pages' per-expert size implies, and one
 # GPU's share of the layer split eight ways. Decode-sized ones are HBM-bound
 # and rotate tokens like the headline case; the rest are rated against MFMA.
-EXTRA = ("batched_decode", "skewed", "decode_i3072", "prefill_i3072", "decode_tp8")
-# reported by default: the other graded configurations and the page-implied
-# expert width at decode
-DEFAULT_EXTRA = "batched_decode,skewed,decode_i3072"
+EXTRA = ("batched_decode", "skewed", "decode_i3072", "prefill_i3072", "decode_tp8",
+         "prefill_a4", "batched_decode_a8", "skewed_a4")
+# reported by default: the other graded configurations, the page-implied
+# expert width at decode, and the pages' quantised-activation precisions
+# (MXFP4 activations at prefill, FP8 at batched decode)
+DEFAULT_EXTRA = "batched_decode,skewed,decode_i3072,prefill_a4,batched_decode_a8"
 
 
 def extra_case(lm, hip, name, dev, steps, packed: bool, path=None):
     from workloads import get_workload
+    act, mfma_peak = "bf16", BF16_PEAK_TFLOPS
+    for suf, (a, pk) in ACT_SUFFIX.items():
+        if name.endswith(suf):   # quantised activations: packed experts only
+            name, act, mfma_peak, packed = name[: -len(suf)], a, pk, True
     d = get_workload(name).dims
     hbm = d.T <= 64
     # single tokens take the one-kernel path on row-major experts
     packed = packed and d.T > 1 and path is None
     res = run_case(lm, hip, name, dev, steps if hbm else max(3, steps // 20), 3, rotate=hbm,
-                   traced_steps=5, packed=packed, path=path)
+                   traced_steps=5, packed=packed, path=path, act=act)
     tb, tf, _, _ = algorithmic(d, res["D"], res["w"].logits_given)
     sec = res["ms"] * 1e-3
+    # with quantised activations the routed GEMMs' MFMA ridge (fp8 625, fp4
+    # 1262 flop/byte at 8 TB/s) is far above the layer's intensity even at
+    # prefill: their roofline is HBM's
+    bound = "hbm" if hbm or (act != "bf16" and
+                             tf / tb < mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)) else "mfma"
     out = {"T": d.T, "L": d.L, "E": d.E, "k": d.k, "I": d.I, "S": d.S, "Is": d.Is,
            "distinct_experts": round(res["D"], 1), "ms_per_step": round(res["ms"], 5),
            "gb_s": round(tb / sec / 1e9, 1), "tflop_s": round(tf / sec / 1e12, 2),
            "algorithmic_bytes": round(tb), "algorithmic_flops": round(tf),
            "layout": "packed" if packed else "row-major",
            "path": taken_path(res, lm),
-           "roofline": roofline_for(res, "hbm" if hbm else "mfma", lm),
+           "act_format": act,
+           "roofline": roofline_for(res, bound, lm),
            "stage_us": stage_us(res, lm)}
-    out["frac_of_peak"] = round(out["gb_s"] / HBM_PEAK_GBS if hbm
-                                else out["tflop_s"] / BF16_PEAK_TFLOPS, 4)
+    out["frac_of_peak"] = round(out["gb_s"] / HBM_PEAK_GBS if bound == "hbm"
+                                else out["tflop_s"] / mfma_peak, 4)
     log(f"{name}: {res['ms']:.4f} ms/step, {out['gb_s']} GB/s, {out['tflop_s']} TFLOP/s")
     return out
 

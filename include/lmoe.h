@@ -138,7 +138,9 @@ typedef struct lmoe_routing {
 #define LMOE_FUSED_MULTI_BYTES ((size_t)800 << 20)
 
 /* Bytes of device workspace lmoe_route / lmoe_forward need for these
- * dimensions (the same value serves both). Returns 0 for invalid dims.
+ * dimensions (the same value serves every entry point and option, the
+ * quantised activations of lmoe_exec.act_format included). Returns 0 for
+ * invalid dims.
  * The workspace must be zero-filled before its first use; every call leaves
  * its first LMOE_COUNTER_BYTES (the decode kernels' dependency counters)
  * zeroed again, so a workspace can be reused across calls and dimensions.
@@ -204,11 +206,27 @@ typedef struct lmoe_exec {
   /* LMOE_PATH_AUTO (0): the implementation lmoe_path_name reports;
    * LMOE_PATH_GROUPED: the grouped kernels whatever T;
    * LMOE_PATH_FUSED: a fused decode kernel wherever its limits allow one
-   * (lmoe_path_name's conditions without the byte threshold), else grouped */
+   * (lmoe_path_name's conditions without the byte threshold), else grouped;
+   * any other value is LMOE_ERR_SHAPE */
   int32_t path;
+  /* The routed experts' activation precision. LMOE_ACT_BF16 (0): bf16
+   * activations (w4a16, the layer's reference numerics). LMOE_ACT_E4M3 and
+   * LMOE_ACT_E2M1: the routed GEMMs' inputs (each token's row for gate/up, h
+   * after its bf16 rounding for down) quantised to FP8 E4M3 or FP4 E2M1
+   * elements with one E8M0 scale per 32 values along K, and multiplied with
+   * the MXFP4 weights on gfx950's scaled MFMA. dev48.org "Kimi K3 on AMD
+   * Instinct GPUs with TokenSpeed", precision table, row "Routed-expert
+   * GEMMs": FP8/MXFP4 for small decode, MXFP4/MXFP4 for prefill; the pages
+   * give no activation scale granularity, the weights' MX scheme is taken:
+   * scale exponent floor(log2 max|v|) - emax (8 for E4M3, 2 for E2M1),
+   * elements rounded to nearest, ties to the even code, saturating at 448 /
+   * 6. The shared experts and the router stay bf16. Only with
+   * lmoe_forward_packed and L, I multiples of 128 (else LMOE_ERR_SHAPE). */
+  int32_t act_format;
 } lmoe_exec;
 
 enum { LMOE_PATH_AUTO = 0, LMOE_PATH_GROUPED = 1, LMOE_PATH_FUSED = 2 };
+enum { LMOE_ACT_BF16 = 0, LMOE_ACT_E4M3 = 1, LMOE_ACT_E2M1 = 2 };
 
 /* lmoe_forward with the shared experts' stream chosen by the caller instead
  * of the library's per-device second stream: exec NULL (or its side_stream
@@ -376,6 +394,16 @@ const char* lmoe_path_name(const lmoe_dims* dims, int logits_given);
  * K % 32 == 0, rows >= 0. Errors: LMOE_ERR_NULL, _SHAPE, _ALIGN, _HIP. */
 int lmoe_debug_dequant_mxfp4(const uint8_t* q, const uint8_t* s, int32_t rows, int32_t K,
                              uint16_t* out, void* stream);
+
+/* Test hook: quantise a bf16 matrix with the device routine the quantised
+ * activation path uses (lmoe_exec.act_format).
+ *   src    bf16 [rows][K] device;  act_format LMOE_ACT_E4M3 or LMOE_ACT_E2M1
+ *   codes  E4M3: u8 [rows][K]; E2M1: u8 [rows][K/2], element 2m in the low
+ *          nibble of byte m (device)
+ *   exps   u8 [rows][K/32] E8M0 (device)
+ * K % 32 == 0, rows >= 0. Errors: LMOE_ERR_NULL, _SHAPE, _ALIGN, _HIP. */
+int lmoe_debug_quantize_act(const uint16_t* src, int32_t rows, int32_t K, int32_t act_format,
+                            uint8_t* codes, uint8_t* exps, void* stream);
 
 /* Measurement hook: read every byte of p (device, 16-byte aligned, bytes a
  * multiple of 16) once with 16-byte loads from `blocks` workgroups of 256

@@ -47,7 +47,8 @@ COUNTER_BYTES = 256 << 10
 EXPORTS = ("lmoe_workspace_bytes", "lmoe_route", "lmoe_forward", "lmoe_forward_ex",
            "lmoe_forward_traced", "lmoe_wait_errors", "lmoe_forward_noalloc", "lmoe_stage_name", "lmoe_path_name",
            "lmoe_debug_dequant_mxfp4", "lmoe_status_string", "lmoe_packed_sizes_of",
-           "lmoe_pack_weights", "lmoe_forward_packed", "lmoe_debug_read_stream")
+           "lmoe_pack_weights", "lmoe_forward_packed", "lmoe_debug_read_stream",
+           "lmoe_debug_quantize_act")
 # members of lmoe_packed_sizes / the packed routed-expert arrays
 PACKED_KEYS = ("gu_q", "gu_s", "down_q", "down_s")
 
@@ -75,18 +76,20 @@ class lmoe_routing(ctypes.Structure):
 class lmoe_exec(ctypes.Structure):
     _fields_ = [("side_stream", ctypes.c_void_p), ("fork_event", ctypes.c_void_p),
                 ("join_event", ctypes.c_void_p), ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
-                ("path", ctypes.c_int32)]
+                ("path", ctypes.c_int32), ("act_format", ctypes.c_int32)]
 
 
 # lmoe_exec.path
 PATH_AUTO, PATH_GROUPED, PATH_FUSED = 0, 1, 2
+# lmoe_exec.act_format
+ACT_BF16, ACT_E4M3, ACT_E2M1 = 0, 1, 2
 
 
-def _exec(side_stream, fork_event, join_event, stage_events, path=PATH_AUTO):
-    if side_stream is None and stage_events is None and path == PATH_AUTO:
+def _exec(side_stream, fork_event, join_event, stage_events, path=PATH_AUTO, act=ACT_BF16):
+    if side_stream is None and stage_events is None and path == PATH_AUTO and act == ACT_BF16:
         return None
     ex = lmoe_exec(side_stream and int(side_stream), fork_event and int(fork_event),
-                   join_event and int(join_event), None, int(path))
+                   join_event and int(join_event), None, int(path), int(act))
     if stage_events is not None:
         if len(stage_events) != NUM_STAGE_EVENTS:
             raise ValueError(f"need {NUM_STAGE_EVENTS} events")
@@ -158,6 +161,9 @@ def _load() -> ctypes.CDLL:
     lib.lmoe_path_name.restype = ctypes.c_char_p
     lib.lmoe_stage_name.argtypes = [ctypes.c_int]
     lib.lmoe_stage_name.restype = ctypes.c_char_p
+    lib.lmoe_debug_quantize_act.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            vp, vp, vp]
+    lib.lmoe_debug_quantize_act.restype = ctypes.c_int
     lib.lmoe_debug_read_stream.argtypes = [vp, sz, vp, i32, vp]
     lib.lmoe_debug_read_stream.restype = ctypes.c_int
     lib.lmoe_debug_dequant_mxfp4.argtypes = [vp, vp, i32, i32, vp, vp]
@@ -246,7 +252,7 @@ def forward(dims, x, weights: Mapping, logits_given: bool, routing: Optional[Map
 
 def forward_ex(dims, x, weights: Mapping, logits_given: bool, routing: Optional[Mapping], out,
                ws, side_stream=None, fork_event=None, join_event=None, stream=None,
-               stage_events=None, path=PATH_AUTO) -> None:
+               stage_events=None, path=PATH_AUTO, act=ACT_BF16) -> None:
     """forward() with the shared experts on the caller's side_stream (an int
     hipStream_t), forked and joined by the caller's fork_event / join_event
     (int hipEvent_t); side_stream None runs every stage on `stream`.
@@ -256,7 +262,7 @@ def forward_ex(dims, x, weights: Mapping, logits_given: bool, routing: Optional[
     d = _dims(dims)
     r = _routing(routing)
     w = _weights(weights)
-    ex = _exec(side_stream, fork_event, join_event, stage_events, path)
+    ex = _exec(side_stream, fork_event, join_event, stage_events, path, act)
     code = _lib.lmoe_forward_ex(ctypes.byref(d), _ptr(x), ctypes.byref(w),
                                 int(bool(logits_given)),
                                 ctypes.byref(r) if r is not None else None, _ptr(out), _ptr(ws),
@@ -299,13 +305,14 @@ def pack_weights(dims, weights: Mapping, packed: Mapping, stream=None) -> None:
 
 def forward_packed(dims, x, weights: Mapping, logits_given: bool, routing: Optional[Mapping],
                    out, ws, side_stream=None, fork_event=None, join_event=None,
-                   stream=None, stage_events=None) -> None:
+                   stream=None, stage_events=None, act=ACT_BF16) -> None:
     """forward_ex() on tile-packed routed experts: `weights` holds router_w,
-    the PACKED_KEYS arrays and the shared-expert tensors."""
+    the PACKED_KEYS arrays and the shared-expert tensors. act: the routed
+    experts' activation format (ACT_BF16, ACT_E4M3, ACT_E2M1)."""
     d = _dims(dims)
     r = _routing(routing)
     w = lmoe_packed_weights(*[_ptr(weights.get(n)) for n, _ in lmoe_packed_weights._fields_])
-    ex = _exec(side_stream, fork_event, join_event, stage_events)
+    ex = _exec(side_stream, fork_event, join_event, stage_events, act=act)
     code = _lib.lmoe_forward_packed(ctypes.byref(d), _ptr(x), ctypes.byref(w),
                                     int(bool(logits_given)),
                                     ctypes.byref(r) if r is not None else None, _ptr(out),
@@ -356,6 +363,15 @@ def debug_read_stream(buf, sink, blocks: int, stream=None) -> None:
     code = _lib.lmoe_debug_read_stream(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                        int(blocks), _stream(stream))
     _check("lmoe_debug_read_stream", code)
+
+
+def debug_quantize_act(src, rows: int, K: int, act: int, codes, exps, stream=None) -> None:
+    """Quantise a bf16 [rows][K] device tensor with the device routine of the
+    quantised activation path (act ACT_E4M3 or ACT_E2M1) into codes and
+    exponent bytes (lmoe_debug_quantize_act)."""
+    code = _lib.lmoe_debug_quantize_act(_ptr(src), int(rows), int(K), int(act), _ptr(codes),
+                                        _ptr(exps), _stream(stream))
+    _check("lmoe_debug_quantize_act", code)
 
 
 def debug_dequant_mxfp4(q, s, rows: int, K: int, out, stream=None) -> None:

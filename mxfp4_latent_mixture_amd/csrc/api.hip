@@ -74,7 +74,7 @@ Plan make_packed_plan(const lmoe_dims& d) {
   return p;
 }
 
-Workspace carve_workspace(const Plan& p, void* base) {
+Workspace carve_workspace(const Plan& p, void* base, bool with_q) {
   const lmoe_dims& d = p.d;
   Workspace w = {};
   size_t off = 0;
@@ -100,6 +100,12 @@ Workspace carve_workspace(const Plan& p, void* base) {
   w.h_sh = reinterpret_cast<uint16_t*>(take(S * T * Is * 2));
   w.y = reinterpret_cast<float*>(take(R * L * 4));
   w.y_sh = reinterpret_cast<float*>(take(S * T * L * 4));
+  if (with_q) {  // last, so the layout before does not depend on it
+    w.xq = reinterpret_cast<uint8_t*>(take(T * L));
+    w.xq_s = reinterpret_cast<uint8_t*>(take(T * L / 32));
+    w.hq = reinterpret_cast<uint8_t*>(take(R * I));
+    w.hq_s = reinterpret_cast<uint8_t*>(take(R * I / 32));
+  }
   w.bytes = off;
   return w;
 }
@@ -303,7 +309,8 @@ enum class SideMode { kLibrary, kCaller };
 static int forward_impl(const lmoe_dims* dims, const uint16_t* x, const lmoe_weights* wts,
                         int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
                         size_t ws_bytes, void* stream, const hipEvent_t* ev, SideMode mode,
-                        const lmoe_exec* exec, const PackedWeights* pk = nullptr) {
+                        const lmoe_exec* exec, const PackedWeights* pk = nullptr,
+                        bool ws_with_q = true) {
   if (!dims || !wts) return LMOE_ERR_NULL;
   if (!dims_ok(*dims)) return LMOE_ERR_SHAPE;
   int st = check_routing(r, logits_given);
@@ -341,6 +348,11 @@ static int forward_impl(const lmoe_dims* dims, const uint16_t* x, const lmoe_wei
   if (pk && ((int64_t)dims->T * dims->L >= (int64_t(1) << 32) ||
              (int64_t)dims->T * dims->k * dims->I >= (int64_t(1) << 32)))
     return LMOE_ERR_SHAPE;
+  // quantised activations: tile-packed experts only, K multiples of 128
+  const int act = (mode == SideMode::kCaller && exec) ? exec->act_format : LMOE_ACT_BF16;
+  if (act != LMOE_ACT_BF16 &&
+      (act != LMOE_ACT_E4M3 && act != LMOE_ACT_E2M1 || !pk || dims->L % 128 || dims->I % 128))
+    return LMOE_ERR_SHAPE;
   Plan p = pk ? make_packed_plan(*dims) : make_plan(*dims);
   if (mode == SideMode::kCaller && exec) {
     if (exec->path == LMOE_PATH_GROUPED) {
@@ -351,7 +363,9 @@ static int forward_impl(const lmoe_dims* dims, const uint16_t* x, const lmoe_wei
       return LMOE_ERR_SHAPE;
     }
   }
-  Workspace wsp = carve_workspace(p, ws);
+  // the workspace is the one lmoe_workspace_bytes sizes (the no-alloc
+  // scratch, bf16 only, leaves out the quantised activations)
+  Workspace wsp = carve_workspace(p, ws, ws_with_q);
   if (ws_bytes < wsp.bytes) return LMOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((p.fused_decode || p.fused_multi) && !logits_given)
@@ -375,7 +389,7 @@ static int forward_impl(const lmoe_dims* dims, const uint16_t* x, const lmoe_wei
     }
   }
   auto routed = [&](hipStream_t rs, const hipEvent_t* rev) {
-    return pk ? launch_routed_packed(p, x, *pk, wsp, rt.perm, rs, rev)
+    return pk ? launch_routed_packed(p, x, *pk, wsp, rt.perm, rs, rev, act)
               : launch_routed(p, x, w, wsp, rt.perm, rs, rev);
   };
   if (!side.s) {
@@ -465,7 +479,7 @@ extern "C" int lmoe_forward_noalloc(const lmoe_dims* dims, const uint16_t* x,
                                     const lmoe_routing* r, uint16_t* out, void* stream) {
   if (!dims || !wts) return LMOE_ERR_NULL;
   if (!dims_ok(*dims)) return LMOE_ERR_SHAPE;
-  const size_t need = carve_workspace(make_plan(*dims), nullptr).bytes;
+  const size_t need = carve_workspace(make_plan(*dims), nullptr, false).bytes;
   if (need > LMOE_NOALLOC_SCRATCH_BYTES) return LMOE_ERR_WORKSPACE;
   if (dims->T == 0) return forward_impl(dims, x, wts, logits_given, r, out, nullptr, 0, stream,
                                         nullptr, SideMode::kCaller, nullptr);
@@ -483,7 +497,7 @@ extern "C" int lmoe_forward_noalloc(const lmoe_dims* dims, const uint16_t* x,
     if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
   }
   return forward_impl(dims, x, wts, logits_given, r, out, ws, LMOE_NOALLOC_SCRATCH_BYTES, stream,
-                      nullptr, SideMode::kCaller, nullptr);
+                      nullptr, SideMode::kCaller, nullptr, nullptr, false);
 }
 
 extern "C" int lmoe_wait_errors(void* ws, size_t ws_bytes, int32_t* count, void* stream) {
@@ -573,6 +587,19 @@ extern "C" int lmoe_debug_read_stream(const void* p, size_t bytes, uint32_t* sin
   if (!aligned16(p) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return LMOE_ERR_ALIGN;
   if (bytes == 0) return LMOE_OK;
   hipError_t e = launch_read_stream(p, bytes, sink, blocks, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
+}
+
+extern "C" int lmoe_debug_quantize_act(const uint16_t* src, int32_t rows, int32_t K,
+                                       int32_t act_format, uint8_t* codes, uint8_t* exps,
+                                       void* stream) {
+  if (rows < 0 || K <= 0 || K % 32) return LMOE_ERR_SHAPE;
+  if (act_format != LMOE_ACT_E4M3 && act_format != LMOE_ACT_E2M1) return LMOE_ERR_SHAPE;
+  if (rows == 0) return LMOE_OK;
+  if (!src || !codes || !exps) return LMOE_ERR_NULL;
+  if (!aligned16(src) || !aligned16(codes)) return LMOE_ERR_ALIGN;
+  hipError_t e = launch_quantize_act(src, rows, K, act_format == LMOE_ACT_E4M3, codes, exps,
+                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
 }
 

@@ -86,6 +86,10 @@ struct Workspace {
   uint16_t* h_sh;     // [S][T][Is] bf16
   float* y;           // [R][L] fp32 route partials, sorted route order
   float* y_sh;        // [S][T][L] fp32
+  // quantised activations of the packed path (LMOE_ACT_E4M3 / _E2M1 only;
+  // sized for E4M3, one byte a value): x [T][L] and h [R][I], exponents
+  // [T][L/32] and [R][I/32]
+  uint8_t *xq, *xq_s, *hq, *hq_s;
   // fused decode (one launch per token)
   size_t bytes;       // total bytes needed
 };
@@ -130,7 +134,9 @@ constexpr int kPackedRows = 96;
 Plan make_plan(const lmoe_dims& d);
 // The plan of the packed path: 128-route row tiles.
 Plan make_packed_plan(const lmoe_dims& d);
-Workspace carve_workspace(const Plan& p, void* base);
+// with_q: room for the quantised activations (every public workspace size
+// includes it; the no-alloc entry point, bf16 only, does not)
+Workspace carve_workspace(const Plan& p, void* base, bool with_q = true);
 
 // ---- kernel launchers (route.hip) ----
 hipError_t launch_router(const Plan& p, const uint16_t* x, const uint16_t* wr, float* part,
@@ -166,9 +172,13 @@ inline hipError_t record_stage(const hipEvent_t* ev, int stage, hipStream_t s) {
 PackedSizes packed_sizes(const lmoe_dims& d);
 hipError_t launch_pack(const lmoe_dims& d, const lmoe_weights& w, uint8_t* gu_q, uint8_t* gu_s,
                        uint8_t* dn_q, uint8_t* dn_s, hipStream_t s);
+// act: LMOE_ACT_BF16, or quantised activations (E4M3 / E2M1 with E8M0
+// scales per 32, quantised into the workspace first)
 hipError_t launch_routed_packed(const Plan& p, const uint16_t* x, const PackedWeights& w,
                                 const Workspace& ws, const int32_t* perm, hipStream_t s,
-                                const hipEvent_t* ev);
+                                const hipEvent_t* ev, int act);
+hipError_t launch_quantize_act(const uint16_t* src, int64_t rows, int K, bool fp8, uint8_t* codes,
+                               uint8_t* exps, hipStream_t s);
 
 // ---- single-token decode (decode.hip) ----
 void make_decode_args(const Plan& p, DecodeArgs& a);

@@ -191,6 +191,11 @@ struct PkArgs {
   float* y_out;          // plain: fp32 [rows][N]
   int64_t out_stride;
   int n_tiles_n;         // column workgroups per row tile
+  // quantised activations (gemm_packed_q_kernel): row r's codes at
+  // aq + r * aq_stride, its exponents at as + r * K / 32
+  const uint8_t* aq;
+  const uint8_t* as;
+  int64_t aq_stride;
 };
 
 constexpr int kPkRows = 96;    // routes per row tile (three 32-row MFMA tiles)
@@ -427,16 +432,372 @@ __global__ __launch_bounds__(kPkThreads, 8 / kPkWaves) void gemm_packed_kernel(P
   }
 }
 
+// ---------------------------------------------------------------------------
+// Quantised activations: FP8 E4M3 or FP4 E2M1 elements with one E8M0 scale
+// per 32 values along K (the routed-expert precisions of dev48.org "Kimi K3
+// on AMD Instinct GPUs with TokenSpeed", precision table, row "Routed-expert
+// GEMMs"; the MX scheme of the weights for the scale). A block's scale
+// exponent is floor(log2 max|v|) minus the element format's largest exponent
+// (8 for E4M3 = 1.75 * 2^8, 2 for E2M1 = 1.5 * 2^2), clamped to the E8M0
+// range, 2^0 for a block of zeros; each element is v / 2^X (exact: a power of
+// two) rounded to nearest with ties to the even code, saturating at 448 / 6.
+// Codes: E4M3 one byte per value, E2M1 two per byte (element 2m in the low
+// nibble of byte m); exponents one byte per block.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_code(float q) {
+  const float a = fabsf(q);
+  uint32_t code;
+  if (a >= 448.f) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {  // below 2^-6: multiples of 2^-9, exact scaling
+    code = (uint32_t)rintf(a * 512.f);
+  } else {
+    const uint32_t bits = __float_as_uint(a);
+    const uint32_t e = (bits >> 23) - 120u;  // biased by 7
+    const uint32_t m = bits & 0x7FFFFFu;
+    const uint32_t r = m + 0x7FFFFu + ((m >> 20) & 1u);  // nearest, ties to even
+    code = min((e << 3) + (r >> 20), 0x7Eu);             // a carry moves to e
+  }
+  return code | ((__float_as_uint(q) >> 24) & 0x80u);
+}
+
+__device__ __forceinline__ uint32_t e2m1_code(float q) {
+  const float a = fabsf(q);
+  // midpoints of 0, .5, 1, 1.5, 2, 3, 4, 6; a tie goes to the even code
+  const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                     (a >= 3.5f) + (a > 5.0f);
+  return c | ((__float_as_uint(q) >> 28) & 0x8u);
+}
+
+// floor(log2 a) of a finite a > 0 (fp32 subnormals included)
+__device__ __forceinline__ int ilog2f(float a) {
+  const uint32_t bits = __float_as_uint(a);
+  const int e = (int)(bits >> 23);
+  if (e) return e - 127;
+  return (31 - __clz(bits & 0x7FFFFFu)) - 149;
+}
+
+// One thread per 32-value block of a bf16 [rows][K] matrix.
+template <bool FP8>
+__global__ __launch_bounds__(256) void quantize_act_kernel(const uint16_t* __restrict__ src,
+                                                           int64_t blocks, int K,
+                                                           uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ exps) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= blocks) return;
+  const int nb = K / 32;
+  const int64_t row = b / nb;
+  const int blk = (int)(b - row * nb);
+  const uint16_t* p = src + row * K + blk * 32;
+  u32x4_t v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = load16(p + 8 * i);
+  float f[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[8 * i + 2 * j] = __uint_as_float(v[i][j] << 16);
+      f[8 * i + 2 * j + 1] = __uint_as_float(v[i][j] & 0xFFFF0000u);
+    }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  const int emax = FP8 ? 8 : 2;
+  const int X = amax > 0.f ? min(max(ilog2f(amax) - emax, -127), 127) : 0;
+  exps[b] = (uint8_t)(X + 127);
+  if constexpr (FP8) {
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      w[i] = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[i] |= e4m3_code(ldexpf(f[4 * i + j], -X)) << (8 * j);
+    }
+    u32x4_t* d = reinterpret_cast<u32x4_t*>(codes + row * K + blk * 32);
+    d[0] = u32x4_t{w[0], w[1], w[2], w[3]};
+    d[1] = u32x4_t{w[4], w[5], w[6], w[7]};
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[i] = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[i] |= e2m1_code(ldexpf(f[8 * i + j], -X)) << (4 * j);
+    }
+    *reinterpret_cast<u32x4_t*>(codes + row * (K / 2) + blk * 16) =
+        u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+}
+
+hipError_t launch_quantize_act(const uint16_t* src, int64_t rows, int K, bool fp8, uint8_t* codes,
+                               uint8_t* exps, hipStream_t s) {
+  const int64_t blocks = rows * (K / 32);
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)((blocks + 255) / 256));
+  if (fp8)
+    hipLaunchKernelGGL(quantize_act_kernel<true>, grid, dim3(256), 0, s, src, blocks, K, codes,
+                       exps);
+  else
+    hipLaunchKernelGGL(quantize_act_kernel<false>, grid, dim3(256), 0, s, src, blocks, K, codes,
+                       exps);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM of quantised activations and packed MXFP4 weights on the
+// scaled MFMA, v_mfma_scale_f32_32x32x64_f8f6f4 (32 rows x 32 columns x 64 K,
+// an E8M0 scale per 32 K of each row and column). Its operand layouts, as
+// measured on gfx950 with an in-bounds probe: lane l = (row r = l % 32,
+// half h = l / 32); an FP4 operand holds K 32h .. 32h+31 (element e in nibble
+// e, low nibble first), an FP8 operand K 16h .. 16h+15 in bytes 0..15 and
+// K 32+16h .. 32+16h+15 in bytes 16..31; in both the lane's scale register
+// scales K 32h .. 32h+31 of its row.
+//
+// Same tiling as gemm_packed_kernel. In chunk c (128 K), step s (0, 1) takes
+// MX blocks 4c + s (K half 0) and 4c + 2 + s (K half 1): for the weights
+// that is packed block 4c + 2h + s of lane (r, h), as loaded; for the
+// activations the same blocks of the row from LDS. The chunk's activation
+// codes (64 or 128 bytes a row) and exponents (4 bytes a row) are copied to
+// LDS by global-to-LDS loads, each wave 32 of 128 row slots (rows past the
+// tile repeat its last row), segments XOR-swizzled by row so that the 16
+// rows an LDS read serves hit distinct banks. K must be a multiple of 128.
+// ---------------------------------------------------------------------------
+template <bool FP8>
+struct QCfg {
+  static constexpr int kRowB = FP8 ? 128 : 64;  // code bytes of a row per chunk
+  static constexpr int kRowsPerCopy = 1024 / kRowB;
+  static constexpr int kCopies = 32 / kRowsPerCopy;  // code copies per wave and chunk
+  // physical 16-byte segment of logical segment g in row r
+  static __device__ __forceinline__ int seg(int r, int g) {
+    return FP8 ? g ^ ((r >> 1) & 7) : g ^ ((r >> 2) & 3);
+  }
+};
+
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+
+template <bool FP8>
+using QChunk = uint8_t[128 * QCfg<FP8>::kRowB];
+using QExp = uint32_t[256];  // wave w's 32 rows at 64 w .. 64 w + 31
+
+template <bool GLU, bool FP8, int MT>
+__device__ __forceinline__ void pkq_body(const PkArgs& a, int e, int p0, int cnt, int nt,
+                                         QChunk<FP8>& sq0, QChunk<FP8>& sq1, QChunk<FP8>& sq2,
+                                         QExp& se0, QExp& se1, QExp& se2,
+                                         const uint32_t* s_row) {
+  using C = QCfg<FP8>;
+  auto qslot = [&](int r) -> QChunk<FP8>& { return r == 0 ? sq0 : r == 1 ? sq1 : sq2; };
+  auto eslot = [&](int r) -> QExp& { return r == 0 ? se0 : r == 1 ? se1 : se2; };
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int r32 = lane & 31, hh = lane >> 5;
+  int bt[kPkNB];
+  const uint8_t* qb[kPkNB];
+  const uint8_t* sb[kPkNB];
+#pragma unroll
+  for (int t = 0; t < kPkNB; ++t) {
+    bt[t] = (nt * kPkWaves + wave) * kPkNB + t;
+    const int btc = min(bt[t], a.N32 - 1);
+    qb[t] = a.q + e * a.q_estride + (int64_t)btc * a.K128 * 2048 + lane * 16;
+    sb[t] = a.s + e * a.s_estride + (int64_t)btc * a.K512 * 512 + lane * 8;
+  }
+  f32x16_t acc[MT][kPkNB];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int t = 0; t < kPkNB; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][t][i] = 0.f;
+
+  const int kb = a.K / 32;  // exponent bytes of an activation row
+  // this wave's 32 row slots of chunk c into LDS buffer `buf`
+  auto copy_a = [&](int c, int buf) {
+    const int cc = min(c, a.K128 - 1);
+#pragma unroll
+    for (int i = 0; i < C::kCopies; ++i) {
+      const int row0 = wave * 32 + i * C::kRowsPerCopy;
+      const int row = row0 + lane / (C::kRowB / 16);
+      const int g = C::seg(row, lane % (C::kRowB / 16));
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(a.aq + (int64_t)s_row[row] * a.aq_stride +
+                                        cc * C::kRowB + g * 16),
+          (__attribute__((address_space(3))) void*)(&qslot(buf)[row0 * C::kRowB]), 16, 0, 0);
+    }
+    // lane l < 32: the exponents of row 32 w + l; lanes 32..63 repeat them
+    // into the wave's spare slots
+    const int row = wave * 32 + (lane & 31);
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const void*>(a.as + (int64_t)s_row[row] * kb + cc * 4),
+        (__attribute__((address_space(3))) void*)(&eslot(buf)[wave * 64]), 4, 0, 0);
+  };
+  struct Bq {
+    u32x4_t q[kPkNB][2];
+  };
+  auto load_b = [&](int c, Bq& b) {
+    const int cc = min(c, a.K128 - 1);
+#pragma unroll
+    for (int t = 0; t < kPkNB; ++t)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b.q[t][j] = load16(qb[t] + (int64_t)cc * 2048 + j * 1024);
+  };
+  auto load_ex = [&](int c, uint32_t (&dst)[kPkNB]) {
+    const int cc = min(c, a.K128 - 1);
+#pragma unroll
+    for (int t = 0; t < kPkNB; ++t)
+      dst[t] = *reinterpret_cast<const uint32_t*>(sb[t] + (cc / 4) * 512 + 4 * ((cc >> 1) & 1));
+  };
+  auto compute = [&](int c, int buf, const Bq& b, const uint32_t (&ex)[kPkNB]) {
+    const uint8_t* sq = qslot(buf);
+    const QExp& se = eslot(buf);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      i32x8_t av[MT];
+      int sa[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = mt * 32 + r32;
+        const uint8_t* rp = sq + row * C::kRowB;
+        if constexpr (FP8) {
+          const u32x4_t lo =
+              *reinterpret_cast<const u32x4_t*>(rp + 16 * C::seg(row, 2 * s + hh));
+          const u32x4_t hi =
+              *reinterpret_cast<const u32x4_t*>(rp + 16 * C::seg(row, 4 + 2 * s + hh));
+          av[mt] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        } else {
+          const u32x4_t v =
+              *reinterpret_cast<const u32x4_t*>(rp + 16 * C::seg(row, 2 * hh + s));
+          av[mt] = i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        }
+        sa[mt] = (int)((se[mt * 64 + r32] >> (8 * (2 * hh + s))) & 0xFFu);
+      }
+#pragma unroll
+      for (int t = 0; t < kPkNB; ++t) {
+        const u32x4_t w = b.q[t][s];
+        const i32x8_t bv = i32x8_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+        const int sbv = (int)((ex[t] >> (8 * (2 * (c & 1) + s))) & 0xFFu);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              av[mt], bv, acc[mt][t], FP8 ? 0 : 4, 4, 0, sa[mt], 0, sbv);
+      }
+    }
+  };
+
+  // The pipeline of gemm_packed_kernel: activations and weights two chunks
+  // ahead, exponents one; groups of three chunks with the first peeled.
+  constexpr int U = 3;
+  constexpr int kAhead = C::kCopies + 1 + 2 * kPkNB;  // loads of chunk c + 2
+  constexpr int kWaitAhead = 0x0F70 | kAhead;
+  static_assert(kAhead < 16, "vmcnt field");
+  __syncthreads();  // s_row
+  Bq bq[U];
+  uint32_t ex[kPkNB], ex_next[kPkNB];
+  load_ex(0, ex_next);
+  copy_a(0, 0);
+  load_b(0, bq[0]);
+  copy_a(1, 1);
+  load_b(1, bq[1]);
+  auto group = [&](int cb, bool last) {
+#pragma unroll
+    for (int r = 0; r < U; ++r) {
+      const int c = cb + r;
+      __builtin_amdgcn_s_waitcnt(kWaitAhead);
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int t = 0; t < kPkNB; ++t) ex[t] = ex_next[t];
+      load_ex(c + 1, ex_next);
+      copy_a(c + 2, (r + 2) % U);
+      load_b(c + 2, bq[(r + 2) % U]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (!last || c < a.K128) compute(c, r, bq[r], ex);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const int full = a.K128 / U;
+  if (full > 0) group(0, false);
+  for (int g = 1; g < full; ++g) group(g * U, false);
+  if (a.K128 % U) group(full * U, true);
+  __builtin_amdgcn_s_waitcnt(0);
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < kPkNB; ++t) {
+      if (bt[t] >= a.N32) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = mt * 32 + 8 * (i / 4) + 4 * hh + (i & 3);
+        const float v = acc[mt][t][i];
+        if constexpr (GLU) {
+          const float u = __shfl_down(v, 16, kWave);
+          const int col = bt[t] * 16 + r32;
+          if (r32 < 16 && row < cnt && col < a.N)
+            a.h_out[(int64_t)(p0 + row) * a.out_stride + col] = f32_to_bf16_bits(silu(v) * u);
+        } else {
+          const int col = bt[t] * 32 + r32;
+          if (row < cnt && col < a.N) a.y_out[(int64_t)(p0 + row) * a.out_stride + col] = v;
+        }
+      }
+    }
+}
+
+template <bool GLU, bool FP8>
+__global__ __launch_bounds__(kPkThreads, 8 / kPkWaves) void gemm_packed_q_kernel(PkArgs a) {
+  __shared__ __attribute__((aligned(16))) QChunk<FP8> sq0, sq1, sq2;
+  __shared__ __attribute__((aligned(16))) QExp se0, se1, se2;
+  __shared__ uint32_t s_row[128];  // activation row of each row slot
+  const int b = blockIdx.x;
+  const int s = b / 8;
+  const int nt = s % a.n_tiles_n;
+  const int tile = (s / a.n_tiles_n) * 8 + b % 8;
+  if (tile >= *a.ntiles) return;
+  const int e = __builtin_amdgcn_readfirstlane(a.tiles[3 * tile + 0]);
+  const int p0 = __builtin_amdgcn_readfirstlane(a.tiles[3 * tile + 1]);
+  const int cnt = __builtin_amdgcn_readfirstlane(a.tiles[3 * tile + 2]);
+  for (int r = threadIdx.x; r < 128; r += kPkThreads) {
+    const int p = p0 + min(r, cnt - 1);
+    s_row[r] = (uint32_t)(a.gather ? a.gather[p] / a.gather_div : p);
+  }
+  switch ((cnt + 31) / 32) {
+    case 1: pkq_body<GLU, FP8, 1>(a, e, p0, cnt, nt, sq0, sq1, sq2, se0, se1, se2, s_row); break;
+    case 2: pkq_body<GLU, FP8, 2>(a, e, p0, cnt, nt, sq0, sq1, sq2, se0, se1, se2, s_row); break;
+    default: pkq_body<GLU, FP8, 3>(a, e, p0, cnt, nt, sq0, sq1, sq2, se0, se1, se2, s_row); break;
+  }
+}
+
 hipError_t launch_routed_packed(const Plan& p, const uint16_t* x, const PackedWeights& w,
                                 const Workspace& ws, const int32_t* perm, hipStream_t s,
-                                const hipEvent_t* ev) {
+                                const hipEvent_t* ev, int act) {
   const lmoe_dims& d = p.d;
   const int rounds = (p.max_tiles + 7) / 8;
+  const bool q = act != LMOE_ACT_BF16, fp8 = act == LMOE_ACT_E4M3;
   hipError_t err;
+  auto launch = [&](bool glu, const PkArgs& a) {
+    const dim3 grid((unsigned)(rounds * 8 * a.n_tiles_n));
+    if (!q && glu)
+      hipLaunchKernelGGL(gemm_packed_kernel<true>, grid, dim3(kPkThreads), 0, s, a);
+    else if (!q)
+      hipLaunchKernelGGL(gemm_packed_kernel<false>, grid, dim3(kPkThreads), 0, s, a);
+    else if (glu && fp8)
+      hipLaunchKernelGGL((gemm_packed_q_kernel<true, true>), grid, dim3(kPkThreads), 0, s, a);
+    else if (glu)
+      hipLaunchKernelGGL((gemm_packed_q_kernel<true, false>), grid, dim3(kPkThreads), 0, s, a);
+    else if (fp8)
+      hipLaunchKernelGGL((gemm_packed_q_kernel<false, true>), grid, dim3(kPkThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_packed_q_kernel<false, false>), grid, dim3(kPkThreads), 0, s, a);
+    return hipGetLastError();
+  };
   {  // gate/up + GLU
+    if (q && (err = launch_quantize_act(x, d.T, d.L, fp8, ws.xq, ws.xq_s, s)) != hipSuccess)
+      return err;
     PkArgs a = {};
     a.act = x;
     a.act_stride = d.L;
+    a.aq = ws.xq;
+    a.as = ws.xq_s;
+    a.aq_stride = fp8 ? d.L : d.L / 2;
     a.gather = perm;
     a.gather_div = d.k;
     a.tiles = ws.tiles;
@@ -453,15 +814,18 @@ hipError_t launch_routed_packed(const Plan& p, const uint16_t* x, const PackedWe
     a.h_out = ws.h;
     a.out_stride = d.I;
     a.n_tiles_n = (a.N32 + kPkWaves * kPkNB - 1) / (kPkWaves * kPkNB);
-    hipLaunchKernelGGL(gemm_packed_kernel<true>, dim3((unsigned)(rounds * 8 * a.n_tiles_n)),
-                       dim3(kPkThreads), 0, s, a);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = launch(true, a)) != hipSuccess) return err;
     if ((err = record_stage(ev, LMOE_STAGE_GATEUP, s)) != hipSuccess) return err;
   }
   {  // down
+    if (q && (err = launch_quantize_act(ws.h, p.R, d.I, fp8, ws.hq, ws.hq_s, s)) != hipSuccess)
+      return err;
     PkArgs a = {};
     a.act = ws.h;
     a.act_stride = d.I;
+    a.aq = ws.hq;
+    a.as = ws.hq_s;
+    a.aq_stride = fp8 ? d.I : d.I / 2;
     a.tiles = ws.tiles;
     a.ntiles = ws.ntiles;
     a.q = w.down_q;
@@ -476,9 +840,7 @@ hipError_t launch_routed_packed(const Plan& p, const uint16_t* x, const PackedWe
     a.y_out = ws.y;
     a.out_stride = d.L;
     a.n_tiles_n = (a.N32 + kPkWaves * kPkNB - 1) / (kPkWaves * kPkNB);
-    hipLaunchKernelGGL(gemm_packed_kernel<false>, dim3((unsigned)(rounds * 8 * a.n_tiles_n)),
-                       dim3(kPkThreads), 0, s, a);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = launch(false, a)) != hipSuccess) return err;
     err = record_stage(ev, LMOE_STAGE_DOWN, s);
   }
   return err;

@@ -24,13 +24,15 @@ from lmoe_testutil import (log, upload, alloc_routing, run_forward, check_out, l
 EXPERT_KEYS = ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")
 
 
-def full_small(lm, dev, w: Workload, packed: bool = False):
-    """Every token of a layer small enough for the whole oracle."""
+def full_small(lm, dev, w: Workload, packed: bool = False, act: str = "bf16"):
+    """Every token of a layer small enough for the whole oracle (act: the
+    routed experts' activation format, packed path only)."""
     d = w.dims
     inp = gen_all(w)
     dinp = upload(inp, dev)
-    got, r = run_forward(lm, w, dinp, packed=packed)
-    what = f"{w.name}{' packed' if packed else ''}"
+    act_code = {"bf16": lm.ACT_BF16, "e4m3": lm.ACT_E4M3, "e2m1": lm.ACT_E2M1}[act]
+    got, r = run_forward(lm, w, dinp, packed=packed, act=act_code)
+    what = f"{w.name}{' packed' if packed else ''}{'' if act == 'bf16' else ' ' + act}"
     if w.logits_given:
         lg = inp["logits"]
         check_routing_exact(r, lg, d.k, what)
@@ -41,10 +43,11 @@ def full_small(lm, dev, w: Workload, packed: bool = False):
         assert same.mean() >= 0.9
         lg = r["logits"]
         check_routing_exact(r, lg, d.k, f"{what} (on the GPU logits)")
-    ref = O.forward(inp["x"], None, inp, inp, d.k, logits=lg)
+    ref = O.forward(inp["x"], None, inp, inp, d.k, logits=lg, act=act)
     get = lambda e: {key: inp[key][e] for key in EXPERT_KEYS}
     check_out(got, ref["out64"], f"{what} T={d.T}",
-              allowance_fn=flip_allowance_fn(inp["x"], ref["idx"], ref["w"], get, inp, d.L, d.I))
+              allowance_fn=flip_allowance_fn(inp["x"], ref["idx"], ref["w"], get, inp, d.L, d.I,
+                                             act=act))
     return got
 
 
@@ -99,7 +102,7 @@ def full_size(lm, dev, w: Workload, n_sample, packed: bool = False):
               allowance_fn=flip_allowance_fn(inp["x"], idx, wts, get, inp, d.L, d.I))
 
 
-def every_token_isolated(lm, dev, w: Workload, packed: bool = False, path=None):
+def every_token_isolated(lm, dev, w: Workload, packed: bool = False, path=None, act: str = "bf16"):
     """Every token at full size. The workload runs with its real router,
     routing and shapes, but every expert outside a kept set has all gate codes
     zero, so its routes give h = bf16(silu(0) u) = 0 and y = 0: each output is
@@ -134,7 +137,8 @@ def every_token_isolated(lm, dev, w: Workload, packed: bool = False, path=None):
     mask = torch.ones(d.E, dtype=torch.bool, device=dev)
     mask[keep] = False
     dinp["gate_q"].view(d.E, -1)[mask] = 0
-    got, r = run_forward(lm, w, dinp, packed=packed, path=path)
+    act_code = {"bf16": lm.ACT_BF16, "e4m3": lm.ACT_E4M3, "e2m1": lm.ACT_E2M1}[act]
+    got, r = run_forward(lm, w, dinp, packed=packed, path=path, act=act_code)
     del dinp, ws
     torch.cuda.empty_cache()
     idx0 = r0["topk_idx"].cpu().numpy()
@@ -153,13 +157,13 @@ def every_token_isolated(lm, dev, w: Workload, packed: bool = False, path=None):
         gate = O.dequant_mxfp4(ex["gate_q"], ex["gate_s"], d.I, d.L)
         up = O.dequant_mxfp4(ex["up_q"], ex["up_s"], d.I, d.L)
         down = O.dequant_mxfp4(ex["down_q"], ex["down_s"], d.L, d.I)
-        _, y[rows, slots] = O.glu_ffn(x64[rows], gate, up, down)
+        _, y[rows, slots] = O.glu_ffn(x64[rows], gate, up, down, act)
     ysh = np.stack([O.glu_ffn(x64, O.f64_from_bf16(inp["sh_gate"][s]),
                               O.f64_from_bf16(inp["sh_up"][s]),
                               O.f64_from_bf16(inp["sh_down"][s]))[1] for s in range(d.S)])
     o64, _ = O.combine(y, wts, ysh)
     del y
-    check_out(got, o64, f"{w.name}{' packed' if packed else ''} every token "
-              f"({len(keep)} experts kept)",
+    check_out(got, o64, f"{w.name}{' packed' if packed else ''}"
+              f"{'' if act == 'bf16' else ' ' + act} every token ({len(keep)} experts kept)",
               allowance_fn=flip_allowance_fn(inp["x"], idx, wts, lambda e: gen_expert(w, e), inp,
-                                             d.L, d.I, experts=set(keep)))
+                                             d.L, d.I, experts=set(keep), act=act))

@@ -61,7 +61,7 @@ def pack_on_device(lm, d, dev_inp: Dict[str, object]) -> Dict[str, object]:
 
 
 def run_forward(lm, w: Workload, dev_inp: Dict[str, object], routing: Optional[dict] = None,
-                packed: bool = False, path: Optional[int] = None):
+                packed: bool = False, path: Optional[int] = None, act: int = 0):
     """Run lmoe_forward (or, packed, lmoe_pack_weights then
     lmoe_forward_packed; or, with `path`, lmoe_forward_ex on that path);
     returns (out bf16 bits numpy, routing dict of numpy)."""
@@ -76,7 +76,8 @@ def run_forward(lm, w: Workload, dev_inp: Dict[str, object], routing: Optional[d
     ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
     if packed:
         pk = pack_on_device(lm, d, dev_inp)
-        lm.forward_packed(d, dev_inp["x"], {**dev_inp, **pk}, w.logits_given, routing, out, ws)
+        lm.forward_packed(d, dev_inp["x"], {**dev_inp, **pk}, w.logits_given, routing, out, ws,
+                          act=act)
     elif path is not None:
         lm.forward_ex(d, dev_inp["x"], dev_inp, w.logits_given, routing, out, ws, path=path)
     else:
@@ -105,9 +106,16 @@ def out_bound(ref64: np.ndarray, rms: Optional[float] = None) -> np.ndarray:
 # 16 leaves a margin of four. A larger H_ACC widens the allowance below, a
 # smaller one can only make the check stricter.
 H_ACC = 16.0
+# The FP8 (E4M3) x FP4 scaled MFMA does not sum its products to fp32
+# accuracy: on random operands (40 x 2048 outputs of 512 products each,
+# in-bounds probe on gfx950) its error reached 392 * 2^-24 * sum |a b|, while
+# FP4 x FP4 sums were exact. The quantised-activation tests model g and u of
+# the E4M3 path with four times that.
+H_ACC_E4M3 = 1600.0
 
 
-def h_flip_allowance(x64: np.ndarray, gate: np.ndarray, up: np.ndarray, down: np.ndarray):
+def h_flip_allowance(x64: np.ndarray, gate: np.ndarray, up: np.ndarray, down: np.ndarray,
+                     act: str = "bf16"):
     """Allowance for one expert's GLU, per row of x64 and output column:
     where fp32 g and u may round h = bf16(silu(g) u) to the other side of a
     bf16 rounding midpoint than the float64 oracle does, the two h differ by
@@ -116,12 +124,17 @@ def h_flip_allowance(x64: np.ndarray, gate: np.ndarray, up: np.ndarray, down: np
     nearest rounding midpoint is at most the propagated evaluation error
     (H_ACC model for g and u, 8 fp32 ulp for silu and the product); each
     counted element adds twice its bf16 spacing (covering the spacing change
-    at a power of two) times |down[l, i]|. Returns [rows][L]."""
-    g = x64 @ gate.T
-    u = x64 @ up.T
-    ax = np.abs(x64)
-    dg = H_ACC * 2.0 ** -24 * (ax @ np.abs(gate).T)
-    du = H_ACC * 2.0 ** -24 * (ax @ np.abs(up).T)
+    at a power of two) times |down[l, i]|. With quantised activations (act
+    E4M3 / E2M1) the GLU reads the quantised x, and a flipped h may also move
+    its quantised value by one step of the element grid (times the block
+    scale), which is added for the counted elements. Returns [rows][L]."""
+    xa = O.act_values(x64, act)
+    g = xa @ gate.T
+    u = xa @ up.T
+    ax = np.abs(xa)
+    hacc = H_ACC_E4M3 if act == "e4m3" else H_ACC
+    dg = hacc * 2.0 ** -24 * (ax @ np.abs(gate).T)
+    du = hacc * 2.0 ** -24 * (ax @ np.abs(up).T)
     with np.errstate(over="ignore", invalid="ignore"):
         sig = 1.0 / (1.0 + np.exp(-g))
         s = g * sig
@@ -134,13 +147,27 @@ def h_flip_allowance(x64: np.ndarray, gate: np.ndarray, up: np.ndarray, down: np
     half = np.ldexp(1.0, (e - 8).astype(np.int64))       # half the bf16 spacing at |v|
     near = (av > 0) & (np.abs(np.abs(v - h) - half) <= dv)
     flip = np.where(near, 4.0 * half, 0.0)               # twice the spacing
+    if act != "bf16" and near.any():
+        codes, exps = O.mx_quantize(h, act)
+        scale = np.repeat(O.e8m0_scale(exps), 32, axis=-1).reshape(h.shape)
+        mags = np.unique(np.abs(O.format_values(np.arange(16 if act == "e2m1" else 127), act)))
+        k = np.clip(np.searchsorted(mags, np.abs(h) / scale), 1, mags.size - 1)
+        step = np.maximum(mags[k] - mags[k - 1], mags[np.minimum(k + 1, mags.size - 1)] - mags[k])
+        flip = flip + np.where(near, step * scale, 0.0)
+        # a flipped block maximum can move the block's scale exponent by one,
+        # which requantises all 32 values of the block: each may then move by
+        # a step of the grid at twice the scale
+        blk = np.abs(h).reshape(h.shape[:-1] + (-1, 32))
+        top = (blk == blk.max(axis=-1, keepdims=True)) & near.reshape(blk.shape)
+        moved = np.repeat(top.any(axis=-1), 32, axis=-1).reshape(h.shape)
+        flip = flip + np.where(moved, 2.0 * step * scale, 0.0)
     return flip @ np.abs(down).T
 
 
 def flip_allowance_fn(x_bits: np.ndarray, idx: np.ndarray, w: np.ndarray,
                       get_expert: Callable[[int], Dict[str, np.ndarray]],
                       shared: Optional[Dict[str, np.ndarray]], L: int, I: int,
-                      experts: Optional[set] = None):
+                      experts: Optional[set] = None, act: str = "bf16"):
     """fn(rows) -> [len(rows)][L]: the h-rounding allowance of those rows of
     x (h_flip_allowance of each selected expert, weighted by the token's
     softmax weight as in the combine, plus each shared expert with weight 1).
@@ -159,7 +186,7 @@ def flip_allowance_fn(x_bits: np.ndarray, idx: np.ndarray, w: np.ndarray,
             gate = O.dequant_mxfp4(ex["gate_q"], ex["gate_s"], I, L)
             up = O.dequant_mxfp4(ex["up_q"], ex["up_s"], I, L)
             down = O.dequant_mxfp4(ex["down_q"], ex["down_s"], L, I)
-            a = h_flip_allowance(x64[rr], gate, up, down)
+            a = h_flip_allowance(x64[rr], gate, up, down, act)
             acc[rr] += np.asarray(w, np.float64)[rows[rr], jj][:, None] * a
         if shared is not None:
             for sidx in range(shared["sh_gate"].shape[0]):

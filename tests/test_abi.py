@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
                             "lmoe_forward_ex", "lmoe_forward_traced", "lmoe_wait_errors",
                             "lmoe_forward_noalloc", "lmoe_packed_sizes_of",
                             "lmoe_pack_weights", "lmoe_forward_packed",
-                            "lmoe_debug_read_stream",
+                            "lmoe_debug_read_stream", "lmoe_debug_quantize_act",
                             "lmoe_stage_name", "lmoe_path_name",
                             "lmoe_debug_dequant_mxfp4", "lmoe_status_string"]), names
 
@@ -178,6 +178,41 @@ def test_dequant_hook_rejects_bad_arguments(lm):
     assert f(None, 0x2000, 4, 64, 0x3000, None) == lm.LMOE_ERR_NULL
     assert f(0x1008, 0x2000, 4, 64, 0x3000, None) == lm.LMOE_ERR_ALIGN
     assert f(0x1000, 0x2000, 0, 64, 0x3000, None) == lm.LMOE_OK
+
+
+def test_quantize_hook_rejects_bad_arguments(lm):
+    f = lm._lib.lmoe_debug_quantize_act
+    assert f(0x1000, 4, 48, lm.ACT_E4M3, 0x2000, 0x3000, None) == lm.LMOE_ERR_SHAPE
+    assert f(0x1000, -1, 64, lm.ACT_E4M3, 0x2000, 0x3000, None) == lm.LMOE_ERR_SHAPE
+    assert f(0x1000, 4, 64, lm.ACT_BF16, 0x2000, 0x3000, None) == lm.LMOE_ERR_SHAPE
+    assert f(0x1000, 4, 64, 7, 0x2000, 0x3000, None) == lm.LMOE_ERR_SHAPE
+    assert f(None, 4, 64, lm.ACT_E2M1, 0x2000, 0x3000, None) == lm.LMOE_ERR_NULL
+    assert f(0x1000, 4, 64, lm.ACT_E2M1, 0x2000, None, None) == lm.LMOE_ERR_NULL
+    assert f(0x1008, 4, 64, lm.ACT_E2M1, 0x2000, 0x3000, None) == lm.LMOE_ERR_ALIGN
+    assert f(0x1000, 0, 64, lm.ACT_E2M1, 0x2000, 0x3000, None) == lm.LMOE_OK
+
+
+def test_act_format_rejected_outside_the_packed_path(lm):
+    """Quantised activations run only on tile-packed experts with L and I
+    multiples of 128; every other request is refused on the host."""
+    d = lm._dims(K3)
+    w = _weights(lm)
+    for act in (lm.ACT_E4M3, lm.ACT_E2M1, 3):
+        ex = lm.lmoe_exec(None, None, None, None, 0, act)
+        assert lm._lib.lmoe_forward_ex(ctypes.byref(d), 0x20000000, ctypes.byref(w), 0, None,
+                                       0x30000000, 0x40000000, 1 << 40, None,
+                                       ctypes.byref(ex)) == lm.LMOE_ERR_SHAPE
+    P = (0x50000000, 0x51000000, 0x52000000, 0x53000000)
+    pw = lm.lmoe_packed_weights(0x10000000, *P, 0x11000000, 0x12000000, 0x13000000)
+    odd = lm._dims((4, 3584 - 32, 896, 16, 2048, 2, 2048))     # L % 128 != 0
+    ex = lm.lmoe_exec(None, None, None, None, 0, lm.ACT_E2M1)
+    assert lm._lib.lmoe_forward_packed(ctypes.byref(odd), 0x20000000, ctypes.byref(pw), 0, None,
+                                       0x30000000, 0x40000000, 1 << 40, None,
+                                       ctypes.byref(ex)) == lm.LMOE_ERR_SHAPE
+    bad = lm.lmoe_exec(None, None, None, None, 0, 5)
+    assert lm._lib.lmoe_forward_packed(ctypes.byref(d), 0x20000000, ctypes.byref(pw), 0, None,
+                                       0x30000000, 0x40000000, 1 << 40, None,
+                                       ctypes.byref(bad)) == lm.LMOE_ERR_SHAPE
 
 
 def test_forward_ex_rejects_bad_arguments(lm):
