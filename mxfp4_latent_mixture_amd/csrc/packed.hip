@@ -198,6 +198,18 @@ struct PkArgs {
   int64_t aq_stride;
 };
 
+// Weight tiles are read once. A workgroup of one 32-row tile (batched
+// decode: a few routes per expert) streams them with the non-temporal hint,
+// measured faster there (gate/up 773 -> 734 us at K3 T=64 with MXFP4
+// activations); with more row tiles (prefill) the plain load measured faster.
+template <int MT>
+__device__ __forceinline__ u32x4_t load_w(const uint8_t* p) {
+  if constexpr (MT == 1)
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  else
+    return load16(p);
+}
+
 constexpr int kPkRows = 96;    // routes per row tile (three 32-row MFMA tiles)
 constexpr int kPkKc = 128;     // K values per chunk
 constexpr int kPkWaves = 4;    // waves per workgroup (two workgroups per CU)
@@ -273,7 +285,7 @@ __device__ __forceinline__ void pk_body(const PkArgs& a, int e, int p0, int cnt,
 #pragma unroll
     for (int t = 0; t < kPkNB; ++t)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b.q[t][j] = load16(qb[t] + (int64_t)cc * 2048 + j * 1024);
+      for (int j = 0; j < 2; ++j) b.q[t][j] = load_w<MT>(qb[t] + (int64_t)cc * 2048 + j * 1024);
   };
   // the exponents of chunk c: the dword of its window (four chunks) that
   // holds them, bytes 2 (c % 2) + j
@@ -563,6 +575,13 @@ hipError_t launch_quantize_act(const uint16_t* src, int64_t rows, int K, bool fp
 // tile repeat its last row), segments XOR-swizzled by row so that the 16
 // rows an LDS read serves hit distinct banks. K must be a multiple of 128.
 // ---------------------------------------------------------------------------
+// ring slots of the quantised GEMM's pipeline (chunks in flight + 1)
+#ifndef LMOE_QRING
+#define LMOE_QRING 4
+#endif
+constexpr int kQRing = LMOE_QRING;
+static_assert(kQRing >= 3 && kQRing <= 5, "ring of three to five slots");
+
 template <bool FP8>
 struct QCfg {
   static constexpr int kRowB = FP8 ? 128 : 64;  // code bytes of a row per chunk
@@ -583,11 +602,18 @@ using QExp = uint32_t[256];  // wave w's 32 rows at 64 w .. 64 w + 31
 template <bool GLU, bool FP8, int MT>
 __device__ __forceinline__ void pkq_body(const PkArgs& a, int e, int p0, int cnt, int nt,
                                          QChunk<FP8>& sq0, QChunk<FP8>& sq1, QChunk<FP8>& sq2,
-                                         QExp& se0, QExp& se1, QExp& se2,
+                                         QChunk<FP8>& sq3, QChunk<FP8>& sq4, QExp& se0,
+                                         QExp& se1, QExp& se2, QExp& se3, QExp& se4,
                                          const uint32_t* s_row) {
   using C = QCfg<FP8>;
-  auto qslot = [&](int r) -> QChunk<FP8>& { return r == 0 ? sq0 : r == 1 ? sq1 : sq2; };
-  auto eslot = [&](int r) -> QExp& { return r == 0 ? se0 : r == 1 ? se1 : se2; };
+  // one LDS array per ring slot: a read of one slot then never waits for the
+  // copy into another
+  auto qslot = [&](int r) -> QChunk<FP8>& {
+    return r == 0 ? sq0 : r == 1 ? sq1 : r == 2 ? sq2 : r == 3 ? sq3 : sq4;
+  };
+  auto eslot = [&](int r) -> QExp& {
+    return r == 0 ? se0 : r == 1 ? se1 : r == 2 ? se2 : r == 3 ? se3 : se4;
+  };
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int r32 = lane & 31, hh = lane >> 5;
@@ -630,23 +656,23 @@ __device__ __forceinline__ void pkq_body(const PkArgs& a, int e, int p0, int cnt
         reinterpret_cast<const void*>(a.as + (int64_t)s_row[row] * kb + cc * 4),
         (__attribute__((address_space(3))) void*)(&eslot(buf)[wave * 64]), 4, 0, 0);
   };
+  // a chunk's weight codes and the exponent word that covers it
   struct Bq {
     u32x4_t q[kPkNB][2];
+    uint32_t ex[kPkNB];
   };
   auto load_b = [&](int c, Bq& b) {
     const int cc = min(c, a.K128 - 1);
 #pragma unroll
     for (int t = 0; t < kPkNB; ++t)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b.q[t][j] = load16(qb[t] + (int64_t)cc * 2048 + j * 1024);
-  };
-  auto load_ex = [&](int c, uint32_t (&dst)[kPkNB]) {
-    const int cc = min(c, a.K128 - 1);
+      for (int j = 0; j < 2; ++j) b.q[t][j] = load_w<MT>(qb[t] + (int64_t)cc * 2048 + j * 1024);
 #pragma unroll
     for (int t = 0; t < kPkNB; ++t)
-      dst[t] = *reinterpret_cast<const uint32_t*>(sb[t] + (cc / 4) * 512 + 4 * ((cc >> 1) & 1));
+      b.ex[t] =
+          *reinterpret_cast<const uint32_t*>(sb[t] + (cc / 4) * 512 + 4 * ((cc >> 1) & 1));
   };
-  auto compute = [&](int c, int buf, const Bq& b, const uint32_t (&ex)[kPkNB]) {
+  auto compute = [&](int c, int buf, const Bq& b) {
     const uint8_t* sq = qslot(buf);
     const QExp& se = eslot(buf);
 #pragma unroll
@@ -675,7 +701,7 @@ __device__ __forceinline__ void pkq_body(const PkArgs& a, int e, int p0, int cnt
       for (int t = 0; t < kPkNB; ++t) {
         const u32x4_t w = b.q[t][s];
         const i32x8_t bv = i32x8_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
-        const int sbv = (int)((ex[t] >> (8 * (2 * (c & 1) + s))) & 0xFFu);
+        const int sbv = (int)((b.ex[t] >> (8 * (2 * (c & 1) + s))) & 0xFFu);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           acc[mt][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -684,33 +710,33 @@ __device__ __forceinline__ void pkq_body(const PkArgs& a, int e, int p0, int cnt
     }
   };
 
-  // The pipeline of gemm_packed_kernel: activations and weights two chunks
-  // ahead, exponents one; groups of three chunks with the first peeled.
-  constexpr int U = 3;
-  constexpr int kAhead = C::kCopies + 1 + 2 * kPkNB;  // loads of chunk c + 2
-  constexpr int kWaitAhead = 0x0F70 | kAhead;
-  static_assert(kAhead < 16, "vmcnt field");
+  // A ring of U chunks (LDS for the activations, registers for the weights
+  // and their exponents), loaded U - 1 chunks ahead; chunk c's loads are
+  // complete once only the loads of the U - 2 later chunks are outstanding.
+  // Groups of U chunks, the first peeled so both loop edges carry the same
+  // loads.
+  constexpr int U = kQRing;
+  constexpr int kPerChunk = C::kCopies + 1 + 3 * kPkNB;  // loads issued per chunk
+  constexpr int kAhead = (U - 2) * kPerChunk;
+  static_assert(kAhead < 64, "vmcnt field");
+  constexpr int kWaitAhead = 0x0F70 | (kAhead & 15) | ((kAhead >> 4) << 14);
   __syncthreads();  // s_row
   Bq bq[U];
-  uint32_t ex[kPkNB], ex_next[kPkNB];
-  load_ex(0, ex_next);
-  copy_a(0, 0);
-  load_b(0, bq[0]);
-  copy_a(1, 1);
-  load_b(1, bq[1]);
+#pragma unroll
+  for (int i = 0; i < U - 1; ++i) {
+    copy_a(i, i);
+    load_b(i, bq[i]);
+  }
   auto group = [&](int cb, bool last) {
 #pragma unroll
     for (int r = 0; r < U; ++r) {
       const int c = cb + r;
       __builtin_amdgcn_s_waitcnt(kWaitAhead);
       __builtin_amdgcn_s_barrier();
-#pragma unroll
-      for (int t = 0; t < kPkNB; ++t) ex[t] = ex_next[t];
-      load_ex(c + 1, ex_next);
-      copy_a(c + 2, (r + 2) % U);
-      load_b(c + 2, bq[(r + 2) % U]);
+      copy_a(c + U - 1, (r + U - 1) % U);
+      load_b(c + U - 1, bq[(r + U - 1) % U]);
       __builtin_amdgcn_sched_barrier(0);
-      if (!last || c < a.K128) compute(c, r, bq[r], ex);
+      if (!last || c < a.K128) compute(c, r, bq[r]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -744,8 +770,9 @@ __device__ __forceinline__ void pkq_body(const PkArgs& a, int e, int p0, int cnt
 
 template <bool GLU, bool FP8>
 __global__ __launch_bounds__(kPkThreads, 8 / kPkWaves) void gemm_packed_q_kernel(PkArgs a) {
-  __shared__ __attribute__((aligned(16))) QChunk<FP8> sq0, sq1, sq2;
-  __shared__ __attribute__((aligned(16))) QExp se0, se1, se2;
+  // kQRing of the five slots are used
+  __shared__ __attribute__((aligned(16))) QChunk<FP8> sq0, sq1, sq2, sq3, sq4;
+  __shared__ __attribute__((aligned(16))) QExp se0, se1, se2, se3, se4;
   __shared__ uint32_t s_row[128];  // activation row of each row slot
   const int b = blockIdx.x;
   const int s = b / 8;
@@ -759,11 +786,15 @@ __global__ __launch_bounds__(kPkThreads, 8 / kPkWaves) void gemm_packed_q_kernel
     const int p = p0 + min(r, cnt - 1);
     s_row[r] = (uint32_t)(a.gather ? a.gather[p] / a.gather_div : p);
   }
+#define LMOE_PKQ(MT)                                                                      \
+  pkq_body<GLU, FP8, MT>(a, e, p0, cnt, nt, sq0, sq1, sq2, sq3, sq4, se0, se1, se2, se3, se4, \
+                         s_row)
   switch ((cnt + 31) / 32) {
-    case 1: pkq_body<GLU, FP8, 1>(a, e, p0, cnt, nt, sq0, sq1, sq2, se0, se1, se2, s_row); break;
-    case 2: pkq_body<GLU, FP8, 2>(a, e, p0, cnt, nt, sq0, sq1, sq2, se0, se1, se2, s_row); break;
-    default: pkq_body<GLU, FP8, 3>(a, e, p0, cnt, nt, sq0, sq1, sq2, se0, se1, se2, s_row); break;
+    case 1: LMOE_PKQ(1); break;
+    case 2: LMOE_PKQ(2); break;
+    default: LMOE_PKQ(3); break;
   }
+#undef LMOE_PKQ
 }
 
 hipError_t launch_routed_packed(const Plan& p, const uint16_t* x, const PackedWeights& w,
