@@ -31,4 +31,10 @@ from .lmoe_oracle import (  # noqa: F401
     mx_quantize,
     mx_dequant,
     act_values,
+    RMS_EPS,
+    shared_gate_up_rows,
+    moe_input,
+    rms_norm,
+    moe_tail,
+    block_forward,
 )

@@ -35,6 +35,12 @@ What the layer computes, step by step, and where the pages state it:
             weight 1 (Bringing up Kimi-K3, "The model we hadn't run").
   combine   out[t] = bf16(sum_j w[t,j] y[t,j] + sum_s ysh[s,t]) in that order
             (TokenSpeed section 4.3, fused combine of the selected experts).
+  block     around the layer, the MoE input step (router scores, latent
+            input and shared gate/up from one packed projection of the hidden
+            input, TokenSpeed section 4.3) and the tail (routed RMSNorm,
+            latent -> hidden up-projection, plus the shared output and the
+            residual, sections 4.2-4.3 and 6): moe_input, rms_norm, moe_tail,
+            block_forward, with the readings stated at their definitions.
 
 Readings where the pages are silent: element 2m of a row is the low nibble of
 byte m; E8M0 byte 255 is NaN; NaN logits rank below -inf, equal NaNs by index;
@@ -432,3 +438,117 @@ def forward(x_bits: np.ndarray, router_bits: Optional[np.ndarray],
     return {"logits": logits, "idx": idx, "w": w, "counts": counts,
             "offsets": offsets, "perm": perm, "inv": inv,
             "out64": out64, "out": out_bits}
+
+
+# ----------------------------------------------------------------------------
+# The MoE block around the layer: input step and tail
+# ----------------------------------------------------------------------------
+#
+# TokenSpeed section 4.3 computes the three projections of the MoE input, the
+# router scores, the routed experts' latent input (hidden -> latent) and the
+# shared experts' gate/up values, as one matrix multiply over weights stored
+# one after another, with the shared activation applied in its epilogue.
+# Sections 4.2 and 6 describe the tail: the routed result (a 3584-wide latent
+# vector) is RMS-normalised and projected up to the 7168-wide hidden width,
+# then the shared experts' full-width output and the running residual are
+# added; partials travel as BF16, reductions and normalisation use FP32
+# internally.
+#
+# Readings (the pages fix neither layout nor epsilon):
+#   W_in rows, in order: E router rows, L latent rows, then for each shared
+#     expert s its gate and up rows interleaved in groups of 16 (rows
+#     E + L + 2*Is*s + 32*j + c: gate row 16*j + c for c < 16, up row
+#     16*j + c - 16 otherwise). h column s*Is + 16*j + c is
+#     bf16(silu(g) * u) of that group.
+#   logits = fp32(z_router); x = bf16(z_latent).
+#   RMSNorm: n = bf16(r / sqrt(mean(r^2) + eps) * gamma), eps = 1e-6, in
+#     exact arithmetic here (FP32 on the GPU), rounded once.
+#   The shared experts' output is one BF16 partial, the sum over experts:
+#     sh = bf16(h W_sd^T) with W_sd [H][S*Is] holding the experts' down
+#     matrices side by side along K.
+#   out = bf16(n W_up^T + sh + residual), rounded once.
+
+RMS_EPS = 1e-6
+
+
+def shared_gate_up_rows(E: int, L: int, S: int, Is: int):
+    """Row indices into W_in of every shared expert's gate and up matrices:
+    (gate [S][Is], up [S][Is]) under the interleaved reading above."""
+    gate = np.empty((S, Is), np.int64)
+    up = np.empty((S, Is), np.int64)
+    for s in range(S):
+        base = E + L + 2 * Is * s
+        for i in range(Is):
+            j, c = divmod(i, 16)
+            gate[s, i] = base + 32 * j + c
+            up[s, i] = base + 32 * j + 16 + c
+    return gate, up
+
+
+def moe_input(u_bits: np.ndarray, w_in_bits: np.ndarray, E: int, L: int, S: int,
+              Is: int) -> Dict[str, np.ndarray]:
+    """The MoE input step on hidden rows u (bf16 bits [T][H]) with the packed
+    input weight W_in (bf16 bits [E + L + 2 S Is][H]).
+
+    Returns logits float32 [T][E], x bf16 bits [T][L], h bf16 bits
+    [T][S*Is] and z float64 [T][rows] (the exact product)."""
+    u = f64_from_bf16(u_bits)
+    w = f64_from_bf16(w_in_bits)
+    assert w.shape[0] == E + L + 2 * S * Is, "W_in rows"
+    z = u @ w.T
+    logits = f32_round(z[:, :E]).astype(np.float32)
+    x = bf16_from_f64(z[:, E:E + L])
+    gate_rows, up_rows = shared_gate_up_rows(E, L, S, Is)
+    T = u.shape[0]
+    h = np.empty((T, S * Is), np.uint16)
+    for s in range(S):
+        g = z[:, gate_rows[s]]
+        v = z[:, up_rows[s]]
+        h[:, s * Is:(s + 1) * Is] = bf16_from_f64(silu(g) * v)
+    return {"logits": logits, "x": x, "h": h, "z": z}
+
+
+def rms_norm(r_bits: np.ndarray, gamma_bits: np.ndarray, eps: float = RMS_EPS) -> np.ndarray:
+    """n = bf16(r / sqrt(mean(r^2) + eps) * gamma) per row of r (bf16 bits
+    [T][L]); gamma bf16 bits [L]. Returns bf16 bits [T][L]."""
+    r = f64_from_bf16(r_bits)
+    gamma = f64_from_bf16(gamma_bits)
+    ms = np.mean(r * r, axis=1, keepdims=True)
+    return bf16_from_f64(r / np.sqrt(ms + eps) * gamma[None, :])
+
+
+def moe_tail(routed_bits: np.ndarray, h_bits: np.ndarray, gamma_bits: np.ndarray,
+             w_up_bits: np.ndarray, w_sd_bits: np.ndarray, residual_bits: np.ndarray,
+             eps: float = RMS_EPS) -> Dict[str, np.ndarray]:
+    """The MoE tail: routed latent result (bf16 bits [T][L]), shared
+    activations h (bf16 bits [T][S*Is]), gamma [L], W_up [H][L],
+    W_sd [H][S*Is], residual [T][H]. Returns n, sh (bf16 bits), out64
+    (float64 [T][H]) and out (bf16 bits [T][H])."""
+    n = rms_norm(routed_bits, gamma_bits, eps)
+    sh = bf16_from_f64(f64_from_bf16(h_bits) @ f64_from_bf16(w_sd_bits).T)
+    out64 = (f64_from_bf16(n) @ f64_from_bf16(w_up_bits).T + f64_from_bf16(sh)
+             + f64_from_bf16(residual_bits))
+    return {"n": n, "sh": sh, "out64": out64, "out": bf16_from_f64(out64)}
+
+
+def block_forward(u_bits: np.ndarray, residual_bits: np.ndarray, w_in_bits: np.ndarray,
+                  experts: Mapping[str, np.ndarray], gamma_bits: np.ndarray,
+                  w_up_bits: np.ndarray, w_sd_bits: np.ndarray, E: int, L: int, S: int,
+                  Is: int, k: int, logits: Optional[np.ndarray] = None,
+                  act: str = "bf16") -> Dict[str, np.ndarray]:
+    """Input step, the routed layer (no shared experts of its own: here they
+    read the hidden input) and the tail. logits, when given, replace the
+    input step's router scores for the routing (the GPU's own logits in the
+    parity tests). Returns the intermediates of all three."""
+    inp = moe_input(u_bits, w_in_bits, E, L, S, Is)
+    lg = inp["logits"] if logits is None else np.asarray(logits, np.float32)
+    Hd = u_bits.shape[1]
+    no_shared = {"sh_gate": np.zeros((0, 0, L), np.uint16),
+                 "sh_up": np.zeros((0, 0, L), np.uint16),
+                 "sh_down": np.zeros((0, L, 0), np.uint16)}
+    routed = forward(inp["x"], None, experts, no_shared, k, logits=lg, act=act)
+    tail = moe_tail(routed["out"], inp["h"], gamma_bits, w_up_bits, w_sd_bits,
+                    residual_bits)
+    assert tail["out"].shape == (u_bits.shape[0], Hd)
+    return {"input": inp, "routed": routed, "tail": tail, "out": tail["out"],
+            "out64": tail["out64"]}

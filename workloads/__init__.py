@@ -15,10 +15,11 @@ from .gen import (
     gen_shared,
     gen_logits,
     gen_all,
+    gen_block,
 )
 
 __all__ = [
     "Dims", "Workload", "WORKLOADS", "get_workload",
     "gen_x", "gen_router", "gen_expert", "gen_experts", "gen_shared",
-    "gen_logits", "gen_all",
+    "gen_logits", "gen_all", "gen_block",
 ]

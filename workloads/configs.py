@@ -28,6 +28,18 @@ plus the same layer at the widths the pages imply or shard to:
                   width (dev48.org "Kimi K3 on AMD Instinct GPUs with
                   TokenSpeed", Figure 2), the router whole
 plus smaller parity shapes with ragged tails (not multiples of any tile).
+
+Block workloads (H > 0) add the MoE input step and tail around the layer
+(TokenSpeed sections 4.2-4.4): the 7168-wide hidden input u, the running
+residual, the packed input weight (router, hidden -> latent, shared gate/up),
+the routed RMSNorm weight, the latent -> hidden up-projection and the shared
+experts' down projection to the hidden width. There the shared experts (S, Is)
+read the hidden input; the routed layer inside has none of its own.
+  block_tiny      T=8,    H=512,  L=256,  E=32,  k=4,  I=Is=128 (seed 20)
+  block_ragged    T=37,   H=448,  L=320,  E=96,  k=6,  I=Is=192, S=1 (seed 21)
+  block_decode    T=1,    H=7168, the K3 layer (seed 22)
+  block_batched   T=64,   same (seed 24)
+  block_prefill   T=4096, same (seed 23)
 """
 from __future__ import annotations
 
@@ -44,6 +56,7 @@ class Dims:
     I: int   # routed-expert intermediate width
     S: int   # shared experts (always on, weight 1)
     Is: int  # shared-expert intermediate width
+    H: int = 0  # hidden width of the MoE block (0: the layer alone)
 
     @property
     def routes(self) -> int:
@@ -105,6 +118,18 @@ WORKLOADS = {
     "decode_tp8": Workload(
         "decode_tp8", 1, Dims(T=1, **{**_K3, "I": 256, "Is": 256}),
         note="one GPU's eighth of every routed and shared expert, router whole"),
+    "block_tiny": Workload(
+        "block_tiny", 20, Dims(T=8, L=256, E=32, k=4, I=128, S=2, Is=128, H=512),
+        scales=("uniform", 120, 130), note="MoE block around the tiny layer"),
+    "block_ragged": Workload(
+        "block_ragged", 21, Dims(T=37, L=320, E=96, k=6, I=192, S=1, Is=192, H=448),
+        scales=("uniform", 118, 132), note="MoE block with ragged tiles"),
+    "block_decode": Workload(
+        "block_decode", 22, Dims(T=1, H=7168, **_K3), note="K3 MoE block, one token"),
+    "block_batched": Workload(
+        "block_batched", 24, Dims(T=64, H=7168, **_K3), note="K3 MoE block, 64 rows"),
+    "block_prefill": Workload(
+        "block_prefill", 23, Dims(T=4096, H=7168, **_K3), note="K3 MoE block, prefill chunk"),
     # Parity shapes: several tiles plus ragged tails in every dimension.
     "ragged": Workload(
         "ragged", 10, Dims(T=37, L=416, E=48, k=6, I=352, S=2, Is=224),

@@ -17,6 +17,18 @@ Byte layouts produced here (the layout the layer consumes):
   sh_down    bf16 bits, uint16 [S][L][Is]
   logits     float32 [T][E]  (given-logits workloads only)
 
+MoE block workloads (dims.H > 0), all bf16 bits:
+  u          uint16 [T][H]                      N(0, 1), the normalised MoE input
+  residual   uint16 [T][H]                      N(0, 1)
+  w_in       uint16 [E + L + 2 S Is][H]         router rows N(0, router_std),
+             latent rows N(0, 1/sqrt(H)), then per shared expert its gate and
+             up rows N(0, shared_std) interleaved in groups of 16 (16 gate
+             rows, then the 16 up rows of the same columns)
+  norm_w     uint16 [L]                         N(1, 0.1), the routed RMSNorm weight
+  w_up       uint16 [H][L]                      N(0, 1/sqrt(L))
+  w_sd       uint16 [H][S Is]                   N(0, shared_std), the shared
+             experts' down matrices side by side along the input dimension
+
 Codes are uniform over all 16 E2M1 values, which makes every byte uniform over
 0..255. Normal samples are drawn in float64 and rounded to nearest-even bf16.
 """
@@ -38,6 +50,12 @@ TID_SH_GATE = 9
 TID_SH_UP = 10
 TID_SH_DOWN = 11
 TID_LOGITS = 12
+TID_U = 13
+TID_RESIDUAL = 14
+TID_W_IN = 15      # sub 0 router rows, 1 latent rows, 2 + 2 s / 3 + 2 s gate / up of expert s
+TID_NORM_W = 16
+TID_W_UP = 17
+TID_W_SD = 18
 
 
 def _rng(seed: int, tid: int, sub: int = 0) -> np.random.Generator:
@@ -180,3 +198,32 @@ def gen_all(w: Workload, threads: Optional[int] = None) -> Dict[str, np.ndarray]
     if w.logits_given:
         out["logits"] = gen_logits(w)
     return out
+
+
+def gen_block(w: Workload) -> Dict[str, np.ndarray]:
+    """The MoE block's own inputs and weights (dims.H > 0); the routed
+    experts come from gen_expert / gen_experts as for the layer."""
+    d = w.dims
+    T, H, L, E, S, Is = d.T, d.H, d.L, d.E, d.S, d.Is
+    assert H > 0 and Is % 16 == 0
+    u = _rng(w.seed, TID_U).normal(0.0, 1.0, size=(T, H))
+    res = _rng(w.seed, TID_RESIDUAL).normal(0.0, 1.0, size=(T, H))
+    rows = [_rng(w.seed, TID_W_IN, 0).normal(0.0, w.router_std, size=(E, H)),
+            _rng(w.seed, TID_W_IN, 1).normal(0.0, 1.0 / np.sqrt(H), size=(L, H))]
+    for s in range(S):
+        g = _rng(w.seed, TID_W_IN, 2 + 2 * s).normal(0.0, w.shared_std, size=(Is, H))
+        v = _rng(w.seed, TID_W_IN, 3 + 2 * s).normal(0.0, w.shared_std, size=(Is, H))
+        # 16 gate rows, then the 16 up rows of the same columns
+        rows.append(np.stack([g.reshape(Is // 16, 16, H), v.reshape(Is // 16, 16, H)],
+                             axis=1).reshape(2 * Is, H))
+    w_in = np.concatenate(rows, axis=0)
+    return {
+        "u": _normal_to_bf16_bits(u),
+        "residual": _normal_to_bf16_bits(res),
+        "w_in": _normal_to_bf16_bits(w_in),
+        "norm_w": _normal_to_bf16_bits(_rng(w.seed, TID_NORM_W).normal(1.0, 0.1, size=L)),
+        "w_up": _normal_to_bf16_bits(
+            _rng(w.seed, TID_W_UP).normal(0.0, 1.0 / np.sqrt(L), size=(H, L))),
+        "w_sd": _normal_to_bf16_bits(
+            _rng(w.seed, TID_W_SD).normal(0.0, w.shared_std, size=(H, S * Is))),
+    }
