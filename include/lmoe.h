@@ -315,6 +315,84 @@ int lmoe_forward_packed(const lmoe_dims* dims, const uint16_t* x, const lmoe_pac
                         int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,
                         size_t ws_bytes, void* stream, const lmoe_exec* exec);
 
+/* ---- The MoE block around the layer ----
+ * In Kimi-K3 the layer sits inside a block (dev48.org "Kimi K3 on AMD
+ * Instinct GPUs with TokenSpeed", sections 4.2-4.4 and 6): one packed
+ * projection of the normalised hidden input u gives the router scores, the
+ * routed experts' latent input and the shared experts' gate/up values, the
+ * shared activation applied in its epilogue (section 4.3); the routed layer
+ * runs in the latent; the tail RMS-normalises the routed result, projects it
+ * up to the hidden width and adds the shared experts' output and the running
+ * residual (sections 4.2, 4.3 and 6). Here the shared experts read u and
+ * write the hidden width, as in K3; the layer inside has none of its own.
+ *
+ * Block dimensions: T, L, E, k, I as lmoe_dims, and
+ *   H   hidden width (H % 64 == 0, 64..16384)
+ *   S   shared experts (0..8), Is their intermediate width (Is % 32 == 0 and
+ *       S * Is % 64 == 0 when S > 0)
+ * with also L % 64 == 0 and E % 32 == 0. Kimi-K3: H = 7168. */
+typedef struct lmoe_block_dims {
+  int32_t T, H, L, E, k, I, S, Is;
+} lmoe_block_dims;
+
+/* The block's own weights, bf16 device pointers, row-major:
+ *   w_in    [E + L + 2*S*Is][H]  the three input projections one after another
+ *           (section 4.3): E router rows, L rows of the hidden -> latent
+ *           projection, then for each shared expert s its gate and up rows
+ *           interleaved in groups of 16: row E + L + 2*Is*s + 32*j + c is
+ *           gate row 16*j + c for c < 16 and up row 16*j + c - 16 otherwise
+ *   norm_w  [L]        weight of the routed RMSNorm
+ *   w_up    [H][L]     latent -> hidden up-projection
+ *   w_sd    [H][S*Is]  the shared experts' down projections side by side
+ *                      along the input dimension (NULL when S == 0) */
+typedef struct lmoe_block_weights {
+  const uint16_t* w_in;
+  const uint16_t* norm_w;
+  const uint16_t* w_up;
+  const uint16_t* w_sd;
+} lmoe_block_weights;
+
+/* Workspace bytes for lmoe_moe_input, lmoe_moe_tail and lmoe_block_forward
+ * (0 for invalid dims). It must be zero-filled before its first use, as the
+ * layer's (it contains one). */
+size_t lmoe_block_workspace_bytes(const lmoe_block_dims* dims);
+
+/* The MoE input step (TokenSpeed section 4.3): z = u W_in^T in one GEMM,
+ * accumulated in fp32, with
+ *   logits float [T][E]     = z's router columns
+ *   x      bf16 [T][L]      = bf16(z's latent columns)
+ *   h_sh   bf16 [T][S*Is]   = bf16(silu(g) * v) for each shared expert's
+ *                             gate and up columns g, v (NULL when S == 0)
+ * u bf16 [T][H]. All device pointers. Errors: LMOE_ERR_NULL, _SHAPE, _ALIGN,
+ * _WORKSPACE, _HIP. */
+int lmoe_moe_input(const lmoe_block_dims* dims, const uint16_t* u, const uint16_t* w_in,
+                   float* logits, uint16_t* x, uint16_t* h_sh, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* The MoE tail (sections 4.2, 4.3 and 6): with the routed result routed
+ * bf16 [T][L], the shared activations h_sh bf16 [T][S*Is] and the residual
+ * bf16 [T][H],
+ *   n   = bf16(routed * (1 / sqrt(mean(routed^2) + 1e-6)) * norm_w), fp32 inside
+ *   sh  = bf16(h_sh w_sd^T)                    (zero when S == 0)
+ *   out = bf16(n w_up^T + sh + residual)       bf16 [T][H]
+ * All device pointers. Errors: as lmoe_moe_input. */
+int lmoe_moe_tail(const lmoe_block_dims* dims, const uint16_t* routed, const uint16_t* h_sh,
+                  const uint16_t* norm_w, const uint16_t* w_up, const uint16_t* w_sd,
+                  const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* The whole block: lmoe_moe_input, then the layer (lmoe_forward with the
+ * input step's logits given, no shared experts of its own) on the latent
+ * rows with the routed experts of `experts` (lmoe_weights' layout; its
+ * router and shared members are ignored), then lmoe_moe_tail; out bf16
+ * [T][H]. r: optional routing outputs as lmoe_forward's; here r->logits,
+ * when non-NULL, receives the input step's router scores. Every kernel runs
+ * on `stream`. Errors: as lmoe_moe_input. */
+int lmoe_block_forward(const lmoe_block_dims* dims, const uint16_t* u, const uint16_t* residual,
+                       const lmoe_block_weights* bw, const lmoe_weights* experts,
+                       const lmoe_routing* r, uint16_t* out, void* ws, size_t ws_bytes,
+                       void* stream);
+
 /* Size of the device scratch lmoe_forward_noalloc uses: one static array per
  * GPU, held from the library's first such call on that GPU until the process
  * ends. */

@@ -19,8 +19,12 @@ Functions mirror the C ABI in include/lmoe.h:
                  join_event)
   debug_dequant_mxfp4(q, s, rows, K, out)
   status_string(code)
+  block_workspace_bytes(bdims)
+  moe_input(bdims, u, w_in, logits, x, h_sh, ws)
+  moe_tail(bdims, routed, h_sh, norm_w, w_up, w_sd, residual, out, ws)
+  block_forward(bdims, u, residual, block_weights, experts, routing, out, ws)
 `dims` is a Dims-like object (attributes T, L, E, k, I, S, Is) or a tuple in
-that order; tensors are torch CUDA tensors (bf16 data may be torch.bfloat16,
+that order, `bdims` likewise with attributes T, H, L, E, k, I, S, Is; tensors are torch CUDA tensors (bf16 data may be torch.bfloat16,
 torch.int16 or torch.uint16 views), `weights` and `routing` are dicts keyed by
 the C struct member names.
 """
@@ -48,7 +52,8 @@ EXPORTS = ("lmoe_workspace_bytes", "lmoe_route", "lmoe_forward", "lmoe_forward_e
            "lmoe_forward_traced", "lmoe_wait_errors", "lmoe_forward_noalloc", "lmoe_stage_name", "lmoe_path_name",
            "lmoe_debug_dequant_mxfp4", "lmoe_status_string", "lmoe_packed_sizes_of",
            "lmoe_pack_weights", "lmoe_forward_packed", "lmoe_debug_read_stream",
-           "lmoe_debug_quantize_act")
+           "lmoe_debug_quantize_act", "lmoe_block_workspace_bytes", "lmoe_moe_input",
+           "lmoe_moe_tail", "lmoe_block_forward")
 # members of lmoe_packed_sizes / the packed routed-expert arrays
 PACKED_KEYS = ("gu_q", "gu_s", "down_q", "down_s")
 
@@ -97,6 +102,14 @@ def _exec(side_stream, fork_event, join_event, stage_events, path=PATH_AUTO, act
         ex.stage_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
         ex._keep = arr
     return ex
+
+
+class lmoe_block_dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "H", "L", "E", "k", "I", "S", "Is")]
+
+
+class lmoe_block_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_in", "norm_w", "w_up", "w_sd")]
 
 
 class lmoe_packed_sizes(ctypes.Structure):
@@ -168,6 +181,17 @@ def _load() -> ctypes.CDLL:
     lib.lmoe_debug_read_stream.restype = ctypes.c_int
     lib.lmoe_debug_dequant_mxfp4.argtypes = [vp, vp, i32, i32, vp, vp]
     lib.lmoe_debug_dequant_mxfp4.restype = ctypes.c_int
+    bdp = ctypes.POINTER(lmoe_block_dims)
+    lib.lmoe_block_workspace_bytes.argtypes = [bdp]
+    lib.lmoe_block_workspace_bytes.restype = sz
+    lib.lmoe_moe_input.argtypes = [bdp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lmoe_moe_input.restype = ctypes.c_int
+    lib.lmoe_moe_tail.argtypes = [bdp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lmoe_moe_tail.restype = ctypes.c_int
+    lib.lmoe_block_forward.argtypes = [bdp, vp, vp, ctypes.POINTER(lmoe_block_weights),
+                                       ctypes.POINTER(lmoe_weights),
+                                       ctypes.POINTER(lmoe_routing), vp, vp, sz, vp]
+    lib.lmoe_block_forward.restype = ctypes.c_int
     lib.lmoe_status_string.argtypes = [ctypes.c_int]
     lib.lmoe_status_string.restype = ctypes.c_char_p
     return lib
@@ -378,3 +402,54 @@ def debug_dequant_mxfp4(q, s, rows: int, K: int, out, stream=None) -> None:
     code = _lib.lmoe_debug_dequant_mxfp4(_ptr(q), _ptr(s), int(rows), int(K), _ptr(out),
                                          _stream(stream))
     _check("lmoe_debug_dequant_mxfp4", code)
+
+
+def _bdims(d) -> lmoe_block_dims:
+    if isinstance(d, lmoe_block_dims):
+        return d
+    if isinstance(d, (tuple, list)):
+        return lmoe_block_dims(*[int(v) for v in d])
+    return lmoe_block_dims(int(d.T), int(d.H), int(d.L), int(d.E), int(d.k), int(d.I),
+                           int(d.S), int(d.Is))
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size() if t is not None else 0
+
+
+def block_workspace_bytes(bdims) -> int:
+    d = _bdims(bdims)
+    return int(_lib.lmoe_block_workspace_bytes(ctypes.byref(d)))
+
+
+def moe_input(bdims, u, w_in, logits, x, h_sh, ws, stream=None) -> None:
+    """The MoE input step (lmoe_moe_input): router scores, latent rows and
+    the shared experts' activations from one packed projection of u."""
+    d = _bdims(bdims)
+    code = _lib.lmoe_moe_input(ctypes.byref(d), _ptr(u), _ptr(w_in), _ptr(logits), _ptr(x),
+                               _ptr(h_sh), _ptr(ws), _nbytes(ws), _stream(stream))
+    _check("lmoe_moe_input", code)
+
+
+def moe_tail(bdims, routed, h_sh, norm_w, w_up, w_sd, residual, out, ws, stream=None) -> None:
+    """The MoE tail (lmoe_moe_tail): RMSNorm of the routed result, the
+    up-projection, plus the shared output and the residual."""
+    d = _bdims(bdims)
+    code = _lib.lmoe_moe_tail(ctypes.byref(d), _ptr(routed), _ptr(h_sh), _ptr(norm_w),
+                              _ptr(w_up), _ptr(w_sd), _ptr(residual), _ptr(out), _ptr(ws),
+                              _nbytes(ws), _stream(stream))
+    _check("lmoe_moe_tail", code)
+
+
+def block_forward(bdims, u, residual, block_weights: Mapping, experts: Mapping,
+                  routing: Optional[Mapping], out, ws, stream=None) -> None:
+    """The whole MoE block (lmoe_block_forward): block_weights holds w_in,
+    norm_w, w_up, w_sd; experts the routed MXFP4 arrays (lmoe_weights keys)."""
+    d = _bdims(bdims)
+    bw = lmoe_block_weights(*[_ptr(block_weights.get(n)) for n, _ in lmoe_block_weights._fields_])
+    w = _weights(experts)
+    r = _routing(routing)
+    code = _lib.lmoe_block_forward(ctypes.byref(d), _ptr(u), _ptr(residual), ctypes.byref(bw),
+                                   ctypes.byref(w), ctypes.byref(r) if r is not None else None,
+                                   _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream))
+    _check("lmoe_block_forward", code)

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "liblmoe.so")
-SOURCES = ["api.hip", "route.hip", "experts.hip", "decode.hip", "decode_multi.hip", "packed.hip"]
+SOURCES = ["api.hip", "route.hip", "experts.hip", "decode.hip", "decode_multi.hip", "packed.hip", "dense.hip"]
 ARCH = "gfx950"
 
 

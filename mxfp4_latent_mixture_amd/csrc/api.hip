@@ -612,3 +612,199 @@ extern "C" int lmoe_debug_dequant_mxfp4(const uint8_t* q, const uint8_t* s, int3
   hipError_t e = launch_dequant(q, s, rows, K, out, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
 }
+
+// ---------------------------------------------------------------------------
+// The MoE block around the layer: input step, layer, tail (dense.hip).
+// ---------------------------------------------------------------------------
+namespace {
+
+bool block_dims_ok(const lmoe_block_dims& b) {
+  const lmoe_dims d = {b.T, b.L, b.E, b.k, b.I, 0, 0};
+  if (!dims_ok(d)) return false;
+  if (b.H < 64 || b.H > 16384 || b.H % 64) return false;
+  if (b.L % 64 || b.E % 32) return false;
+  if (b.S < 0 || b.S > 8) return false;
+  if (b.S > 0 && (b.Is < 32 || b.Is > 16384 || b.Is % 32 || (b.S * b.Is) % 64)) return false;
+  return true;
+}
+
+lmoe_dims layer_dims(const lmoe_block_dims& b) { return {b.T, b.L, b.E, b.k, b.I, 0, 0}; }
+
+int block_shared(const lmoe_block_dims& b) { return b.S > 0 ? b.S * b.Is : 0; }
+
+// Workspace of the block: the layer's own workspace first, then the block's
+// buffers, then the K-split partial tiles (sized for the largest GEMM).
+struct BlockWs {
+  void* layer;
+  size_t layer_bytes;
+  float* logits;    // [T][E]
+  uint16_t* x;      // [T][L]
+  uint16_t* h_sh;   // [T][S*Is]
+  uint16_t* routed; // [T][L]
+  uint16_t* n;      // [T][L]
+  uint16_t* sh;     // [T][H]
+  float* part;
+  size_t bytes;
+};
+
+BlockWs carve_block(const lmoe_block_dims& b, void* base) {
+  BlockWs w = {};
+  const lmoe_dims ld = layer_dims(b);
+  w.layer_bytes = carve_workspace(make_plan(ld), nullptr).bytes;
+  size_t off = 0;
+  char* p = static_cast<char*>(base);
+  auto take = [&](size_t bytes) -> char* {
+    char* r = p ? p + off : nullptr;
+    off = align_up(off + bytes, 256);
+    return r;
+  };
+  const size_t T = b.T, SI = block_shared(b);
+  w.layer = take(w.layer_bytes);
+  w.logits = reinterpret_cast<float*>(take(T * b.E * 4));
+  w.x = reinterpret_cast<uint16_t*>(take(T * b.L * 2));
+  w.h_sh = reinterpret_cast<uint16_t*>(take(T * SI * 2));
+  w.routed = reinterpret_cast<uint16_t*>(take(T * b.L * 2));
+  w.n = reinterpret_cast<uint16_t*>(take(T * b.L * 2));
+  w.sh = reinterpret_cast<uint16_t*>(take(T * (size_t)b.H * 2));
+  const size_t parts = std::max({dense_plan(b.T, b.E + b.L + 2 * (int)SI, b.H).part_floats,
+                                 SI ? dense_plan(b.T, b.H, (int)SI).part_floats : (size_t)0,
+                                 dense_plan(b.T, b.H, b.L).part_floats});
+  w.part = reinterpret_cast<float*>(take(std::max(parts, (size_t)1) * 4));
+  w.bytes = off;
+  return w;
+}
+
+int run_moe_input(const lmoe_block_dims& b, const uint16_t* u, const uint16_t* w_in,
+                  float* logits, uint16_t* x, uint16_t* h_sh, const BlockWs& ws, hipStream_t s) {
+  const int SI = block_shared(b);
+  DenseArgs a = {};
+  a.a = u;
+  a.lda = b.H;
+  a.b = w_in;
+  a.ldb = b.H;
+  a.M = b.T;
+  a.N = b.E + b.L + 2 * SI;
+  a.K = b.H;
+  a.n_f32 = b.E;
+  a.n_bf16 = b.L;
+  a.f32_out = logits;
+  a.ld_f32 = b.E;
+  a.bf_out = x;
+  a.ld_bf = b.L;
+  a.glu_out = h_sh;
+  a.ld_glu = SI;
+  return launch_dense(a, dense_plan(a.M, a.N, a.K), ws.part, s) == hipSuccess ? LMOE_OK
+                                                                              : LMOE_ERR_HIP;
+}
+
+int run_moe_tail(const lmoe_block_dims& b, const uint16_t* routed, const uint16_t* h_sh,
+                 const uint16_t* norm_w, const uint16_t* w_up, const uint16_t* w_sd,
+                 const uint16_t* residual, uint16_t* out, const BlockWs& ws, hipStream_t s) {
+  const int SI = block_shared(b);
+  if (launch_rmsnorm(routed, norm_w, b.T, b.L, 1e-6f, ws.n, s) != hipSuccess) return LMOE_ERR_HIP;
+  if (SI) {  // sh = bf16(h_sh w_sd^T)
+    DenseArgs a = {};
+    a.a = h_sh;
+    a.lda = SI;
+    a.b = w_sd;
+    a.ldb = SI;
+    a.M = b.T;
+    a.N = b.H;
+    a.K = SI;
+    a.n_bf16 = b.H;
+    a.bf_out = ws.sh;
+    a.ld_bf = b.H;
+    if (launch_dense(a, dense_plan(a.M, a.N, a.K), ws.part, s) != hipSuccess)
+      return LMOE_ERR_HIP;
+  }
+  DenseArgs a = {};  // out = bf16(n w_up^T + sh + residual)
+  a.a = ws.n;
+  a.lda = b.L;
+  a.b = w_up;
+  a.ldb = b.L;
+  a.M = b.T;
+  a.N = b.H;
+  a.K = b.L;
+  a.n_bf16 = b.H;
+  a.bf_out = out;
+  a.ld_bf = b.H;
+  a.add0 = SI ? ws.sh : nullptr;
+  a.add1 = residual;
+  a.ld_add = b.H;
+  return launch_dense(a, dense_plan(a.M, a.N, a.K), ws.part, s) == hipSuccess ? LMOE_OK
+                                                                              : LMOE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" size_t lmoe_block_workspace_bytes(const lmoe_block_dims* dims) {
+  if (!dims || !block_dims_ok(*dims)) return 0;
+  return carve_block(*dims, nullptr).bytes;
+}
+
+extern "C" int lmoe_moe_input(const lmoe_block_dims* dims, const uint16_t* u,
+                              const uint16_t* w_in, float* logits, uint16_t* x, uint16_t* h_sh,
+                              void* ws, size_t ws_bytes, void* stream) {
+  if (!dims) return LMOE_ERR_NULL;
+  if (!block_dims_ok(*dims)) return LMOE_ERR_SHAPE;
+  if (dims->T == 0) return LMOE_OK;
+  if (!u || !w_in || !logits || !x || !ws || (dims->S > 0 && !h_sh)) return LMOE_ERR_NULL;
+  const void* ptrs[] = {u, w_in, logits, x, h_sh, ws};
+  for (const void* q : ptrs)
+    if (check_opt_ptr(q)) return LMOE_ERR_ALIGN;
+  BlockWs w = carve_block(*dims, ws);
+  if (ws_bytes < w.bytes) return LMOE_ERR_WORKSPACE;
+  return run_moe_input(*dims, u, w_in, logits, x, h_sh, w, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int lmoe_moe_tail(const lmoe_block_dims* dims, const uint16_t* routed,
+                             const uint16_t* h_sh, const uint16_t* norm_w, const uint16_t* w_up,
+                             const uint16_t* w_sd, const uint16_t* residual, uint16_t* out,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (!dims) return LMOE_ERR_NULL;
+  if (!block_dims_ok(*dims)) return LMOE_ERR_SHAPE;
+  if (dims->T == 0) return LMOE_OK;
+  if (!routed || !norm_w || !w_up || !residual || !out || !ws) return LMOE_ERR_NULL;
+  if (dims->S > 0 && (!h_sh || !w_sd)) return LMOE_ERR_NULL;
+  const void* ptrs[] = {routed, h_sh, norm_w, w_up, w_sd, residual, out, ws};
+  for (const void* q : ptrs)
+    if (check_opt_ptr(q)) return LMOE_ERR_ALIGN;
+  BlockWs w = carve_block(*dims, ws);
+  if (ws_bytes < w.bytes) return LMOE_ERR_WORKSPACE;
+  return run_moe_tail(*dims, routed, h_sh, norm_w, w_up, w_sd, residual, out, w,
+                      static_cast<hipStream_t>(stream));
+}
+
+extern "C" int lmoe_block_forward(const lmoe_block_dims* dims, const uint16_t* u,
+                                  const uint16_t* residual, const lmoe_block_weights* bw,
+                                  const lmoe_weights* experts, const lmoe_routing* r,
+                                  uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!dims || !bw || !experts) return LMOE_ERR_NULL;
+  if (!block_dims_ok(*dims)) return LMOE_ERR_SHAPE;
+  if (dims->T == 0) return LMOE_OK;
+  if (!u || !residual || !out || !ws || !bw->w_in || !bw->norm_w || !bw->w_up)
+    return LMOE_ERR_NULL;
+  if (dims->S > 0 && !bw->w_sd) return LMOE_ERR_NULL;
+  const void* ptrs[] = {u, residual, out, ws, bw->w_in, bw->norm_w, bw->w_up, bw->w_sd};
+  for (const void* q : ptrs)
+    if (check_opt_ptr(q)) return LMOE_ERR_ALIGN;
+  BlockWs w = carve_block(*dims, ws);
+  if (ws_bytes < w.bytes) return LMOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the routing outputs the caller asked for; the logits are the input
+  // step's, given to the layer
+  lmoe_routing rr = {};
+  if (r) rr = *r;
+  if (!rr.logits) rr.logits = w.logits;
+  int st = run_moe_input(*dims, u, bw->w_in, rr.logits, w.x, w.h_sh, w, s);
+  if (st) return st;
+  lmoe_weights lw = *experts;
+  lw.router_w = nullptr;
+  lw.sh_gate = lw.sh_up = lw.sh_down = nullptr;
+  const lmoe_dims ld = layer_dims(*dims);
+  st = forward_impl(&ld, w.x, &lw, 1, &rr, w.routed, w.layer, w.layer_bytes, stream, nullptr,
+                    SideMode::kCaller, nullptr);
+  if (st) return st;
+  return run_moe_tail(*dims, w.routed, w.h_sh, bw->norm_w, bw->w_up, bw->w_sd, residual, out, w,
+                      s);
+}

@@ -1,0 +1,303 @@
+// Dense bf16 GEMMs of the MoE block around the layer (dev48.org "Kimi K3 on
+// AMD Instinct GPUs with TokenSpeed", sections 4.2-4.4): the packed input
+// projection (router scores, latent input and the shared experts' gate/up in
+// one multiply, the shared activation in its epilogue), the shared experts'
+// down projection, and the tail's latent -> hidden up-projection that adds
+// the shared output and the residual. Plus the routed RMSNorm.
+//
+// C = A B^T with A bf16 [M][K] (token rows) and B bf16 [N][K] (weight rows,
+// the storage the pages describe: matrices one after another, row-major).
+// A workgroup computes a BM x 128 tile of C over its K range in chunks of 64,
+// with both operands staged in LDS by global-to-LDS loads: one load
+// instruction moves 1 KB, 8 rows x 128 contiguous bytes, so weight rows are
+// streamed with full cache lines. The 16-byte segments of a staged row are
+// XOR-swizzled by the row's low three bits, so the eight rows an MFMA operand
+// read serves at once sit in eight different bank groups. Four waves; each
+// computes its part of the tile with v_mfma_f32_32x32x16_bf16 from operands
+// read out of LDS. NS chunks are in flight (one LDS array per slot: a read of
+// one slot never waits for the copy into another).
+//
+// Small M (decode) splits K over blockIdx.y so that the weight stream is
+// spread over enough workgroups; the fp32 partial tiles are then summed in a
+// fixed order by a finishing kernel that applies the epilogue, so results do
+// not depend on timing.
+
+#include "lmoe_internal.h"
+#include "lmoe_device.h"
+
+namespace lmoe {
+
+constexpr int kDnBN = 128;   // columns per workgroup tile
+constexpr int kDnBK = 64;    // K per chunk
+constexpr int kDnWaves = 4;
+constexpr int kDnThreads = 64 * kDnWaves;
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Epilogue of one output element (non-GLU columns) and of one GLU pair.
+__device__ __forceinline__ void dense_store(const DenseArgs& a, int m, int n, float v) {
+  if (n < a.n_f32) {
+    a.f32_out[(int64_t)m * a.ld_f32 + n] = v;
+  } else if (n < a.n_f32 + a.n_bf16) {
+    const int c = n - a.n_f32;
+    float r = v;
+    if (a.add0) r += bf16_bits_to_f32(a.add0[(int64_t)m * a.ld_add + c]);
+    if (a.add1) r += bf16_bits_to_f32(a.add1[(int64_t)m * a.ld_add + c]);
+    a.bf_out[(int64_t)m * a.ld_bf + c] = f32_to_bf16_bits(r);
+  }
+}
+// column n (in the GLU segment, a gate column: n - glu_base mod 32 < 16)
+__device__ __forceinline__ void dense_store_glu(const DenseArgs& a, int m, int n, float g,
+                                                float u) {
+  const int c = n - (a.n_f32 + a.n_bf16);
+  const int col = (c >> 5) * 16 + (c & 15);
+  a.glu_out[(int64_t)m * a.ld_glu + col] = f32_to_bf16_bits(silu(g) * u);
+}
+
+// physical 16-byte segment of logical segment g (0..7) of staged row r
+__device__ __forceinline__ int dn_seg(int r, int g) { return g ^ (r & 7); }
+
+template <int BM>
+struct DnCfg {
+  static constexpr int WM = BM >= 64 ? 2 : 1;       // waves along M
+  static constexpr int WN = kDnWaves / WM;          // waves along N
+  static constexpr int TM = BM / WM / 32;           // 32-row MFMA tiles per wave
+  static constexpr int TN = kDnBN / WN / 32;        // 32-column MFMA tiles per wave
+  static constexpr int kRows = BM + kDnBN;          // staged rows per chunk (A then B)
+  static constexpr int kCopies = kRows / 8 / kDnWaves;  // DMA instructions per wave and chunk
+  static_assert(kCopies * 8 * kDnWaves == kRows, "rows shared evenly by the waves");
+};
+
+template <int BM>
+using DnSlot = uint8_t[DnCfg<BM>::kRows * 128];
+
+// The tile of workgroup b: tiles are ordered in groups of G row tiles, all
+// columns of a group before the next, and the chip's eight XCDs (workgroup b
+// runs on XCD b % 8) each take one contiguous range of that order, so the
+// workgroups running together on one XCD share a few A and B tiles in its L2.
+__device__ __forceinline__ bool dense_tile(const DenseArgs& a, int* rt, int* ct) {
+  const int b = blockIdx.x;
+  const int n_tiles = a.n_rt * a.n_ct;
+  const int per_xcd = (n_tiles + 7) / 8;
+  const int t = (b & 7) * per_xcd + (b >> 3);
+  if ((b >> 3) >= per_xcd || t >= n_tiles) return false;
+  const int G = a.group_rows;
+  const int grp = t / (G * a.n_ct);
+  const int w = t - grp * G * a.n_ct;
+  const int rows_in = min(G, a.n_rt - grp * G);
+  *rt = grp * G + w % rows_in;
+  *ct = w / rows_in;
+  return true;
+}
+
+template <int BM, int NS>
+__global__ __launch_bounds__(kDnThreads, 2) void dense_gemm_kernel(DenseArgs a) {
+  using C = DnCfg<BM>;
+  __shared__ __attribute__((aligned(16))) DnSlot<BM> s0, s1, s2, s3;
+  auto slot = [&](int r) -> DnSlot<BM>& {
+    return r == 0 ? s0 : r == 1 ? s1 : r == 2 ? s2 : s3;
+  };
+  static_assert(NS >= 2 && NS <= 4, "two to four slots");
+  int rt, ct;
+  if (!dense_tile(a, &rt, &ct)) return;
+  const int m0 = rt * BM, n0 = ct * kDnBN;
+  const int kz = blockIdx.y;
+  const int kb = kz * a.k_per;                       // first K of this split
+  const int nk = min(a.k_per, a.K - kb) / kDnBK;     // chunks
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r32 = lane & 31, hh = lane >> 5;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+
+  // this wave's DMA sources: staged rows wave*8*kCopies + 8 i + lane / 8
+  const uint16_t* src[C::kCopies];
+#pragma unroll
+  for (int i = 0; i < C::kCopies; ++i) {
+    const int row = (wave * C::kCopies + i) * 8 + (lane >> 3);
+    const int g = dn_seg(row, lane & 7);
+    const uint16_t* p;
+    if (row < BM)
+      p = a.a + (int64_t)min(m0 + row, a.M - 1) * a.lda;
+    else
+      p = a.b + (int64_t)min(n0 + row - BM, a.N - 1) * a.ldb;
+    src[i] = p + kb + g * 8;
+  }
+  auto copy = [&](int c, int buf) {
+    const int cc = min(c, nk - 1);
+#pragma unroll
+    for (int i = 0; i < C::kCopies; ++i)
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(src[i] + cc * kDnBK),
+          (__attribute__((address_space(3))) void*)(&slot(buf)[(wave * C::kCopies + i) * 8 * 128]),
+          16, 0, 0);
+  };
+
+  f32x16_t acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  auto compute = [&](int buf) {
+    const uint8_t* sp = slot(buf);
+#pragma unroll
+    for (int s = 0; s < kDnBK / 16; ++s) {
+      bf16x8_t av[C::TM], bv[C::TN];
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) {
+        const int row = wm * (BM / C::WM) + i * 32 + r32;
+        av[i] = *reinterpret_cast<const bf16x8_t*>(sp + row * 128 + 16 * dn_seg(row, 2 * s + hh));
+      }
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int row = BM + wn * (kDnBN / C::WN) + j * 32 + r32;
+        bv[j] = *reinterpret_cast<const bf16x8_t*>(sp + row * 128 + 16 * dn_seg(row, 2 * s + hh));
+      }
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // chunk c's copies are complete once only the copies of the NS - 2 later
+  // chunks are outstanding
+  constexpr int kAhead = (NS - 2) * C::kCopies;
+  static_assert(kAhead < 64, "vmcnt field");
+  constexpr int kWait = 0x0F70 | (kAhead & 15) | ((kAhead >> 4) << 14);
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) copy(i, i);
+  auto group = [&](int cb, bool last) {
+#pragma unroll
+    for (int r = 0; r < NS; ++r) {
+      const int c = cb + r;
+      __builtin_amdgcn_s_waitcnt(kWait);
+      __builtin_amdgcn_s_barrier();
+      copy(c + NS - 1, (r + NS - 1) % NS);
+      __builtin_amdgcn_sched_barrier(0);
+      if (!last || c < nk) compute(r);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const int full = nk / NS;
+  if (full > 0) group(0, false);
+  for (int g = 1; g < full; ++g) group(g * NS, false);
+  if (nk % NS) group(full * NS, true);
+  __builtin_amdgcn_s_waitcnt(0);
+
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int nb = n0 + wn * (kDnBN / C::WN) + j * 32;  // first column of the MFMA tile
+      const int n = nb + r32;
+      const bool glu = nb >= a.n_f32 + a.n_bf16;          // the same for the whole tile
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wm * (BM / C::WM) + i * 32 + 8 * (e / 4) + 4 * hh + (e & 3);
+        const float v = acc[i][j][e];
+        if (a.part) {
+          if (m < a.M && n < a.N) a.part[((int64_t)kz * a.M + m) * a.N + n] = v;
+        } else if (glu) {
+          const float u = __shfl_down(v, 16, 64);
+          if (r32 < 16 && m < a.M && n < a.N) dense_store_glu(a, m, n, v, u);
+        } else if (m < a.M && n < a.N) {
+          dense_store(a, m, n, v);
+        }
+      }
+    }
+}
+
+// Sum of the K-split partial tiles in split order, then the epilogue: one
+// thread per output element (a GLU thread takes its gate and up columns).
+__global__ __launch_bounds__(256) void dense_finish_kernel(DenseArgs a, int ksplit) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.M * a.N) return;
+  const int m = (int)(i / a.N), n = (int)(i - (int64_t)m * a.N);
+  const int gb = a.n_f32 + a.n_bf16;
+  if (n >= gb && ((n - gb) & 16)) return;  // up columns: read by their gate column's thread
+  float v = 0.f;
+  for (int z = 0; z < ksplit; ++z) v += a.part[((int64_t)z * a.M + m) * a.N + n];
+  if (n >= gb) {
+    float u = 0.f;
+    for (int z = 0; z < ksplit; ++z) u += a.part[((int64_t)z * a.M + m) * a.N + n + 16];
+    dense_store_glu(a, m, n, v, u);
+  } else {
+    dense_store(a, m, n, v);
+  }
+}
+
+// Routed RMSNorm: n = bf16(r * (1 / sqrt(mean(r^2) + eps)) * gamma), one
+// workgroup per row, the squares summed in fp32.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ r,
+                                                      const uint16_t* __restrict__ gamma,
+                                                      int L, float eps,
+                                                      uint16_t* __restrict__ out) {
+  __shared__ float part[4];
+  const int row = blockIdx.x;
+  const uint16_t* rr = r + (int64_t)row * L;
+  float s = 0.f;
+  for (int i = threadIdx.x; i < L; i += 256) {
+    const float v = bf16_bits_to_f32(rr[i]);
+    s += v * v;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+  const float inv = 1.f / sqrtf(tot / (float)L + eps);
+  for (int i = threadIdx.x; i < L; i += 256)
+    out[(int64_t)row * L + i] =
+        f32_to_bf16_bits(bf16_bits_to_f32(rr[i]) * inv * bf16_bits_to_f32(gamma[i]));
+}
+
+DensePlan dense_plan(int M, int N, int K) {
+  DensePlan p;
+  p.bm = M <= 32 ? 32 : M <= 64 ? 64 : 128;
+  const int n_rt = (M + p.bm - 1) / p.bm, n_ct = (N + kDnBN - 1) / kDnBN;
+  const int tiles = n_rt * n_ct;
+  // spread small-M weight streams over about 1024 workgroups
+  int ks = 1;
+  const int nkc = K / kDnBK;
+  while (tiles * ks < 1024 && ks * 2 <= nkc && ks < 16) ks *= 2;
+  const int per = (nkc + ks - 1) / ks;
+  p.ksplit = (nkc + per - 1) / per;
+  p.k_per = per * kDnBK;
+  p.part_floats = p.ksplit > 1 ? (size_t)p.ksplit * M * N : 0;
+  return p;
+}
+
+hipError_t launch_dense(DenseArgs a, const DensePlan& p, float* part, hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  a.n_rt = (a.M + p.bm - 1) / p.bm;
+  a.n_ct = (a.N + kDnBN - 1) / kDnBN;
+  a.group_rows = 4;
+  a.k_per = p.k_per;
+  a.part = p.ksplit > 1 ? part : nullptr;
+  const int n_tiles = a.n_rt * a.n_ct;
+  const dim3 grid((unsigned)(8 * ((n_tiles + 7) / 8)), (unsigned)p.ksplit);
+  if (p.bm == 32)
+    hipLaunchKernelGGL((dense_gemm_kernel<32, 3>), grid, dim3(kDnThreads), 0, s, a);
+  else if (p.bm == 64)
+    hipLaunchKernelGGL((dense_gemm_kernel<64, 3>), grid, dim3(kDnThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((dense_gemm_kernel<128, 2>), grid, dim3(kDnThreads), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || p.ksplit == 1) return err;
+  const int64_t n = (int64_t)a.M * a.N;
+  hipLaunchKernelGGL(dense_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
+                     p.ksplit);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const uint16_t* r, const uint16_t* gamma, int T, int L, float eps,
+                          uint16_t* out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)T), dim3(256), 0, s, r, gamma, L, eps, out);
+  return hipGetLastError();
+}
+
+}  // namespace lmoe

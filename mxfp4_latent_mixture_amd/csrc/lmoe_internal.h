@@ -192,6 +192,44 @@ hipError_t launch_decode_multi(const DecodeArgs& a, hipStream_t s, const hipEven
 // and resets it
 hipError_t launch_read_errors(int32_t* ctr, int32_t* count, hipStream_t s);
 
+// ---- dense bf16 GEMMs of the MoE block (dense.hip) ----
+// C = A B^T, A bf16 [M][K] (row stride lda), B bf16 [N][K] (ldb), K a
+// multiple of 64. Output columns fall in three consecutive segments:
+// [0, n_f32) stored as fp32 (f32_out, ld_f32); [n_f32, n_f32 + n_bf16)
+// stored as bf16 after adding the optional bf16 addends add0, add1 (same
+// column numbering, ld_add); the rest GLU pairs: in each 32 columns the first
+// 16 are gate and the next 16 up values of 16 consecutive outputs,
+// bf16(silu(g) * u) to glu_out (ld_glu). Segment starts are multiples of 32.
+struct DenseArgs {
+  const uint16_t* a;
+  int64_t lda;
+  const uint16_t* b;
+  int64_t ldb;
+  int M, N, K;
+  int n_f32, n_bf16;
+  float* f32_out;
+  int64_t ld_f32;
+  uint16_t* bf_out;
+  int64_t ld_bf;
+  uint16_t* glu_out;
+  int64_t ld_glu;
+  const uint16_t* add0;
+  const uint16_t* add1;
+  int64_t ld_add;
+  // set by launch_dense
+  int n_rt, n_ct, group_rows, k_per;
+  float* part;  // K-split partial tiles [ksplit][M][N] (split launches only)
+};
+struct DensePlan {
+  int bm;              // rows per workgroup tile (32, 64, 128)
+  int ksplit, k_per;   // K splits and K per split
+  size_t part_floats;  // workspace for the partial tiles
+};
+DensePlan dense_plan(int M, int N, int K);
+hipError_t launch_dense(DenseArgs a, const DensePlan& p, float* part, hipStream_t s);
+hipError_t launch_rmsnorm(const uint16_t* r, const uint16_t* gamma, int T, int L, float eps,
+                          uint16_t* out, hipStream_t s);
+
 hipError_t launch_read_stream(const void* p, size_t bytes, uint32_t* sink, int blocks,
                               hipStream_t s);
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* sc, int rows, int K, uint16_t* out,

@@ -31,7 +31,9 @@ def test_header_declares_the_boundary():
                             "lmoe_pack_weights", "lmoe_forward_packed",
                             "lmoe_debug_read_stream", "lmoe_debug_quantize_act",
                             "lmoe_stage_name", "lmoe_path_name",
-                            "lmoe_debug_dequant_mxfp4", "lmoe_status_string"]), names
+                            "lmoe_debug_dequant_mxfp4", "lmoe_status_string",
+                            "lmoe_block_workspace_bytes", "lmoe_moe_input", "lmoe_moe_tail",
+                            "lmoe_block_forward"]), names
 
 
 def test_library_exports_every_declared_symbol(lm):
@@ -342,3 +344,52 @@ def test_binding_rejects_host_tensors(lm):
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):
         lm._ptr(torch.zeros(4))
+
+
+K3_BLOCK = (1, 7168, 3584, 896, 16, 2048, 2, 2048)   # T, H, L, E, k, I, S, Is
+
+
+def test_block_workspace_bytes_valid_and_invalid(lm):
+    assert lm.block_workspace_bytes(K3_BLOCK) > lm.workspace_bytes(
+        (1, 3584, 896, 16, 2048, 0, 0))
+    assert lm.block_workspace_bytes((4096,) + K3_BLOCK[1:]) > lm.block_workspace_bytes(K3_BLOCK)
+    assert lm.block_workspace_bytes((1, 7168, 3584, 896, 16, 2048, 0, 0)) > 0
+    for bad in [(1, 7160, 3584, 896, 16, 2048, 2, 2048),   # H % 64
+                (1, 7168, 3552, 896, 16, 2048, 2, 2048),   # L % 64
+                (1, 7168, 3584, 900, 16, 2048, 2, 2048),   # E % 32
+                (1, 7168, 3584, 896, 16, 2048, 1, 32),     # S * Is % 64
+                (1, 7168, 3584, 896, 16, 2048, 9, 2048),   # S > 8
+                (1, 7168, 3584, 896, 33, 2048, 2, 2048),   # k > 32
+                (-1, 7168, 3584, 896, 16, 2048, 2, 2048)]:
+        assert lm.block_workspace_bytes(bad) == 0, bad
+
+
+def test_block_calls_reject_bad_arguments_on_the_host(lm):
+    d = lm.lmoe_block_dims(*K3_BLOCK)
+    big = 1 << 40
+    p = [0x10000000 + 0x100000 * i for i in range(12)]
+    mi, mt = lm._lib.lmoe_moe_input, lm._lib.lmoe_moe_tail
+    assert mi(None, p[0], p[1], p[2], p[3], p[4], p[5], big, None) == lm.LMOE_ERR_NULL
+    assert mi(ctypes.byref(d), None, p[1], p[2], p[3], p[4], p[5], big, None) == lm.LMOE_ERR_NULL
+    assert mi(ctypes.byref(d), p[0], p[1], p[2], p[3], None, p[5], big, None) == lm.LMOE_ERR_NULL
+    assert mi(ctypes.byref(d), p[0] + 8, p[1], p[2], p[3], p[4], p[5], big,
+              None) == lm.LMOE_ERR_ALIGN
+    assert mi(ctypes.byref(d), p[0], p[1], p[2], p[3], p[4], p[5], 1024,
+              None) == lm.LMOE_ERR_WORKSPACE
+    bad = lm.lmoe_block_dims(1, 7160, 3584, 896, 16, 2048, 2, 2048)
+    assert mi(ctypes.byref(bad), p[0], p[1], p[2], p[3], p[4], p[5], big,
+              None) == lm.LMOE_ERR_SHAPE
+    assert mt(ctypes.byref(d), p[0], p[1], p[2], p[3], None, p[5], p[6], p[7], big,
+              None) == lm.LMOE_ERR_NULL
+    assert mt(ctypes.byref(d), p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], 1024,
+              None) == lm.LMOE_ERR_WORKSPACE
+    bw = lm.lmoe_block_weights(p[0], p[1], p[2], None)
+    w = lm.lmoe_weights(*[p[3]] * 10)
+    bf = lm._lib.lmoe_block_forward
+    assert bf(ctypes.byref(d), p[4], p[5], ctypes.byref(bw), ctypes.byref(w), None, p[6], p[7],
+              big, None) == lm.LMOE_ERR_NULL          # S > 0 needs w_sd
+    assert bf(ctypes.byref(d), p[4], p[5], None, ctypes.byref(w), None, p[6], p[7], big,
+              None) == lm.LMOE_ERR_NULL
+    d0 = lm.lmoe_block_dims(0, *K3_BLOCK[1:])
+    assert bf(ctypes.byref(d0), None, None, ctypes.byref(bw), ctypes.byref(w), None, None, None,
+              0, None) == lm.LMOE_OK
