@@ -162,6 +162,8 @@ KERNEL_SOURCES = {
     "chunk_": "route.hip",
     "permute_kernel": "route.hip",
     "combine_kernel": "experts.hip",
+    "dense_": "dense.hip",
+    "rmsnorm": "dense.hip",
 }
 
 
@@ -700,6 +702,127 @@ def extra_case(lm, hip, name, dev, steps, packed: bool, path=None):
 # path choice) and on tile-packed experts (lmoe_forward_packed), at each T;
 # all stream the D distinct experts' weights. `auto` is what lmoe_forward
 # takes for that shape.
+BLOCKS = ("block_decode", "block_batched", "block_prefill")
+DEFAULT_BLOCKS = "block_decode,block_prefill"
+
+
+def block_algorithmic(d, D: int):
+    """Algorithmic bytes and flops of the MoE block's input step, tail and
+    the whole block (input step + the layer without shared experts + tail):
+    every weight read once, the activations in and out once."""
+    T, H, L, E, SI = d.T, d.H, d.L, d.E, d.S * d.Is
+    n_in = E + L + 2 * SI
+    inp_b = 2 * H * n_in + 2 * T * H + 4 * T * E + 2 * T * L + 2 * T * SI
+    inp_f = 2 * T * H * n_in
+    tail_b = 2 * H * (L + SI) + 2 * T * (L + SI) + 2 * L + 4 * T * H
+    tail_f = 2 * T * H * (L + SI)
+    lay = type(d)(T=T, L=L, E=E, k=d.k, I=d.I, S=0, Is=0)
+    lb, lf, _, _ = algorithmic(lay, D, True)
+    return {"input": (inp_b, inp_f), "tail": (tail_b, tail_f),
+            "block": (inp_b + lb + tail_b, inp_f + lf + tail_f)}
+
+
+def block_case(lm, hip, name, dev, steps):
+    """The MoE block around the layer (lmoe_moe_input, lmoe_moe_tail,
+    lmoe_block_forward), timed with HIP events on the launch stream. Up to 64
+    tokens the calls rotate over 2 copies of the block's dense weights and 64
+    tokens' inputs, so weights are read from HBM each step, as in serving."""
+    import torch
+    from workloads import get_workload, gen_block, gen_experts
+    w = get_workload(name)
+    d = w.dims
+    T, SI = d.T, d.S * d.Is
+    rotate = T <= 64
+    n_tok = N_TOKENS if rotate else 1
+    reps = 2 if rotate else 1
+    t0 = time.time()
+    ex = gen_experts(w)
+    experts = {k: upload(v, dev) for k, v in ex.items()}
+    del ex
+    b = gen_block(w.with_T(T * n_tok))
+    dense = [{k: upload(b[k], dev) for k in ("w_in", "norm_w", "w_up", "w_sd")}]
+    for _ in range(reps - 1):
+        dense.append({k: v.clone() for k, v in dense[0].items()})
+    u_pool, res_pool = upload(b["u"], dev), upload(b["residual"], dev)
+    del b
+    log(f"{name}: inputs generated and resident in {time.time() - t0:.1f}s")
+    ws = torch.zeros(lm.block_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    logits = torch.empty((T, d.E), dtype=torch.float32, device=dev)
+    x = torch.empty((T, d.L), dtype=torch.int16, device=dev)
+    h = torch.empty((T, max(SI, 1)), dtype=torch.int16, device=dev)
+    routed = torch.empty((T, d.L), dtype=torch.int16, device=dev)
+    out = torch.empty((T, d.H), dtype=torch.int16, device=dev)
+    r = {"logits": logits, "counts": torch.empty((d.E,), dtype=torch.int32, device=dev)}
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def rows(i, pool):
+        j = i % n_tok
+        return pool[j * T:(j + 1) * T]
+
+    def f_input(i):
+        dw = dense[i % reps]
+        return lambda: lm.moe_input(d, rows(i, u_pool), dw["w_in"], logits, x, h, ws)
+
+    def f_tail(i):
+        dw = dense[i % reps]
+        return lambda: lm.moe_tail(d, routed, h, dw["norm_w"], dw["w_up"], dw["w_sd"],
+                                   rows(i, res_pool), out, ws)
+
+    def f_block(i):
+        dw = dense[i % reps]
+        return lambda: lm.block_forward(d, rows(i, u_pool), rows(i, res_pool), dw, experts, r,
+                                        out, ws)
+
+    # distinct experts per step (untimed), and a routed result for the tail
+    D = []
+    for i in range(n_tok):
+        f_block(i)()
+        D.append(int((r["counts"] > 0).sum().item()))
+    routed.copy_(x)
+    sleep_cycles = hold_cycles(hip, stream, HOLD_MS)
+    e0, e1 = hip.event(), hip.event()
+    n = steps if rotate else max(3, steps // 20)
+
+    def timed(make):
+        for i in range(2):
+            make(i)()
+        calls = [make(i) for i in range(n)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(sleep_cycles)
+        hip.record(e0, stream)
+        for c in calls:
+            c()
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        return hip.elapsed_ms(e0, e1) / n
+
+    alg = block_algorithmic(d, float(np.mean(D)))
+    out_d = {"T": T, "H": d.H, "L": d.L, "E": d.E, "k": d.k, "I": d.I, "S": d.S, "Is": d.Is,
+             "distinct_experts": round(float(np.mean(D)), 1), "steps": n}
+    for leg, make, kernel in (("input", f_input, "dense_gemm_kernel"),
+                              ("tail", f_tail, "dense_gemm_kernel"),
+                              ("block", f_block, None)):
+        ms = timed(make)
+        nb, nf = alg[leg]
+        sec = ms * 1e-3
+        hbm = nf / nb < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        e = {"us": round(ms * 1e3, 2), "gb_s": round(nb / sec / 1e9, 1),
+             "tflop_s": round(nf / sec / 1e12, 2), "algorithmic_bytes": round(nb),
+             "algorithmic_flops": round(nf)}
+        if kernel:   # the leg's GEMMs (and their K-split finish) as one unit
+            ach = nb / sec / 1e9 if hbm else nf / sec / 1e12
+            peak = HBM_PEAK_GBS if hbm else BF16_PEAK_TFLOPS
+            e["roofline"] = {"bound": "hbm" if hbm else "mfma", "achieved": round(ach, 2),
+                             "peak": peak, "unit": "GB/s" if hbm else "TFLOP/s",
+                             "frac": round(ach / peak, 4), "kernel": kernel,
+                             "traffic": measured_traffic(kernel, name)}
+        out_d[leg] = e
+        log(f"{name} {leg}: {ms * 1e3:.1f} us, {e['gb_s']} GB/s, {e['tflop_s']} TFLOP/s")
+    del experts, dense, u_pool, res_pool, ws
+    torch.cuda.empty_cache()
+    return out_d
+
+
 SMALL_T = (2, 4, 8, 16)
 
 
@@ -736,6 +859,9 @@ def main():
     ap.add_argument("--extra", default=DEFAULT_EXTRA,
                     help="comma-separated further workloads to report, 'all', or 'none': "
                          + ", ".join(EXTRA))
+    ap.add_argument("--block", default=DEFAULT_BLOCKS,
+                    help="MoE-block workloads to report (input step, tail, whole block): "
+                         + ", ".join(BLOCKS) + ", or 'none'")
     ap.add_argument("--no-small-t", action="store_true",
                     help="skip the 2..16-token decode sweep (fused kernel against the "
                          "grouped path)")
@@ -844,6 +970,9 @@ def main():
                 result["extra"][n + "_rowmajor"] = extra_case(lm, hip, n, dev, args.steps, False)
             else:
                 result["extra"][n] = extra_case(lm, hip, n, dev, args.steps, packed)
+    if args.block and args.block != "none":
+        result["block"] = {n: block_case(lm, hip, n, dev, args.steps)
+                           for n in args.block.split(",")}
     if not args.no_small_t:
         result["decode_small_t"] = small_t_sweep(lm, hip, dev, max(20, args.steps // 2))
     if not args.no_cpu:
