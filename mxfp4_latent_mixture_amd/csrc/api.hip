@@ -165,15 +165,16 @@ static int run_route(const Plan& p, const Workspace& ws, const uint16_t* x, cons
 }
 
 // T == 1, or 2..16 tokens: the whole layer as one persistent kernel. Stage
-// events: the kernel's time lands on the router stage.
+// events: the kernel's time lands on the router stage. With given logits
+// (r->logits) the router items publish them instead of computing them.
 static int run_fused_decode(const Plan& p, const Workspace& ws, const uint16_t* x,
                             const lmoe_weights& w, const lmoe_routing* r, uint16_t* out,
-                            hipStream_t s, const hipEvent_t* ev) {
+                            hipStream_t s, const hipEvent_t* ev, bool logits_given) {
   DecodeArgs a;
   if (p.fused_multi)
-    make_decode_multi_args(p, a);
+    make_decode_multi_args(p, a, logits_given);
   else
-    make_decode_args(p, a);
+    make_decode_args(p, a, logits_given);
   a.x = x;
   a.wr = w.router_w;
   a.gq = w.gate_q;
@@ -197,7 +198,8 @@ static int run_fused_decode(const Plan& p, const Workspace& ws, const uint16_t* 
   a.y = ws.y;
   a.ysh = ws.y_sh;
   a.out = out;
-  a.logits_out = r ? r->logits : nullptr;
+  a.logits_out = (r && !logits_given) ? r->logits : nullptr;
+  a.logits_in = logits_given ? r->logits : nullptr;
   a.idx = idx;
   a.w = wt;
   a.counts = counts;
@@ -368,8 +370,8 @@ static int forward_impl(const lmoe_dims* dims, const uint16_t* x, const lmoe_wei
   Workspace wsp = carve_workspace(p, ws, ws_with_q);
   if (ws_bytes < wsp.bytes) return LMOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((p.fused_decode || p.fused_multi) && !logits_given)
-    return run_fused_decode(p, wsp, x, w, r, out, s, ev);
+  if (p.fused_decode || p.fused_multi)
+    return run_fused_decode(p, wsp, x, w, r, out, s, ev, logits_given != 0);
   Routing rt;
   // Traced calls keep every stage on the caller's stream, in order, so each
   // stage's events time it alone.
@@ -568,8 +570,9 @@ extern "C" int lmoe_forward_traced(const lmoe_dims* dims, const uint16_t* x,
 extern "C" const char* lmoe_path_name(const lmoe_dims* dims, int logits_given) {
   if (!dims || !dims_ok(*dims)) return "invalid";
   Plan p = make_plan(*dims);
-  if (p.fused_decode && !logits_given) return "fused_decode";
-  if (p.fused_multi && !logits_given) return "fused_multi";
+  (void)logits_given;  // given logits take the same paths (published, not computed)
+  if (p.fused_decode) return "fused_decode";
+  if (p.fused_multi) return "fused_multi";
   return "grouped";
 }
 

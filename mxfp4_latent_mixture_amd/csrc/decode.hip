@@ -110,10 +110,19 @@ __device__ __forceinline__ void store_glu(uint16_t* dst, float g, float u_src, i
 }
 
 // ---------------------------------------------------------------------------
-// Router: the logit of expert e, fp32 sum of x[l] W[e][l] over the row.
+// Router: the logit of expert e, fp32 sum of x[l] W[e][l] over the row. With
+// given logits, item e publishes logits 64 e .. 64 e + 63 instead.
 // ---------------------------------------------------------------------------
 __device__ void router_item(const DecodeArgs& a, int e, const uint16_t* xs) {
   const int lane = lane_id();
+  if (a.logits_in) {
+    const int g = e * kWave + lane;
+    if (g < a.E)
+      __hip_atomic_store(reinterpret_cast<uint64_t*>(a.ctr + kCtrLogit) + g,
+                         (1ull << 32) | __float_as_uint(a.logits_in[g]), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   const uint32_t bytes = (uint32_t)a.E * a.L * 2;
   const rsrc_t r = make_rsrc(a.wr, bytes);
   const int row = e * a.L * 2;
@@ -483,7 +492,7 @@ static int decode_grid(size_t lds_bytes) {
   return grid;
 }
 
-void make_decode_args(const Plan& p, DecodeArgs& a) {
+void make_decode_args(const Plan& p, DecodeArgs& a, bool logits_given) {
   const lmoe_dims& d = p.d;
   a.T = 1;
   a.L = d.L;
@@ -492,7 +501,7 @@ void make_decode_args(const Plan& p, DecodeArgs& a) {
   a.I = d.I;
   a.S = d.S;
   a.Is = d.Is;
-  a.n_router = d.E;
+  a.n_router = logits_given ? (d.E + kWave - 1) / kWave : d.E;
   a.n_groups = d.k;
   a.xstride = d.L;
   a.shgu_per_expert = d.S > 0 ? (d.Is + 7) / 8 : 0;

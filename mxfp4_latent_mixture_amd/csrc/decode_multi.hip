@@ -90,9 +90,19 @@ __device__ __forceinline__ int* part_ctr(const DecodeArgs& a, int t, int b) {
 
 // ---------------------------------------------------------------------------
 // Router: expert e's logit for every token, fp32 dot products of bf16 pairs.
+// With given logits, item e publishes entries 64 e .. 64 e + 63 of the
+// [T][E] logits instead.
 // ---------------------------------------------------------------------------
 __device__ void router_m(const DecodeArgs& a, int e, const uint16_t* xs) {
   const int lane = lane_id();
+  if (a.logits_in) {
+    const int g = e * kWave + lane;
+    if (g < a.T * a.E)
+      __hip_atomic_store(logit_word(a, g / a.E, g % a.E),
+                         (1ull << 32) | __float_as_uint(a.logits_in[g]), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   const rsrc_t r = make_rsrc(a.wr, (uint32_t)a.E * a.L * 2);
   const int row = e * a.L * 2;
   constexpr int kMaxChunks = kDecodeMaxWidth * 2 / 1024;
@@ -610,7 +620,7 @@ size_t decode_multi_lds_bytes(const lmoe_dims& d) {
   return (size_t)d.T * (d.L + 8) * 2 + sizeof(GroupLds) + kWavesPerWg * sizeof(TopkScratch);
 }
 
-void make_decode_multi_args(const Plan& p, DecodeArgs& a) {
+void make_decode_multi_args(const Plan& p, DecodeArgs& a, bool logits_given) {
   const lmoe_dims& d = p.d;
   a.T = d.T;
   a.L = d.L;
@@ -621,7 +631,7 @@ void make_decode_multi_args(const Plan& p, DecodeArgs& a) {
   a.Is = d.Is;
   const int R = d.T * d.k;
   a.n_groups = std::min(d.E, R);
-  a.n_router = d.E;
+  a.n_router = logits_given ? (d.T * d.E + kWave - 1) / kWave : d.E;
   a.shgu_per_expert = d.S > 0 ? (d.Is + 7) / 8 : 0;
   a.n_shgu = d.S * a.shgu_per_expert;
   a.gu_per_route = (d.I + 15) / 16;

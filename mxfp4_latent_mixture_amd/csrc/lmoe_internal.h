@@ -101,6 +101,7 @@ struct DecodeArgs {
   const uint16_t *shg, *shu, *shd;
   int T, L, E, k, I, S, Is;
   float* logits_out;   // optional [T][E]
+  const float* logits_in;  // given logits [T][E] (router items publish them), or null
   int32_t* idx;
   float* w;
   int32_t *counts, *offsets, *perm, *inv;
@@ -181,10 +182,11 @@ hipError_t launch_quantize_act(const uint16_t* src, int64_t rows, int K, bool fp
                                uint8_t* exps, hipStream_t s);
 
 // ---- single-token decode (decode.hip) ----
-void make_decode_args(const Plan& p, DecodeArgs& a);
+// logits_given: the router items publish given logits, 64 per item
+void make_decode_args(const Plan& p, DecodeArgs& a, bool logits_given = false);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, const hipEvent_t* ev);
 // ---- 2..16-token decode (decode_multi.hip) ----
-void make_decode_multi_args(const Plan& p, DecodeArgs& a);
+void make_decode_multi_args(const Plan& p, DecodeArgs& a, bool logits_given = false);
 // LDS bytes the multi-token kernel needs (tokens and grouping tables)
 size_t decode_multi_lds_bytes(const lmoe_dims& d);
 hipError_t launch_decode_multi(const DecodeArgs& a, hipStream_t s, const hipEvent_t* ev);

@@ -61,12 +61,12 @@ def test_traced_forward_rejects_missing_events(lm):
 
 def test_path_names(lm):
     assert lm.path_name(K3) == "fused_decode"
-    assert lm.path_name(K3, True) == "grouped"
+    assert lm.path_name(K3, True) == "fused_decode"   # given logits are published
     # two and three K3 tokens: one kernel, one token per MFMA row; from four
     # the grouped kernels stream the weights faster
     for T in (2, 3):
         assert lm.path_name((T,) + K3[1:]) == "fused_multi"
-        assert lm.path_name((T,) + K3[1:], True) == "grouped"
+        assert lm.path_name((T,) + K3[1:], True) == "fused_multi"
     for T in (4, 5, 16, 17):
         assert lm.path_name((T,) + K3[1:]) == "grouped"
     assert lm.path_name((64,) + K3[1:]) == "grouped"

@@ -188,20 +188,33 @@ def test_fused_decode_k3_back_to_back(lm, dev):
     _run_tokens(lm, dev, w, 4)
 
 
-def test_single_token_with_given_logits_uses_grouped_path(lm, dev):
+@pytest.mark.parametrize("T", [1, 3, 16])
+def test_given_logits_take_the_fused_kernels(lm, dev, T):
+    """Given logits (ties straddling the top-k boundary, a NaN, -inf) on the
+    one-kernel paths: the router items publish them instead of computing
+    them. Routing bit-exact against the oracle's steps on the same logits,
+    outputs against the oracle, counters zero after, the logits untouched."""
     import torch
-    w = Workload("given1", 51, Dims(T=1, L=256, E=32, k=4, I=128, S=2, Is=128),
-                 scales=("uniform", 120, 130), logits_given=True)
+    w = Workload(f"given{T}", 51, Dims(T=T, L=256, E=32, k=4, I=128, S=2, Is=128),
+                 scales=("uniform", 120, 130), logits_given=True, tie_frac=0.5, tie_group=6)
     d = w.dims
-    assert lm.path_name(d, True) == "grouped"
+    assert lm.path_name(d, True) == ("fused_decode" if T == 1 else "fused_multi")
     inp = gen_all(w)
+    inp["logits"][0, 5] = np.nan
+    inp["logits"][-1, 7] = -np.inf
     dinp = upload(inp, dev)
     r = alloc_routing(d, dev)
     r["logits"] = dinp["logits"]
-    out = torch.empty((1, d.L), dtype=torch.int16, device=dev)
+    out = torch.empty((T, d.L), dtype=torch.int16, device=dev)
     ws = torch.zeros(lm.workspace_bytes(d), dtype=torch.uint8, device=dev)
     lm.forward(d, dinp["x"], dinp, True, r, out, ws)
     torch.cuda.synchronize()
-    ref = O.forward(inp["x"], inp["router_w"], inp, inp, d.k, logits=inp["logits"])
-    assert np.array_equal(r["topk_idx"].cpu().numpy(), ref["idx"])
-    check_out(out.cpu().numpy().view(np.uint16), ref["out64"], "given-logits T=1")
+    res = {k: v.cpu().numpy() for k, v in r.items()}
+    assert np.array_equal(res["logits"].view(np.uint32), inp["logits"].view(np.uint32))
+    check_routing_exact(res, inp["logits"], d.k, f"given logits T={T}")
+    ref = O.forward(inp["x"], None, inp, inp, d.k, logits=inp["logits"])
+    check_out(out.cpu().numpy().view(np.uint16), ref["out64"], f"given logits T={T}",
+              allowance_fn=flip_allowance_fn(inp["x"], ref["idx"], ref["w"],
+                                             lambda e: _expert(inp, e), inp, d.L, d.I))
+    ctr = ws[:CTR_BYTES].view(torch.int32).cpu().numpy()
+    assert not ctr.any(), f"counters left non-zero at {np.nonzero(ctr)[0][:8]}"

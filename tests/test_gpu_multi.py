@@ -212,8 +212,9 @@ def test_multi_decode_path_limits(lm):
         assert lm.path_name((T,) + K3) == "fused_multi"
     for T in (4, 5, 16, 17):
         assert lm.path_name((T,) + K3) == "grouped"
-    for T in (2, 16):
-        assert lm.path_name((T,) + K3, True) == "grouped"
+    # given logits take the same paths: the router items publish them
+    assert lm.path_name((2,) + K3, True) == "fused_multi"
+    assert lm.path_name((16,) + K3, True) == "grouped"
     small = (256, 32, 4, 128, 2, 128)
     for T in (2, 9, 16):
         assert lm.path_name((T,) + small) == "fused_multi"
