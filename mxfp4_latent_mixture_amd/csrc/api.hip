@@ -669,9 +669,11 @@ BlockWs carve_block(const lmoe_block_dims& b, void* base) {
   w.routed = reinterpret_cast<uint16_t*>(take(T * b.L * 2));
   w.n = reinterpret_cast<uint16_t*>(take(T * b.L * 2));
   w.sh = reinterpret_cast<uint16_t*>(take(T * (size_t)b.H * 2));
-  const size_t parts = std::max({dense_plan(b.T, b.E + b.L + 2 * (int)SI, b.H).part_floats,
-                                 SI ? dense_plan(b.T, b.H, (int)SI).part_floats : (size_t)0,
-                                 dense_plan(b.T, b.H, b.L).part_floats});
+  // the input GEMM's partials, or the tail's two products' (in one launch)
+  const size_t parts =
+      std::max(dense_plan(b.T, b.E + b.L + 2 * (int)SI, b.H).part_floats,
+               (SI ? dense_plan(b.T, b.H, (int)SI).part_floats : (size_t)0) +
+                   dense_plan(b.T, b.H, b.L).part_floats);
   w.part = reinterpret_cast<float*>(take(std::max(parts, (size_t)1) * 4));
   w.bytes = off;
   return w;
@@ -705,6 +707,31 @@ int run_moe_tail(const lmoe_block_dims& b, const uint16_t* routed, const uint16_
                  const uint16_t* residual, uint16_t* out, const BlockWs& ws, hipStream_t s) {
   const int SI = block_shared(b);
   if (launch_rmsnorm(routed, norm_w, b.T, b.L, 1e-6f, ws.n, s) != hipSuccess) return LMOE_ERR_HIP;
+  const DensePlan pu = dense_plan(b.T, b.H, b.L);
+  const DensePlan ps = SI ? dense_plan(b.T, b.H, SI) : pu;
+  if (SI && pu.ksplit > 1 && ps.ksplit > 1) {
+    // few tokens: both products K-split in one launch, one finishing pass
+    // adds bf16(h_sh w_sd^T) and the residual to n w_up^T
+    DenseArgs a = {};
+    a.a = ws.n;
+    a.lda = b.L;
+    a.b = w_up;
+    a.ldb = b.L;
+    a.K = b.L;
+    a.a2 = h_sh;
+    a.lda2 = SI;
+    a.b2 = w_sd;
+    a.ldb2 = SI;
+    a.K2 = SI;
+    a.M = b.T;
+    a.N = b.H;
+    a.n_bf16 = b.H;
+    a.bf_out = out;
+    a.ld_bf = b.H;
+    a.add1 = residual;
+    a.ld_add = b.H;
+    return launch_dense_pair(a, pu, ps, ws.part, s) == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
+  }
   if (SI) {  // sh = bf16(h_sh w_sd^T)
     DenseArgs a = {};
     a.a = h_sh;
@@ -717,8 +744,7 @@ int run_moe_tail(const lmoe_block_dims& b, const uint16_t* routed, const uint16_
     a.n_bf16 = b.H;
     a.bf_out = ws.sh;
     a.ld_bf = b.H;
-    if (launch_dense(a, dense_plan(a.M, a.N, a.K), ws.part, s) != hipSuccess)
-      return LMOE_ERR_HIP;
+    if (launch_dense(a, ps, ws.part, s) != hipSuccess) return LMOE_ERR_HIP;
   }
   DenseArgs a = {};  // out = bf16(n w_up^T + sh + residual)
   a.a = ws.n;
@@ -734,8 +760,7 @@ int run_moe_tail(const lmoe_block_dims& b, const uint16_t* routed, const uint16_
   a.add0 = SI ? ws.sh : nullptr;
   a.add1 = residual;
   a.ld_add = b.H;
-  return launch_dense(a, dense_plan(a.M, a.N, a.K), ws.part, s) == hipSuccess ? LMOE_OK
-                                                                              : LMOE_ERR_HIP;
+  return launch_dense(a, pu, ws.part, s) == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
 }
 
 }  // namespace

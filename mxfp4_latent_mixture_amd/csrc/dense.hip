@@ -35,12 +35,14 @@ constexpr int kDnThreads = 64 * kDnWaves;
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Epilogue of one output element (non-GLU columns) and of one GLU pair.
-__device__ __forceinline__ void dense_store(const DenseArgs& a, int m, int n, float v) {
+// extra: the second product's bf16-rounded sum (launch_dense_pair), else 0.
+__device__ __forceinline__ void dense_store(const DenseArgs& a, int m, int n, float v,
+                                            float extra = 0.f) {
   if (n < a.n_f32) {
     a.f32_out[(int64_t)m * a.ld_f32 + n] = v;
   } else if (n < a.n_f32 + a.n_bf16) {
     const int c = n - a.n_f32;
-    float r = v;
+    float r = v + extra;
     if (a.add0) r += bf16_bits_to_f32(a.add0[(int64_t)m * a.ld_add + c]);
     if (a.add1) r += bf16_bits_to_f32(a.add1[(int64_t)m * a.ld_add + c]);
     a.bf_out[(int64_t)m * a.ld_bf + c] = f32_to_bf16_bits(r);
@@ -101,9 +103,16 @@ __global__ __launch_bounds__(kDnThreads, 2) void dense_gemm_kernel(DenseArgs a) 
   int rt, ct;
   if (!dense_tile(a, &rt, &ct)) return;
   const int m0 = rt * BM, n0 = ct * kDnBN;
-  const int kz = blockIdx.y;
-  const int kb = kz * a.k_per;                       // first K of this split
-  const int nk = min(a.k_per, a.K - kb) / kDnBK;     // chunks
+  // the first product, or (blockIdx.y >= ks1) the second one of a pair
+  const bool second = (int)blockIdx.y >= a.ks1;
+  const int kz = second ? (int)blockIdx.y - a.ks1 : (int)blockIdx.y;
+  const uint16_t* A = second ? a.a2 : a.a;
+  const uint16_t* B = second ? a.b2 : a.b;
+  const int64_t lda = second ? a.lda2 : a.lda, ldb = second ? a.ldb2 : a.ldb;
+  const int K = second ? a.K2 : a.K, k_per = second ? a.k_per2 : a.k_per;
+  float* part = second ? a.part2 : a.part;
+  const int kb = kz * k_per;                         // first K of this split
+  const int nk = min(k_per, K - kb) / kDnBK;         // chunks
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r32 = lane & 31, hh = lane >> 5;
   const int wm = wave / C::WN, wn = wave % C::WN;
@@ -116,9 +125,9 @@ __global__ __launch_bounds__(kDnThreads, 2) void dense_gemm_kernel(DenseArgs a) 
     const int g = dn_seg(row, lane & 7);
     const uint16_t* p;
     if (row < BM)
-      p = a.a + (int64_t)min(m0 + row, a.M - 1) * a.lda;
+      p = A + (int64_t)min(m0 + row, a.M - 1) * lda;
     else
-      p = a.b + (int64_t)min(n0 + row - BM, a.N - 1) * a.ldb;
+      p = B + (int64_t)min(n0 + row - BM, a.N - 1) * ldb;
     src[i] = p + kb + g * 8;
   }
   auto copy = [&](int c, int buf) {
@@ -198,8 +207,8 @@ __global__ __launch_bounds__(kDnThreads, 2) void dense_gemm_kernel(DenseArgs a) 
       for (int e = 0; e < 16; ++e) {
         const int m = m0 + wm * (BM / C::WM) + i * 32 + 8 * (e / 4) + 4 * hh + (e & 3);
         const float v = acc[i][j][e];
-        if (a.part) {
-          if (m < a.M && n < a.N) a.part[((int64_t)kz * a.M + m) * a.N + n] = v;
+        if (part) {
+          if (m < a.M && n < a.N) part[((int64_t)kz * a.M + m) * a.N + n] = v;
         } else if (glu) {
           const float u = __shfl_down(v, 16, 64);
           if (r32 < 16 && m < a.M && n < a.N) dense_store_glu(a, m, n, v, u);
@@ -212,7 +221,8 @@ __global__ __launch_bounds__(kDnThreads, 2) void dense_gemm_kernel(DenseArgs a) 
 
 // Sum of the K-split partial tiles in split order, then the epilogue: one
 // thread per output element (a GLU thread takes its gate and up columns).
-__global__ __launch_bounds__(256) void dense_finish_kernel(DenseArgs a, int ksplit) {
+// ksplit2 > 0: a pair, the second product's sum rounded to bf16 and added.
+__global__ __launch_bounds__(256) void dense_finish_kernel(DenseArgs a, int ksplit, int ksplit2) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)a.M * a.N) return;
   const int m = (int)(i / a.N), n = (int)(i - (int64_t)m * a.N);
@@ -225,7 +235,12 @@ __global__ __launch_bounds__(256) void dense_finish_kernel(DenseArgs a, int kspl
     for (int z = 0; z < ksplit; ++z) u += a.part[((int64_t)z * a.M + m) * a.N + n + 16];
     dense_store_glu(a, m, n, v, u);
   } else {
-    dense_store(a, m, n, v);
+    float extra = 0.f;
+    if (ksplit2) {
+      for (int z = 0; z < ksplit2; ++z) extra += a.part2[((int64_t)z * a.M + m) * a.N + n];
+      extra = bf16_bits_to_f32(f32_to_bf16_bits(extra));
+    }
+    dense_store(a, m, n, v, extra);
   }
 }
 
@@ -259,15 +274,43 @@ DensePlan dense_plan(int M, int N, int K) {
   p.bm = M <= 32 ? 32 : M <= 64 ? 64 : 128;
   const int n_rt = (M + p.bm - 1) / p.bm, n_ct = (N + kDnBN - 1) / kDnBN;
   const int tiles = n_rt * n_ct;
-  // spread small-M weight streams over about 1024 workgroups
-  int ks = 1;
   const int nkc = K / kDnBK;
-  while (tiles * ks < 1024 && ks * 2 <= nkc && ks < 16) ks *= 2;
-  const int per = (nkc + ks - 1) / ks;
+  // Fewer tiles than resident workgroups (two per CU): split K. The split
+  // count minimises (rounds of resident workgroups) x (chunks each streams,
+  // plus about two chunks of start-up), so the grid fills whole rounds with
+  // long-lived workgroups rather than leaving a last round half empty.
+  constexpr int kSlots = 512;
+  int best = 1;
+  if (tiles < kSlots) {
+    double best_cost = 1e30;
+    for (int ks = 1; ks <= std::min(nkc, 64); ++ks) {
+      const int per = (nkc + ks - 1) / ks;
+      const int kse = (nkc + per - 1) / per;
+      const double rounds = (double)((tiles * kse + kSlots - 1) / kSlots);
+      const double cost = rounds * (per + 2) + (kse > 1 ? 1.0 : 0.0);  // + the finishing pass
+      if (cost < best_cost - 1e-9) {
+        best_cost = cost;
+        best = kse;
+      }
+    }
+  }
+  const int per = (nkc + best - 1) / best;
   p.ksplit = (nkc + per - 1) / per;
   p.k_per = per * kDnBK;
   p.part_floats = p.ksplit > 1 ? (size_t)p.ksplit * M * N : 0;
   return p;
+}
+
+static hipError_t launch_gemm_grid(const DenseArgs& a, int bm, int ky, hipStream_t s) {
+  const int n_tiles = a.n_rt * a.n_ct;
+  const dim3 grid((unsigned)(8 * ((n_tiles + 7) / 8)), (unsigned)ky);
+  if (bm == 32)
+    hipLaunchKernelGGL((dense_gemm_kernel<32, 3>), grid, dim3(kDnThreads), 0, s, a);
+  else if (bm == 64)
+    hipLaunchKernelGGL((dense_gemm_kernel<64, 3>), grid, dim3(kDnThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((dense_gemm_kernel<128, 2>), grid, dim3(kDnThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_dense(DenseArgs a, const DensePlan& p, float* part, hipStream_t s) {
@@ -276,20 +319,34 @@ hipError_t launch_dense(DenseArgs a, const DensePlan& p, float* part, hipStream_
   a.n_ct = (a.N + kDnBN - 1) / kDnBN;
   a.group_rows = 4;
   a.k_per = p.k_per;
+  a.ks1 = p.ksplit;  // no second product
   a.part = p.ksplit > 1 ? part : nullptr;
-  const int n_tiles = a.n_rt * a.n_ct;
-  const dim3 grid((unsigned)(8 * ((n_tiles + 7) / 8)), (unsigned)p.ksplit);
-  if (p.bm == 32)
-    hipLaunchKernelGGL((dense_gemm_kernel<32, 3>), grid, dim3(kDnThreads), 0, s, a);
-  else if (p.bm == 64)
-    hipLaunchKernelGGL((dense_gemm_kernel<64, 3>), grid, dim3(kDnThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((dense_gemm_kernel<128, 2>), grid, dim3(kDnThreads), 0, s, a);
-  hipError_t err = hipGetLastError();
+  a.part2 = nullptr;
+  hipError_t err = launch_gemm_grid(a, p.bm, p.ksplit, s);
   if (err != hipSuccess || p.ksplit == 1) return err;
   const int64_t n = (int64_t)a.M * a.N;
   hipLaunchKernelGGL(dense_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
-                     p.ksplit);
+                     p.ksplit, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_pair(DenseArgs a, const DensePlan& p1, const DensePlan& p2, float* part,
+                             hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  if (p1.bm != p2.bm || p1.ksplit < 2 || p2.ksplit < 2) return hipErrorInvalidValue;
+  a.n_rt = (a.M + p1.bm - 1) / p1.bm;
+  a.n_ct = (a.N + kDnBN - 1) / kDnBN;
+  a.group_rows = 4;
+  a.k_per = p1.k_per;
+  a.k_per2 = p2.k_per;
+  a.ks1 = p1.ksplit;
+  a.part = part;
+  a.part2 = part + p1.part_floats;
+  hipError_t err = launch_gemm_grid(a, p1.bm, p1.ksplit + p2.ksplit, s);
+  if (err != hipSuccess) return err;
+  const int64_t n = (int64_t)a.M * a.N;
+  hipLaunchKernelGGL(dense_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
+                     p1.ksplit, p2.ksplit);
   return hipGetLastError();
 }
 

@@ -218,9 +218,19 @@ struct DenseArgs {
   const uint16_t* add0;
   const uint16_t* add1;
   int64_t ld_add;
-  // set by launch_dense
-  int n_rt, n_ct, group_rows, k_per;
+  // A second product of the same shape [M][N] with its own A, B and K
+  // (launch_dense_pair): its K-split partial sums are summed, rounded to bf16
+  // and added before add0 / add1, as the tail's shared partial is.
+  const uint16_t* a2;
+  int64_t lda2;
+  const uint16_t* b2;
+  int64_t ldb2;
+  int K2;
+  // set by the launchers
+  int n_rt, n_ct, group_rows, k_per, k_per2;
+  int ks1;      // K splits of the first product (blockIdx.y >= ks1: the second)
   float* part;  // K-split partial tiles [ksplit][M][N] (split launches only)
+  float* part2; // the second product's [ksplit2][M][N]
 };
 struct DensePlan {
   int bm;              // rows per workgroup tile (32, 64, 128)
@@ -229,6 +239,11 @@ struct DensePlan {
 };
 DensePlan dense_plan(int M, int N, int K);
 hipError_t launch_dense(DenseArgs a, const DensePlan& p, float* part, hipStream_t s);
+// Two products of the same [M][N] shape in one launch, both K-split
+// (p1.ksplit > 1 and p2.ksplit > 1, the same tile rows): out = epilogue of
+// (A B^T + bf16(A2 B2^T)). part: p1.part_floats + p2.part_floats floats.
+hipError_t launch_dense_pair(DenseArgs a, const DensePlan& p1, const DensePlan& p2, float* part,
+                             hipStream_t s);
 hipError_t launch_rmsnorm(const uint16_t* r, const uint16_t* gamma, int T, int L, float eps,
                           uint16_t* out, hipStream_t s);
 
