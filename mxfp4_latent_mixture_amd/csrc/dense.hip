@@ -27,10 +27,7 @@
 
 namespace lmoe {
 
-constexpr int kDnBN = 128;   // columns per workgroup tile
 constexpr int kDnBK = 64;    // K per chunk
-constexpr int kDnWaves = 4;
-constexpr int kDnThreads = 64 * kDnWaves;
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -59,19 +56,21 @@ __device__ __forceinline__ void dense_store_glu(const DenseArgs& a, int m, int n
 // physical 16-byte segment of logical segment g (0..7) of staged row r
 __device__ __forceinline__ int dn_seg(int r, int g) { return g ^ (r & 7); }
 
-template <int BM>
+// A BM x BN workgroup tile computed by NW waves, WM of them along M.
+template <int BM, int BN, int NW>
 struct DnCfg {
   static constexpr int WM = BM >= 64 ? 2 : 1;       // waves along M
-  static constexpr int WN = kDnWaves / WM;          // waves along N
+  static constexpr int WN = NW / WM;                // waves along N
   static constexpr int TM = BM / WM / 32;           // 32-row MFMA tiles per wave
-  static constexpr int TN = kDnBN / WN / 32;        // 32-column MFMA tiles per wave
-  static constexpr int kRows = BM + kDnBN;          // staged rows per chunk (A then B)
-  static constexpr int kCopies = kRows / 8 / kDnWaves;  // DMA instructions per wave and chunk
-  static_assert(kCopies * 8 * kDnWaves == kRows, "rows shared evenly by the waves");
+  static constexpr int TN = BN / WN / 32;           // 32-column MFMA tiles per wave
+  static constexpr int kRows = BM + BN;             // staged rows per chunk (A then B)
+  static constexpr int kCopies = kRows / 8 / NW;    // DMA instructions per wave and chunk
+  static_assert(kCopies * 8 * NW == kRows, "rows shared evenly by the waves");
+  static_assert(TM >= 1 && TN >= 1, "at least one MFMA tile per wave");
 };
 
-template <int BM>
-using DnSlot = uint8_t[DnCfg<BM>::kRows * 128];
+template <int BM, int BN, int NW>
+using DnSlot = uint8_t[DnCfg<BM, BN, NW>::kRows * 128];
 
 // The tile of workgroup b: tiles are ordered in groups of G row tiles, all
 // columns of a group before the next, and the chip's eight XCDs (workgroup b
@@ -92,17 +91,18 @@ __device__ __forceinline__ bool dense_tile(const DenseArgs& a, int* rt, int* ct)
   return true;
 }
 
-template <int BM, int NS>
-__global__ __launch_bounds__(kDnThreads, 2) void dense_gemm_kernel(DenseArgs a) {
-  using C = DnCfg<BM>;
-  __shared__ __attribute__((aligned(16))) DnSlot<BM> s0, s1, s2, s3;
-  auto slot = [&](int r) -> DnSlot<BM>& {
+template <int BM, int BN, int NW, int NS>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void dense_gemm_kernel(DenseArgs a) {
+  using C = DnCfg<BM, BN, NW>;
+  using Slot = DnSlot<BM, BN, NW>;
+  __shared__ __attribute__((aligned(16))) Slot s0, s1, s2, s3;
+  auto slot = [&](int r) -> Slot& {
     return r == 0 ? s0 : r == 1 ? s1 : r == 2 ? s2 : s3;
   };
   static_assert(NS >= 2 && NS <= 4, "two to four slots");
   int rt, ct;
   if (!dense_tile(a, &rt, &ct)) return;
-  const int m0 = rt * BM, n0 = ct * kDnBN;
+  const int m0 = rt * BM, n0 = ct * BN;
   // the first product, or (blockIdx.y >= ks1) the second one of a pair
   const bool second = (int)blockIdx.y >= a.ks1;
   const int kz = second ? (int)blockIdx.y - a.ks1 : (int)blockIdx.y;
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kDnThreads, 2) void dense_gemm_kernel(DenseArgs a) 
       }
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
-        const int row = BM + wn * (kDnBN / C::WN) + j * 32 + r32;
+        const int row = BM + wn * (BN / C::WN) + j * 32 + r32;
         bv[j] = *reinterpret_cast<const bf16x8_t*>(sp + row * 128 + 16 * dn_seg(row, 2 * s + hh));
       }
 #pragma unroll
@@ -196,14 +196,16 @@ __global__ __launch_bounds__(kDnThreads, 2) void dense_gemm_kernel(DenseArgs a) 
   if (nk % NS) group(full * NS, true);
   __builtin_amdgcn_s_waitcnt(0);
 
-#pragma unroll
+  // fully unrolled, so every accumulator index is a constant (registers,
+  // not scratch)
+#pragma clang loop unroll(full)
   for (int i = 0; i < C::TM; ++i)
-#pragma unroll
+#pragma clang loop unroll(full)
     for (int j = 0; j < C::TN; ++j) {
-      const int nb = n0 + wn * (kDnBN / C::WN) + j * 32;  // first column of the MFMA tile
+      const int nb = n0 + wn * (BN / C::WN) + j * 32;  // first column of the MFMA tile
       const int n = nb + r32;
       const bool glu = nb >= a.n_f32 + a.n_bf16;          // the same for the whole tile
-#pragma unroll
+#pragma clang loop unroll(full)
       for (int e = 0; e < 16; ++e) {
         const int m = m0 + wm * (BM / C::WM) + i * 32 + 8 * (e / 4) + 4 * hh + (e & 3);
         const float v = acc[i][j][e];
@@ -272,7 +274,14 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
 DensePlan dense_plan(int M, int N, int K) {
   DensePlan p;
   p.bm = M <= 32 ? 32 : M <= 64 ? 64 : 128;
-  const int n_rt = (M + p.bm - 1) / p.bm, n_ct = (N + kDnBN - 1) / kDnBN;
+  p.bn = 128;
+#ifndef LMOE_DENSE_BIG
+#define LMOE_DENSE_BIG 1
+#endif
+  // enough rows for several 256-row tiles: 256 x 256 tiles of eight waves,
+  // 128 x 64 each (0.75 KB of operand reads per MFMA, against 1 KB at 64 x 64)
+  if (LMOE_DENSE_BIG && M >= 512 && N >= 1024) p.bm = p.bn = 256;
+  const int n_rt = (M + p.bm - 1) / p.bm, n_ct = (N + p.bn - 1) / p.bn;
   const int tiles = n_rt * n_ct;
   const int nkc = K / kDnBK;
   // Fewer tiles than resident workgroups (two per CU): split K. The split
@@ -305,18 +314,20 @@ static hipError_t launch_gemm_grid(const DenseArgs& a, int bm, int ky, hipStream
   const int n_tiles = a.n_rt * a.n_ct;
   const dim3 grid((unsigned)(8 * ((n_tiles + 7) / 8)), (unsigned)ky);
   if (bm == 32)
-    hipLaunchKernelGGL((dense_gemm_kernel<32, 3>), grid, dim3(kDnThreads), 0, s, a);
+    hipLaunchKernelGGL((dense_gemm_kernel<32, 128, 4, 3>), grid, dim3(256), 0, s, a);
   else if (bm == 64)
-    hipLaunchKernelGGL((dense_gemm_kernel<64, 3>), grid, dim3(kDnThreads), 0, s, a);
+    hipLaunchKernelGGL((dense_gemm_kernel<64, 128, 4, 3>), grid, dim3(256), 0, s, a);
+  else if (bm == 128)
+    hipLaunchKernelGGL((dense_gemm_kernel<128, 128, 4, 2>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((dense_gemm_kernel<128, 2>), grid, dim3(kDnThreads), 0, s, a);
+    hipLaunchKernelGGL((dense_gemm_kernel<256, 256, 8, 2>), grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_dense(DenseArgs a, const DensePlan& p, float* part, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   a.n_rt = (a.M + p.bm - 1) / p.bm;
-  a.n_ct = (a.N + kDnBN - 1) / kDnBN;
+  a.n_ct = (a.N + p.bn - 1) / p.bn;
   a.group_rows = 4;
   a.k_per = p.k_per;
   a.ks1 = p.ksplit;  // no second product
@@ -333,9 +344,10 @@ hipError_t launch_dense(DenseArgs a, const DensePlan& p, float* part, hipStream_
 hipError_t launch_dense_pair(DenseArgs a, const DensePlan& p1, const DensePlan& p2, float* part,
                              hipStream_t s) {
   if (a.M == 0) return hipSuccess;
-  if (p1.bm != p2.bm || p1.ksplit < 2 || p2.ksplit < 2) return hipErrorInvalidValue;
+  if (p1.bm != p2.bm || p1.bn != p2.bn || p1.ksplit < 2 || p2.ksplit < 2)
+    return hipErrorInvalidValue;
   a.n_rt = (a.M + p1.bm - 1) / p1.bm;
-  a.n_ct = (a.N + kDnBN - 1) / kDnBN;
+  a.n_ct = (a.N + p1.bn - 1) / p1.bn;
   a.group_rows = 4;
   a.k_per = p1.k_per;
   a.k_per2 = p2.k_per;

@@ -233,7 +233,7 @@ struct DenseArgs {
   float* part2; // the second product's [ksplit2][M][N]
 };
 struct DensePlan {
-  int bm;              // rows per workgroup tile (32, 64, 128)
+  int bm, bn;          // workgroup tile: 32, 64, 128 x 128 rows, or 256 x 256
   int ksplit, k_per;   // K splits and K per split
   size_t part_floats;  // workspace for the partial tiles
 };

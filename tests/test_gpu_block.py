@@ -216,7 +216,7 @@ def test_moe_tail_prefill_sampled(lm, dev):
     run_tail(lm, dev, w, gen_block(w), np.random.default_rng(9), rows)
 
 
-@pytest.mark.parametrize("T", [65, 300])
+@pytest.mark.parametrize("T", [65, 300, 600])
 def test_input_and_tail_k3_ragged_tiles(lm, dev, T):
     """Token counts that take 64- and 128-row tiles with K splits and a
     ragged last row tile."""
