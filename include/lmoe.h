@@ -308,8 +308,8 @@ typedef struct lmoe_packed_weights {
  * MFMA over expert groups of up to 128 routes. Every token count runs the
  * grouped path (routing kernels, grouped GEMMs, combine). exec as in
  * lmoe_forward_ex (NULL: every stage on `stream`). The workspace is the one
- * lmoe_workspace_bytes gives. T * L and T * k * I must stay below 2^32
- * (LMOE_ERR_SHAPE otherwise; 131072 tokens at the Kimi-K3 widths).
+ * lmoe_workspace_bytes gives. T * L and T * k * I must stay below 2^31
+ * (LMOE_ERR_SHAPE otherwise; 65536 tokens at the Kimi-K3 widths).
  * Errors: as lmoe_forward_ex. */
 int lmoe_forward_packed(const lmoe_dims* dims, const uint16_t* x, const lmoe_packed_weights* w,
                         int logits_given, const lmoe_routing* r, uint16_t* out, void* ws,

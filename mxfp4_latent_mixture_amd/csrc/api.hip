@@ -346,9 +346,9 @@ static int forward_impl(const lmoe_dims* dims, const uint16_t* x, const lmoe_wei
                         w.up_s, w.down_q, w.down_s, w.sh_gate, w.sh_up, w.sh_down};
   for (const void* q : ptrs)
     if (check_opt_ptr(q)) return LMOE_ERR_ALIGN;
-  // the packed GEMMs address activation rows with 32-bit element offsets
-  if (pk && ((int64_t)dims->T * dims->L >= (int64_t(1) << 32) ||
-             (int64_t)dims->T * dims->k * dims->I >= (int64_t(1) << 32)))
+  // the packed GEMMs address activation rows with 32-bit byte offsets
+  if (pk && ((int64_t)dims->T * dims->L >= (int64_t(1) << 31) ||
+             (int64_t)dims->T * dims->k * dims->I >= (int64_t(1) << 31)))
     return LMOE_ERR_SHAPE;
   // quantised activations: tile-packed experts only, K multiples of 128
   const int act = (mode == SideMode::kCaller && exec) ? exec->act_format : LMOE_ACT_BF16;

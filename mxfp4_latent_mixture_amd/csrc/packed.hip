@@ -229,13 +229,19 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <bool GLU, int MT>
+// KA: K is a multiple of the 128-value chunk, so no copy needs clamping and
+// each copy's row offset is fixed: computed once, a chunk only adds a
+// uniform base (the compiler then issues the copies with a scalar base and
+// a 32-bit offset, no per-chunk address arithmetic).
+template <bool GLU, int MT, bool KA>
 __device__ __forceinline__ void pk_body(const PkArgs& a, int e, int p0, int cnt, int nt,
                                         PkChunk<kPkRows>& sx0, PkChunk<kPkRows>& sx1,
                                         PkChunk<kPkRows>& sx2, const uint32_t* s_arow) {
   auto slot = [&](int r) -> PkChunk<kPkRows>& { return r == 0 ? sx0 : r == 1 ? sx1 : sx2; };
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // the wave index in a scalar register: the copies' LDS addresses are then
+  // scalar too
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r32 = lane & 31, hh = lane >> 5;
   // this wave's weight tiles (clamped: tiles past the matrix read the last
   // one, their columns are never stored)
@@ -264,21 +270,40 @@ __device__ __forceinline__ void pk_body(const PkArgs& a, int e, int p0, int cnt,
   // wave issues the same number, so the waits below count the same loads in
   // every wave); lane l moves the 16-byte segment at physical slot l % 16 of
   // row l / 16, which holds logical segment (l % 16) ^ (row % 16)
+  // KA: byte offset of each copy's 16-byte segment in chunk 0
+  uint32_t xoff[KA ? kCopies : 1];
+  if constexpr (KA) {
+    __syncthreads();  // s_arow
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) {
+      const int row = wave * kCopies * 4 + i * 4 + (lane >> 4);
+      const int seg = (lane & 15) ^ (row & 15);
+      xoff[i] = (s_arow[row] + seg * 8) * 2;  // < 2^32: checked on the host
+    }
+  }
   auto copy_x = [&](int c, int buf) {
     const int cc = min(c, a.K128 - 1);
 #pragma unroll
     for (int i = 0; i < kCopies; ++i) {
       const int row0 = wave * kCopies * 4 + i * 4;
-      const int row = row0 + (lane >> 4);
-      const int seg = (lane & 15) ^ (row & 15);
-      const int k = min(cc * kPkKc + seg * 8, a.K - 8);
+      const void* src;
+      if constexpr (KA) {
+        src = reinterpret_cast<const uint8_t*>(a.act) + (size_t)cc * kPkKc * 2 + xoff[i];
+      } else {
+        const int row = row0 + (lane >> 4);
+        const int seg = (lane & 15) ^ (row & 15);
+        const int k = min(cc * kPkKc + seg * 8, a.K - 8);
+        src = a.act + s_arow[row] + k;
+      }
       __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(a.act + s_arow[row] + k),
-          (__attribute__((address_space(3))) void*)(&slot(buf)[row0][0]), 16, 0, 0);
+          src, (__attribute__((address_space(3))) void*)(&slot(buf)[row0][0]), 16, 0, 0);
     }
   };
+  // a chunk's weight codes and the exponent word that covers it: the dword
+  // of its window (four chunks), bytes 2 (c % 2) + j
   struct Bq {
     u32x4_t q[kPkNB][2];
+    uint32_t ex[kPkNB];
   };
   auto load_b = [&](int c, Bq& b) {
     const int cc = min(c, a.K128 - 1);
@@ -286,23 +311,19 @@ __device__ __forceinline__ void pk_body(const PkArgs& a, int e, int p0, int cnt,
     for (int t = 0; t < kPkNB; ++t)
 #pragma unroll
       for (int j = 0; j < 2; ++j) b.q[t][j] = load_w<MT>(qb[t] + (int64_t)cc * 2048 + j * 1024);
-  };
-  // the exponents of chunk c: the dword of its window (four chunks) that
-  // holds them, bytes 2 (c % 2) + j
-  auto load_ex = [&](int c, uint32_t (&dst)[kPkNB]) {
-    const int cc = min(c, a.K128 - 1);
 #pragma unroll
     for (int t = 0; t < kPkNB; ++t)
-      dst[t] = *reinterpret_cast<const uint32_t*>(sb[t] + (cc / 4) * 512 + 4 * ((cc >> 1) & 1));
+      b.ex[t] =
+          *reinterpret_cast<const uint32_t*>(sb[t] + (cc / 4) * 512 + 4 * ((cc >> 1) & 1));
   };
-  auto compute = [&](int c, int buf, const Bq& b, const uint32_t (&ex)[kPkNB]) {
+  auto compute = [&](int c, int buf, const Bq& b) {
     // blocks past K are packed as zero codes with exponent 127: zeros
     float scale[kPkNB][2];
 #pragma unroll
     for (int t = 0; t < kPkNB; ++t)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        scale[t][j] = e8m0_to_f32((ex[t] >> (8 * (2 * (c & 1) + j))) & 0xffu);
+        scale[t][j] = e8m0_to_f32((b.ex[t] >> (8 * (2 * (c & 1) + j))) & 0xffu);
     // step st = 4 j + m of the chunk; the operands of step st + 1 (LDS
     // reads and dequantisation) are prepared while step st multiplies
     bf16x8_t av[2][MT], bv[2][kPkNB];
@@ -345,25 +366,22 @@ __device__ __forceinline__ void pk_body(const PkArgs& a, int e, int p0, int cnt,
     }
   };
 
-  // Activations (in a ring of three LDS buffers) and weights (in a ring of
-  // three register buffers) stay two chunks ahead, the exponents one. In
-  // chunk c the loads are issued in the order exponents (c + 1), activations
-  // (c + 2), weights (c + 2); so at the top of chunk c + 1, waiting until at
-  // most the loads of chunk c + 2 are outstanding (vector memory
-  // loads complete in issue order) leaves everything chunk c + 1 needs
-  // landed while the next chunk's loads stay in flight across the barrier.
+  // Activations (in a ring of three LDS buffers) and weights with their
+  // exponents (in a ring of three register buffers) stay two chunks ahead:
+  // in chunk c the loads of chunk c + 2 are issued, so at the top of chunk
+  // c + 1, waiting until at most those are outstanding (vector memory loads
+  // complete in issue order) leaves everything chunk c + 1 needs landed
+  // while the next chunk's loads stay in flight across the barrier.
   // Groups of three chunks are unrolled so ring slots are fixed registers and
   // buffers; the first group runs before the loop (both edges into the loop
   // then carry the same loads in flight, which keeps the compiler's waits
   // exact) and a last, partial group after it.
   constexpr int U = 3;
-  constexpr int kAhead = kCopies + 2 * kPkNB;        // loads of chunk c + 2
+  constexpr int kAhead = kCopies + 3 * kPkNB;        // loads of chunk c + 2
   constexpr int kWaitAhead = 0x0F70 | kAhead;        // vmcnt(kAhead)
   static_assert(kAhead < 16, "vmcnt field");
   __syncthreads();  // s_arow
   Bq bq[U];
-  uint32_t ex[kPkNB], ex_next[kPkNB];
-  load_ex(0, ex_next);
   copy_x(0, 0);
   load_b(0, bq[0]);
   copy_x(1, 1);
@@ -374,13 +392,10 @@ __device__ __forceinline__ void pk_body(const PkArgs& a, int e, int p0, int cnt,
       const int c = cb + r;
       __builtin_amdgcn_s_waitcnt(kWaitAhead);
       __builtin_amdgcn_s_barrier();
-#pragma unroll
-      for (int t = 0; t < kPkNB; ++t) ex[t] = ex_next[t];
-      load_ex(c + 1, ex_next);
       copy_x(c + 2, (r + 2) % U);
       load_b(c + 2, bq[(r + 2) % U]);
       __builtin_amdgcn_sched_barrier(0);
-      if (!last || c < a.K128) compute(c, r, bq[r], ex);
+      if (!last || c < a.K128) compute(c, r, bq[r]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -416,7 +431,7 @@ __device__ __forceinline__ void pk_body(const PkArgs& a, int e, int p0, int cnt,
     }
 }
 
-template <bool GLU>
+template <bool GLU, bool KA>
 __global__ __launch_bounds__(kPkThreads, 8 / kPkWaves) void gemm_packed_kernel(PkArgs a) {
   __shared__ __attribute__((aligned(16))) PkChunk<kPkRows> sx0, sx1, sx2;
   __shared__ uint32_t s_arow[kPkRows];  // element offset of each row in act
@@ -438,9 +453,9 @@ __global__ __launch_bounds__(kPkThreads, 8 / kPkWaves) void gemm_packed_kernel(P
     s_arow[r] = (uint32_t)(row * a.act_stride);  // < 2^32: checked on the host
   }
   switch ((cnt + 31) / 32) {
-    case 1: pk_body<GLU, 1>(a, e, p0, cnt, nt, sx0, sx1, sx2, s_arow); break;
-    case 2: pk_body<GLU, 2>(a, e, p0, cnt, nt, sx0, sx1, sx2, s_arow); break;
-    default: pk_body<GLU, 3>(a, e, p0, cnt, nt, sx0, sx1, sx2, s_arow); break;
+    case 1: pk_body<GLU, 1, KA>(a, e, p0, cnt, nt, sx0, sx1, sx2, s_arow); break;
+    case 2: pk_body<GLU, 2, KA>(a, e, p0, cnt, nt, sx0, sx1, sx2, s_arow); break;
+    default: pk_body<GLU, 3, KA>(a, e, p0, cnt, nt, sx0, sx1, sx2, s_arow); break;
   }
 }
 
@@ -806,11 +821,18 @@ hipError_t launch_routed_packed(const Plan& p, const uint16_t* x, const PackedWe
   hipError_t err;
   auto launch = [&](bool glu, const PkArgs& a) {
     const dim3 grid((unsigned)(rounds * 8 * a.n_tiles_n));
-    if (!q && glu)
-      hipLaunchKernelGGL(gemm_packed_kernel<true>, grid, dim3(kPkThreads), 0, s, a);
-    else if (!q)
-      hipLaunchKernelGGL(gemm_packed_kernel<false>, grid, dim3(kPkThreads), 0, s, a);
-    else if (glu && fp8)
+    const bool ka = a.K % kPkKc == 0;
+    if (!q && glu) {
+      if (ka)
+        hipLaunchKernelGGL((gemm_packed_kernel<true, true>), grid, dim3(kPkThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((gemm_packed_kernel<true, false>), grid, dim3(kPkThreads), 0, s, a);
+    } else if (!q) {
+      if (ka)
+        hipLaunchKernelGGL((gemm_packed_kernel<false, true>), grid, dim3(kPkThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((gemm_packed_kernel<false, false>), grid, dim3(kPkThreads), 0, s, a);
+    } else if (glu && fp8)
       hipLaunchKernelGGL((gemm_packed_q_kernel<true, true>), grid, dim3(kPkThreads), 0, s, a);
     else if (glu)
       hipLaunchKernelGGL((gemm_packed_q_kernel<true, false>), grid, dim3(kPkThreads), 0, s, a);

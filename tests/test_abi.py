@@ -393,3 +393,13 @@ def test_block_calls_reject_bad_arguments_on_the_host(lm):
     d0 = lm.lmoe_block_dims(0, *K3_BLOCK[1:])
     assert bf(ctypes.byref(d0), None, None, ctypes.byref(bw), ctypes.byref(w), None, None, None,
               0, None) == lm.LMOE_OK
+
+
+def test_packed_forward_rejects_offsets_beyond_32_bits(lm):
+    """The packed GEMMs address activation rows with 32-bit byte offsets:
+    T * k * I (and T * L) must stay below 2^31."""
+    pw = lm.lmoe_packed_weights(*[0x10000000 + 0x100000 * i for i in range(8)])
+    for T, want in ((65536, lm.LMOE_ERR_SHAPE), (65535, lm.LMOE_ERR_WORKSPACE)):
+        d = lm.lmoe_dims(T, 3584, 896, 16, 2048, 2, 2048)
+        assert lm._lib.lmoe_forward_packed(ctypes.byref(d), 0x20000000, ctypes.byref(pw), 0, None,
+                                           0x30000000, 0x40000000, 1024, None, None) == want, T
