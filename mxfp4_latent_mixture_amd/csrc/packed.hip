@@ -630,7 +630,9 @@ __device__ __forceinline__ void pkq_body(const PkArgs& a, int e, int p0, int cnt
     return r == 0 ? se0 : r == 1 ? se1 : r == 2 ? se2 : r == 3 ? se3 : se4;
   };
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // the wave index in a scalar register: the copies' LDS addresses are then
+  // scalar too
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r32 = lane & 31, hh = lane >> 5;
   int bt[kPkNB];
   const uint8_t* qb[kPkNB];
@@ -651,24 +653,31 @@ __device__ __forceinline__ void pkq_body(const PkArgs& a, int e, int p0, int cnt
       for (int i = 0; i < 16; ++i) acc[m][t][i] = 0.f;
 
   const int kb = a.K / 32;  // exponent bytes of an activation row
+  // byte offsets, in chunk 0, of this wave's copies (K is a multiple of the
+  // chunk, so a chunk only adds a uniform base): codes, then exponents
+  __syncthreads();  // s_row
+  uint32_t qoff[C::kCopies], eoff;
+#pragma unroll
+  for (int i = 0; i < C::kCopies; ++i) {
+    const int row = wave * 32 + i * C::kRowsPerCopy + lane / (C::kRowB / 16);
+    const int g = C::seg(row, lane % (C::kRowB / 16));
+    qoff[i] = s_row[row] * (uint32_t)a.aq_stride + g * 16;  // < 2^32: checked on the host
+  }
+  // lane l < 32: the exponents of row 32 w + l; lanes 32..63 repeat them
+  // into the wave's spare slots
+  eoff = s_row[wave * 32 + (lane & 31)] * (uint32_t)kb;
   // this wave's 32 row slots of chunk c into LDS buffer `buf`
   auto copy_a = [&](int c, int buf) {
     const int cc = min(c, a.K128 - 1);
 #pragma unroll
     for (int i = 0; i < C::kCopies; ++i) {
       const int row0 = wave * 32 + i * C::kRowsPerCopy;
-      const int row = row0 + lane / (C::kRowB / 16);
-      const int g = C::seg(row, lane % (C::kRowB / 16));
       __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(a.aq + (int64_t)s_row[row] * a.aq_stride +
-                                        cc * C::kRowB + g * 16),
+          a.aq + (size_t)cc * C::kRowB + qoff[i],
           (__attribute__((address_space(3))) void*)(&qslot(buf)[row0 * C::kRowB]), 16, 0, 0);
     }
-    // lane l < 32: the exponents of row 32 w + l; lanes 32..63 repeat them
-    // into the wave's spare slots
-    const int row = wave * 32 + (lane & 31);
     __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<const void*>(a.as + (int64_t)s_row[row] * kb + cc * 4),
+        a.as + (size_t)cc * 4 + eoff,
         (__attribute__((address_space(3))) void*)(&eslot(buf)[wave * 64]), 4, 0, 0);
   };
   // a chunk's weight codes and the exponent word that covers it
@@ -735,7 +744,6 @@ __device__ __forceinline__ void pkq_body(const PkArgs& a, int e, int p0, int cnt
   constexpr int kAhead = (U - 2) * kPerChunk;
   static_assert(kAhead < 64, "vmcnt field");
   constexpr int kWaitAhead = 0x0F70 | (kAhead & 15) | ((kAhead >> 4) << 14);
-  __syncthreads();  // s_row
   Bq bq[U];
 #pragma unroll
   for (int i = 0; i < U - 1; ++i) {
