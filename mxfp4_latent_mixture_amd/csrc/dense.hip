@@ -113,7 +113,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dense_gemm_kernel(DenseArgs a
   float* part = second ? a.part2 : a.part;
   const int kb = kz * k_per;                         // first K of this split
   const int nk = min(k_per, K - kb) / kDnBK;         // chunks
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index in a scalar register: the copies' LDS addresses are then
+  // scalar too
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r32 = lane & 31, hh = lane >> 5;
   const int wm = wave / C::WN, wn = wave % C::WN;
 
