@@ -32,25 +32,26 @@ constexpr int kDnBK = 64;    // K per chunk
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Epilogue of one output element (non-GLU columns) and of one GLU pair.
-// extra: the second product's bf16-rounded sum (launch_dense_pair), else 0.
+// extra: the second product's bf16-rounded sum (launch_dense_pair), else 0;
+// zo: the output offset of problem blockIdx.z (launch_dense_batched).
 __device__ __forceinline__ void dense_store(const DenseArgs& a, int m, int n, float v,
-                                            float extra = 0.f) {
+                                            float extra = 0.f, int64_t zo = 0) {
   if (n < a.n_f32) {
-    a.f32_out[(int64_t)m * a.ld_f32 + n] = v;
+    a.f32_out[zo + (int64_t)m * a.ld_f32 + n] = v;
   } else if (n < a.n_f32 + a.n_bf16) {
     const int c = n - a.n_f32;
     float r = v + extra;
     if (a.add0) r += bf16_bits_to_f32(a.add0[(int64_t)m * a.ld_add + c]);
     if (a.add1) r += bf16_bits_to_f32(a.add1[(int64_t)m * a.ld_add + c]);
-    a.bf_out[(int64_t)m * a.ld_bf + c] = f32_to_bf16_bits(r);
+    a.bf_out[zo + (int64_t)m * a.ld_bf + c] = f32_to_bf16_bits(r);
   }
 }
 // column n (in the GLU segment, a gate column: n - glu_base mod 32 < 16)
 __device__ __forceinline__ void dense_store_glu(const DenseArgs& a, int m, int n, float g,
-                                                float u) {
+                                                float u, int64_t zo = 0) {
   const int c = n - (a.n_f32 + a.n_bf16);
   const int col = (c >> 5) * 16 + (c & 15);
-  a.glu_out[(int64_t)m * a.ld_glu + col] = f32_to_bf16_bits(silu(g) * u);
+  a.glu_out[zo + (int64_t)m * a.ld_glu + col] = f32_to_bf16_bits(silu(g) * u);
 }
 
 // physical 16-byte segment of logical segment g (0..7) of staged row r
@@ -106,8 +107,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dense_gemm_kernel(DenseArgs a
   // the first product, or (blockIdx.y >= ks1) the second one of a pair
   const bool second = (int)blockIdx.y >= a.ks1;
   const int kz = second ? (int)blockIdx.y - a.ks1 : (int)blockIdx.y;
-  const uint16_t* A = second ? a.a2 : a.a;
-  const uint16_t* B = second ? a.b2 : a.b;
+  const int z = blockIdx.z;
+  const int64_t zo = z * a.out_zstride;  // output offset of problem z
+  const uint16_t* A = (second ? a.a2 : a.a) + z * a.a_zstride;
+  const uint16_t* B = (second ? a.b2 : a.b) + z * a.b_zstride;
+  const uint16_t* Bup = a.b_up ? a.b_up + z * a.b_zstride : nullptr;
   const int64_t lda = second ? a.lda2 : a.lda, ldb = second ? a.ldb2 : a.ldb;
   const int K = second ? a.K2 : a.K, k_per = second ? a.k_per2 : a.k_per;
   float* part = second ? a.part2 : a.part;
@@ -126,10 +130,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dense_gemm_kernel(DenseArgs a
     const int row = (wave * C::kCopies + i) * 8 + (lane >> 3);
     const int g = dn_seg(row, lane & 7);
     const uint16_t* p;
-    if (row < BM)
+    if (row < BM) {
       p = A + (int64_t)min(m0 + row, a.M - 1) * lda;
-    else
-      p = B + (int64_t)min(n0 + row - BM, a.N - 1) * ldb;
+    } else {
+      const int v = min(n0 + row - BM, a.N - 1);
+      if (Bup)  // 16 gate rows, then the 16 up rows of the same outputs
+        p = ((v & 16) ? Bup : B) + (int64_t)((v >> 5) * 16 + (v & 15)) * ldb;
+      else
+        p = B + (int64_t)v * ldb;
+    }
     src[i] = p + kb + g * 8;
   }
   auto copy = [&](int c, int buf) {
@@ -215,9 +224,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dense_gemm_kernel(DenseArgs a
           if (m < a.M && n < a.N) part[((int64_t)kz * a.M + m) * a.N + n] = v;
         } else if (glu) {
           const float u = __shfl_down(v, 16, 64);
-          if (r32 < 16 && m < a.M && n < a.N) dense_store_glu(a, m, n, v, u);
+          if (r32 < 16 && m < a.M && n < a.N) dense_store_glu(a, m, n, v, u, zo);
         } else if (m < a.M && n < a.N) {
-          dense_store(a, m, n, v);
+          dense_store(a, m, n, v, 0.f, zo);
         }
       }
     }
@@ -340,6 +349,30 @@ hipError_t launch_dense(DenseArgs a, const DensePlan& p, float* part, hipStream_
   const int64_t n = (int64_t)a.M * a.N;
   hipLaunchKernelGGL(dense_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
                      p.ksplit, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_batched(DenseArgs a, int nz, hipStream_t s) {
+  if (a.M == 0 || nz == 0) return hipSuccess;
+  DensePlan p = dense_plan(a.M, a.N, a.K);
+  p.ksplit = 1;  // no K split across problems
+  p.k_per = a.K;
+  a.n_rt = (a.M + p.bm - 1) / p.bm;
+  a.n_ct = (a.N + p.bn - 1) / p.bn;
+  a.group_rows = 4;
+  a.k_per = p.k_per;
+  a.ks1 = 1;
+  a.part = a.part2 = nullptr;
+  const int n_tiles = a.n_rt * a.n_ct;
+  const dim3 grid((unsigned)(8 * ((n_tiles + 7) / 8)), 1, (unsigned)nz);
+  if (p.bm == 32)
+    hipLaunchKernelGGL((dense_gemm_kernel<32, 128, 4, 3>), grid, dim3(256), 0, s, a);
+  else if (p.bm == 64)
+    hipLaunchKernelGGL((dense_gemm_kernel<64, 128, 4, 3>), grid, dim3(256), 0, s, a);
+  else if (p.bm == 128)
+    hipLaunchKernelGGL((dense_gemm_kernel<128, 128, 4, 2>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((dense_gemm_kernel<256, 256, 8, 2>), grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -736,6 +736,41 @@ hipError_t launch_shared(const Plan& p, const uint16_t* x, const lmoe_weights& w
                          const Workspace& ws, hipStream_t s, const hipEvent_t* ev) {
   const lmoe_dims& d = p.d;
   hipError_t err = hipSuccess;
+  if (d.S > 0 && d.T > 64 && d.L % 64 == 0 && d.Is % 64 == 0) {
+    // the block's dense GEMMs (dense.hip), one launch for all S experts:
+    // gate/up with the GLU over the separate gate and up matrices, then down
+    DenseArgs g = {};
+    g.a = x;
+    g.lda = d.L;
+    g.b = w.sh_gate;
+    g.b_up = w.sh_up;
+    g.ldb = d.L;
+    g.b_zstride = (int64_t)d.Is * d.L;
+    g.M = d.T;
+    g.N = 2 * d.Is;
+    g.K = d.L;
+    g.glu_out = ws.h_sh;
+    g.ld_glu = d.Is;
+    g.out_zstride = (int64_t)d.T * d.Is;
+    if ((err = launch_dense_batched(g, d.S, s)) != hipSuccess) return err;
+    if ((err = record_stage(ev, LMOE_STAGE_SHARED_GATEUP, s)) != hipSuccess) return err;
+    DenseArgs dn = {};
+    dn.a = ws.h_sh;
+    dn.lda = d.Is;
+    dn.a_zstride = (int64_t)d.T * d.Is;
+    dn.b = w.sh_down;
+    dn.ldb = d.Is;
+    dn.b_zstride = (int64_t)d.L * d.Is;
+    dn.M = d.T;
+    dn.N = d.L;
+    dn.K = d.Is;
+    dn.n_f32 = d.L;
+    dn.f32_out = ws.y_sh;
+    dn.ld_f32 = d.L;
+    dn.out_zstride = (int64_t)d.T * d.L;
+    if ((err = launch_dense_batched(dn, d.S, s)) != hipSuccess) return err;
+    return record_stage(ev, LMOE_STAGE_SHARED_DOWN, s);
+  }
   if (d.S > 0) {
     const bool sh_large = d.T > 64;
     const int rows = sh_large ? kDenseRows : kSmallRows;

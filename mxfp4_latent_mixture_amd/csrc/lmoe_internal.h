@@ -226,6 +226,13 @@ struct DenseArgs {
   const uint16_t* b2;
   int64_t ldb2;
   int K2;
+  // b_up: a GLU over two matrices: the B rows of each 32-column group are
+  // 16 rows of b (gate) then the same 16 rows of b_up (up), output columns
+  // numbering the 2N' virtual rows (N = 2N'). Null: B is b.
+  const uint16_t* b_up;
+  // independent problems along blockIdx.z (e.g. the shared experts): each
+  // pointer advances by its stride per z (without K splits)
+  int64_t a_zstride, b_zstride, out_zstride;
   // set by the launchers
   int n_rt, n_ct, group_rows, k_per, k_per2;
   int ks1;      // K splits of the first product (blockIdx.y >= ks1: the second)
@@ -239,6 +246,9 @@ struct DensePlan {
 };
 DensePlan dense_plan(int M, int N, int K);
 hipError_t launch_dense(DenseArgs a, const DensePlan& p, float* part, hipStream_t s);
+// nz independent problems of one shape in one launch (blockIdx.z), no K
+// split; pointers advance by the DenseArgs z strides.
+hipError_t launch_dense_batched(DenseArgs a, int nz, hipStream_t s);
 // Two products of the same [M][N] shape in one launch, both K-split
 // (p1.ksplit > 1 and p2.ksplit > 1, the same tile rows): out = epilogue of
 // (A B^T + bf16(A2 B2^T)). part: p1.part_floats + p2.part_floats floats.
