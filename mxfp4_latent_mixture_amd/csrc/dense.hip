@@ -258,18 +258,29 @@ __global__ __launch_bounds__(256) void dense_finish_kernel(DenseArgs a, int kspl
 }
 
 // Routed RMSNorm: n = bf16(r * (1 / sqrt(mean(r^2) + eps)) * gamma), one
-// workgroup per row, the squares summed in fp32.
+// workgroup per row, the squares summed in fp32. The row is read once, 16
+// bytes per thread and step (L % 8 == 0), and kept in registers for the
+// scaling pass (up to kRmsVec vectors per thread: L <= 16384).
+constexpr int kRmsVec = 8;
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ r,
                                                       const uint16_t* __restrict__ gamma,
                                                       int L, float eps,
                                                       uint16_t* __restrict__ out) {
   __shared__ float part[4];
   const int row = blockIdx.x;
-  const uint16_t* rr = r + (int64_t)row * L;
+  const u32x4_t* rr = reinterpret_cast<const u32x4_t*>(r + (int64_t)row * L);
+  const int nv = L / 8;
+  u32x4_t v[kRmsVec];
   float s = 0.f;
-  for (int i = threadIdx.x; i < L; i += 256) {
-    const float v = bf16_bits_to_f32(rr[i]);
-    s += v * v;
+#pragma unroll
+  for (int j = 0; j < kRmsVec; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    v[j] = i < nv ? rr[i] : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float lo = __uint_as_float(v[j][q] << 16), hi = __uint_as_float(v[j][q] & 0xFFFF0000u);
+      s += lo * lo + hi * hi;
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
@@ -277,9 +288,24 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
   __syncthreads();
   const float tot = (part[0] + part[1]) + (part[2] + part[3]);
   const float inv = 1.f / sqrtf(tot / (float)L + eps);
-  for (int i = threadIdx.x; i < L; i += 256)
-    out[(int64_t)row * L + i] =
-        f32_to_bf16_bits(bf16_bits_to_f32(rr[i]) * inv * bf16_bits_to_f32(gamma[i]));
+  const u32x4_t* gv = reinterpret_cast<const u32x4_t*>(gamma);
+  u32x4_t* ov = reinterpret_cast<u32x4_t*>(out + (int64_t)row * L);
+#pragma unroll
+  for (int j = 0; j < kRmsVec; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    if (i < nv) {
+      const u32x4_t g = gv[i];
+      u32x4_t o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = __uint_as_float(v[j][q] << 16) * inv * __uint_as_float(g[q] << 16);
+        const float hi =
+            __uint_as_float(v[j][q] & 0xFFFF0000u) * inv * __uint_as_float(g[q] & 0xFFFF0000u);
+        o[q] = (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+      }
+      ov[i] = o;
+    }
+  }
 }
 
 DensePlan dense_plan(int M, int N, int K) {
