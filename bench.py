@@ -467,7 +467,10 @@ def kernel_units(res, lm):
     sh_large = d.T > 64
     act = res.get("act", "bf16")
     if act == "bf16":
-        packed_kernel = {"gate_up": "gemm_packed_kernel<true>", "down": "gemm_packed_kernel<false>"}
+        # second template argument: K a multiple of the 128-value chunk
+        ka = lambda K: "true" if K % 128 == 0 else "false"
+        packed_kernel = {"gate_up": f"gemm_packed_kernel<true, {ka(d.L)}>",
+                         "down": f"gemm_packed_kernel<false, {ka(d.I)}>"}
     else:
         f8 = "true" if act == "e4m3" else "false"
         packed_kernel = {"gate_up": f"gemm_packed_q_kernel<true, {f8}>",
