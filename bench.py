@@ -155,6 +155,7 @@ KERNEL_SOURCES = {
     "pack_": "packed.hip",
     "quantize_act": "packed.hip",
     "read_stream": "experts.hip",
+    "mfma_rate": "measure.hip",
     "gemm_large": "experts.hip",
     "gemm_small": "experts.hip",
     "router_kernel": "route.hip",
@@ -488,8 +489,8 @@ def read_ceiling(lm, hip, dev, gib: int = 4, reps: int = 10):
     import torch
     stream = torch.cuda.current_stream().cuda_stream
     buf = torch.zeros(gib << 30, dtype=torch.uint8, device=dev)
-    best = None
-    for blocks in (1024, 2048, 4096, 8192):
+    best, by_grid = None, {}
+    for blocks in (256, 512, 1024, 2048, 4096, 8192):
         sink = torch.empty(blocks, dtype=torch.int32, device=dev)
         lm.debug_read_stream(buf, sink, blocks)
         times = []
@@ -501,11 +502,44 @@ def read_ceiling(lm, hip, dev, gib: int = 4, reps: int = 10):
             times.append(hip.elapsed_ms(e0, e1))
         ms = float(np.median(times))
         gbs = buf.numel() / (ms * 1e-3) / 1e9
+        by_grid[str(blocks)] = round(gbs, 1)
         if best is None or gbs > best["gb_s"]:
             best = {"gb_s": round(gbs, 1), "workgroups": blocks, "bytes": buf.numel(),
                     "kernel": "read_stream_kernel"}
+    best["gb_s_by_workgroups"] = by_grid
     del buf
     torch.cuda.empty_cache()
+    return best
+
+
+def mfma_ceiling(lm, hip, dev, reps: int = 5):
+    """The bf16 MFMA rate this GPU sustains under full load:
+    lmoe_debug_mfma_rate (every wave issuing independent 32x32x16 bf16 MFMAs
+    on random register operands), median of `reps` timed launches at each of
+    a few grid sizes; the best is the ceiling."""
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    iters = 4096
+    best, by_grid = None, {}
+    for blocks in (512, 1024, 2048):
+        sink = torch.empty(blocks, dtype=torch.int32, device=dev)
+        lm.debug_mfma_rate(iters, sink, blocks)
+        times = []
+        for _ in range(reps):
+            e0, e1 = hip.event(), hip.event()
+            hip.record(e0, stream)
+            lm.debug_mfma_rate(iters, sink, blocks)
+            hip.record(e1, stream)
+            times.append(hip.elapsed_ms(e0, e1))
+        ms = float(np.median(times))
+        flops = blocks * 4 * iters * 8 * 32768
+        tfl = flops / (ms * 1e-3) / 1e12
+        by_grid[str(blocks)] = round(tfl, 1)
+        if best is None or tfl > best["tflop_s"]:
+            best = {"tflop_s": round(tfl, 1), "workgroups": blocks, "flops": flops,
+                    "frac_of_peak": round(tfl / BF16_PEAK_TFLOPS, 4),
+                    "kernel": "mfma_rate_kernel"}
+    best["tflop_s_by_workgroups"] = by_grid
     return best
 
 
@@ -872,7 +906,7 @@ def main():
                     help="routed-expert layout of the multi-token cases (single tokens run "
                          "the one-kernel path on row-major experts)")
     ap.add_argument("--no-ceiling", action="store_true",
-                    help="skip the plain HBM read ceiling measurement")
+                    help="skip the plain HBM read and sustained MFMA ceiling measurements")
     ap.add_argument("--traffic-from", default="",
                     help="merge into profiles/pmc_traffic.json the FETCH_SIZE / WRITE_SIZE "
                          "counter runs in this directory (subfolders fetch/ and write/) and exit")
@@ -908,10 +942,13 @@ def main():
         log(f"calibration copy of {n} bytes done")
         del a, b
 
-    ceiling = None
+    ceiling = mceil = None
     if not args.no_ceiling:
         ceiling = read_ceiling(lm, hip, dev)
         log(f"plain HBM read ceiling: {ceiling['gb_s']} GB/s ({ceiling['workgroups']} workgroups)")
+        mceil = mfma_ceiling(lm, hip, dev)
+        log(f"sustained bf16 MFMA rate: {mceil['tflop_s']} TFLOP/s "
+            f"({mceil['workgroups']} workgroups)")
     dec = run_case(lm, hip, "decode", dev, args.steps, args.warmup, rotate=True,
                    traced_steps=min(args.steps, 50))
     d = dec["w"].dims
@@ -942,6 +979,7 @@ def main():
                          "frac_of_read_ceiling": round(value / ceiling["gb_s"], 4)}
                         if ceiling else {})},
         "hbm_read_ceiling": ceiling,
+        "mfma_ceiling": mceil,
         "algorithmic_bytes_per_step": round(tb),
         "warm_gb_s": round(tb / (dec["warm_ms"] * 1e-3) / 1e9, 2),
         "stage_us": stage_us(dec, lm),
@@ -963,6 +1001,11 @@ def main():
             "roofline": roofline_for(pf, "mfma", lm),
             "stage_us": stage_us(pf, lm),
         }
+        if mceil:
+            rf = result["prefill"]["roofline"]
+            rf["mfma_ceiling_tflop_s"] = mceil["tflop_s"]
+            rf["frac_of_mfma_ceiling"] = round(rf["achieved"] / mceil["tflop_s"], 4)
+            result["prefill"]["frac_of_mfma_ceiling"] = round(tfl / mceil["tflop_s"], 4)
     if args.extra and args.extra != "none":
         names = EXTRA if args.extra == "all" else tuple(args.extra.split(","))
         result["extra"] = {}

@@ -494,6 +494,18 @@ int lmoe_debug_quantize_act(const uint16_t* src, int32_t rows, int32_t K, int32_
 int lmoe_debug_read_stream(const void* p, size_t bytes, uint32_t* sink, int32_t blocks,
                            void* stream);
 
+/* Measurement hook: `blocks` workgroups of four waves each run `iters`
+ * rounds of eight independent 32x32x16 bf16 MFMAs (32768 flops each) on
+ * register operands and write one word per workgroup to sink (uint32
+ * [blocks] device). blocks * 4 * iters * 8 * 32768 flops over the launch's
+ * duration is the bf16 MFMA rate this GPU sustains under full load: the
+ * practical ceiling the prefill GEMMs are measured against next to the
+ * 2.5 PFLOP/s figure (dev48.org "Kimi K3 on AMD Instinct GPUs with
+ * TokenSpeed", section 4.4: at prefill sizes the layer is bound by the
+ * matrix cores). Errors: LMOE_ERR_NULL, _SHAPE (iters < 0, blocks outside
+ * 1..65536), _ALIGN, _HIP. */
+int lmoe_debug_mfma_rate(int32_t iters, uint32_t* sink, int32_t blocks, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* lmoe_status_string(int status);
 

@@ -51,7 +51,7 @@ COUNTER_BYTES = 256 << 10
 EXPORTS = ("lmoe_workspace_bytes", "lmoe_route", "lmoe_forward", "lmoe_forward_ex",
            "lmoe_forward_traced", "lmoe_wait_errors", "lmoe_forward_noalloc", "lmoe_stage_name", "lmoe_path_name",
            "lmoe_debug_dequant_mxfp4", "lmoe_status_string", "lmoe_packed_sizes_of",
-           "lmoe_pack_weights", "lmoe_forward_packed", "lmoe_debug_read_stream",
+           "lmoe_pack_weights", "lmoe_forward_packed", "lmoe_debug_read_stream", "lmoe_debug_mfma_rate",
            "lmoe_debug_quantize_act", "lmoe_block_workspace_bytes", "lmoe_moe_input",
            "lmoe_moe_tail", "lmoe_block_forward")
 # members of lmoe_packed_sizes / the packed routed-expert arrays
@@ -179,6 +179,8 @@ def _load() -> ctypes.CDLL:
     lib.lmoe_debug_quantize_act.restype = ctypes.c_int
     lib.lmoe_debug_read_stream.argtypes = [vp, sz, vp, i32, vp]
     lib.lmoe_debug_read_stream.restype = ctypes.c_int
+    lib.lmoe_debug_mfma_rate.argtypes = [i32, vp, i32, vp]
+    lib.lmoe_debug_mfma_rate.restype = ctypes.c_int
     lib.lmoe_debug_dequant_mxfp4.argtypes = [vp, vp, i32, i32, vp, vp]
     lib.lmoe_debug_dequant_mxfp4.restype = ctypes.c_int
     bdp = ctypes.POINTER(lmoe_block_dims)
@@ -379,6 +381,14 @@ def path_name(dims, logits_given: bool = False) -> str:
 
 def stage_name(i: int) -> str:
     return _lib.lmoe_stage_name(int(i)).decode()
+
+
+def debug_mfma_rate(iters: int, sink, blocks: int, stream=None) -> None:
+    """`blocks` workgroups of four waves each issue iters * 8 bf16 32x32x16
+    MFMAs on register operands (the sustained MFMA rate); one word per
+    workgroup lands in the int32 device tensor sink."""
+    code = _lib.lmoe_debug_mfma_rate(int(iters), _ptr(sink), int(blocks), _stream(stream))
+    _check("lmoe_debug_mfma_rate", code)
 
 
 def debug_read_stream(buf, sink, blocks: int, stream=None) -> None:

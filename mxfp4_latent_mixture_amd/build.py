@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "liblmoe.so")
-SOURCES = ["api.hip", "route.hip", "experts.hip", "decode.hip", "decode_multi.hip", "packed.hip", "dense.hip"]
+SOURCES = ["api.hip", "route.hip", "experts.hip", "decode.hip", "decode_multi.hip", "packed.hip", "dense.hip",
+           "measure.hip"]
 ARCH = "gfx950"
 
 

@@ -11,6 +11,9 @@
 
 namespace lmoe {
 
+// measure.hip
+hipError_t launch_mfma_rate(int iters, uint32_t* sink, int blocks, hipStream_t s);
+
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 static bool dims_ok(const lmoe_dims& d) {
@@ -590,6 +593,14 @@ extern "C" int lmoe_debug_read_stream(const void* p, size_t bytes, uint32_t* sin
   if (!aligned16(p) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return LMOE_ERR_ALIGN;
   if (bytes == 0) return LMOE_OK;
   hipError_t e = launch_read_stream(p, bytes, sink, blocks, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
+}
+
+extern "C" int lmoe_debug_mfma_rate(int32_t iters, uint32_t* sink, int32_t blocks, void* stream) {
+  if (!sink) return LMOE_ERR_NULL;
+  if (iters < 0 || blocks < 1 || blocks > 65536) return LMOE_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(sink) & 3u) return LMOE_ERR_ALIGN;
+  hipError_t e = launch_mfma_rate(iters, sink, blocks, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
 }
 

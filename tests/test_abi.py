@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
                             "lmoe_forward_ex", "lmoe_forward_traced", "lmoe_wait_errors",
                             "lmoe_forward_noalloc", "lmoe_packed_sizes_of",
                             "lmoe_pack_weights", "lmoe_forward_packed",
-                            "lmoe_debug_read_stream", "lmoe_debug_quantize_act",
+                            "lmoe_debug_read_stream", "lmoe_debug_mfma_rate", "lmoe_debug_quantize_act",
                             "lmoe_stage_name", "lmoe_path_name",
                             "lmoe_debug_dequant_mxfp4", "lmoe_status_string",
                             "lmoe_block_workspace_bytes", "lmoe_moe_input", "lmoe_moe_tail",
@@ -338,6 +338,15 @@ def test_read_stream_rejects_bad_arguments(lm):
     assert f(0x1008, 1024, 0x2000, 4, None) == lm.LMOE_ERR_ALIGN
     assert f(0x1000, 1024, 0x2002, 4, None) == lm.LMOE_ERR_ALIGN
     assert f(0x1000, 0, 0x2000, 4, None) == lm.LMOE_OK
+
+
+def test_mfma_rate_rejects_bad_arguments(lm):
+    f = lm._lib.lmoe_debug_mfma_rate
+    assert f(16, None, 4, None) == lm.LMOE_ERR_NULL
+    assert f(-1, 0x2000, 4, None) == lm.LMOE_ERR_SHAPE
+    assert f(16, 0x2000, 0, None) == lm.LMOE_ERR_SHAPE
+    assert f(16, 0x2000, 65537, None) == lm.LMOE_ERR_SHAPE
+    assert f(16, 0x2002, 4, None) == lm.LMOE_ERR_ALIGN
 
 
 def test_binding_rejects_host_tensors(lm):
