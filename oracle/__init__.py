@@ -3,9 +3,8 @@
 TEST INFRASTRUCTURE ONLY. This package is the plain, slow, float64 statement
 of what the layer computes. It is imported by the test suite, by the smoke
 check in __graft_entry__.py and by the bench's CPU-baseline leg, and by
-nothing else: the
-product path (the HIP library and its Python binding) never imports, links or
-calls it, and it shares no code with that path. Inputs come from the seeded
+nothing else: the product path (the HIP library and its Python binding)
+never imports, links or calls it, and it shares no code with that path. Inputs come from the seeded
 generators in the separate `workloads` package.
 """
 from .lmoe_oracle import (  # noqa: F401
