@@ -196,6 +196,11 @@ struct PkArgs {
   const uint8_t* aq;
   const uint8_t* as;
   int64_t aq_stride;
+  // quantised gate/up: h quantised in the epilogue, the down GEMM's input
+  // (codes at hq_out + row * hq_stride, exponents at hqs_out + row * N / 32)
+  uint8_t* hq_out;
+  uint8_t* hqs_out;
+  int64_t hq_stride;
 };
 
 // Weight tiles are read once. A workgroup of one 32-row tile (batched
@@ -728,8 +733,11 @@ __device__ __forceinline__ void pkq_body(const PkArgs& a, int e, int p0, int cnt
         const int sbv = (int)((b.ex[t] >> (8 * (2 * (c & 1) + s))) & 0xFFu);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          acc[mt][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              av[mt], bv, acc[mt][t], FP8 ? 0 : 4, 4, 0, sa[mt], 0, sbv);
+          acc[mt][t] =
+              GLU ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        bv, av[mt], acc[mt][t], 4, FP8 ? 0 : 4, 0, sbv, 0, sa[mt])
+                  : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        av[mt], bv, acc[mt][t], FP8 ? 0 : 4, 4, 0, sa[mt], 0, sbv);
       }
     }
   };
@@ -769,26 +777,98 @@ __device__ __forceinline__ void pkq_body(const PkArgs& a, int e, int p0, int cnt
   if (a.K128 % U) group(full * U, true);
   __builtin_amdgcn_s_waitcnt(0);
 
+  if constexpr (GLU) {
+    // h = bf16(silu(g) u), then quantised as the down GEMM's input with the
+    // activation quantiser's arithmetic (quantize_act_kernel), so h is never
+    // written in bf16. The MFMAs took the weight tile as operand A: slot i
+    // of lane l is weight row 8 (i / 4) + 4 (l / 32) + i % 4 of packed tile
+    // bt (rows 0..15 gates of intermediate columns 16 bt .. 16 bt + 15, rows
+    // 16..31 their ups) for route mt * 32 + l % 32; slots 0..3 pair with
+    // 8..11 and 4..7 with 12..15. The wave's two tiles (bt even) cover the 32
+    // columns of one MX block: lane l holds columns 4 (l / 32) + 0..3 and
+    // 8 + 4 (l / 32) + 0..3 of each tile, lane l ^ 32 the others, so the
+    // block's maximum takes one exchange.
+    constexpr int emax = FP8 ? 8 : 2;
+    const int blk = bt[0] >> 1;  // the wave's MX block of h columns
+    const bool live = bt[0] < a.N32 && 32 * blk < a.N;  // I is a multiple of 32
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = mt * 32 + r32;
+      float f[16];  // local column 16 t + 8 h + 4 hh + k of the block is f[8 t + 4 h + k]
 #pragma unroll
-    for (int t = 0; t < kPkNB; ++t) {
-      if (bt[t] >= a.N32) continue;
+      for (int t = 0; t < kPkNB; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = mt * 32 + 8 * (i / 4) + 4 * hh + (i & 3);
-        const float v = acc[mt][t][i];
-        if constexpr (GLU) {
-          const float u = __shfl_down(v, 16, kWave);
-          const int col = bt[t] * 16 + r32;
-          if (r32 < 16 && row < cnt && col < a.N)
-            a.h_out[(int64_t)(p0 + row) * a.out_stride + col] = f32_to_bf16_bits(silu(v) * u);
-        } else {
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float g = acc[mt][t][4 * h + k], u = acc[mt][t][8 + 4 * h + k];
+            f[8 * t + 4 * h + k] = bf16_bits_to_f32(f32_to_bf16_bits(silu(g) * u));
+          }
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+      const int X = amax > 0.f ? min(max(ilog2f(amax) - emax, -127), 127) : 0;
+      const int64_t r = (int64_t)(p0 + row);
+      const bool ok = live && row < cnt;
+      if constexpr (FP8) {
+        // byte c of the block's 32 is column c: this lane's four runs of four
+        // at bytes 16 t + 8 h + 4 hh; lane hh = 0 gathers its partner's and
+        // writes the 32 bytes
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          w[q] = 0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) w[q] |= e4m3_code(ldexpf(f[4 * q + k], -X)) << (8 * k);
+        }
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = __shfl_xor(w[q], 32, kWave);
+        if (hh == 0 && ok) {
+          u32x4_t* d = reinterpret_cast<u32x4_t*>(a.hq_out + r * a.hq_stride + 32 * blk);
+          d[0] = u32x4_t{w[0], o[0], w[1], o[1]};
+          d[1] = u32x4_t{w[2], o[2], w[3], o[3]};
+        }
+      } else {
+        // element c in nibble c % 2 of byte c / 2: this lane's four runs of
+        // four values are two bytes each, at bytes 8 t + 4 h + 2 hh
+        uint32_t w[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          uint32_t lo = 0, hi = 0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            lo |= e2m1_code(ldexpf(f[8 * q + k], -X)) << (4 * k);
+            hi |= e2m1_code(ldexpf(f[8 * q + 4 + k], -X)) << (4 * k);
+          }
+          w[q] = lo | (hi << 16);  // runs (t = q, h = 0) and (t = q, h = 1)
+        }
+        uint32_t o[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) o[q] = __shfl_xor(w[q], 32, kWave);
+        if (hh == 0 && ok)
+          *reinterpret_cast<u32x4_t*>(a.hq_out + r * a.hq_stride + 16 * blk) =
+              u32x4_t{(w[0] & 0xFFFFu) | (o[0] << 16), (w[0] >> 16) | (o[0] & 0xFFFF0000u),
+                      (w[1] & 0xFFFFu) | (o[1] << 16), (w[1] >> 16) | (o[1] & 0xFFFF0000u)};
+      }
+      if (hh == 1 && ok) a.hqs_out[r * (a.N / 32) + blk] = (uint8_t)(X + 127);
+    }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < kPkNB; ++t) {
+        if (bt[t] >= a.N32) continue;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = mt * 32 + 8 * (i / 4) + 4 * hh + (i & 3);
           const int col = bt[t] * 32 + r32;
-          if (row < cnt && col < a.N) a.y_out[(int64_t)(p0 + row) * a.out_stride + col] = v;
+          if (row < cnt && col < a.N)
+            a.y_out[(int64_t)(p0 + row) * a.out_stride + col] = acc[mt][t][i];
         }
       }
-    }
+  }
 }
 
 template <bool GLU, bool FP8>
@@ -874,13 +954,15 @@ hipError_t launch_routed_packed(const Plan& p, const uint16_t* x, const PackedWe
     a.N = d.I;
     a.h_out = ws.h;
     a.out_stride = d.I;
+    a.hq_out = ws.hq;
+    a.hqs_out = ws.hq_s;
+    a.hq_stride = fp8 ? d.I : d.I / 2;
     a.n_tiles_n = (a.N32 + kPkWaves * kPkNB - 1) / (kPkWaves * kPkNB);
     if ((err = launch(true, a)) != hipSuccess) return err;
     if ((err = record_stage(ev, LMOE_STAGE_GATEUP, s)) != hipSuccess) return err;
   }
   {  // down
-    if (q && (err = launch_quantize_act(ws.h, p.R, d.I, fp8, ws.hq, ws.hq_s, s)) != hipSuccess)
-      return err;
+    // (the quantised gate/up kernel wrote h quantised already)
     PkArgs a = {};
     a.act = ws.h;
     a.act_stride = d.I;
