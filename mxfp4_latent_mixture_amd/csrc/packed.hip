@@ -355,7 +355,8 @@ __device__ __forceinline__ void pk_body(const PkArgs& a, int e, int p0, int cnt,
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int t = 0; t < kPkNB; ++t)
-          acc[mt][t] = mfma32(av[st & 1][mt], bv[st & 1][t], acc[mt][t]);
+          acc[mt][t] = GLU ? mfma32(bv[st & 1][t], av[st & 1][mt], acc[mt][t])
+                           : mfma32(av[st & 1][mt], bv[st & 1][t], acc[mt][t]);
       if (st < 7) prep(st + 1, av[(st + 1) & 1], bv[(st + 1) & 1]);
       // interleave: after each of the first MT MFMAs one operand read of the
       // next step, after each of the others a share of its conversions
@@ -410,30 +411,55 @@ __device__ __forceinline__ void pk_body(const PkArgs& a, int e, int p0, int cnt,
   if (a.K128 % U) group(full * U, true);
   __builtin_amdgcn_s_waitcnt(0);
 
-  // output slot i of lane l: row 8 (i / 4) + 4 (l / 32) + i % 4 of the MFMA
-  // tile, column l % 32
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  if constexpr (GLU) {
+    // The MFMAs took the weight tile as operand A and the routes as operand
+    // B: slot i of lane l is weight row 8 (i / 4) + 4 (l / 32) + i % 4 of
+    // packed tile bt (rows 0..15 the gates of intermediate columns
+    // 16 bt .. 16 bt + 15, rows 16..31 their ups) for route mt * 32 + l % 32.
+    // Slots 0..3 (gates of columns 4 (l / 32) + 0..3) pair with slots 8..11,
+    // slots 4..7 (columns 8 + 4 (l / 32) + 0..3) with 12..15: each lane
+    // finishes eight h values of its route in place and stores them as two
+    // runs of four.
 #pragma unroll
     for (int t = 0; t < kPkNB; ++t) {
       if (bt[t] >= a.N32) continue;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = mt * 32 + 8 * (i / 4) + 4 * hh + (i & 3);
-        const float v = acc[mt][t][i];
-        if constexpr (GLU) {
-          // column c < 16: gate of intermediate column 16 bt + c; up from
-          // lane + 16
-          const float u = __shfl_down(v, 16, kWave);
-          const int col = bt[t] * 16 + r32;
-          if (r32 < 16 && row < cnt && col < a.N)
-            a.h_out[(int64_t)(p0 + row) * a.out_stride + col] = f32_to_bf16_bits(silu(v) * u);
-        } else {
-          const int col = bt[t] * 32 + r32;
-          if (row < cnt && col < a.N) a.y_out[(int64_t)(p0 + row) * a.out_stride + col] = v;
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = mt * 32 + r32;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint32_t w[2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const float h0 = silu(acc[mt][t][4 * h + 2 * k]) * acc[mt][t][8 + 4 * h + 2 * k];
+            const float h1 =
+                silu(acc[mt][t][4 * h + 2 * k + 1]) * acc[mt][t][8 + 4 * h + 2 * k + 1];
+            w[k] = (uint32_t)f32_to_bf16_bits(h0) | ((uint32_t)f32_to_bf16_bits(h1) << 16);
+          }
+          const int col = bt[t] * 16 + 8 * h + 4 * hh;  // I is a multiple of 32
+          if (row < cnt && col < a.N)
+            *reinterpret_cast<u32x2_t*>(a.h_out + (int64_t)(p0 + row) * a.out_stride + col) =
+                u32x2_t{w[0], w[1]};
         }
       }
     }
+  } else {
+    // output slot i of lane l: row 8 (i / 4) + 4 (l / 32) + i % 4 of the MFMA
+    // tile, column l % 32
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < kPkNB; ++t) {
+        if (bt[t] >= a.N32) continue;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = mt * 32 + 8 * (i / 4) + 4 * hh + (i & 3);
+          const int col = bt[t] * 32 + r32;
+          if (row < cnt && col < a.N)
+            a.y_out[(int64_t)(p0 + row) * a.out_stride + col] = acc[mt][t][i];
+        }
+      }
+  }
 }
 
 template <bool GLU, bool KA>
