@@ -13,9 +13,9 @@
 // and E8M0 bytes, reordered (layout in include/lmoe.h, lmoe_pack_weights).
 //
 // Gate and up are interleaved in one packed matrix GU of 2I rows: packed
-// tile n holds gate rows 16n .. 16n+15 then up rows 16n .. 16n+15, so an
-// MFMA output tile carries g in columns 0..15 and u in columns 16..31 for the
-// same 16 intermediate columns, and the GLU needs one lane exchange.
+// tile n holds gate rows 16n .. 16n+15 then up rows 16n .. 16n+15, so one
+// MFMA output tile carries g and u of the same 16 intermediate columns (with
+// the weights as operand A, in slots i and i + 8 of the same lane).
 //
 // Per expert e and route r of token t (dev48.org "Kimi K3 on AMD Instinct GPUs
 // with TokenSpeed", section 4): h_r = bf16(silu(x_t Gq_e^T) * (x_t Uq_e^T)),
@@ -168,11 +168,16 @@ hipError_t launch_pack(const lmoe_dims& d, const lmoe_weights& w, uint8_t* gu_q,
 // chunk's activation rows are copied into LDS by 16-byte global-to-LDS loads
 // (no registers), segments XOR-swizzled by row so the MFMA operand reads of
 // 16 rows hit distinct banks; the chunk's weights (two 1 KB loads per tile)
-// are loaded into registers one chunk ahead; two LDS buffers and one barrier
-// per chunk. Lane (r, h) = (l % 32, l / 32) takes, in chunk c, MX blocks
-// 4c + 2h and 4c + 2h + 1 (the packed order), so the A operand of MFMA step
-// (j, m) is activation segment 8h + 4j + m of the chunk row. Exponents come
-// one 8-byte load per tile per four chunks.
+// are loaded into registers two chunks ahead; three LDS buffers and one
+// barrier per chunk. Lane (r, h) = (l % 32, l / 32) takes, in chunk c, MX
+// blocks 4c + 2h and 4c + 2h + 1 (the packed order), so the activation
+// operand of MFMA step (j, m) is segment 8h + 4j + m of the chunk row. The
+// operand layouts of A and B are alike (lane l: row or column l % 32, K
+// 8 (l / 32) .. + 7 of the step), so either side can take the weights: the
+// down GEMM puts the routes in A (each lane stores two whole 128-byte lines
+// of fp32 y per instruction), the gate/up GEMM the weights in A (each lane
+// holds one route's gates and ups). Exponents come one 4-byte load per tile
+// per chunk.
 // ---------------------------------------------------------------------------
 struct PkArgs {
   const uint16_t* act;  // bf16 rows; row of sorted position p: gather ? gather[p] / div : p
