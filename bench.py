@@ -474,8 +474,14 @@ def kernel_units(res, lm):
                          "down": f"gemm_packed_kernel<false, {ka(d.I)}>"}
     else:
         f8 = "true" if act == "e4m3" else "false"
-        packed_kernel = {"gate_up": f"gemm_packed_q_kernel<true, {f8}>",
-                         "down": f"gemm_packed_q_kernel<false, {f8}>"}
+        # MXFP4 activations with K a multiple of 256 up to 4096: the
+        # pair-copy kernel
+        a4 = lambda K: act == "e2m1" and K % 256 == 0 and K <= 4096
+        packed_kernel = {
+            "gate_up": ("gemm_packed_a4_kernel<true>" if a4(d.L)
+                        else f"gemm_packed_q_kernel<true, {f8}>"),
+            "down": ("gemm_packed_a4_kernel<false>" if a4(d.I)
+                     else f"gemm_packed_q_kernel<false, {f8}>")}
     return [((packed_kernel.get(s) if res.get("packed") else None)
              or stage_kernel(s, large, sh_large, d, logits_given), sb[s], sf[s],
              res["stage_ms"][s] * 1e-3)

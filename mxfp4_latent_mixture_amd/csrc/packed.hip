@@ -650,6 +650,107 @@ template <bool FP8>
 using QChunk = uint8_t[128 * QCfg<FP8>::kRowB];
 using QExp = uint32_t[256];  // wave w's 32 rows at 64 w .. 64 w + 31
 
+// The quantised GEMMs' epilogue: GLU writes h quantised for the down GEMM,
+// plain writes the fp32 route partials.
+template <bool GLU, bool FP8, int MT>
+__device__ __forceinline__ void pkq_store(const PkArgs& a, const f32x16_t (&acc)[MT][kPkNB],
+                                          const int (&bt)[kPkNB], int p0, int cnt) {
+  const int lane = threadIdx.x & 63;
+  const int r32 = lane & 31, hh = lane >> 5;
+  if constexpr (GLU) {
+    // h = bf16(silu(g) u), then quantised as the down GEMM's input with the
+    // activation quantiser's arithmetic (quantize_act_kernel), so h is never
+    // written in bf16. The MFMAs took the weight tile as operand A: slot i
+    // of lane l is weight row 8 (i / 4) + 4 (l / 32) + i % 4 of packed tile
+    // bt (rows 0..15 gates of intermediate columns 16 bt .. 16 bt + 15, rows
+    // 16..31 their ups) for route mt * 32 + l % 32; slots 0..3 pair with
+    // 8..11 and 4..7 with 12..15. The wave's two tiles (bt even) cover the 32
+    // columns of one MX block: lane l holds columns 4 (l / 32) + 0..3 and
+    // 8 + 4 (l / 32) + 0..3 of each tile, lane l ^ 32 the others, so the
+    // block's maximum takes one exchange.
+    constexpr int emax = FP8 ? 8 : 2;
+    const int blk = bt[0] >> 1;  // the wave's MX block of h columns
+    const bool live = bt[0] < a.N32 && 32 * blk < a.N;  // I is a multiple of 32
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = mt * 32 + r32;
+      float f[16];  // local column 16 t + 8 h + 4 hh + k of the block is f[8 t + 4 h + k]
+#pragma unroll
+      for (int t = 0; t < kPkNB; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float g = acc[mt][t][4 * h + k], u = acc[mt][t][8 + 4 * h + k];
+            f[8 * t + 4 * h + k] = bf16_bits_to_f32(f32_to_bf16_bits(silu(g) * u));
+          }
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+      const int X = amax > 0.f ? min(max(ilog2f(amax) - emax, -127), 127) : 0;
+      const int64_t r = (int64_t)(p0 + row);
+      const bool ok = live && row < cnt;
+      if constexpr (FP8) {
+        // byte c of the block's 32 is column c: this lane's four runs of four
+        // at bytes 16 t + 8 h + 4 hh; lane hh = 0 gathers its partner's and
+        // writes the 32 bytes
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          w[q] = 0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) w[q] |= e4m3_code(ldexpf(f[4 * q + k], -X)) << (8 * k);
+        }
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = __shfl_xor(w[q], 32, kWave);
+        if (hh == 0 && ok) {
+          u32x4_t* d = reinterpret_cast<u32x4_t*>(a.hq_out + r * a.hq_stride + 32 * blk);
+          d[0] = u32x4_t{w[0], o[0], w[1], o[1]};
+          d[1] = u32x4_t{w[2], o[2], w[3], o[3]};
+        }
+      } else {
+        // element c in nibble c % 2 of byte c / 2: this lane's four runs of
+        // four values are two bytes each, at bytes 8 t + 4 h + 2 hh
+        uint32_t w[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          uint32_t lo = 0, hi = 0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            lo |= e2m1_code(ldexpf(f[8 * q + k], -X)) << (4 * k);
+            hi |= e2m1_code(ldexpf(f[8 * q + 4 + k], -X)) << (4 * k);
+          }
+          w[q] = lo | (hi << 16);  // runs (t = q, h = 0) and (t = q, h = 1)
+        }
+        uint32_t o[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) o[q] = __shfl_xor(w[q], 32, kWave);
+        if (hh == 0 && ok)
+          *reinterpret_cast<u32x4_t*>(a.hq_out + r * a.hq_stride + 16 * blk) =
+              u32x4_t{(w[0] & 0xFFFFu) | (o[0] << 16), (w[0] >> 16) | (o[0] & 0xFFFF0000u),
+                      (w[1] & 0xFFFFu) | (o[1] << 16), (w[1] >> 16) | (o[1] & 0xFFFF0000u)};
+      }
+      if (hh == 1 && ok) a.hqs_out[r * (a.N / 32) + blk] = (uint8_t)(X + 127);
+    }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < kPkNB; ++t) {
+        if (bt[t] >= a.N32) continue;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = mt * 32 + 8 * (i / 4) + 4 * hh + (i & 3);
+          const int col = bt[t] * 32 + r32;
+          if (row < cnt && col < a.N)
+            a.y_out[(int64_t)(p0 + row) * a.out_stride + col] = acc[mt][t][i];
+        }
+      }
+  }
+}
+
 template <bool GLU, bool FP8, int MT>
 __device__ __forceinline__ void pkq_body(const PkArgs& a, int e, int p0, int cnt, int nt,
                                          QChunk<FP8>& sq0, QChunk<FP8>& sq1, QChunk<FP8>& sq2,
@@ -808,98 +909,7 @@ __device__ __forceinline__ void pkq_body(const PkArgs& a, int e, int p0, int cnt
   if (a.K128 % U) group(full * U, true);
   __builtin_amdgcn_s_waitcnt(0);
 
-  if constexpr (GLU) {
-    // h = bf16(silu(g) u), then quantised as the down GEMM's input with the
-    // activation quantiser's arithmetic (quantize_act_kernel), so h is never
-    // written in bf16. The MFMAs took the weight tile as operand A: slot i
-    // of lane l is weight row 8 (i / 4) + 4 (l / 32) + i % 4 of packed tile
-    // bt (rows 0..15 gates of intermediate columns 16 bt .. 16 bt + 15, rows
-    // 16..31 their ups) for route mt * 32 + l % 32; slots 0..3 pair with
-    // 8..11 and 4..7 with 12..15. The wave's two tiles (bt even) cover the 32
-    // columns of one MX block: lane l holds columns 4 (l / 32) + 0..3 and
-    // 8 + 4 (l / 32) + 0..3 of each tile, lane l ^ 32 the others, so the
-    // block's maximum takes one exchange.
-    constexpr int emax = FP8 ? 8 : 2;
-    const int blk = bt[0] >> 1;  // the wave's MX block of h columns
-    const bool live = bt[0] < a.N32 && 32 * blk < a.N;  // I is a multiple of 32
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int row = mt * 32 + r32;
-      float f[16];  // local column 16 t + 8 h + 4 hh + k of the block is f[8 t + 4 h + k]
-#pragma unroll
-      for (int t = 0; t < kPkNB; ++t)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float g = acc[mt][t][4 * h + k], u = acc[mt][t][8 + 4 * h + k];
-            f[8 * t + 4 * h + k] = bf16_bits_to_f32(f32_to_bf16_bits(silu(g) * u));
-          }
-      float amax = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-      const int X = amax > 0.f ? min(max(ilog2f(amax) - emax, -127), 127) : 0;
-      const int64_t r = (int64_t)(p0 + row);
-      const bool ok = live && row < cnt;
-      if constexpr (FP8) {
-        // byte c of the block's 32 is column c: this lane's four runs of four
-        // at bytes 16 t + 8 h + 4 hh; lane hh = 0 gathers its partner's and
-        // writes the 32 bytes
-        uint32_t w[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          w[q] = 0;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) w[q] |= e4m3_code(ldexpf(f[4 * q + k], -X)) << (8 * k);
-        }
-        uint32_t o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = __shfl_xor(w[q], 32, kWave);
-        if (hh == 0 && ok) {
-          u32x4_t* d = reinterpret_cast<u32x4_t*>(a.hq_out + r * a.hq_stride + 32 * blk);
-          d[0] = u32x4_t{w[0], o[0], w[1], o[1]};
-          d[1] = u32x4_t{w[2], o[2], w[3], o[3]};
-        }
-      } else {
-        // element c in nibble c % 2 of byte c / 2: this lane's four runs of
-        // four values are two bytes each, at bytes 8 t + 4 h + 2 hh
-        uint32_t w[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          uint32_t lo = 0, hi = 0;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            lo |= e2m1_code(ldexpf(f[8 * q + k], -X)) << (4 * k);
-            hi |= e2m1_code(ldexpf(f[8 * q + 4 + k], -X)) << (4 * k);
-          }
-          w[q] = lo | (hi << 16);  // runs (t = q, h = 0) and (t = q, h = 1)
-        }
-        uint32_t o[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) o[q] = __shfl_xor(w[q], 32, kWave);
-        if (hh == 0 && ok)
-          *reinterpret_cast<u32x4_t*>(a.hq_out + r * a.hq_stride + 16 * blk) =
-              u32x4_t{(w[0] & 0xFFFFu) | (o[0] << 16), (w[0] >> 16) | (o[0] & 0xFFFF0000u),
-                      (w[1] & 0xFFFFu) | (o[1] << 16), (w[1] >> 16) | (o[1] & 0xFFFF0000u)};
-      }
-      if (hh == 1 && ok) a.hqs_out[r * (a.N / 32) + blk] = (uint8_t)(X + 127);
-    }
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int t = 0; t < kPkNB; ++t) {
-        if (bt[t] >= a.N32) continue;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = mt * 32 + 8 * (i / 4) + 4 * hh + (i & 3);
-          const int col = bt[t] * 32 + r32;
-          if (row < cnt && col < a.N)
-            a.y_out[(int64_t)(p0 + row) * a.out_stride + col] = acc[mt][t][i];
-        }
-      }
-  }
+  pkq_store<GLU, FP8, MT>(a, acc, bt, p0, cnt);
 }
 
 template <bool GLU, bool FP8>
@@ -931,6 +941,202 @@ __global__ __launch_bounds__(kPkThreads, 8 / kPkWaves) void gemm_packed_q_kernel
 #undef LMOE_PKQ
 }
 
+// ---------------------------------------------------------------------------
+// The MXFP4-activation GEMM when K is a multiple of 256 and at most 4096
+// (the K3 layer: 3584 and 2048). A row's codes for one 128-K chunk are 64
+// bytes, half a cache line, and its exponents for the chunk one 4-byte word:
+// copied chunk by chunk from gathered rows, each row's line is requested
+// twice and each exponent word costs a line of its own. Here the tile's
+// exponents (96 rows x K / 32 bytes) are copied into an LDS table once, at
+// the start, and the codes of two chunks travel together as whole 128-byte
+// lines into one of two double slots, laid out and swizzled like the FP8
+// rows. Otherwise the tiling, the weight ring (three chunks ahead) and the
+// epilogue are those of gemm_packed_q_kernel.
+// ---------------------------------------------------------------------------
+constexpr int kA4MaxK = 4096;
+constexpr int kA4TabW = kA4MaxK / 128 + 1;  // words a row (one of padding, so rows fall on odd strides)
+constexpr int kA4TabLoads = (kPkRows * kA4TabW + 4 * 64 - 1) / (4 * 64);  // per wave, at most
+using A4Tab = uint32_t[kA4TabLoads * 4 * 64];
+
+template <bool GLU, int MT>
+__device__ __forceinline__ void pka4_body(const PkArgs& a, int e, int p0, int cnt, int nt,
+                                          QChunk<true>& d0, QChunk<true>& d1, A4Tab& tab,
+                                          const uint32_t* s_row) {
+  using C = QCfg<true>;  // 128-byte rows: the codes of a chunk pair
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int r32 = lane & 31, hh = lane >> 5;
+  int bt[kPkNB];
+  const uint8_t* qb[kPkNB];
+  const uint8_t* sb[kPkNB];
+#pragma unroll
+  for (int t = 0; t < kPkNB; ++t) {
+    bt[t] = (nt * kPkWaves + wave) * kPkNB + t;
+    const int btc = min(bt[t], a.N32 - 1);
+    qb[t] = a.q + e * a.q_estride + (int64_t)btc * a.K128 * 2048 + lane * 16;
+    sb[t] = a.s + e * a.s_estride + (int64_t)btc * a.K512 * 512 + lane * 8;
+  }
+  f32x16_t acc[MT][kPkNB];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int t = 0; t < kPkNB; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][t][i] = 0.f;
+
+  const int kw = a.K128;    // exponent words of a row (one per chunk)
+  const int tw = kw + 1;    // table stride in words (K128 is even: odd)
+  const int kb = a.K / 32;  // exponent bytes of an activation row
+  __syncthreads();          // s_row
+  // the exponent table: word q of the table is word q % tw of row q / tw
+  // (the padding word and positions past the MT * 32 rows load a harmless
+  // word)
+  {
+    const int loads = (MT * 32 * tw + 4 * 64 - 1) / (4 * 64);
+    for (int j = 0; j < loads; ++j) {
+      const int q = (wave * loads + j) * 64 + lane;
+      const int row = q / tw, d = q - row * tw;
+      const bool live = row < MT * 32 && d < kw;
+      const uint8_t* src = a.as + (size_t)s_row[live ? row : 0] * kb + (live ? d : 0) * 4;
+      __builtin_amdgcn_global_load_lds(
+          src, (__attribute__((address_space(3))) void*)(&tab[(wave * loads + j) * 64]), 4, 0,
+          0);
+    }
+  }
+  int trow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) trow[mt] = (mt * 32 + r32) * tw;
+  // the MT * 32 rows are shared by the waves: MT copies of 8 rows of 128
+  // bytes each (every wave issues the same number, so the waits below count
+  // the same loads in every wave); byte offsets in chunk pair 0
+  constexpr int kCopies = MT;
+  static_assert(kCopies * C::kRowsPerCopy * kPkWaves == MT * 32, "rows shared evenly");
+  uint32_t qoff[kCopies];
+#pragma unroll
+  for (int i = 0; i < kCopies; ++i) {
+    const int row = (wave * kCopies + i) * C::kRowsPerCopy + lane / 8;
+    qoff[i] = s_row[row] * (uint32_t)a.aq_stride + C::seg(row, lane % 8) * 16;
+  }
+  // the codes of chunks 2 cp and 2 cp + 1 into a double slot
+  auto copy_pair = [&](int cp, QChunk<true>& dst) {
+    const int cc = min(cp, a.K128 / 2 - 1);
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) {
+      const int row0 = (wave * kCopies + i) * C::kRowsPerCopy;
+      __builtin_amdgcn_global_load_lds(
+          a.aq + (size_t)cc * C::kRowB + qoff[i],
+          (__attribute__((address_space(3))) void*)(&dst[row0 * C::kRowB]), 16, 0, 0);
+    }
+  };
+  struct Bq {
+    u32x4_t q[kPkNB][2];
+    uint32_t ex[kPkNB];
+  };
+  auto load_b = [&](int c, Bq& b) {
+    const int cc = min(c, a.K128 - 1);
+#pragma unroll
+    for (int t = 0; t < kPkNB; ++t)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b.q[t][j] = load_w<MT>(qb[t] + (int64_t)cc * 2048 + j * 1024);
+#pragma unroll
+    for (int t = 0; t < kPkNB; ++t)
+      b.ex[t] =
+          *reinterpret_cast<const uint32_t*>(sb[t] + (cc / 4) * 512 + 4 * ((cc >> 1) & 1));
+  };
+  // chunk c (half `half` of its double slot)
+  auto compute = [&](int c, int half, const QChunk<true>& sq, const Bq& b) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      i32x8_t av[MT];
+      int sa[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = mt * 32 + r32;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
+            sq + row * C::kRowB + 16 * C::seg(row, 4 * half + 2 * hh + s));
+        av[mt] = i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        sa[mt] = (int)((tab[trow[mt] + c] >> (8 * (2 * hh + s))) & 0xFFu);
+      }
+#pragma unroll
+      for (int t = 0; t < kPkNB; ++t) {
+        const u32x4_t w = b.q[t][s];
+        const i32x8_t bv = i32x8_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+        const int sbv = (int)((b.ex[t] >> (8 * (2 * (c & 1) + s))) & 0xFFu);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt][t] = GLU ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                 bv, av[mt], acc[mt][t], 4, 4, 0, sbv, 0, sa[mt])
+                           : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                 av[mt], bv, acc[mt][t], 4, 4, 0, sa[mt], 0, sbv);
+      }
+    }
+  };
+
+  // Weights in a ring of four register buffers, three chunks ahead; codes
+  // in double slots D0 (chunks 4g, 4g + 1) and D1 (4g + 2, 4g + 3), each
+  // pair copied at the even chunk two before it. Before chunk c, the loads
+  // issued after its last one are: c even (its codes, copied at c - 2,
+  // were last): the weights of c + 1 and c + 2; c odd (its weights, loaded
+  // at c - 3, were last): the weights of c + 1, the next pair, the weights
+  // of c + 2. The table went out before everything.
+  constexpr int kW = 3 * kPkNB;  // weight loads a chunk
+  constexpr int kEven = 2 * kW, kOdd = 2 * kW + kCopies;
+  static_assert(kOdd < 64, "vmcnt field");
+  constexpr int kWaitEven = 0x0F70 | (kEven & 15) | ((kEven >> 4) << 14);
+  constexpr int kWaitOdd = 0x0F70 | (kOdd & 15) | ((kOdd >> 4) << 14);
+  Bq bq[4];
+  copy_pair(0, d0);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) load_b(i, bq[i]);
+  auto group = [&](int cb, bool last) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = cb + r;
+      if (r & 1)
+        __builtin_amdgcn_s_waitcnt(kWaitOdd);
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitEven);
+      __builtin_amdgcn_s_barrier();
+      if (r == 0) copy_pair(c / 2 + 1, d1);
+      if (r == 2) copy_pair(c / 2 + 1, d0);
+      load_b(c + 3, bq[(r + 3) & 3]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (!last || c < a.K128) compute(c, r & 1, r < 2 ? d0 : d1, bq[r]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const int full = a.K128 / 4;
+  for (int g = 0; g < full; ++g) group(g * 4, false);
+  if (a.K128 % 4) group(full * 4, true);
+  __builtin_amdgcn_s_waitcnt(0);
+
+  pkq_store<GLU, false, MT>(a, acc, bt, p0, cnt);
+}
+
+template <bool GLU>
+__global__ __launch_bounds__(kPkThreads, 8 / kPkWaves) void gemm_packed_a4_kernel(PkArgs a) {
+  __shared__ __attribute__((aligned(16))) QChunk<true> d0, d1;
+  __shared__ __attribute__((aligned(16))) A4Tab tab;
+  __shared__ uint32_t s_row[128];  // activation row of each row slot
+  const int b = blockIdx.x;
+  const int s = b / 8;
+  const int nt = s % a.n_tiles_n;
+  const int tile = (s / a.n_tiles_n) * 8 + b % 8;
+  if (tile >= *a.ntiles) return;
+  const int e = __builtin_amdgcn_readfirstlane(a.tiles[3 * tile + 0]);
+  const int p0 = __builtin_amdgcn_readfirstlane(a.tiles[3 * tile + 1]);
+  const int cnt = __builtin_amdgcn_readfirstlane(a.tiles[3 * tile + 2]);
+  for (int r = threadIdx.x; r < 128; r += kPkThreads) {
+    const int p = p0 + min(r, cnt - 1);
+    s_row[r] = (uint32_t)(a.gather ? a.gather[p] / a.gather_div : p);
+  }
+  switch ((cnt + 31) / 32) {
+    case 1: pka4_body<GLU, 1>(a, e, p0, cnt, nt, d0, d1, tab, s_row); break;
+    case 2: pka4_body<GLU, 2>(a, e, p0, cnt, nt, d0, d1, tab, s_row); break;
+    default: pka4_body<GLU, 3>(a, e, p0, cnt, nt, d0, d1, tab, s_row); break;
+  }
+}
+
 hipError_t launch_routed_packed(const Plan& p, const uint16_t* x, const PackedWeights& w,
                                 const Workspace& ws, const int32_t* perm, hipStream_t s,
                                 const hipEvent_t* ev, int act) {
@@ -951,6 +1157,11 @@ hipError_t launch_routed_packed(const Plan& p, const uint16_t* x, const PackedWe
         hipLaunchKernelGGL((gemm_packed_kernel<false, true>), grid, dim3(kPkThreads), 0, s, a);
       else
         hipLaunchKernelGGL((gemm_packed_kernel<false, false>), grid, dim3(kPkThreads), 0, s, a);
+    } else if (!fp8 && a.K % 256 == 0 && a.K <= kA4MaxK) {
+      if (glu)
+        hipLaunchKernelGGL((gemm_packed_a4_kernel<true>), grid, dim3(kPkThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((gemm_packed_a4_kernel<false>), grid, dim3(kPkThreads), 0, s, a);
     } else if (glu && fp8)
       hipLaunchKernelGGL((gemm_packed_q_kernel<true, true>), grid, dim3(kPkThreads), 0, s, a);
     else if (glu)

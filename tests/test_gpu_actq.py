@@ -104,6 +104,10 @@ SMALL = [
     Workload("q_k3w", 62, Dims(T=1200, L=3584, E=48, k=4, I=2048, S=2, Is=2048)),
     Workload("q_noshared", 63, Dims(T=33, L=256, E=16, k=1, I=256, S=0, Is=0),
              scales=("uniform", 118, 132)),
+    # K a multiple of 256 (the MXFP4 pair-copy kernel) with 6 and 4 chunks:
+    # a ring group of four left half full, and groups of 1-3 row tiles
+    Workload("q_pairs", 65, Dims(T=400, L=768, E=12, k=3, I=512, S=1, Is=256),
+             scales=("uniform", 118, 132)),
 ]
 
 
