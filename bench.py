@@ -559,6 +559,13 @@ def stage_us(res, lm):
     return {k: round(v * 1e3, 1) for k, v in res["stage_ms"].items()}
 
 
+def traffic_workload(res) -> str:
+    """The workload name the PMC summary files a run under: the workload,
+    plus _a8 / _a4 for quantised activations (as `--extra` names them)."""
+    suffix = {a: suf for suf, (a, _) in ACT_SUFFIX.items()}.get(res.get("act", "bf16"), "")
+    return res["w"].name + suffix
+
+
 def roofline_for(res, bound: str, lm):
     """Roofline of the kernel with the longest average launch."""
     units = [u for u in kernel_units(res, lm) if (u[1] if bound == "hbm" else u[2]) > 0]
@@ -573,7 +580,7 @@ def roofline_for(res, bound: str, lm):
         achieved, peak, unit = flops / sec / 1e12, mfma_peak, "TFLOP/s"
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4),
-            "traffic": measured_traffic(kernel, res["w"].name),
+            "traffic": measured_traffic(kernel, traffic_workload(res)),
             "kernel": kernel, "kernel_us": round(sec * 1e6, 2),
             "algorithmic_bytes": round(nbytes), "algorithmic_flops": round(flops)}
 

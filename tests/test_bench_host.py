@@ -98,3 +98,13 @@ def test_kernel_sources_hash_only_their_files():
         bench.sources_sha("gemm_small_kernel<true, true, true>")
     assert bench.sources_sha() not in (bench.sources_sha("decode_kernel"),
                                        bench.sources_sha("gemm_large_kernel<true, true, true>"))
+
+
+def test_quantised_runs_look_up_their_own_counters():
+    """Counter summaries of quantised-activation runs are filed under the
+    workload name `--extra` gives them (prefill_a4, batched_decode_a8)."""
+    w = get_workload("prefill")
+    assert bench.traffic_workload({"w": w, "act": "e2m1"}) == "prefill_a4"
+    assert bench.traffic_workload({"w": w, "act": "e4m3"}) == "prefill_a8"
+    assert bench.traffic_workload({"w": w, "act": "bf16"}) == "prefill"
+    assert bench.traffic_workload({"w": w}) == "prefill"
