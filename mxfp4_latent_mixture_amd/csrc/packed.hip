@@ -744,8 +744,12 @@ __device__ __forceinline__ void pkq_store(const PkArgs& a, const f32x16_t (&acc)
         for (int i = 0; i < 16; ++i) {
           const int row = mt * 32 + 8 * (i / 4) + 4 * hh + (i & 3);
           const int col = bt[t] * 32 + r32;
+          // the partials are read once, by the combine: streamed past the
+          // caches (down with MXFP4 activations 824 -> 795 us at K3 prefill;
+          // the bf16 kernel measured no difference)
           if (row < cnt && col < a.N)
-            a.y_out[(int64_t)(p0 + row) * a.out_stride + col] = acc[mt][t][i];
+            __builtin_nontemporal_store(acc[mt][t][i],
+                                        &a.y_out[(int64_t)(p0 + row) * a.out_stride + col]);
         }
       }
   }
