@@ -564,7 +564,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int l = (int)(id % L4) * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   // routes in groups of 8: indices and weights first, then the partial rows,
-  // so the loads of a group are in flight together
+  // so the loads of a group are in flight together. Each partial is read
+  // once: non-temporal loads (K3 prefill 214-220 -> 188 us)
   for (int j0 = 0; j0 < k; j0 += 8) {
     int pos[8];
     float wj[8];
@@ -574,18 +575,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       pos[u] = j < k ? inv[t * k + j] : 0;
       wj[u] = j < k ? w[t * k + j] : 0.f;
     }
-    float4 v[8];
+    f32x4_t v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      v[u] = (j0 + u < k) ? *reinterpret_cast<const float4*>(y + (int64_t)pos[u] * L + l)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[u] = (j0 + u < k) ? __builtin_nontemporal_load(
+                                reinterpret_cast<const f32x4_t*>(y + (int64_t)pos[u] * L + l))
+                          : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (j0 + u < k) {
-        acc.x = fmaf(wj[u], v[u].x, acc.x);
-        acc.y = fmaf(wj[u], v[u].y, acc.y);
-        acc.z = fmaf(wj[u], v[u].z, acc.z);
-        acc.w = fmaf(wj[u], v[u].w, acc.w);
+        acc.x = fmaf(wj[u], v[u][0], acc.x);
+        acc.y = fmaf(wj[u], v[u][1], acc.y);
+        acc.z = fmaf(wj[u], v[u][2], acc.z);
+        acc.w = fmaf(wj[u], v[u][3], acc.w);
       }
     }
   }
