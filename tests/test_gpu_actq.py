@@ -108,6 +108,10 @@ SMALL = [
     # a ring group of four left half full, and groups of 1-3 row tiles
     Workload("q_pairs", 65, Dims(T=400, L=768, E=12, k=3, I=512, S=1, Is=256),
              scales=("uniform", 118, 132)),
+    # the same kernel with about 50 routes an expert: mostly two 32-row MFMA
+    # tiles a group (K = 512 and 256: 4 and 2 chunks)
+    Workload("q_pairs_mt2", 66, Dims(T=300, L=512, E=24, k=4, I=256, S=1, Is=256),
+             scales=("uniform", 118, 132)),
 ]
 
 
